@@ -1,0 +1,291 @@
+"""Plain CPU oracle for the Grouped Query Experts (GQE) attention layer.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg use this module. The GPU library never imports, calls or
+links it, and it shares no code with the GPU library: it is NumPy only, in
+float64 by default, written as the plain definition of each step.
+
+Sources (cited by page title and section):
+
+[GQE-review]  "论文综述：分组查询专家——在 GQA 自注意力上引入混合专家"
+              (paper.oopus.info), §二 核心方法与创新: the router equation
+              p_{i,g} = softmax(r_g(x_i)), the TopK equation, the three output
+              parts, the renormalised weight w_{i,g,m}, the weighted sum
+              ō_i and the output y_i = Concat(O_i, ō_i, s(x_i)) W_O.
+[GQE-summary] "Grouped Query Experts: Mixture-of-Experts on GQA Self-Attention"
+              (1kpapers.com), In brief: k experts per group, dense KV heads,
+              9 of 16 query-attention computations.
+[GQA-zone]    "AI 大模型之 GQA" (zone.ci): §4.1 KV-byte formula, §4.3 the
+              logical broadcast of KV heads, §技术深化 "分组不是把查询头合并"
+              (head i reads KV head floor(i/(H/G)); additive mask; absolute
+              query position), §工程实操 non-square causal mask.
+[MQA-GQA-171] "MQA、GQA、稀疏/滑动窗口注意力及混合范式" (171host.com): the
+              GQA and MQA numeric examples and the KV-cache byte examples.
+
+Readings where the pages are silent (each is listed in the design notes):
+  * r_g is affine: z = x W_r[g]^T (+ optional bias b_r[g]); no other form is
+    given.
+  * TopK keeps the k largest scores, ties going to the lower expert index;
+    the selected indices are stored in ascending order. Selecting on the
+    logits z gives the same set as selecting on p, because softmax is strictly
+    increasing in z within one group.
+  * The hard slots of one group are laid out in ascending expert index; the
+    groups are laid out g = 0..G-1.
+  * ō_i sums over every group g and every selected m (one d-vector).
+  * The shared head is query column block N and reads KV head 0, causally,
+    with scale 1/sqrt(d) and no routing weight.
+  * W_O has shape ((G*k + 2) * d, D_out), no bias.
+  * A key j is visible to a query at absolute position p iff j <= p.
+
+parity pinned: every function here is checked against values and identities
+fixed by the pages or by mathematics in the CPU tests (worked examples,
+closed forms, reductions to dense GQA/MHA/MQA, repeat-KV equivalence, brute
+force on tiny inputs).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "softmax", "topk_select", "route_logits", "route_select", "route",
+    "build_lists", "attend_rows", "prefill", "decode", "assemble", "out_proj",
+    "layer", "kv_bytes", "prefill_flops", "check_dims",
+]
+
+
+def check_dims(N: int, G: int, k: int) -> int:
+    """Reject unsupported head configurations; return M = N/G.
+
+    [GQA-zone] §4.4 and §工程实操 (扩展验证组合): the group count must divide the
+    query-head count, and unsupported H/G combinations are rejected explicitly,
+    never mapped silently.
+    """
+    if G <= 0 or N <= 0 or N % G != 0:
+        raise ValueError(f"unsupported head configuration N={N}, G={G}: G must divide N")
+    M = N // G
+    if not 1 <= k <= M:
+        raise ValueError(f"unsupported top-k k={k} for M={M} experts per group")
+    return M
+
+
+def softmax(z: np.ndarray, axis: int = -1) -> np.ndarray:
+    """softmax with the usual max subtraction (exact in real arithmetic)."""
+    z = np.asarray(z, dtype=np.float64)
+    zmax = np.max(z, axis=axis, keepdims=True)
+    e = np.exp(z - zmax)
+    return e / np.sum(e, axis=axis, keepdims=True)
+
+
+def topk_select(scores: np.ndarray, k: int) -> np.ndarray:
+    """TopK over the last axis: indices of the k largest scores, ascending.
+
+    [GQE-review] §二 路由器, the TopK equation K_g(x_i) = TopK_m(p_{i,g,m}, k).
+    Ties go to the lower index (a stable sort of the negated scores keeps
+    equal scores in index order).
+    """
+    order = np.argsort(-np.asarray(scores), axis=-1, kind="stable")
+    return np.sort(order[..., :k], axis=-1).astype(np.int64)
+
+
+def route_logits(x: np.ndarray, w_r: np.ndarray, G: int, M: int,
+                 b_r: np.ndarray | None = None) -> np.ndarray:
+    """Router scores z_{i,g} = r_g(x_i) in R^M for every token and group.
+
+    [GQE-review] §二 路由器: one router r_g per GQA group scores the group's M
+    query-head experts. x: [T, D]; w_r: [G*M, D]; b_r: [G*M] or None.
+    Returns z [T, G, M].
+    """
+    z = np.asarray(x, dtype=np.float64) @ np.asarray(w_r, dtype=np.float64).T
+    if b_r is not None:
+        z = z + np.asarray(b_r, dtype=np.float64)[None, :]
+    return z.reshape(z.shape[0], G, M)
+
+
+def route_select(z: np.ndarray, k: int):
+    """Softmax, TopK and renormalised weights from router scores z [T, G, M].
+
+    [GQE-review] §二: p = softmax(z); K_g = TopK(p, k);
+    w_{i,g,m} = p_{i,g,m} / sum_{m' in K_g} p_{i,g,m'}.
+    Returns (p [T,G,M], idx [T,G,k] ascending, w [T,G,k]).
+    """
+    p = softmax(z, axis=-1)
+    idx = topk_select(z, k)
+    p_sel = np.take_along_axis(p, idx, axis=-1)
+    w = p_sel / np.sum(p_sel, axis=-1, keepdims=True)
+    return p, idx, w
+
+
+def route(x, w_r, G: int, M: int, k: int, b_r=None):
+    """Full router: returns (z, p, idx, w) as route_logits + route_select."""
+    z = route_logits(x, w_r, G, M, b_r)
+    p, idx, w = route_select(z, k)
+    return z, p, idx, w
+
+
+def build_lists(idx: np.ndarray, M: int):
+    """Per-(sequence, group, expert) token lists.
+
+    idx: [B, S, G, k] selected experts. For each (b, g) the list of expert m
+    holds, in ascending order, the positions of the tokens whose selection in
+    group g contains m; the lists of m = 0..M-1 are stored one after another.
+    Returns (list_off [B, G, M+1], list_tok [B, G, k*S]) with list m occupying
+    list_tok[b, g, list_off[b,g,m]:list_off[b,g,m+1]].
+    """
+    B, S, G, k = idx.shape
+    off = np.zeros((B, G, M + 1), dtype=np.int64)
+    tok = np.zeros((B, G, k * S), dtype=np.int64)
+    for b in range(B):
+        for g in range(G):
+            pos = 0
+            for m in range(M):
+                rows = np.nonzero(np.any(idx[b, :, g, :] == m, axis=-1))[0]
+                off[b, g, m] = pos
+                tok[b, g, pos:pos + rows.size] = rows
+                pos += rows.size
+            off[b, g, M] = pos
+    return off, tok
+
+
+def attend_rows(q: np.ndarray, pos: np.ndarray, K: np.ndarray, V: np.ndarray,
+                row_chunk: int = 1024) -> np.ndarray:
+    """Causal scaled dot-product attention of query rows against one KV head.
+
+    o_r = sum_{j <= pos_r} softmax_j(q_r . k_j / sqrt(d)) v_j.
+    [GQA-zone] §技术深化: scores Q K^T / sqrt(d), additive mask (0 where
+    visible, -inf where not) decided by the query's absolute position, softmax,
+    then V. q: [n, d]; pos: [n] absolute positions; K, V: [S, d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    n, d = q.shape
+    out = np.zeros((n, V.shape[-1]), dtype=np.float64)
+    for r0 in range(0, n, row_chunk):
+        qr, pr = q[r0:r0 + row_chunk], pos[r0:r0 + row_chunk]
+        if qr.shape[0] == 0:
+            continue
+        L = int(pr.max()) + 1
+        s = (qr @ K[:L].T) / np.sqrt(d)
+        mask = np.where(np.arange(L)[None, :] <= pr[:, None], 0.0, -np.inf)
+        s = s + mask
+        s = s - np.max(s, axis=1, keepdims=True)
+        e = np.exp(s)
+        out[r0:r0 + qr.shape[0]] = (e / np.sum(e, axis=1, keepdims=True)) @ V[:L]
+    return out
+
+
+def prefill(Q, K, V, idx, M: int, positions=None):
+    """Sparse-query causal attention for a prefill of S tokens per sequence.
+
+    Q: [B, S, N+1, d] (head N is the shared head); K, V: [B, G, S, d];
+    idx: [B, S, G, k] selected experts. For token i, group g and slot j the
+    head is h = g*M + idx[b,i,g,j] and it attends KV head g
+    ([GQA-zone] §技术深化: query head i reads KV head floor(i/(H/G)));
+    only selected heads are computed ([GQE-review] §二, unselected heads are
+    skipped). The shared head attends KV head 0 for every token.
+    positions: token positions to compute (default: all S).
+    Returns (O_r [B, P, G, k, d], O_s [B, P, d]) for the P positions.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, S, H1, d = Q.shape
+    G = K.shape[1]
+    k = idx.shape[-1]
+    N = H1 - 1
+    check_dims(N, G, k)
+    pos = np.arange(S) if positions is None else np.asarray(positions, dtype=np.int64)
+    O_r = np.zeros((B, pos.size, G, k, d))
+    O_s = np.zeros((B, pos.size, d))
+    for b in range(B):
+        for g in range(G):
+            for j in range(k):
+                heads = g * M + idx[b, pos, g, j]
+                O_r[b, :, g, j] = attend_rows(Q[b, pos, heads, :], pos, K[b, g], V[b, g])
+        O_s[b] = attend_rows(Q[b, pos, N, :], pos, K[b, 0], V[b, 0])
+    return O_r, O_s
+
+
+def decode(q, K, V, kv_len, idx, M: int):
+    """Sparse-query attention of q_len new tokens per sequence against a cache.
+
+    q: [B, q_len, N+1, d]; K, V: [B, G, S_max, d]; kv_len: [B] valid cache
+    length including the new tokens; idx: [B, q_len, G, k].
+    New token t of sequence b sits at absolute position kv_len[b]-q_len+t and
+    sees keys j <= that position ([GQA-zone] §技术深化 and §工程实操: in decode
+    Sq is small and Sk is the full history, so the causal mask must use the
+    query's absolute position, not a top-left triangle).
+    Returns (O_r [B, q_len, G, k, d], O_s [B, q_len, d]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, L, H1, d = q.shape
+    G = K.shape[1]
+    k = idx.shape[-1]
+    N = H1 - 1
+    check_dims(N, G, k)
+    O_r = np.zeros((B, L, G, k, d))
+    O_s = np.zeros((B, L, d))
+    for b in range(B):
+        n = int(kv_len[b])
+        if n < L or n > K.shape[2]:
+            raise ValueError("kv_len must satisfy q_len <= kv_len <= S_max")
+        pos = n - L + np.arange(L)
+        for g in range(G):
+            for j in range(k):
+                heads = g * M + idx[b, :, g, j]
+                O_r[b, :, g, j] = attend_rows(q[b, np.arange(L), heads, :], pos,
+                                              K[b, g, :n], V[b, g, :n])
+        O_s[b] = attend_rows(q[b, :, N, :], pos, K[b, 0, :n], V[b, 0, :n])
+    return O_r, O_s
+
+
+def assemble(O_r, w, O_s) -> np.ndarray:
+    """Slot vector A_i = Concat(O_i, ō_i, s(x_i)) for every token.
+
+    [GQE-review] §二 输出怎么拼起来: hard-selected slot O_i (the selected heads'
+    outputs, concatenated), renormalised weighted-sum slot
+    ō_i = sum w_{i,g,m} o_{i,g,m} (summed over all groups), and the shared
+    head's output s(x_i).
+    O_r: [T, G, k, d]; w: [T, G, k]; O_s: [T, d]. Returns [T, (G*k+2)*d].
+    """
+    O_r = np.asarray(O_r, dtype=np.float64)
+    T, G, k, d = O_r.shape
+    hard = O_r.reshape(T, G * k * d)
+    obar = np.sum(np.asarray(w, dtype=np.float64)[..., None] * O_r, axis=(1, 2))
+    return np.concatenate([hard, obar, np.asarray(O_s, dtype=np.float64)], axis=1)
+
+
+def out_proj(O_r, w, O_s, W_O) -> np.ndarray:
+    """y_i = Concat(O_i, ō_i, s(x_i)) W_O  ([GQE-review] §二, the y equation)."""
+    return assemble(O_r, w, O_s) @ np.asarray(W_O, dtype=np.float64)
+
+
+def layer(x, w_r, Q, K, V, W_O, G: int, k: int, b_r=None):
+    """Whole prefill layer: route, attend, assemble, project. Returns a dict."""
+    B, S, H1, d = np.asarray(Q).shape
+    N = H1 - 1
+    M = check_dims(N, G, k)
+    z, p, idx, w = route(np.asarray(x).reshape(B * S, -1), w_r, G, M, k, b_r)
+    idx4 = idx.reshape(B, S, G, k)
+    O_r, O_s = prefill(Q, K, V, idx4, M)
+    T = B * S
+    y = out_proj(O_r.reshape(T, G, k, d), w, O_s.reshape(T, d), W_O)
+    return dict(z=z, p=p, idx=idx, w=w, O_r=O_r, O_s=O_s, y=y)
+
+
+def kv_bytes(B: int, L: int, G: int, d: int, S: int, b: int) -> int:
+    """KV-cache bytes 2*B*L*G*S*d*b ([GQA-zone] §4.1 and §缓存省下多少).
+
+    L is the layer count, b the bytes per element; K and V both count.
+    """
+    return 2 * B * L * G * S * d * b
+
+
+def prefill_flops(B: int, S: int, G: int, k: int, d: int) -> int:
+    """Matmul FLOP of the sparse causal prefill, counting visible pairs only.
+
+    Per (selected row, visible key): 2d for q.k and 2d for p.v. Each token has
+    G*k selected rows plus one shared row; token i sees i+1 keys.
+    """
+    return 4 * d * (G * k + 1) * B * S * (S + 1) // 2

@@ -1,0 +1,364 @@
+"""Pins that fix the CPU oracle without comparing it to itself.
+
+Each ``pin_*`` takes the oracle module and raises AssertionError when the
+oracle disagrees with a value printed on the pages, a closed form, a
+reduction to a textbook/library routine, or the scalar brute force. The
+mutation test runs every pin against deliberately broken copies of the
+oracle to show each plausible mistake is caught by at least one of them.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import bruteforce
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _close(a, b, tol=1e-12, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} != {b.shape}"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs error {err:.3e} > {tol:.1e}"
+
+
+def _one_token_layer(O, Q, K, V, G, k, z):
+    """Run the oracle's routing+attention+assembly for a single token.
+
+    Q: [H+1, d] (last row shared), K, V: [G, d]; z: router scores [G, M].
+    """
+    H1, d = Q.shape
+    M = (H1 - 1) // G
+    _, idx, w = O.route_select(np.asarray(z, dtype=np.float64)[None], k)
+    Q4 = np.asarray(Q, dtype=np.float64)[None, None]
+    K4 = np.asarray(K, dtype=np.float64)[None, :, None, :]
+    V4 = np.asarray(V, dtype=np.float64)[None, :, None, :]
+    O_r, O_s = O.prefill(Q4, K4, V4, idx.reshape(1, 1, G, k), M)
+    A = O.assemble(O_r.reshape(1, G, k, d), w, O_s.reshape(1, d))
+    return O_r.reshape(-1), A.reshape(-1)
+
+
+# --------------------------------------------------------------------------
+# Worked examples printed on the pages
+# --------------------------------------------------------------------------
+
+def pin_gqa_worked_example(O):
+    """GQA example, 4 heads / 2 groups: k = M reduces GQE's hard slot to the
+    dense GQA concatenation [1,0,1,0,0,1,0,1]."""
+    g = _golden("gqa_worked_example.json")
+    Q = np.vstack([np.array(g["Q"], float), [[0.3, -0.7]]])  # + shared head
+    hard, _ = _one_token_layer(O, Q, np.array(g["K"], float), np.array(g["V"], float),
+                               G=g["G"], k=g["h"] // g["G"], z=np.zeros((g["G"], g["h"] // g["G"])))
+    _close(hard, g["concat"], what="GQA worked example")
+
+
+def pin_mqa_worked_example(O):
+    """MQA example: 2 heads sharing one KV head -> [1,0,1,0]."""
+    g = _golden("mqa_worked_example.json")
+    Q = np.vstack([np.array(g["Q"], float), [[1.0, 0.0]]])
+    hard, _ = _one_token_layer(O, Q, np.array(g["K"], float), np.array(g["V"], float),
+                               G=1, k=2, z=np.zeros((1, 2)))
+    _close(hard, g["concat"], what="MQA worked example")
+    assert abs(1.0 / math.sqrt(g["d"]) - g["scaled_score"]) < 1e-4
+
+
+def pin_three_slot_assembly(O):
+    """Derived from the GQA example and the three-part output: with a zero
+    router (p = 1/2, 1/2), k=2 gives A = [1,0,1,0,0,1,0,1 | 1,1 | 1,0] and
+    k=1 (tie -> expert 0, w = 1) gives A = [1,0,0,1 | 1,1 | 1,0]. The shared
+    head reads KV head 0 whatever its query."""
+    g = _golden("gqa_worked_example.json")
+    Q = np.vstack([np.array(g["Q"], float), [[0.3, -0.7]]])
+    K, V = np.array(g["K"], float), np.array(g["V"], float)
+    _, A2 = _one_token_layer(O, Q, K, V, G=2, k=2, z=np.zeros((2, 2)))
+    _close(A2, [1, 0, 1, 0, 0, 1, 0, 1, 1, 1, 1, 0], what="k=2 slot vector")
+    _, A1 = _one_token_layer(O, Q, K, V, G=2, k=1, z=np.zeros((2, 2)))
+    _close(A1, [1, 0, 0, 1, 1, 1, 1, 0], what="k=1 slot vector")
+
+
+def pin_kv_bytes(O):
+    for c in _golden("kv_bytes.json")["cases"]:
+        got = O.kv_bytes(c["B"], c["L"], c["G"], c["d"], c["S"], c["b"])
+        assert got == c["bytes"], f"kv_bytes {c['label']}: {got} != {c['bytes']}"
+
+
+def pin_nonsquare_causal(O):
+    """Queries at positions 5 and 6 over keys 0..6 see 6 and 7 keys. With
+    K = 0 (uniform weights) and V_j = j + 10*g, the outputs are the means
+    2.5 and 3.0 (+10g); the top-left-triangle bug would give 0 and 0.5."""
+    c = _golden("nonsquare_causal.json")
+    H, G, L, n = c["H"], c["G"], 2, c["kv_len"]
+    M, d = H // G, 4
+    K = np.zeros((1, G, n, d))
+    V = np.zeros((1, G, n, d))
+    for gg in range(G):
+        V[0, gg, :, :] = (np.arange(n) + 10.0 * gg)[:, None]
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, L, H + 1, d))
+    idx = np.tile(np.arange(M), (1, L, G, 1))  # k = M: every head
+    O_r, O_s = O.decode(q, K, V, np.array([n]), idx, M)
+    vis = np.array(c["visible_keys"], float)
+    want = (vis - 1) / 2.0  # mean of 0..vis-1
+    for gg in range(G):
+        for j in range(M):
+            _close(O_r[0, :, gg, j, 0], want + 10.0 * gg, 1e-12, f"non-square causal g={gg}")
+    _close(O_s[0, :, 0], want, 1e-12, "non-square causal shared head")
+    # head -> KV mapping of the page
+    for h, kv in enumerate(c["head_to_kv"]):
+        assert h // M == kv
+
+
+# --------------------------------------------------------------------------
+# Closed forms
+# --------------------------------------------------------------------------
+
+def pin_router_closed_forms(O):
+    """z = x W_r^T (+b): one-hot tokens read out router columns; TopK ties go
+    to the lower index; w renormalises p over the selected set."""
+    rng = np.random.default_rng(5)
+    G, M, D = 3, 4, 6
+    w_r = rng.standard_normal((G * M, D))
+    b_r = rng.standard_normal(G * M)
+    x = np.eye(D)
+    z = O.route_logits(x, w_r, G, M, b_r)
+    for j in range(D):
+        _close(z[j].reshape(-1), w_r[:, j] + b_r, 1e-15, "router column read-out")
+    # p = [.1,.2,.3,.4] -> top-2 = {2,3}, w = [3/7, 4/7]
+    zz = np.log(np.array([[[1.0, 2.0, 3.0, 4.0]]]))
+    p, idx, w = O.route_select(zz, 2)
+    _close(p[0, 0], [0.1, 0.2, 0.3, 0.4], 1e-15, "softmax of log-probabilities")
+    assert idx[0, 0].tolist() == [2, 3]
+    _close(w[0, 0], [3 / 7, 4 / 7], 1e-15, "renormalised weights")
+    # ties: [1,1,0,1] top-2 -> {0,1}; [0,0,0,0] top-1 -> {0}; top-3 of [2,5,5,5] -> {1,2,3}
+    assert O.route_select(np.array([[[1.0, 1.0, 0.0, 1.0]]]), 2)[1][0, 0].tolist() == [0, 1]
+    assert O.route_select(np.zeros((1, 1, 4)), 1)[1][0, 0].tolist() == [0]
+    assert O.route_select(np.array([[[2.0, 5.0, 5.0, 5.0]]]), 3)[1][0, 0].tolist() == [1, 2, 3]
+    # the largest, not the smallest; ascending storage
+    assert O.route_select(np.array([[[9.0, -1.0, 4.0, 7.0]]]), 2)[1][0, 0].tolist() == [0, 3]
+    # k = 1: w is exactly 1
+    _, _, w1 = O.route_select(rng.standard_normal((50, 2, 4)), 1)
+    assert np.all(w1 == 1.0)
+
+
+def pin_single_key_attention(O):
+    """With one visible key the softmax weight is 1 and o = v_0 exactly, for
+    any query; with two keys and scores a, b the weights are the logistic
+    function of (a-b)/sqrt(d)."""
+    rng = np.random.default_rng(8)
+    d = 4
+    K = rng.standard_normal((3, d))
+    V = rng.standard_normal((3, d))
+    q = rng.standard_normal((1, d))
+    _close(O.attend_rows(q, np.array([0]), K, V), V[:1], 1e-15, "one key")
+    s = (q @ K[:2].T).ravel() / math.sqrt(d)
+    a = 1.0 / (1.0 + math.exp(s[1] - s[0]))
+    _close(O.attend_rows(q, np.array([1]), K, V)[0], a * V[0] + (1 - a) * V[1], 1e-14, "two keys")
+
+
+# --------------------------------------------------------------------------
+# Reductions to library routines
+# --------------------------------------------------------------------------
+
+def _sdpa(q, k, v):
+    """torch CPU scaled_dot_product_attention, causal, fp64. q,k,v: [H,S,d]."""
+    with torch.no_grad():
+        o = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+            is_causal=True)
+    return o[0].numpy()
+
+
+def _rand_qkv(rng, B, S, N, G, d):
+    Q = rng.standard_normal((B, S, N + 1, d))
+    K = rng.standard_normal((B, G, S, d))
+    V = rng.standard_normal((B, G, S, d)) + 10.0 * np.arange(G)[None, :, None, None]
+    return Q, K, V
+
+
+def pin_repeat_kv_equivalence(O):
+    """k = M (every expert selected) turns the hard slots into dense GQA.
+    Explicit head mapping must equal attention on np.repeat-expanded K/V
+    (the page's mapping-vs-repeat check, here with the causal mask), and
+    torch's causal SDPA on the repeated K/V."""
+    rng = np.random.default_rng(11)
+    for (B, S, N, G, d) in [(2, 9, 8, 2, 4), (1, 13, 6, 3, 8)]:
+        M = N // G
+        Q, K, V = _rand_qkv(rng, B, S, N, G, d)
+        idx = np.broadcast_to(np.arange(M), (B, S, G, M)).copy()
+        O_r, O_s = O.prefill(Q, K, V, idx, M)
+        for b in range(B):
+            Kr = np.repeat(K[b], M, axis=0)  # [N, S, d]
+            Vr = np.repeat(V[b], M, axis=0)
+            q = Q[b, :, :N, :].transpose(1, 0, 2)  # [N, S, d]
+            sc = q @ Kr.transpose(0, 2, 1) / np.sqrt(d)
+            sc = np.where(np.tril(np.ones((S, S), bool))[None], sc, -np.inf)
+            sc = np.exp(sc - sc.max(-1, keepdims=True))
+            ref = (sc / sc.sum(-1, keepdims=True)) @ Vr  # [N, S, d]
+            got = O_r[b].reshape(S, N, d).transpose(1, 0, 2)
+            _close(got, ref, 1e-12, "mapping vs repeat-KV")
+            _close(got, _sdpa(q, Kr, Vr), 1e-12, "mapping vs torch SDPA")
+            _close(O_s[b], _sdpa(Q[b, :, N][None], K[b, :1], V[b, :1])[0], 1e-12, "shared head vs SDPA")
+
+
+def pin_mha_mqa_reductions(O):
+    """G = H (M = 1, k = 1) is MHA: slot g is head g on its own KV head and
+    ō is the plain sum of all heads. G = 1 is MQA: every head reads KV 0."""
+    rng = np.random.default_rng(12)
+    B, S, d = 1, 7, 4
+    for N, G in [(4, 4), (4, 1)]:
+        M = N // G
+        k = M
+        Q, K, V = _rand_qkv(rng, B, S, N, G, d)
+        D = 5
+        x = rng.standard_normal((B * S, D))
+        w_r = rng.standard_normal((N, D))
+        W_O = rng.standard_normal(((G * k + 2) * d, 3))
+        out = O.layer(x, w_r, Q, K, V, W_O, G, k)
+        kvmap = np.arange(N) // M
+        heads = np.stack([_sdpa(Q[0, :, h][None], K[0, kvmap[h]][None], V[0, kvmap[h]][None])[0]
+                          for h in range(N)], axis=1)  # [S, N, d]
+        _close(out["O_r"][0].reshape(S, N, d), heads, 1e-12, f"N={N} G={G} head outputs")
+        if M == 1:
+            A = O.assemble(out["O_r"].reshape(S, G, 1, d), out["w"], out["O_s"].reshape(S, d))
+            _close(A[:, G * d:G * d + d], heads.sum(1), 1e-12, "MHA: ō is the sum of heads")
+
+
+# --------------------------------------------------------------------------
+# Brute force and invariants
+# --------------------------------------------------------------------------
+
+def pin_bruteforce(O):
+    """Scalar loops on tiny inputs match the vectorised oracle to 1e-12."""
+    rng = np.random.default_rng(13)
+    for (S, D, N, G, k, d, Dout, bias) in [(6, 5, 4, 2, 1, 3, 4, False), (9, 7, 8, 2, 3, 4, 5, True),
+                                           (5, 4, 6, 3, 2, 2, 3, False), (7, 6, 8, 1, 5, 8, 2, True),
+                                           (4, 3, 4, 4, 1, 2, 2, False)]:
+        M = N // G
+        x = rng.standard_normal((S, D))
+        w_r = rng.standard_normal((G * M, D))
+        b_r = rng.standard_normal(G * M) if bias else None
+        if not bias and M > 1:  # plant exact router ties: expert 1 copies expert 0
+            for g in range(G):
+                w_r[g * M + 1] = w_r[g * M]
+        Q, K, V = _rand_qkv(rng, 1, S, N, G, d)
+        W_O = rng.standard_normal(((G * k + 2) * d, Dout))
+        out = O.layer(x, w_r, Q, K, V, W_O, G, k, b_r)
+        bf = bruteforce.layer(x.tolist(), w_r.tolist(), Q[0].tolist(), K[0].tolist(), V[0].tolist(),
+                              W_O.tolist(), G, k, None if b_r is None else b_r.tolist())
+        assert out["idx"].reshape(S, G, k).tolist() == bf["idx"], "brute-force selection"
+        _close(out["w"].reshape(S, G, k), bf["w"], 1e-12, "brute-force weights")
+        A = O.assemble(out["O_r"].reshape(S, G, k, d), out["w"], out["O_s"].reshape(S, d))
+        _close(A, bf["A"], 1e-12, "brute-force slot vectors")
+        _close(out["y"], bf["y"], 1e-11, "brute-force y")
+
+
+def pin_list_invariants(O):
+    """|K_g| = k, sum w = 1, each (b,g) list holds k*S entries, lists strictly
+    ascending, every token in exactly k lists per group."""
+    rng = np.random.default_rng(14)
+    B, S, G, M, k, D = 2, 37, 3, 4, 2, 8
+    x = rng.standard_normal((B * S, D))
+    w_r = rng.standard_normal((G * M, D))
+    z, p, idx, w = O.route(x, w_r, G, M, k)
+    assert idx.shape == (B * S, G, k)
+    assert np.all(np.diff(idx, axis=-1) > 0), "selected experts distinct and ascending"
+    _close(w.sum(-1), np.ones((B * S, G)), 1e-14, "sum of renormalised weights")
+    # the selection is the top-k of p
+    thr = np.sort(p, -1)[..., M - k][..., None]
+    assert np.all(np.take_along_axis(p, idx, -1) >= thr)
+    off, tok = O.build_lists(idx.reshape(B, S, G, k), M)
+    for b in range(B):
+        for g in range(G):
+            assert off[b, g, 0] == 0 and off[b, g, M] == k * S
+            seen = np.zeros(S, int)
+            for m in range(M):
+                lst = tok[b, g, off[b, g, m]:off[b, g, m + 1]]
+                assert np.all(np.diff(lst) > 0)
+                for t in lst:
+                    assert m in idx.reshape(B, S, G, k)[b, t, g]
+                seen[lst] += 1
+            assert np.all(seen == k)
+
+
+def pin_causality_and_compaction(O):
+    """Outputs of token i do not depend on tokens after i, nor on how the
+    other tokens were routed; decode at position p equals prefill row p."""
+    rng = np.random.default_rng(15)
+    B, S, N, G, d, k = 1, 12, 8, 2, 4, 2
+    M = N // G
+    Q, K, V = _rand_qkv(rng, B, S, N, G, d)
+    idx = np.sort(rng.permuted(np.tile(np.arange(M), (B, S, G, 1)), axis=-1)[..., :k], -1)
+    O_r, O_s = O.prefill(Q, K, V, idx, M)
+    i = 6
+    Q2, K2, V2 = Q.copy(), K.copy(), V.copy()
+    Q2[:, i + 1:] += 1.0
+    K2[:, :, i + 1:] -= 2.0
+    V2[:, :, i + 1:] *= 3.0
+    # reroute every other token (a fresh valid selection), keep token i's
+    idx2 = np.sort(rng.permuted(np.tile(np.arange(M), (B, S, G, 1)), axis=-1)[..., :k], -1)
+    idx2[:, i] = idx[:, i]
+    assert np.any(idx2 != idx)
+    O_r2, O_s2 = O.prefill(Q2, K2, V2, idx2, M)
+    _close(O_r2[:, i], O_r[:, i], 1e-13, "causality / compaction independence")
+    _close(O_s2[:, i], O_s[:, i], 1e-13, "shared head causality")
+    # decode of the token at position p against the first p+1 keys
+    for p in (0, 5, S - 1):
+        Od, Osd = O.decode(Q[:, p:p + 1], K, V, np.array([p + 1]), idx[:, p:p + 1], M)
+        _close(Od[:, 0], O_r[:, p], 1e-13, "decode == prefill row")
+        _close(Osd[:, 0], O_s[:, p], 1e-13, "decode shared == prefill row")
+    # q_len = 2 decode rows equal prefill rows p-1, p
+    Od, _ = O.decode(Q[:, 8:10], K, V, np.array([10]), idx[:, 8:10], M)
+    _close(Od, O_r[:, 8:10], 1e-13, "multi-token decode == prefill rows")
+
+
+def pin_boundary_matrix(O):
+    """q_len in {1,2}, kv_len in {7,17}, G in {1,2,H} with H = 8, distinct KV
+    heads: decode equals the brute-force attention of the visible keys; an
+    unsupported N/G is rejected."""
+    rng = np.random.default_rng(16)
+    H, d = 8, 4
+    for G in (1, 2, H):
+        M = H // G
+        for L in (1, 2):
+            for n in (7, 17):
+                q = rng.standard_normal((1, L, H + 1, d))
+                K = rng.standard_normal((1, G, 20, d))
+                V = rng.standard_normal((1, G, 20, d)) + 10.0 * np.arange(G)[None, :, None, None]
+                idx = np.broadcast_to(np.arange(M), (1, L, G, M)).copy()
+                O_r, O_s = O.decode(q, K, V, np.array([n]), idx, M)
+                for t in range(L):
+                    pos = n - L + t
+                    for h in range(H):
+                        g = h // M
+                        ref = bruteforce.attend(q[0, t, h].tolist(), K[0, g].tolist(),
+                                                V[0, g].tolist(), pos + 1)
+                        _close(O_r[0, t, g, h % M], ref, 1e-12, f"boundary G={G} L={L} n={n}")
+                    ref = bruteforce.attend(q[0, t, H].tolist(), K[0, 0].tolist(), V[0, 0].tolist(), pos + 1)
+                    _close(O_s[0, t], ref, 1e-12, "boundary shared")
+    for bad in [(8, 3, 1), (8, 0, 1), (8, 2, 0), (8, 2, 5)]:
+        try:
+            O.check_dims(*bad)
+        except ValueError:
+            continue
+        raise AssertionError(f"unsupported configuration {bad} was not rejected")
+
+
+def pin_flop_count(O):
+    """Visible (row, key) pairs of the causal prefill by direct count."""
+    for (B, S, G, k, d) in [(1, 5, 2, 1, 4), (3, 11, 4, 2, 8)]:
+        pairs = B * (G * k + 1) * sum(i + 1 for i in range(S))
+        assert O.prefill_flops(B, S, G, k, d) == 4 * d * pairs
+
+
+ALL_PINS = [v for kname, v in sorted(globals().items()) if kname.startswith("pin_")]

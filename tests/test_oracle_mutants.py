@@ -1,0 +1,98 @@
+"""Plant plausible mistakes in copies of the oracle; the pins must catch each.
+
+Each mutant is a text substitution in the oracle's source, executed as a
+fresh module on the CPU. A mutant that passes every pin would mean the pins
+leave that part of the oracle unfixed.
+"""
+import inspect
+import types
+
+import numpy as np
+import pytest
+
+import oracle.gqe_oracle as gqe_oracle
+import pins
+
+SRC = inspect.getsource(gqe_oracle)
+
+MUTANTS = {
+    "topk_ties_to_higher_index": (
+        'order = np.argsort(-np.asarray(scores), axis=-1, kind="stable")',
+        'order = (np.asarray(scores).shape[-1] - 1 - np.argsort(-np.asarray(scores)[..., ::-1], axis=-1, kind="stable"))'),
+    "topk_smallest": (
+        'order = np.argsort(-np.asarray(scores), axis=-1, kind="stable")',
+        'order = np.argsort(np.asarray(scores), axis=-1, kind="stable")'),
+    "topk_unsorted_slots": (
+        'return np.sort(order[..., :k], axis=-1).astype(np.int64)',
+        'return order[..., :k].astype(np.int64)'),
+    "weights_not_renormalised": (
+        "w = p_sel / np.sum(p_sel, axis=-1, keepdims=True)", "w = p_sel"),
+    "weights_from_logits": (
+        "p_sel = np.take_along_axis(p, idx, axis=-1)", "p_sel = np.take_along_axis(z, idx, axis=-1)"),
+    "router_groups_transposed": (
+        "return z.reshape(z.shape[0], G, M)", "return z.reshape(z.shape[0], M, G).transpose(0, 2, 1)"),
+    "router_bias_dropped": (
+        "z = z + np.asarray(b_r, dtype=np.float64)[None, :]", "z = z"),
+    "scale_one_over_d": (
+        "s = (qr @ K[:L].T) / np.sqrt(d)", "s = (qr @ K[:L].T) / d"),
+    "mask_excludes_diagonal": (
+        "np.arange(L)[None, :] <= pr[:, None]", "np.arange(L)[None, :] < pr[:, None] + (pr[:, None] == 0)"),
+    "mask_one_too_many": (
+        "L = int(pr.max()) + 1", "L = min(int(pr.max()) + 2, K.shape[0])\n        pr = pr + 1"),
+    "head_mapping_transposed": (
+        "heads = g * M + idx[b, pos, g, j]", "heads = idx[b, pos, g, j] * G + g"),
+    "shared_head_on_last_group": (
+        "O_s[b] = attend_rows(Q[b, pos, N, :], pos, K[b, 0], V[b, 0])",
+        "O_s[b] = attend_rows(Q[b, pos, N, :], pos, K[b, G - 1], V[b, G - 1])"),
+    "shared_head_uses_head0_query": (
+        "O_s[b] = attend_rows(Q[b, pos, N, :], pos, K[b, 0], V[b, 0])",
+        "O_s[b] = attend_rows(Q[b, pos, 0, :], pos, K[b, 0], V[b, 0])"),
+    "decode_top_left_mask": (
+        "pos = n - L + np.arange(L)", "pos = np.arange(L)"),
+    "decode_shared_head_on_last_group": (
+        "O_s[b] = attend_rows(q[b, :, N, :], pos, K[b, 0, :n], V[b, 0, :n])",
+        "O_s[b] = attend_rows(q[b, :, N, :], pos, K[b, G - 1, :n], V[b, G - 1, :n])"),
+    "obar_mean_over_groups": (
+        "obar = np.sum(np.asarray(w, dtype=np.float64)[..., None] * O_r, axis=(1, 2))",
+        "obar = np.sum(np.asarray(w, dtype=np.float64)[..., None] * O_r, axis=(1, 2)) / G"),
+    "obar_group0_only": (
+        "obar = np.sum(np.asarray(w, dtype=np.float64)[..., None] * O_r, axis=(1, 2))",
+        "obar = np.sum(np.asarray(w, dtype=np.float64)[:, 0, :, None] * O_r[:, 0], axis=1)"),
+    "obar_unweighted": (
+        "obar = np.sum(np.asarray(w, dtype=np.float64)[..., None] * O_r, axis=(1, 2))",
+        "obar = np.sum(O_r, axis=(1, 2))"),
+    "hard_slots_slot_major": (
+        "hard = O_r.reshape(T, G * k * d)", "hard = O_r.transpose(0, 2, 1, 3).reshape(T, G * k * d)"),
+    "slot_parts_swapped": (
+        "return np.concatenate([hard, obar, np.asarray(O_s, dtype=np.float64)], axis=1)",
+        "return np.concatenate([hard, np.asarray(O_s, dtype=np.float64), obar], axis=1)"),
+    "kv_bytes_without_factor_2": (
+        "return 2 * B * L * G * S * d * b", "return B * L * G * S * d * b"),
+    "lists_descending": (
+        "tok[b, g, pos:pos + rows.size] = rows", "tok[b, g, pos:pos + rows.size] = rows[::-1]"),
+    "reject_nothing": (
+        "if G <= 0 or N <= 0 or N % G != 0:", "if G <= 0 or N <= 0:"),
+    "flops_strict_triangle": (
+        "return 4 * d * (G * k + 1) * B * S * (S + 1) // 2", "return 4 * d * (G * k + 1) * B * S * (S - 1) // 2"),
+}
+
+
+def _mutant_module(name):
+    old, new = MUTANTS[name]
+    assert SRC.count(old) == 1, f"mutant {name}: anchor must occur exactly once"
+    mod = types.ModuleType(f"gqe_oracle_mutant_{name}")
+    exec(compile(SRC.replace(old, new), mod.__name__, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _mutant_module(name)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mod)
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin catches the planted mistake '{name}'"
