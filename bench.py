@@ -1,0 +1,306 @@
+"""Benchmark of the GQE layer's hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+One step runs both halves of the hot path on seeded synthetic inputs that
+are resident in HBM before timing starts:
+  * prefill (long context): gqe_route (+ token lists) -> gqe_attn_prefill ->
+    gqe_out_proj on B=1, S=131072, D=1024, N=16, G=8, k=1, d=64, bf16;
+  * decode (long KV): gqe_route -> gqe_attn_decode -> gqe_out_proj for 16
+    sequences x 1 new token against 65536 cached keys each (G=8, d=128, k=2).
+All launches go to torch's current stream; HIP events on that stream bracket
+every call, so per-call durations are measured live.
+
+`value` is the prefill path's algorithmic throughput (router + attention +
+output-projection FLOP / its measured time). `decode` reports the decode
+path's KV-cache bytes per second. `roofline` is for the dominant kernel,
+the prefill attention: attention FLOP per launch / its average launch
+duration against the bf16 dense MFMA peak. `cpu_baseline` times the CPU
+oracle on a bounded sample of the same prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sparse_query_gqa_amd as gqe  # noqa: E402
+import synth  # noqa: E402
+
+PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 MFMA, published
+PEAK_HBM_BPS = 8.0e12      # MI355X HBM3E, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def prefill_path_flops(cfg) -> dict:
+    """Algorithmic FLOP of one prefill-path call (matmul FLOP only)."""
+    T, D, G, M, k, d = cfg.T, cfg.D, cfg.G, cfg.M, cfg.k, cfg.d
+    attn = 4 * d * (G * k + 1) * cfg.B * cfg.S * (cfg.S + 1) // 2
+    router = 2 * T * D * G * M
+    proj = 2 * T * (G * k + 2) * d * D + 2 * T * G * k * d  # W_O GEMM + weighted sum
+    return dict(attention=attn, router=router, out_proj=proj, total=attn + router + proj)
+
+
+def decode_kv_bytes(cfg) -> int:
+    """KV-cache bytes one decode call must read: 2*B*G*kv_len*d*b (one layer)."""
+    return 2 * cfg.B * cfg.G * cfg.kv_len * cfg.d * 2
+
+
+def source_sha(name: str) -> str:
+    with open(os.path.join(ROOT, "sparse_query_gqa_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_file: str, summary: str):
+    """HBM bytes per launch from a committed counter summary, or None when
+    the kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, summary)
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch=(\d+)\s+source_sha=([0-9a-f]+)", txt)
+    if not m or m.group(2) != source_sha(kernel_file):
+        return None
+    return int(m.group(1))
+
+
+def cpu_info() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(cfg, inp, n_rows: int) -> dict:
+    """Time the CPU oracle on a bounded sample of the prefill workload:
+    routing of the sampled tokens, the attention of every selected head and
+    the shared head at those tokens (full causal history each), and their
+    slot assembly + W_O. Throughput = the sample's algorithmic FLOP / time."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    rng = np.random.default_rng(7)
+    pos = np.sort(rng.choice(cfg.S, size=n_rows, replace=False))
+    f64 = synth.to_f64
+    x = f64(inp["x"][pos])
+    w_r = f64(inp["w_r"])
+    q = f64(inp["q"][0:1])
+    kk = f64(inp["k"][0:1])
+    vv = f64(inp["v"][0:1])
+    w_o = f64(inp["w_o"])
+    t0 = time.perf_counter()
+    z, p, idx, w = oracle.route(x, w_r, cfg.G, cfg.M, cfg.k)
+    idx_full = np.zeros((1, cfg.S, cfg.G, cfg.k), np.int64)
+    idx_full[0, pos] = idx
+    o_r, o_s = oracle.prefill(q, kk, vv, idx_full, cfg.M, positions=pos)
+    y = oracle.out_proj(o_r[0], w, o_s[0], w_o)
+    dt = time.perf_counter() - t0
+    assert np.all(np.isfinite(y))
+    d, G, k, D, M = cfg.d, cfg.G, cfg.k, cfg.D, cfg.M
+    flop = (4 * d * (G * k + 1) * int(np.sum(pos + 1)) + 2 * n_rows * D * G * M
+            + 2 * n_rows * (G * k + 2) * d * D)
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_rows} random query positions of the {cfg.name} prefill (all {G * k + 1} "
+                      f"selected+shared rows each, full causal history), fp64 NumPy, {dt:.1f} s; "
+                      f"BLAS threads={threads}, elementwise ops single-threaded; CPU: {cpu_info()}",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_s128k")
+    ap.add_argument("--decode-workload", default="decode_kv64k")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=1536)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
+              f"multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    gqe.load_library()
+
+    cfg = synth.workload(args.workload)
+    dcfg = synth.workload(args.decode_workload)
+    print(f"[bench] generating inputs: {cfg.name}, {dcfg.name}", file=sys.stderr, flush=True)
+    inp = synth.make_prefill_inputs(cfg)
+    dinp = synth.make_decode_inputs(dcfg)
+    g = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
+    dg = {k: (v.to(dev) if v is not None else None) for k, v in dinp.items()}
+    dims = gqe.gqe_dims.from_config(cfg)
+    ddims = gqe.gqe_dims.from_config(dcfg)
+    rdims = gqe.gqe_dims.make(dcfg.B, dcfg.q_len, dcfg.D, dcfg.N, dcfg.G, dcfg.k, dcfg.d, dcfg.dtype)
+
+    # outputs and workspaces, allocated once
+    T, G, M, k, d = cfg.T, cfg.G, cfg.M, cfg.k, cfg.d
+    r_out = dict(logits=None,
+                 topk_idx=torch.empty((T, G, k), dtype=torch.int32, device=dev),
+                 topk_w=torch.empty((T, G, k), dtype=torch.float32, device=dev),
+                 list_off=torch.empty((cfg.B, G, M + 1), dtype=torch.int32, device=dev),
+                 list_tok=torch.empty((cfg.B, G, k * cfg.S), dtype=torch.int32, device=dev))
+    r_ws = torch.empty((max(gqe.gqe_route_workspace_bytes(dims), 16),), dtype=torch.uint8, device=dev)
+    o_r = torch.empty((cfg.B, cfg.S, G, k, d), dtype=torch.bfloat16, device=dev)
+    o_s = torch.empty((cfg.B, cfg.S, d), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((T, cfg.D), dtype=torch.bfloat16, device=dev)
+    dT = dcfg.T
+    d_idx = torch.empty((dT, dcfg.G, dcfg.k), dtype=torch.int32, device=dev)
+    d_w = torch.empty((dT, dcfg.G, dcfg.k), dtype=torch.float32, device=dev)
+    d_ws = gqe.decode_workspace(ddims, dcfg.q_len, dev)
+    d_or = torch.empty((dcfg.B, dcfg.q_len, dcfg.G, dcfg.k, dcfg.d), dtype=torch.bfloat16, device=dev)
+    d_os = torch.empty((dcfg.B, dcfg.q_len, dcfg.d), dtype=torch.bfloat16, device=dev)
+    d_y = torch.empty((dT, dcfg.D), dtype=torch.bfloat16, device=dev)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def step(rec):
+        e = [ev() for _ in range(8)]
+        e[0].record()
+        gqe.gqe_route(dims, g["x"], g["w_r"], g["b_r"], None, r_out["topk_idx"], r_out["topk_w"],
+                      r_out["list_off"], r_out["list_tok"], r_ws)
+        e[1].record()
+        gqe.gqe_attn_prefill(dims, g["q"], g["k"], g["v"], r_out["topk_idx"], o_r, o_s)
+        e[2].record()
+        gqe.gqe_out_proj(dims, T, o_r.view(T, G, k, d), r_out["topk_w"], o_s.view(T, d), g["w_o"], y)
+        e[3].record()
+        gqe.gqe_route(rdims, dg["x"], dg["w_r"], dg["b_r"], None, d_idx, d_w, None, None, None)
+        e[4].record()
+        gqe.gqe_attn_decode(ddims, dcfg.q_len, dg["q"], dg["k"], dg["v"], dg["kv_len"], d_idx,
+                            d_or, d_os, d_ws)
+        e[5].record()
+        gqe.gqe_out_proj(ddims, dT, d_or.view(dT, dcfg.G, dcfg.k, dcfg.d), d_w,
+                         d_os.view(dT, dcfg.d), dg["w_o"], d_y)
+        e[6].record()
+        rec.append(e)
+
+    if args.copy_calibration:
+        a = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    warm = []
+    for _ in range(args.warmup):
+        step(warm)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr,
+          flush=True)
+
+    recs = []
+    t_begin, t_end = ev(), ev()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_begin.record()
+    for _ in range(args.steps):
+        step(recs)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = t_begin.elapsed_time(t_end)
+
+    def span(i, j):
+        return np.array([r[i].elapsed_time(r[j]) for r in recs]) * 1e-3  # seconds
+
+    t_route, t_attn, t_proj = span(0, 1), span(1, 2), span(2, 3)
+    t_prefill = span(0, 3)
+    t_droute, t_dec, t_dproj = span(3, 4), span(4, 5), span(5, 6)
+    t_decode = span(3, 6)
+
+    fl = prefill_path_flops(cfg)
+    value = fl["total"] / t_prefill.mean() / 1e12
+    attn_tflops = fl["attention"] / t_attn.mean() / 1e12
+    kv = decode_kv_bytes(dcfg)
+    dec_gbps = kv / t_dec.mean() / 1e9
+
+    traffic = measured_traffic("prefill.hip", "prefill_long_s128k_pmc.txt")
+    dtraffic = measured_traffic("decode.hip", "decode_kv64k_pmc.txt")
+    result = {
+        "metric": "GQE prefill TFLOP/s & decode KV GB/s at 1 GPU, % of MI355X bf16/HBM peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights; no dataset, random weights)",
+        "config": {
+            "workload": f"{cfg.name} prefill layer + {dcfg.name} decode step",
+            "prefill": {"B": cfg.B, "S": cfg.S, "D": cfg.D, "N": cfg.N, "G": cfg.G, "M": cfg.M,
+                        "k": cfg.k, "head_dim": cfg.d, "shared_head": True},
+            "decode": {"B": dcfg.B, "q_len": dcfg.q_len, "kv_len": dcfg.kv_len, "D": dcfg.D, "N": dcfg.N,
+                       "G": dcfg.G, "M": dcfg.M, "k": dcfg.k, "head_dim": dcfg.d},
+        },
+        "roofline": {
+            "kernel": "prefill_bf16_kernel<64> (gqe_attn_prefill)",
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_FLOPS / 1e12,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops * 1e12 / PEAK_BF16_FLOPS, 4),
+            "traffic": traffic,
+        },
+        "decode": {
+            "value": round(dec_gbps, 1),
+            "unit": "GB/s",
+            "roofline": {
+                "kernel": "decode_split_kernel + decode_combine_kernel (gqe_attn_decode)",
+                "bound": "hbm",
+                "achieved": round(dec_gbps, 1),
+                "peak": PEAK_HBM_BPS / 1e9,
+                "unit": "GB/s",
+                "frac": round(dec_gbps * 1e9 / PEAK_HBM_BPS, 4),
+                "traffic": dtraffic,
+            },
+            "ms_per_call": round(t_dec.mean() * 1e3, 4),
+            "path_ms": round(t_decode.mean() * 1e3, 4),
+        },
+        "breakdown_ms": {
+            "prefill_route": round(t_route.mean() * 1e3, 4),
+            "prefill_attention": round(t_attn.mean() * 1e3, 4),
+            "prefill_out_proj": round(t_proj.mean() * 1e3, 4),
+            "decode_route": round(t_droute.mean() * 1e3, 4),
+            "decode_attention": round(t_dec.mean() * 1e3, 4),
+            "decode_out_proj": round(t_dproj.mean() * 1e3, 4),
+            "attention_min_ms": round(t_attn.min() * 1e3, 4),
+            "attention_max_ms": round(t_attn.max() * 1e3, 4),
+        },
+        "flop_per_step": fl,
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu:
+        print(f"[bench] timing the CPU oracle on {args.cpu_rows} sampled rows", file=sys.stderr, flush=True)
+        cb = cpu_baseline(cfg, inp, args.cpu_rows)
+        result["cpu_baseline"] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in cb.items()}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

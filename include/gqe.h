@@ -1,0 +1,157 @@
+/*
+ * gqe.h - C ABI of the Grouped Query Experts (GQE) attention layer on MI355X.
+ *
+ * The layer (GQE review, paper.oopus.info, section 二 核心方法与创新):
+ *   - N routed query heads split into G groups of M = N/G experts; group g
+ *     owns KV head g. For token i and group g a router scores the M experts,
+ *     p = softmax(r_g(x_i)), and keeps the top k of them (the TopK equation).
+ *   - Only selected heads attend; the KV heads stay dense and are never
+ *     repeated (GQA tutorial, zone.ci, sections 4.3/4.4 and 技术深化).
+ *   - One always-on shared query head (query column block N) attends KV
+ *     head 0.
+ *   - y_i = Concat(O_i, obar_i, s(x_i)) W_O, where O_i are the k*G selected
+ *     head outputs (group-major, ascending expert index within a group),
+ *     obar_i = sum over every group g and selected m of w_{i,g,m} o_{i,g,m}
+ *     with w the softmax probabilities renormalised over the selected set,
+ *     and s(x_i) the shared head's output (the w and obar equations).
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer except those named *_or_null is required. Device
+ *     pointers must be 16-byte aligned; tensors are dense and row-major in
+ *     the layouts given below. The caller owns every buffer (inputs, outputs,
+ *     workspaces); the library allocates, frees and synchronises nothing and
+ *     keeps no state between calls.
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *     All work is enqueued asynchronously on it; faults inside a kernel
+ *     surface at the caller's next synchronisation.
+ *   - Arguments are validated before anything is enqueued. A call that
+ *     returns an error has enqueued nothing and written nothing.
+ *   - Supported: head_dim d in {32, 64, 128}; G >= 1 dividing N; 1 <= k <= M;
+ *     M <= 32 and G*M <= 256; D a multiple of 8; dtype GQE_BF16 or GQE_F32.
+ *     Anything else returns GQE_ERR_UNSUPPORTED: an unsupported head layout
+ *     is rejected, never mapped silently (GQA tutorial, 扩展验证组合).
+ *   - B == 0 or S == 0 is an empty call: GQE_OK, nothing enqueued.
+ *   - Floating-point outputs have the input dtype, except logits and topk_w
+ *     which are always fp32. Arithmetic is fp32 (bf16 inputs: bf16 matrix
+ *     products with fp32 accumulation, fp32 softmax).
+ */
+#ifndef GQE_H
+#define GQE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GQE_OK = 0,
+  GQE_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent sizes */
+  GQE_ERR_UNSUPPORTED = -2, /* head layout, head_dim, top-k or dtype not supported */
+  GQE_ERR_ALIGNMENT = -3,   /* a device pointer is not 16-byte aligned */
+  GQE_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
+  GQE_ERR_HIP = -5          /* the HIP runtime refused a launch */
+} gqe_status;
+
+typedef enum { GQE_BF16 = 0, GQE_F32 = 1 } gqe_dtype;
+
+/* Layer shape. B sequences of S tokens, model width D, N routed query heads,
+ * G KV heads (= groups), top-k per group, head_dim d; M = N/G. The shared
+ * head is always present. For decode, S is the cache capacity S_max. */
+typedef struct {
+  int32_t B, S, D, N, G, k, d;
+  int32_t dtype; /* gqe_dtype */
+} gqe_dims;
+
+/* Human-readable name of a gqe_status value (static storage). */
+const char* gqe_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int gqe_version(void);
+
+/* Bytes of workspace gqe_route needs to build the token lists (0 when the
+ * lists are not requested). */
+size_t gqe_route_workspace_bytes(const gqe_dims* dims);
+
+/* Router, top-k and per-(group, expert) token lists for T = B*S tokens.
+ * GQE review, section 二 路由器: z_{i,g} = x_i W_r[g]^T (+ b_r[g]) in R^M,
+ * p = softmax(z), K_g = TopK(p, k) (taken on z: the same set); ties go to the
+ * lower expert index; w_{i,g,m} = p_m / sum_{m' in K_g} p_{m'}.
+ *   x              [B*S, D]      dtype
+ *   w_router       [G*M, D]      dtype   (row g*M+m scores expert m of group g)
+ *   b_router       [G*M] fp32 or NULL
+ *   logits_or_null [B*S, G, M]   fp32 out (z, bias included)
+ *   topk_idx       [B*S, G, k]   int32 out, expert indices in 0..M-1, ascending
+ *   topk_w         [B*S, G, k]   fp32 out, renormalised weights (sum 1; exactly 1 for k=1)
+ *   list_off_or_null [B, G, M+1] int32 out: list of expert m of group g in
+ *                  sequence b is list_tok[b,g, off[m] : off[m+1]]; off[0]=0, off[M]=k*S
+ *   list_tok_or_null [B, G, k*S] int32 out: token positions (0..S-1), each
+ *                  list strictly ascending
+ *   workspace      >= gqe_route_workspace_bytes(dims) device bytes when the
+ *                  lists are requested, else may be NULL.
+ * list_off and list_tok must be both NULL or both non-NULL. Selection is a
+ * pure function of the emitted fp32 logits: same logits, same indices, bit
+ * for bit. */
+int gqe_route(const gqe_dims* dims, const void* x, const void* w_router,
+              const float* b_router, float* logits_or_null, int32_t* topk_idx,
+              float* topk_w, int32_t* list_off_or_null, int32_t* list_tok_or_null,
+              void* workspace, size_t ws_bytes, void* stream);
+
+/* Sparse-query causal prefill attention.
+ * For token i (absolute position i in its sequence), group g and slot j the
+ * head h = g*M + topk_idx[i,g,j] attends KV head g over keys 0..i:
+ * o = sum_{t<=i} softmax_t(q_{i,h}.k_t / sqrt(d)) v_t (GQA tutorial,
+ * 技术深化: head h reads KV head floor(h/M); additive causal mask; scale
+ * 1/sqrt(d)). The shared head (column block N of q) attends KV head 0.
+ * Unselected heads are never computed (GQE review, section 二).
+ *   q        [B, S, N+1, d]  dtype
+ *   k, v     [B, G, S, d]    dtype  (dense, never repeated per query head)
+ *   topk_idx [B*S, G, k]     int32 (as written by gqe_route)
+ *   o_routed [B, S, G, k, d] dtype out
+ *   o_shared [B, S, d]       dtype out
+ * topk_idx entries outside 0..M-1 are undefined behaviour. */
+int gqe_attn_prefill(const gqe_dims* dims, const void* q, const void* k,
+                     const void* v, const int32_t* topk_idx, void* o_routed,
+                     void* o_shared, void* stream);
+
+/* Bytes of workspace gqe_attn_decode needs (split-sequence partials). */
+size_t gqe_decode_workspace_bytes(const gqe_dims* dims, int32_t q_len);
+
+/* Sparse-query attention of q_len new tokens per sequence against a KV
+ * cache of capacity S_max = dims->S. Token t of sequence b sits at absolute
+ * position kv_len[b] - q_len + t and sees keys 0..that position (GQA
+ * tutorial, 技术深化 and 工程实操: decode masks by the query's absolute
+ * position, never by a top-left triangle). Heads and groups as for prefill.
+ *   q        [B, q_len, N+1, d]   dtype
+ *   k_cache, v_cache [B, G, S_max, d] dtype
+ *   kv_len   [B] int32 device, valid cache length including the new tokens;
+ *            q_len <= kv_len[b] <= S_max is required (not checkable without a
+ *            device sync; a violating entry yields unspecified outputs for
+ *            that sequence)
+ *   topk_idx [B*q_len, G, k] int32
+ *   o_routed [B, q_len, G, k, d] dtype out; o_shared [B, q_len, d] dtype out
+ *   workspace >= gqe_decode_workspace_bytes(dims, q_len) device bytes. */
+int gqe_attn_decode(const gqe_dims* dims, int32_t q_len, const void* q,
+                    const void* k_cache, const void* v_cache,
+                    const int32_t* kv_len, const int32_t* topk_idx,
+                    void* o_routed, void* o_shared, void* workspace,
+                    size_t ws_bytes, void* stream);
+
+/* Slot assembly and output projection for T tokens (GQE review, section 二,
+ * the y equation): A_t = [o_routed[t] (G*k*d values, group-major, slots as
+ * stored), obar_t, o_shared[t]] with obar_t = sum_{g,j} topk_w[t,g,j] *
+ * o_routed[t,g,j,:]; y_t = A_t W_O.
+ *   o_routed [T, G, k, d] dtype; topk_w [T, G, k] fp32; o_shared [T, d] dtype
+ *   w_o      [(G*k+2)*d, D] dtype
+ *   y        [T, D] dtype out
+ * dims->B and dims->S are ignored; T >= 0. */
+int gqe_out_proj(const gqe_dims* dims, int64_t T, const void* o_routed,
+                 const float* topk_w, const void* o_shared, const void* w_o,
+                 void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQE_H */

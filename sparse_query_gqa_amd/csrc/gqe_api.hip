@@ -1,0 +1,183 @@
+// C ABI of the GQE layer: argument validation and launch geometry.
+//
+// Every check runs before anything is enqueued, so a rejected call writes
+// nothing. Unsupported head layouts are rejected rather than mapped
+// (GQA tutorial, zone.ci, 扩展验证组合). Nothing here allocates, frees or
+// synchronises; all work goes onto the caller's stream.
+#include <math.h>
+#include <stdlib.h>
+#include <stdio.h>
+
+#include "../../include/gqe.h"
+#include "gqe_internal.h"
+
+using namespace gqe;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool trace_on() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = getenv("GQE_TRACE");
+    on = (e && *e && *e != '0') ? 1 : 0;
+  }
+  return on == 1;
+}
+
+// Shape checks common to every entry point. Empty (B or S == 0) is valid.
+int check_dims(const gqe_dims* d, bool need_D = true) {
+  if (!d) return GQE_ERR_INVALID_ARG;
+  if (d->B < 0 || d->S < 0 || d->D <= 0 || d->N <= 0 || d->G <= 0 || d->k <= 0 || d->d <= 0)
+    return GQE_ERR_INVALID_ARG;
+  if (d->dtype != GQE_BF16 && d->dtype != GQE_F32) return GQE_ERR_UNSUPPORTED;
+  if (d->N % d->G != 0) return GQE_ERR_UNSUPPORTED;
+  const int M = d->N / d->G;
+  if (d->k > M) return GQE_ERR_UNSUPPORTED;
+  if (M > kMaxExperts || d->G * M > kMaxRouterCols) return GQE_ERR_UNSUPPORTED;
+  if (d->d != 32 && d->d != 64 && d->d != 128) return GQE_ERR_UNSUPPORTED;
+  if (need_D && d->D % 8 != 0) return GQE_ERR_UNSUPPORTED;
+  // every element offset must fit the 64-bit arithmetic used by the kernels
+  // and the int32 token positions
+  if ((int64_t)d->B * d->S > (int64_t)INT32_MAX) return GQE_ERR_UNSUPPORTED;
+  return GQE_OK;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return GQE_OK;
+  if (trace_on()) fprintf(stderr, "[gqe] HIP error: %s\n", hipGetErrorString(e));
+  return GQE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqe_status_string(int status) {
+  switch (status) {
+    case GQE_OK: return "GQE_OK";
+    case GQE_ERR_INVALID_ARG: return "GQE_ERR_INVALID_ARG: null pointer or inconsistent size";
+    case GQE_ERR_UNSUPPORTED: return "GQE_ERR_UNSUPPORTED: head layout, head_dim, top-k or dtype not supported";
+    case GQE_ERR_ALIGNMENT: return "GQE_ERR_ALIGNMENT: device pointer not 16-byte aligned";
+    case GQE_ERR_WORKSPACE: return "GQE_ERR_WORKSPACE: workspace missing or too small";
+    case GQE_ERR_HIP: return "GQE_ERR_HIP: the HIP runtime refused a launch";
+    default: return "unknown gqe status";
+  }
+}
+
+int gqe_version(void) { return 10000; }
+
+size_t gqe_route_workspace_bytes(const gqe_dims* d) {
+  if (check_dims(d) != GQE_OK) return 0;
+  const int64_t nchunk = (d->S + kListChunk - 1) / kListChunk;
+  return (size_t)d->B * d->G * (d->N / d->G) * nchunk * sizeof(int32_t);
+}
+
+int gqe_route(const gqe_dims* d, const void* x, const void* w_router, const float* b_router,
+              float* logits, int32_t* topk_idx, float* topk_w, int32_t* list_off,
+              int32_t* list_tok, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  if (!x || !w_router || !topk_idx || !topk_w) return GQE_ERR_INVALID_ARG;
+  if ((list_off == nullptr) != (list_tok == nullptr)) return GQE_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, w_router, b_router, logits, topk_idx, topk_w, list_off, list_tok};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GQE_ERR_ALIGNMENT;
+  const bool lists = list_off != nullptr;
+  if (lists) {
+    const size_t need = gqe_route_workspace_bytes(d);
+    if (need > 0 && (!workspace || ws_bytes < need)) return GQE_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return GQE_ERR_ALIGNMENT;
+  }
+  const int64_t T = (int64_t)d->B * d->S;
+  if (T == 0) return GQE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  RouteParams rp{x, w_router, b_router, logits, topk_idx, topk_w, T, d->D, d->G, d->N / d->G, d->k};
+  if (trace_on())
+    fprintf(stderr, "[gqe] route T=%lld D=%d G=%d M=%d k=%d lists=%d\n", (long long)T, d->D, d->G,
+            d->N / d->G, d->k, (int)lists);
+  st = hip_status(launch_route(rp, d->dtype == GQE_BF16, s));
+  if (st || !lists) return st;
+  ListParams lp{topk_idx, list_off, list_tok, (int32_t*)workspace, d->B, d->S, d->G, d->N / d->G,
+                d->k, (d->S + kListChunk - 1) / kListChunk};
+  return hip_status(launch_lists(lp, s));
+}
+
+int gqe_attn_prefill(const gqe_dims* d, const void* q, const void* k, const void* v,
+                     const int32_t* topk_idx, void* o_routed, void* o_shared, void* stream) {
+  int st = check_dims(d, false);
+  if (st) return st;
+  if (!q || !k || !v || !topk_idx || !o_routed || !o_shared) return GQE_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, topk_idx, o_routed, o_shared};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GQE_ERR_ALIGNMENT;
+  // rows per (sequence, group) and tile counts must stay in int32
+  if ((int64_t)d->S * d->k > (int64_t)INT32_MAX / 2) return GQE_ERR_UNSUPPORTED;
+  if (d->B == 0 || d->S == 0) return GQE_OK;
+  PrefillParams pp{q, k, v, topk_idx, o_routed, o_shared, d->B, d->S, d->N, d->G, d->N / d->G,
+                   d->k, (float)(1.0 / sqrt((double)d->d))};
+  if (trace_on())
+    fprintf(stderr, "[gqe] prefill B=%d S=%d N=%d G=%d k=%d d=%d dtype=%d\n", d->B, d->S, d->N,
+            d->G, d->k, d->d, d->dtype);
+  return hip_status(launch_prefill(pp, d->d, d->dtype == GQE_BF16, (hipStream_t)stream));
+}
+
+size_t gqe_decode_workspace_bytes(const gqe_dims* d, int32_t q_len) {
+  if (check_dims(d, false) != GQE_OK || q_len <= 0) return 0;
+  const DecodeSplit sp = decode_split(d->B, d->G, d->S, d->k, q_len);
+  const size_t recs = (size_t)d->B * d->G * sp.nsplit * sp.rows;
+  const size_t o_bytes = recs * d->d * sizeof(float);
+  return o_bytes + recs * 2 * sizeof(float);
+}
+
+int gqe_attn_decode(const gqe_dims* d, int32_t q_len, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* kv_len, const int32_t* topk_idx,
+                    void* o_routed, void* o_shared, void* workspace, size_t ws_bytes,
+                    void* stream) {
+  int st = check_dims(d, false);
+  if (st) return st;
+  if (q_len < 0) return GQE_ERR_INVALID_ARG;
+  if (!q || !k_cache || !v_cache || !kv_len || !topk_idx || !o_routed || !o_shared)
+    return GQE_ERR_INVALID_ARG;
+  if (q_len > d->S && d->B > 0) return GQE_ERR_INVALID_ARG;  // kv_len <= S_max cannot hold
+  if ((int64_t)(d->k + 1) * q_len > kMaxDecodeRows) return GQE_ERR_UNSUPPORTED;
+  const void* ptrs[] = {q, k_cache, v_cache, kv_len, topk_idx, o_routed, o_shared};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GQE_ERR_ALIGNMENT;
+  if (d->B == 0 || q_len == 0) return GQE_OK;
+  const size_t need = gqe_decode_workspace_bytes(d, q_len);
+  if (!workspace || ws_bytes < need) return GQE_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GQE_ERR_ALIGNMENT;
+  const DecodeSplit sp = decode_split(d->B, d->G, d->S, d->k, q_len);
+  const size_t recs = (size_t)d->B * d->G * sp.nsplit * sp.rows;
+  float* ws_o = (float*)workspace;
+  float* ws_ml = ws_o + recs * d->d;
+  DecodeParams dp{q, k_cache, v_cache, kv_len, topk_idx, o_routed, o_shared, ws_o, ws_ml,
+                  d->B, q_len, d->S, d->N, d->G, d->N / d->G, d->k, sp.rows, sp.nsplit, sp.chunk,
+                  (float)(1.0 / sqrt((double)d->d))};
+  if (trace_on())
+    fprintf(stderr, "[gqe] decode B=%d L=%d Smax=%d G=%d k=%d d=%d nsplit=%d chunk=%d\n", d->B,
+            q_len, d->S, d->G, d->k, d->d, sp.nsplit, sp.chunk);
+  return hip_status(launch_decode(dp, d->d, d->dtype == GQE_BF16, (hipStream_t)stream));
+}
+
+int gqe_out_proj(const gqe_dims* d, int64_t T, const void* o_routed, const float* topk_w,
+                 const void* o_shared, const void* w_o, void* y, void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  if (T < 0) return GQE_ERR_INVALID_ARG;
+  if (!o_routed || !topk_w || !o_shared || !w_o || !y) return GQE_ERR_INVALID_ARG;
+  const void* ptrs[] = {o_routed, topk_w, o_shared, w_o, y};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GQE_ERR_ALIGNMENT;
+  if ((T + 127) / 128 > (int64_t)UINT32_MAX) return GQE_ERR_UNSUPPORTED;
+  if (T == 0) return GQE_OK;
+  OutProjParams op{o_routed, topk_w, o_shared, w_o, y, T, d->G * d->k, d->d, d->D};
+  if (trace_on())
+    fprintf(stderr, "[gqe] out_proj T=%lld K=%d D=%d\n", (long long)T, (d->G * d->k + 2) * d->d,
+            d->D);
+  return hip_status(launch_out_proj(op, d->dtype == GQE_BF16, (hipStream_t)stream));
+}
+
+}  // extern "C"

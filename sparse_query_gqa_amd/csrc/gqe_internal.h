@@ -1,0 +1,109 @@
+// Internal declarations shared by the HIP kernels and the C ABI layer.
+// Nothing here is part of the public interface (include/gqe.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gqe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Router limits (checked by the ABI layer).
+constexpr int kMaxExperts = 32;      // M
+constexpr int kMaxRouterCols = 256;  // G*M
+// Decode: rows per (sequence, group) kept in registers.
+constexpr int kMaxDecodeRows = 16;   // (k+1)*q_len
+// Token chunk of the list builder (one wavefront).
+constexpr int kListChunk = 64;
+
+struct RouteParams {
+  const void* x;         // [T, D]
+  const void* w;         // [GM, D]
+  const float* bias;     // [GM] or null
+  float* logits;         // [T, G, M] or null
+  int32_t* topk_idx;     // [T, G, k]
+  float* topk_w;         // [T, G, k]
+  int64_t T;
+  int D, G, M, k;
+};
+
+struct ListParams {
+  const int32_t* topk_idx;  // [B*S, G, k]
+  int32_t* list_off;        // [B, G, M+1]
+  int32_t* list_tok;        // [B, G, k*S]
+  int32_t* counts;          // workspace [B, G, M, nchunk]
+  int B, S, G, M, k, nchunk;
+};
+
+struct PrefillParams {
+  const void* q;          // [B, S, N+1, d]
+  const void* k;          // [B, G, S, d]
+  const void* v;          // [B, G, S, d]
+  const int32_t* topk;    // [B*S, G, k]
+  void* o_r;              // [B, S, G, k, d]
+  void* o_s;              // [B, S, d]
+  int B, S, N, G, M, K;
+  float scale;            // 1/sqrt(d)
+};
+
+struct DecodeParams {
+  const void* q;          // [B, L, N+1, d]
+  const void* k;          // [B, G, Smax, d]
+  const void* v;
+  const int32_t* kv_len;  // [B]
+  const int32_t* topk;    // [B*L, G, k]
+  void* o_r;              // [B, L, G, k, d]
+  void* o_s;              // [B, L, d]
+  float* ws_o;            // [B, G, nsplit, R, d]
+  float* ws_ml;           // [B, G, nsplit, R, 2]
+  int B, L, Smax, N, G, M, K, R, nsplit, chunk;
+  float scale;
+};
+
+struct OutProjParams {
+  const void* o_r;        // [T, G*k*d]
+  const float* w;         // [T, G*k]
+  const void* o_s;        // [T, d]
+  const void* w_o;        // [Kd, Dout]
+  void* y;                // [T, Dout]
+  int64_t T;
+  int Gk, d, Dout;
+};
+
+// Decode split geometry shared by the workspace query and the launcher.
+struct DecodeSplit {
+  int rows;    // (k+1)*q_len
+  int chunk;   // keys per split
+  int nsplit;  // ceil(Smax / chunk)
+};
+DecodeSplit decode_split(int B, int G, int Smax, int k, int q_len);
+
+hipError_t launch_route(const RouteParams& p, bool bf16, hipStream_t s);
+hipError_t launch_lists(const ListParams& p, hipStream_t s);
+hipError_t launch_prefill(const PrefillParams& p, int d, bool bf16, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s);
+hipError_t launch_out_proj(const OutProjParams& p, bool bf16, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Small device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf2f(__bf16 h) { return (float)h; }
+__device__ __forceinline__ __bf16 f2bf(float f) { return (__bf16)f; }  // round to nearest even
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace gqe

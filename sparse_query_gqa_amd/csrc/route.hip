@@ -1,0 +1,234 @@
+// Router, top-k selection and per-(group, expert) token lists.
+//
+// GQE review (paper.oopus.info), section 二 路由器: per token i and group g,
+// z = r_g(x_i) in R^M, p = softmax(z), K_g = TopK(p, k), and the renormalised
+// weights w_m = p_m / sum_{m' in K_g} p_{m'}.
+//
+// Router scores are a skinny product z[T, G*M] = x[T, D] W_r^T. For bf16 it
+// runs on MFMA (16x16x32 bf16 -> fp32): one wavefront owns 16 tokens and all
+// G*M experts, streaming x once from HBM with 16-byte loads; W_r (at most
+// 256 x D bf16) stays hot in L2. The fp32 path is a plain VALU dot product.
+// The reduction order is fixed, so the emitted logits - and therefore the
+// selection, which is a pure function of them - are deterministic.
+#include "gqe_internal.h"
+
+namespace gqe {
+
+constexpr int kRouteTok = 16;  // tokens per wavefront / workgroup
+
+// Selection epilogue: z for kRouteTok tokens in LDS ([tok][G*M], bias
+// included). One thread per (token, group): TopK by repeated first-maximum
+// scans (strictly greater wins, so ties keep the lower index), indices
+// written ascending, weights exp(z_m - zmax) / sum over the selected set.
+__device__ void route_select_store(const float* zs, int ntok, int64_t tok0,
+                                   const RouteParams& p) {
+  const int GM = p.G * p.M;
+  for (int e = threadIdx.x; e < ntok * p.G; e += blockDim.x) {
+    const int t = e / p.G, g = e % p.G;
+    const float* z = zs + t * GM + g * p.M;
+    const int64_t tok = tok0 + t;
+    if (p.logits) {
+      for (int m = 0; m < p.M; ++m) p.logits[(tok * p.G + g) * p.M + m] = z[m];
+    }
+    uint32_t chosen = 0;
+    float zmax = -INFINITY;
+    for (int r = 0; r < p.k; ++r) {
+      int best = -1;
+      float bv = 0.f;
+      for (int m = 0; m < p.M; ++m) {
+        if ((chosen >> m) & 1u) continue;
+        if (best < 0 || z[m] > bv) { best = m; bv = z[m]; }
+      }
+      chosen |= 1u << best;
+      if (r == 0) zmax = bv;  // the first pick is the maximum
+    }
+    float den = 0.f;
+    for (int m = 0; m < p.M; ++m)
+      if ((chosen >> m) & 1u) den += expf(z[m] - zmax);
+    int j = 0;
+    const int64_t o = (tok * p.G + g) * p.k;
+    for (int m = 0; m < p.M; ++m) {
+      if ((chosen >> m) & 1u) {
+        p.topk_idx[o + j] = m;
+        p.topk_w[o + j] = expf(z[m] - zmax) / den;
+        ++j;
+      }
+    }
+  }
+}
+
+// bf16 router scores on MFMA. Block = one wavefront, 16 tokens.
+// 16x16x32 operand layout: lane l holds A[l%16][8*(l/16) .. +8] (token row,
+// 8 consecutive features) and B[8*(l/16) .. +8][l%16] (expert column); the
+// result D[4*(l/16)+i][l%16] lands in register i.
+__global__ __launch_bounds__(64) void route_bf16_kernel(RouteParams p) {
+  __shared__ float zs[kRouteTok * kMaxRouterCols];
+  const int lane = threadIdx.x;
+  const int64_t tok0 = (int64_t)blockIdx.x * kRouteTok;
+  const int ntok = (int)((p.T - tok0) < kRouteTok ? (p.T - tok0) : kRouteTok);
+  const int GM = p.G * p.M;
+  const int ntiles = (GM + 15) / 16;
+  const int D = p.D;
+  const __bf16* x = (const __bf16*)p.x;
+  const __bf16* w = (const __bf16*)p.w;
+
+  const int row = lane & 15;
+  const int kof = 8 * (lane >> 4);
+  const bool tok_ok = row < ntok;
+  const __bf16* xrow = x + (tok0 + (tok_ok ? row : 0)) * (int64_t)D;
+
+  f32x4 acc[kMaxRouterCols / 16];
+#pragma unroll
+  for (int e = 0; e < kMaxRouterCols / 16; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bf16x8 zero8 = {};
+  for (int c0 = 0; c0 < D; c0 += 32) {
+    // D is a multiple of 8; a 32-wide step may run past D only in its tail.
+    const int c = c0 + kof;
+    bf16x8 a = (tok_ok && c < D) ? *(const bf16x8*)(xrow + c) : zero8;
+#pragma unroll
+    for (int e = 0; e < kMaxRouterCols / 16; ++e) {
+      if (e < ntiles) {
+        const int ex = e * 16 + row;
+        bf16x8 b = (ex < GM && c < D) ? *(const bf16x8*)(w + (int64_t)ex * D + c) : zero8;
+        acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[e], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < kMaxRouterCols / 16; ++e) {
+    if (e < ntiles) {
+      const int ex = e * 16 + row;  // output column = expert
+      if (ex < GM) {
+        const float bias = p.bias ? p.bias[ex] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 4 * (lane >> 4) + i;
+          zs[t * GM + ex] = acc[e][i] + bias;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  route_select_store(zs, ntok, tok0, p);
+}
+
+// fp32 router scores: one thread per (token, expert), sequential fp32 FMAs.
+__global__ __launch_bounds__(64) void route_f32_kernel(RouteParams p) {
+  __shared__ float zs[kRouteTok * kMaxRouterCols];
+  const int64_t tok0 = (int64_t)blockIdx.x * kRouteTok;
+  const int ntok = (int)((p.T - tok0) < kRouteTok ? (p.T - tok0) : kRouteTok);
+  const int GM = p.G * p.M;
+  const float* x = (const float*)p.x;
+  const float* w = (const float*)p.w;
+  for (int e = threadIdx.x; e < ntok * GM; e += blockDim.x) {
+    const int t = e / GM, ex = e % GM;
+    const float* xr = x + (tok0 + t) * (int64_t)p.D;
+    const float* wr = w + (int64_t)ex * p.D;
+    float s = 0.f;
+    for (int c = 0; c < p.D; ++c) s = fmaf(xr[c], wr[c], s);
+    zs[t * GM + ex] = s + (p.bias ? p.bias[ex] : 0.f);
+  }
+  __syncthreads();
+  route_select_store(zs, ntok, tok0, p);
+}
+
+// ---------------------------------------------------------------------------
+// Token lists: count (per 64-token chunk) -> exclusive scan -> scatter. Ranks
+// inside a chunk come from wavefront ballots, so the lists are ascending and
+// deterministic without atomics.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t selected_mask(const ListParams& p, int b, int t, int g) {
+  if (t >= p.S) return 0u;
+  const int32_t* s = p.topk_idx + (((int64_t)b * p.S + t) * p.G + g) * p.k;
+  uint32_t m = 0;
+  for (int j = 0; j < p.k; ++j) m |= 1u << s[j];
+  return m;
+}
+
+__global__ __launch_bounds__(64) void list_count_kernel(ListParams p) {
+  const int chunk = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int t = chunk * kListChunk + lane;
+  for (int g = 0; g < p.G; ++g) {
+    const uint32_t sel = selected_mask(p, b, t, g);
+    for (int m = 0; m < p.M; ++m) {
+      const uint64_t bal = __ballot((sel >> m) & 1u);
+      if (lane == 0)
+        p.counts[(((int64_t)b * p.G + g) * p.M + m) * p.nchunk + chunk] = __popcll(bal);
+    }
+  }
+}
+
+// One block per (b, g): exclusive scan of the chunk counts of each expert,
+// in place, and the list offsets.
+__global__ __launch_bounds__(256) void list_scan_kernel(ListParams p) {
+  __shared__ int wave_tot[4];
+  __shared__ int carry_s;
+  const int bg = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int running = 0;  // identical in every thread
+  for (int m = 0; m < p.M; ++m) {
+    if (tid == 0) p.list_off[(int64_t)bg * (p.M + 1) + m] = running;
+    int32_t* cnt = p.counts + ((int64_t)bg * p.M + m) * p.nchunk;
+    int carry = 0;
+    for (int c0 = 0; c0 < p.nchunk; c0 += 256) {
+      const int c = c0 + tid;
+      const int v = c < p.nchunk ? cnt[c] : 0;
+      int incl = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+      }
+      if (lane == 63) wave_tot[wv] = incl;
+      __syncthreads();
+      int before = 0, tot = 0;
+      for (int i = 0; i < 4; ++i) {
+        if (i < wv) before += wave_tot[i];
+        tot += wave_tot[i];
+      }
+      if (c < p.nchunk) cnt[c] = running + carry + before + incl - v;
+      carry += tot;
+      __syncthreads();
+    }
+    running += carry;
+  }
+  if (tid == 0) p.list_off[(int64_t)bg * (p.M + 1) + p.M] = running;
+  (void)carry_s;
+}
+
+__global__ __launch_bounds__(64) void list_scatter_kernel(ListParams p) {
+  const int chunk = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int t = chunk * kListChunk + lane;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int g = 0; g < p.G; ++g) {
+    const uint32_t sel = selected_mask(p, b, t, g);
+    const int64_t bg = (int64_t)b * p.G + g;
+    for (int m = 0; m < p.M; ++m) {
+      const bool mine = (sel >> m) & 1u;
+      const uint64_t bal = __ballot(mine);
+      if (mine) {
+        const int pos = p.counts[(bg * p.M + m) * p.nchunk + chunk] + __popcll(bal & below);
+        p.list_tok[bg * ((int64_t)p.k * p.S) + pos] = t;
+      }
+    }
+  }
+}
+
+hipError_t launch_route(const RouteParams& p, bool bf16, hipStream_t s) {
+  const unsigned nblk = (unsigned)((p.T + kRouteTok - 1) / kRouteTok);
+  if (bf16)
+    hipLaunchKernelGGL(route_bf16_kernel, dim3(nblk), dim3(64), 0, s, p);
+  else
+    hipLaunchKernelGGL(route_f32_kernel, dim3(nblk), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_lists(const ListParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(list_count_kernel, dim3(p.nchunk, p.B), dim3(64), 0, s, p);
+  hipLaunchKernelGGL(list_scan_kernel, dim3(p.B * p.G), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(list_scatter_kernel, dim3(p.nchunk, p.B), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace gqe

@@ -1,0 +1,249 @@
+"""Thin ctypes binding of libgqe.so (include/gqe.h).
+
+The ``gqe_*`` functions have the C ABI's names and arguments; they only
+check that the tensors match the declared shapes/dtypes, pass device
+pointers and the current HIP stream, and turn a non-zero status into
+``GQEError``. Every step of the layer runs in the library's HIP kernels;
+there is no other code path. ``route``/``prefill``/``decode``/``out_proj``
+additionally allocate their outputs with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqe.so")
+
+GQE_OK = 0
+GQE_ERR_INVALID_ARG = -1
+GQE_ERR_UNSUPPORTED = -2
+GQE_ERR_ALIGNMENT = -3
+GQE_ERR_WORKSPACE = -4
+GQE_ERR_HIP = -5
+GQE_BF16 = 0
+GQE_F32 = 1
+
+EXPORTED = [
+    "gqe_status_string", "gqe_version", "gqe_route_workspace_bytes", "gqe_route",
+    "gqe_attn_prefill", "gqe_decode_workspace_bytes", "gqe_attn_decode", "gqe_out_proj",
+]
+
+
+class GQEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class gqe_dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "S", "D", "N", "G", "k", "d", "dtype")]
+
+    @classmethod
+    def make(cls, B, S, D, N, G, k, d, dtype) -> "gqe_dims":
+        code = {"bf16": GQE_BF16, torch.bfloat16: GQE_BF16, "f32": GQE_F32,
+                torch.float32: GQE_F32}.get(dtype, dtype)
+        return cls(B, S, D, N, G, k, d, code)
+
+    @classmethod
+    def from_config(cls, cfg) -> "gqe_dims":
+        return cls.make(cfg.B, cfg.S, cfg.D, cfg.N, cfg.G, cfg.k, cfg.d, cfg.dtype)
+
+    @property
+    def M(self) -> int:
+        return self.N // self.G
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == GQE_BF16 else torch.float32
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgqe.so; raises when it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m sparse_query_gqa_amd.build`"
+                           " (the GQE layer has no non-HIP implementation)")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    D = ctypes.POINTER(gqe_dims)
+    sig = {
+        "gqe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "gqe_version": (ctypes.c_int, []),
+        "gqe_route_workspace_bytes": (SZ, [D]),
+        "gqe_route": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "gqe_attn_prefill": (ctypes.c_int, [D, P, P, P, P, P, P, P]),
+        "gqe_decode_workspace_bytes": (SZ, [D, I32]),
+        "gqe_attn_decode": (ctypes.c_int, [D, I32, P, P, P, P, P, P, P, P, SZ, P]),
+        "gqe_out_proj": (ctypes.c_int, [D, I64, P, P, P, P, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().gqe_status_string(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(t: Optional[torch.Tensor], name: str, shape, dtype, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _raise(st: int, where: str):
+    if st != GQE_OK:
+        raise GQEError(st, where)
+
+
+def gqe_route_workspace_bytes(dims: gqe_dims) -> int:
+    return load_library().gqe_route_workspace_bytes(ctypes.byref(dims))
+
+
+def gqe_decode_workspace_bytes(dims: gqe_dims, q_len: int) -> int:
+    return load_library().gqe_decode_workspace_bytes(ctypes.byref(dims), q_len)
+
+
+def gqe_route(dims, x, w_router, b_router, logits, topk_idx, topk_w, list_off, list_tok,
+              workspace, stream=None):
+    T, GM, G, k, dt = dims.B * dims.S, dims.N, dims.G, dims.k, dims.torch_dtype
+    _check(x, "x", (T, dims.D), dt)
+    _check(w_router, "w_router", (GM, dims.D), dt)
+    _check(b_router, "b_router", (GM,), torch.float32, optional=True)
+    _check(logits, "logits", (T, G, dims.M), torch.float32, optional=True)
+    _check(topk_idx, "topk_idx", (T, G, k), torch.int32)
+    _check(topk_w, "topk_w", (T, G, k), torch.float32)
+    _check(list_off, "list_off", (dims.B, G, dims.M + 1), torch.int32, optional=True)
+    _check(list_tok, "list_tok", (dims.B, G, k * dims.S), torch.int32, optional=True)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().gqe_route(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(b_router),
+                                  _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(list_off),
+                                  _ptr(list_tok), _ptr(workspace), ws_bytes, _stream(stream))
+    _raise(st, "gqe_route")
+
+
+def gqe_attn_prefill(dims, q, k, v, topk_idx, o_routed, o_shared, stream=None):
+    B, S, N, G, kk, d, dt = dims.B, dims.S, dims.N, dims.G, dims.k, dims.d, dims.torch_dtype
+    _check(q, "q", (B, S, N + 1, d), dt)
+    _check(k, "k", (B, G, S, d), dt)
+    _check(v, "v", (B, G, S, d), dt)
+    _check(topk_idx, "topk_idx", (B * S, G, kk), torch.int32)
+    _check(o_routed, "o_routed", (B, S, G, kk, d), dt)
+    _check(o_shared, "o_shared", (B, S, d), dt)
+    st = load_library().gqe_attn_prefill(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(topk_idx), _ptr(o_routed), _ptr(o_shared),
+                                         _stream(stream))
+    _raise(st, "gqe_attn_prefill")
+
+
+def gqe_attn_decode(dims, q_len, q, k_cache, v_cache, kv_len, topk_idx, o_routed, o_shared,
+                    workspace, stream=None):
+    B, S, N, G, kk, d, dt = dims.B, dims.S, dims.N, dims.G, dims.k, dims.d, dims.torch_dtype
+    _check(q, "q", (B, q_len, N + 1, d), dt)
+    _check(k_cache, "k_cache", (B, G, S, d), dt)
+    _check(v_cache, "v_cache", (B, G, S, d), dt)
+    _check(kv_len, "kv_len", (B,), torch.int32)
+    _check(topk_idx, "topk_idx", (B * q_len, G, kk), torch.int32)
+    _check(o_routed, "o_routed", (B, q_len, G, kk, d), dt)
+    _check(o_shared, "o_shared", (B, q_len, d), dt)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().gqe_attn_decode(ctypes.byref(dims), q_len, _ptr(q), _ptr(k_cache),
+                                        _ptr(v_cache), _ptr(kv_len), _ptr(topk_idx),
+                                        _ptr(o_routed), _ptr(o_shared), _ptr(workspace), ws_bytes,
+                                        _stream(stream))
+    _raise(st, "gqe_attn_decode")
+
+
+def gqe_out_proj(dims, T, o_routed, topk_w, o_shared, w_o, y, stream=None):
+    G, kk, d, D, dt = dims.G, dims.k, dims.d, dims.D, dims.torch_dtype
+    _check(o_routed, "o_routed", (T, G, kk, d), dt)
+    _check(topk_w, "topk_w", (T, G, kk), torch.float32)
+    _check(o_shared, "o_shared", (T, d), dt)
+    _check(w_o, "w_o", ((G * kk + 2) * d, D), dt)
+    _check(y, "y", (T, D), dt)
+    st = load_library().gqe_out_proj(ctypes.byref(dims), T, _ptr(o_routed), _ptr(topk_w),
+                                     _ptr(o_shared), _ptr(w_o), _ptr(y), _stream(stream))
+    _raise(st, "gqe_out_proj")
+
+
+# --------------------------------------------------------------------------
+# Allocating wrappers
+# --------------------------------------------------------------------------
+
+def route(dims, x, w_router, b_router=None, want_logits=True, want_lists=True, stream=None):
+    dev = x.device
+    T, G, M, k = dims.B * dims.S, dims.G, dims.M, dims.k
+    out = dict(
+        logits=torch.empty((T, G, M), dtype=torch.float32, device=dev) if want_logits else None,
+        topk_idx=torch.empty((T, G, k), dtype=torch.int32, device=dev),
+        topk_w=torch.empty((T, G, k), dtype=torch.float32, device=dev),
+        list_off=torch.empty((dims.B, G, M + 1), dtype=torch.int32, device=dev) if want_lists else None,
+        list_tok=torch.empty((dims.B, G, k * dims.S), dtype=torch.int32, device=dev) if want_lists else None,
+    )
+    ws = None
+    if want_lists:
+        nbytes = gqe_route_workspace_bytes(dims)
+        ws = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=dev)
+    gqe_route(dims, x, w_router, b_router, out["logits"], out["topk_idx"], out["topk_w"],
+              out["list_off"], out["list_tok"], ws, stream)
+    return out
+
+
+def prefill(dims, q, k, v, topk_idx, stream=None):
+    o_r = torch.empty((dims.B, dims.S, dims.G, dims.k, dims.d), dtype=q.dtype, device=q.device)
+    o_s = torch.empty((dims.B, dims.S, dims.d), dtype=q.dtype, device=q.device)
+    gqe_attn_prefill(dims, q, k, v, topk_idx, o_r, o_s, stream)
+    return o_r, o_s
+
+
+def decode_workspace(dims, q_len, device) -> torch.Tensor:
+    nbytes = gqe_decode_workspace_bytes(dims, q_len)
+    return torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=device)
+
+
+def decode(dims, q_len, q, k_cache, v_cache, kv_len, topk_idx, workspace=None, stream=None):
+    if workspace is None:
+        workspace = decode_workspace(dims, q_len, q.device)
+    o_r = torch.empty((dims.B, q_len, dims.G, dims.k, dims.d), dtype=q.dtype, device=q.device)
+    o_s = torch.empty((dims.B, q_len, dims.d), dtype=q.dtype, device=q.device)
+    gqe_attn_decode(dims, q_len, q, k_cache, v_cache, kv_len, topk_idx, o_r, o_s, workspace, stream)
+    return o_r, o_s
+
+
+def out_proj(dims, T, o_routed, topk_w, o_shared, w_o, stream=None):
+    y = torch.empty((T, dims.D), dtype=w_o.dtype, device=w_o.device)
+    gqe_out_proj(dims, T, o_routed.view(T, dims.G, dims.k, dims.d), topk_w.view(T, dims.G, dims.k),
+                 o_shared.view(T, dims.d), w_o, y, stream)
+    return y

@@ -185,3 +185,42 @@ def make_decode_inputs(cfg: GQEConfig, threads: Optional[int] = None) -> dict:
     kv_len = cfg.kv_len if cfg.kv_len is not None else S
     kvl = torch.full((B,), kv_len, dtype=torch.int32)
     return dict(x=x, w_r=w_r, b_r=_router_bias(cfg), q=q, k=kc, v=vc, kv_len=kvl, w_o=w_o)
+
+
+def random_selection(B: int, S: int, G: int, M: int, k: int, seed: int,
+                     skew: bool = False) -> torch.Tensor:
+    """A seeded random choice of k distinct experts per (token, group), stored
+    ascending, as int32 [B*S, G, k]. With ``skew`` the first pick is expert
+    g mod M with probability 3/(M+2) (3:1 against each other expert) and the
+    remaining k-1 are uniform over the rest. Used to drive the attention and
+    projection kernels independently of the router."""
+    rng = np.random.default_rng([seed, 101])
+    T = B * S
+    perm = rng.permuted(np.broadcast_to(np.arange(M), (T, G, M)).copy(), axis=-1)
+    if skew and M > 1:
+        fav = np.arange(G) % M
+        prob = np.ones((G, M))
+        prob[np.arange(G), fav] = 3.0
+        prob /= prob.sum(-1, keepdims=True)
+        u = rng.random((T, G, 1))
+        first = (u > np.cumsum(prob, -1)[None]).sum(-1)  # categorical draw per (t, g)
+        # move `first` to the front of the permutation
+        pos = np.argmax(perm == first[..., None], axis=-1)
+        perm[np.arange(T)[:, None], np.arange(G)[None, :], pos] = perm[..., 0]
+        perm[..., 0] = first
+    sel = np.sort(perm[..., :k], axis=-1).astype(np.int32)
+    return torch.from_numpy(np.ascontiguousarray(sel))
+
+
+def make_slot_inputs(T: int, G: int, k: int, d: int, D: int, dtype: str, seed: int) -> dict:
+    """Seeded stand-ins for attention outputs and routing weights, to drive the
+    output projection on its own: o_routed [T,G,k,d] and o_shared [T,d] ~ N(0,1)/2,
+    weights w [T,G,k] drawn from a flat Dirichlet (positive, summing to 1 per
+    (t, g)), W_O [(G*k+2)*d, D] ~ N(0,1)*0.02."""
+    rng = np.random.default_rng([seed, 202])
+    cast = round_bf16 if dtype == "bf16" else (lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)))
+    o_r = cast(rng.standard_normal((T, G, k, d), dtype=np.float32) * np.float32(0.5))
+    o_s = cast(rng.standard_normal((T, d), dtype=np.float32) * np.float32(0.5))
+    w = torch.from_numpy(rng.dirichlet(np.ones(k), size=(T, G)).astype(np.float32))
+    w_o = cast(rng.standard_normal(((G * k + 2) * d, D), dtype=np.float32) * np.float32(0.02))
+    return dict(o_r=o_r, o_s=o_s, w=w, w_o=w_o)

@@ -1,0 +1,160 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/gqe.h declares, and rejects bad arguments before enqueuing anything.
+
+Fake device pointers are plain aligned (or deliberately misaligned) integers;
+every call here fails validation (or is an empty no-op), so nothing reaches
+the HIP runtime.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_query_gqa_amd as gqe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqe.h")
+
+A = 0x100000   # an aligned fake device address
+MIS = A + 8    # misaligned by 8 bytes
+
+
+def _lib():
+    if not os.path.exists(gqe.LIB_PATH):
+        pytest.skip("libgqe.so not built (run __graft_entry__.build())")
+    return gqe.load_library()
+
+
+def _dims(**kw):
+    base = dict(B=2, S=100, D=64, N=8, G=2, k=2, d=64, dtype=gqe.GQE_BF16)
+    base.update(kw)
+    return gqe.gqe_dims(**base)
+
+
+def P(v=A):
+    return ctypes.c_void_p(v)
+
+
+def test_header_symbols_exported():
+    lib = _lib()
+    src = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**(gqe_[a-z_0-9]+)\s*\(", src, re.M))
+    assert declared == set(gqe.EXPORTED), f"header declares {sorted(declared)}"
+    for name in declared:
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_status_strings_and_version():
+    lib = _lib()
+    for st in (0, -1, -2, -3, -4, -5):
+        s = lib.gqe_status_string(st).decode()
+        assert s.startswith("GQE_")
+    assert lib.gqe_status_string(7).decode() == "unknown gqe status"
+    assert lib.gqe_version() == 10000
+
+
+def route(lib, dims, x=A, w=A, b=None, logits=A, idx=A, wt=A, off=None, tok=None, ws=None, nws=0):
+    return lib.gqe_route(ctypes.byref(dims), P(x), P(w), None if b is None else P(b),
+                         None if logits is None else P(logits), None if idx is None else P(idx),
+                         None if wt is None else P(wt), None if off is None else P(off),
+                         None if tok is None else P(tok), None if ws is None else P(ws), nws, None)
+
+
+def test_route_validation():
+    lib = _lib()
+    assert route(lib, _dims(N=8, G=3)) == gqe.GQE_ERR_UNSUPPORTED     # G does not divide N
+    assert route(lib, _dims(k=5)) == gqe.GQE_ERR_UNSUPPORTED          # k > M
+    assert route(lib, _dims(k=0)) == gqe.GQE_ERR_INVALID_ARG
+    assert route(lib, _dims(d=48)) == gqe.GQE_ERR_UNSUPPORTED
+    assert route(lib, _dims(D=60)) == gqe.GQE_ERR_UNSUPPORTED         # D % 8
+    assert route(lib, _dims(dtype=7)) == gqe.GQE_ERR_UNSUPPORTED
+    assert route(lib, _dims(N=66, G=2, k=1)) == gqe.GQE_ERR_UNSUPPORTED  # M > 32
+    assert route(lib, _dims(N=288, G=9, k=1)) == gqe.GQE_ERR_UNSUPPORTED  # G*M > 256
+    assert route(lib, _dims(B=-1)) == gqe.GQE_ERR_INVALID_ARG
+    assert route(lib, _dims(), x=0) == gqe.GQE_ERR_INVALID_ARG
+    assert route(lib, _dims(), idx=None) == gqe.GQE_ERR_INVALID_ARG
+    assert route(lib, _dims(), x=MIS) == gqe.GQE_ERR_ALIGNMENT
+    assert route(lib, _dims(), logits=MIS) == gqe.GQE_ERR_ALIGNMENT
+    assert route(lib, _dims(), off=A) == gqe.GQE_ERR_INVALID_ARG     # off without tok
+    need = lib.gqe_route_workspace_bytes(ctypes.byref(_dims()))
+    assert need == 2 * 2 * 4 * 2 * 4  # B*G*M*ceil(S/64) int32
+    assert route(lib, _dims(), off=A, tok=A) == gqe.GQE_ERR_WORKSPACE
+    assert route(lib, _dims(), off=A, tok=A, ws=A, nws=need - 1) == gqe.GQE_ERR_WORKSPACE
+    assert route(lib, _dims(), off=A, tok=A, ws=MIS, nws=need) == gqe.GQE_ERR_ALIGNMENT
+    # empty calls succeed without touching the device
+    assert route(lib, _dims(B=0)) == gqe.GQE_OK
+    assert route(lib, _dims(S=0), off=A, tok=A) == gqe.GQE_OK
+
+
+def test_prefill_validation():
+    lib = _lib()
+
+    def call(dims, q=A, k=A, v=A, idx=A, o_r=A, o_s=A):
+        return lib.gqe_attn_prefill(ctypes.byref(dims), P(q), P(k), P(v), P(idx), P(o_r), P(o_s), None)
+
+    assert call(_dims(N=8, G=3)) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(d=256)) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(), q=0) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), o_s=0) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), v=MIS) == gqe.GQE_ERR_ALIGNMENT
+    assert call(_dims(B=0)) == gqe.GQE_OK
+    assert call(_dims(S=0)) == gqe.GQE_OK
+    assert lib.gqe_attn_prefill(None, P(), P(), P(), P(), P(), P(), None) == gqe.GQE_ERR_INVALID_ARG
+
+
+def test_decode_validation():
+    lib = _lib()
+
+    def call(dims, L=1, ws=A, nws=1 << 30, kv=A, q=A):
+        return lib.gqe_attn_decode(ctypes.byref(dims), L, P(q), P(A), P(A), P(kv), P(A), P(A), P(A),
+                                   None if ws is None else P(ws), nws, None)
+
+    d = _dims(S=65536, N=32, G=8, k=2, d=128)
+    need = lib.gqe_decode_workspace_bytes(ctypes.byref(d), 1)
+    assert need > 0
+    assert call(d, ws=None) == gqe.GQE_ERR_WORKSPACE
+    assert call(d, nws=need - 1) == gqe.GQE_ERR_WORKSPACE
+    assert call(d, ws=MIS, nws=need) == gqe.GQE_ERR_ALIGNMENT
+    assert call(d, L=-1) == gqe.GQE_ERR_INVALID_ARG
+    assert call(d, kv=0) == gqe.GQE_ERR_INVALID_ARG
+    assert call(d, q=MIS) == gqe.GQE_ERR_ALIGNMENT
+    assert call(_dims(S=4), L=5) == gqe.GQE_ERR_INVALID_ARG          # q_len > S_max
+    assert call(_dims(S=100, k=2), L=6) == gqe.GQE_ERR_UNSUPPORTED   # (k+1)*q_len > 16
+    assert call(_dims(N=8, G=3)) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(B=0)) == gqe.GQE_OK
+    assert call(d, L=0) == gqe.GQE_OK
+
+
+def test_out_proj_validation():
+    lib = _lib()
+
+    def call(dims, T=10, y=A, w=A):
+        return lib.gqe_out_proj(ctypes.byref(dims), T, P(A), P(A), P(A), P(w), P(y), None)
+
+    assert call(_dims(), T=-1) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), y=0) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), w=MIS) == gqe.GQE_ERR_ALIGNMENT
+    assert call(_dims(D=12)) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(N=8, G=3)) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(), T=0) == gqe.GQE_OK
+
+
+def test_workspace_sizes_closed_form():
+    lib = _lib()
+    d = _dims(B=16, S=65536, N=32, G=8, k=2, d=128)
+    # split geometry: ~8192 blocks over B*G = 128 pairs -> 64 splits of 1024 keys
+    recs = 16 * 8 * 64 * 3
+    assert lib.gqe_decode_workspace_bytes(ctypes.byref(d), 1) == recs * (128 + 2) * 4
+    d2 = _dims(B=1, S=131072, N=16, G=8, k=1)
+    assert lib.gqe_route_workspace_bytes(ctypes.byref(d2)) == 1 * 8 * 2 * 2048 * 4
+    assert lib.gqe_route_workspace_bytes(ctypes.byref(_dims(N=8, G=3))) == 0
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    _lib()
+    dims = _dims(B=1, S=4, D=64, N=4, G=2, k=1, d=32, dtype=gqe.GQE_F32)
+    x = torch.zeros(4, 64)
+    with pytest.raises(ValueError, match="device tensor"):
+        gqe.gqe_route(dims, x, torch.zeros(4, 64), None, None, x, x, None, None, None)

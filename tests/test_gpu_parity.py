@@ -1,0 +1,390 @@
+"""Parity of the HIP path (called through the C ABI) with the CPU oracle.
+
+Tolerances: bf16 inputs with fp32 accumulation -> max |error| <= 2e-2 and
+relative Frobenius error <= 1e-2; fp32 -> max |error| <= 1e-5. Routing
+indices and token lists are compared bit for bit. Small cases are compared
+element by element; the full-size workloads (run in the launch configuration
+the benchmark times) are compared on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_query_gqa_amd as gqe
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+f64 = synth.to_f64
+
+
+def tol(dtype):
+    return (2e-2, 1e-2) if dtype == "bf16" else (1e-5, 1e-6)
+
+
+def assert_close(got, ref, dtype, what):
+    got = f64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    amax, rel = tol(dtype)
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    fro = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)) if got.size else 0.0
+    print(f"{what}: max|err|={err:.3e} rel_fro={fro:.3e}")
+    assert err <= amax, f"{what}: max abs error {err:.3e} > {amax}"
+    assert fro <= rel, f"{what}: relative Frobenius error {fro:.3e} > {rel}"
+
+
+def to_dev(d):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+def dims_of(cfg, **kw):
+    c = cfg.replace(**kw) if kw else cfg
+    return gqe.gqe_dims.from_config(c)
+
+
+def small_cfg(B, S, D, N, G, k, d, dtype="bf16", seed=0, skew=False):
+    return synth.GQEConfig("case", B=B, S=S, D=D, N=N, G=G, k=k, d=d, dtype=dtype, seed=seed, skew=skew)
+
+
+# ---------------------------------------------------------------------------
+# Router
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,S,D,G,M,k", [(1, 1, 8, 1, 1, 1), (2, 77, 40, 3, 4, 2), (1, 130, 64, 8, 2, 1),
+                                         (3, 64, 96, 2, 32, 5), (1, 200, 256, 8, 32, 32),
+                                         (2, 150, 128, 16, 16, 3)])
+def test_route_exact_with_ties(dtype, B, S, D, G, M, k):
+    """Integer-valued x and W_r make every logit exact in fp32, so the
+    selection must equal the oracle's bit for bit, planted ties included
+    (duplicate expert rows; all-zero tokens whose logits all tie)."""
+    rng = np.random.default_rng(B * 1000 + S)
+    T = B * S
+    x = rng.integers(-3, 4, size=(T, D)).astype(np.float32)
+    x[::7] = 0.0
+    w = rng.integers(-2, 3, size=(G * M, D)).astype(np.float32)
+    if M > 1:
+        w[1::M] = w[0::M]  # expert 1 duplicates expert 0 in every group
+    bias = (rng.integers(-4, 5, size=G * M) * 0.5).astype(np.float32)
+    if M > 2:
+        bias[2::M] = bias[0::M]
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    xt, wt = torch.from_numpy(x).to(tdt), torch.from_numpy(w).to(tdt)
+    dims = gqe.gqe_dims.make(B, S, D, G * M, G, k, 32, dtype)
+    out = gqe.route(dims, xt.to(DEV), wt.to(DEV), torch.from_numpy(bias).to(DEV))
+    torch.cuda.synchronize()
+    z = oracle.route_logits(x, w, G, M, bias)
+    p, idx, wref = oracle.route_select(z, k)
+    assert np.array_equal(out["logits"].cpu().numpy().astype(np.float64), z), "logits not exact"
+    assert np.array_equal(out["topk_idx"].cpu().numpy(), idx), "selection differs"
+    assert np.max(np.abs(f64(out["topk_w"]) - wref)) <= 1e-6
+    if k == 1:
+        assert torch.all(out["topk_w"] == 1.0)
+    off, tok = oracle.build_lists(idx.reshape(B, S, G, k), M)
+    assert np.array_equal(out["list_off"].cpu().numpy(), off)
+    assert np.array_equal(out["list_tok"].cpu().numpy(), tok)
+
+
+def _route_check(cfg, inp, out):
+    """Logits within the fp32 bound; indices equal the oracle's wherever the
+    fp64 top-k margin exceeds twice that bound; lists equal the oracle's
+    lists on every (b, g) without an excluded near-tie; and the GPU's
+    selection is consistent with its own logits."""
+    T, G, M, k = cfg.T, cfg.G, cfg.M, cfg.k
+    x, w = f64(inp["x"]), f64(inp["w_r"])
+    b = None if inp["b_r"] is None else f64(inp["b_r"])
+    z = oracle.route_logits(x, w, G, M, b)
+    _, idx, wref = oracle.route_select(z, k)
+    zg = f64(out["logits"])
+    scale = (np.abs(x) @ np.abs(w).T).reshape(T, G, M) + 1.0
+    bound = 1e-5 * scale
+    assert np.all(np.abs(zg - z) <= bound), f"logit error {np.max(np.abs(zg - z) / scale):.3e}"
+    gidx = out["topk_idx"].cpu().numpy()
+    # A (token, group) can only select differently if its fp64 top-k margin is
+    # at most twice the largest logit error in that row; every other pair
+    # must match bit for bit.
+    srt = np.sort(z, -1)
+    margin = (srt[..., M - k] - srt[..., M - k - 1]) if k < M else np.full((T, G), np.inf)
+    row_err = np.abs(zg - z).max(-1)
+    ok = margin > 2 * row_err
+    n_excl = int((~ok).sum())
+    n_diff = int(np.any(gidx != idx, axis=-1).sum())
+    print(f"{cfg.name}: max logit err/scale {np.max(np.abs(zg - z) / scale):.2e}; "
+          f"{n_excl} near-tie (token, group) pairs of {T * G} excluded; {n_diff} differ in total")
+    assert np.array_equal(gidx[ok], idx[ok]), "selection differs outside near-ties"
+    assert n_excl <= max(2, 1e-4 * T * G)
+    assert np.max(np.abs(f64(out["topk_w"])[ok] - wref[ok])) <= 2e-5
+    # GPU selection vs GPU logits: selected >= unselected, ties to lower index
+    sel = np.zeros((T, G, M), bool)
+    np.put_along_axis(sel, gidx.astype(np.int64), True, -1)
+    assert np.all(np.diff(gidx, axis=-1) > 0)
+    if k < M:
+        lo = np.where(sel, zg, np.inf).min(-1)
+        hi = np.where(sel, -np.inf, zg).max(-1)
+        assert np.all(lo >= hi)
+    if cfg.mode == "prefill":
+        S = cfg.S
+        off, tok = oracle.build_lists(gidx.reshape(cfg.B, S, G, k), M)
+        assert np.array_equal(out["list_off"].cpu().numpy(), off)
+        assert np.array_equal(out["list_tok"].cpu().numpy(), tok)
+        off_o, _ = oracle.build_lists(idx.reshape(cfg.B, S, G, k), M)
+        okbg = ok.reshape(cfg.B, S, G).all(1)
+        assert np.array_equal(out["list_off"].cpu().numpy()[okbg], off_o[okbg])
+        counts = np.diff(out["list_off"].cpu().numpy(), axis=-1)
+        print(f"{cfg.name}: per-(g, m) token counts, sequence 0: {counts[0].tolist()}")
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "main_s2k", "long_s128k", "llama_s8k_skew", "decode_kv64k"])
+def test_route_workloads(name):
+    cfg = synth.workload(name)
+    if cfg.mode == "decode":
+        rng = np.random.default_rng(cfg.seed)
+        x = synth.round_bf16(rng.standard_normal((cfg.T, cfg.D), dtype=np.float32))
+        rng.standard_normal(((cfg.N + 1) * cfg.d, cfg.D), dtype=np.float32)  # W_Q draw
+        w_r = synth.round_bf16(rng.standard_normal((cfg.G * cfg.M, cfg.D), dtype=np.float32) * np.float32(0.02))
+        inp = dict(x=x, w_r=w_r, b_r=None)
+        dims = gqe.gqe_dims.make(cfg.B, cfg.q_len, cfg.D, cfg.N, cfg.G, cfg.k, cfg.d, cfg.dtype)
+        out = gqe.route(dims, x.to(DEV), w_r.to(DEV), None, want_lists=False)
+    else:
+        inp = synth.make_prefill_inputs(cfg)
+        out = gqe.route(dims_of(cfg), inp["x"].to(DEV), inp["w_r"].to(DEV),
+                        None if inp["b_r"] is None else inp["b_r"].to(DEV))
+    torch.cuda.synchronize()
+    _route_check(cfg, inp, out)
+
+
+# ---------------------------------------------------------------------------
+# Prefill attention
+# ---------------------------------------------------------------------------
+
+PREFILL_CASES = [
+    # B, S, D, N, G, k, d, dtype, peaked
+    (1, 1, 64, 4, 2, 1, 32, "f32", False),
+    (1, 128, 256, 4, 2, 1, 32, "f32", False),
+    (2, 77, 64, 8, 2, 3, 64, "f32", True),
+    (1, 150, 64, 6, 6, 1, 128, "f32", False),
+    (1, 1, 64, 4, 2, 1, 64, "bf16", False),
+    (1, 7, 64, 8, 1, 2, 64, "bf16", False),
+    (2, 300, 128, 16, 8, 1, 64, "bf16", False),
+    (2, 300, 128, 16, 8, 1, 64, "bf16", True),
+    (1, 517, 128, 32, 8, 2, 128, "bf16", False),
+    (1, 517, 128, 32, 8, 2, 128, "bf16", True),
+    (3, 200, 64, 8, 4, 2, 32, "bf16", True),
+    (1, 129, 64, 8, 8, 1, 64, "bf16", False),
+    (1, 64, 64, 16, 4, 4, 64, "bf16", False),
+]
+
+
+def _prefill_inputs(cfg, peaked):
+    inp = synth.make_prefill_inputs(cfg)
+    if peaked:  # sharpen the softmax: power-of-two scaling is exact in bf16
+        inp["q"] = inp["q"] * 8
+    # distinct KV heads: offset V of group g by 0.25*g, which keeps |o| small enough
+    # that output rounding stays far below the absolute bounds
+    off = (0.25 * torch.arange(cfg.G, dtype=torch.float32)).view(1, cfg.G, 1, 1)
+    inp["v"] = (inp["v"].float() + off).to(cfg.torch_dtype)
+    inp["idx"] = synth.random_selection(cfg.B, cfg.S, cfg.G, cfg.M, cfg.k, cfg.seed + 5)
+    return inp
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_small(case):
+    B, S, D, N, G, k, d, dtype, peaked = case
+    cfg = small_cfg(B, S, D, N, G, k, d, dtype)
+    inp = _prefill_inputs(cfg, peaked)
+    g = to_dev(inp)
+    o_r, o_s = gqe.prefill(dims_of(cfg), g["q"], g["k"], g["v"], g["idx"])
+    torch.cuda.synchronize()
+    idx = inp["idx"].numpy().reshape(B, S, G, k)
+    ref_r, ref_s = oracle.prefill(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), idx, cfg.M)
+    assert_close(o_r, ref_r, dtype, "O_routed")
+    assert_close(o_s, ref_s, dtype, "O_shared")
+
+
+def _sample_positions(S, n=256, seed=1):
+    if S <= n:
+        return np.arange(S)
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, S - 1), size=n - 2, replace=False)
+    return np.sort(np.concatenate([[0, S - 1], mid]))
+
+
+@pytest.mark.parametrize("name", ["main_s2k", "long_s128k", "llama_s8k_skew"])
+def test_prefill_workloads_sampled(name):
+    cfg = synth.workload(name)
+    inp = synth.make_prefill_inputs(cfg)
+    inp["idx"] = synth.random_selection(cfg.B, cfg.S, cfg.G, cfg.M, cfg.k, cfg.seed, skew=cfg.skew)
+    g = to_dev(inp)
+    o_r, o_s = gqe.prefill(dims_of(cfg), g["q"], g["k"], g["v"], g["idx"])
+    torch.cuda.synchronize()
+    pos = _sample_positions(cfg.S)
+    idx = inp["idx"].numpy().reshape(cfg.B, cfg.S, cfg.G, cfg.k)
+    for b in sorted({0, cfg.B - 1}):
+        ref_r, ref_s = oracle.prefill(f64(inp["q"][b:b + 1]), f64(inp["k"][b:b + 1]), f64(inp["v"][b:b + 1]),
+                                      idx[b:b + 1], cfg.M, positions=pos)
+        assert_close(o_r[b:b + 1, pos], ref_r, cfg.dtype, f"{name} b={b} O_routed (sampled)")
+        assert_close(o_s[b:b + 1, pos], ref_s, cfg.dtype, f"{name} b={b} O_shared (sampled)")
+
+
+def test_prefill_deterministic():
+    cfg = small_cfg(2, 300, 128, 16, 8, 1, 64)
+    inp = to_dev(_prefill_inputs(cfg, False))
+    a = gqe.prefill(dims_of(cfg), inp["q"], inp["k"], inp["v"], inp["idx"])
+    b = gqe.prefill(dims_of(cfg), inp["q"], inp["k"], inp["v"], inp["idx"])
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_prefill_causal_and_compaction():
+    """Token i's outputs ignore later tokens and other tokens' routing."""
+    cfg = small_cfg(1, 260, 64, 8, 2, 2, 64)
+    inp = _prefill_inputs(cfg, False)
+    g = to_dev(inp)
+    a_r, a_s = gqe.prefill(dims_of(cfg), g["q"], g["k"], g["v"], g["idx"])
+    i = 131
+    q2, k2, v2 = g["q"].clone(), g["k"].clone(), g["v"].clone()
+    q2[:, i + 1:] = -q2[:, i + 1:]
+    k2[:, :, i + 1:] = k2[:, :, i + 1:] * 2
+    v2[:, :, i + 1:] = v2[:, :, i + 1:] + 1
+    idx2 = synth.random_selection(1, 260, 2, 4, 2, 99).to(DEV)
+    idx2[i] = g["idx"][i]
+    b_r, b_s = gqe.prefill(dims_of(cfg), q2, k2, v2, idx2)
+    assert torch.equal(a_r[:, i], b_r[:, i]) and torch.equal(a_s[:, i], b_s[:, i])
+
+
+# ---------------------------------------------------------------------------
+# Decode attention
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("G", [1, 2, 8])
+@pytest.mark.parametrize("q_len", [1, 2])
+def test_decode_boundary_matrix(dtype, G, q_len):
+    """q_len in {1, 2}, kv_len in {7, 17} (plus one long ragged length),
+    G in {1, 2, H} with H = 8, distinct KV heads."""
+    H, d, Smax = 8, 64, 300
+    M = H // G
+    k = min(M, 2 if q_len == 1 else 1)
+    B = 3
+    rng = np.random.default_rng(G * 10 + q_len)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = torch.from_numpy(rng.standard_normal((B, q_len, H + 1, d), dtype=np.float32)).to(tdt)
+    kc = torch.from_numpy(rng.standard_normal((B, G, Smax, d), dtype=np.float32)).to(tdt)
+    vc = torch.from_numpy((rng.standard_normal((B, G, Smax, d)) + 0.25 * np.arange(G)[None, :, None, None]).astype(np.float32)).to(tdt)
+    kv_len = np.array([7, 17, 293], dtype=np.int32)
+    idx = synth.random_selection(B, q_len, G, M, k, 3)
+    dims = gqe.gqe_dims.make(B, Smax, 64, H, G, k, d, dtype)
+    o_r, o_s = gqe.decode(dims, q_len, q.to(DEV), kc.to(DEV), vc.to(DEV), torch.from_numpy(kv_len).to(DEV),
+                          idx.to(DEV))
+    torch.cuda.synchronize()
+    ref_r, ref_s = oracle.decode(f64(q), f64(kc), f64(vc), kv_len, idx.numpy().reshape(B, q_len, G, k), M)
+    assert_close(o_r, ref_r, dtype, f"decode G={G} q_len={q_len} O_routed")
+    assert_close(o_s, ref_s, dtype, f"decode G={G} q_len={q_len} O_shared")
+
+
+def test_decode_matches_prefill_rows():
+    """Decode of the token at position p against p+1 cached keys equals row p
+    of the prefill (a property that holds at any size)."""
+    cfg = small_cfg(2, 333, 64, 16, 8, 1, 64)
+    inp = to_dev(_prefill_inputs(cfg, False))
+    o_r, o_s = gqe.prefill(dims_of(cfg), inp["q"], inp["k"], inp["v"], inp["idx"])
+    for p in (0, 63, 64, 200, 332):
+        idx_p = inp["idx"].view(2, 333, 8, 1)[:, p].contiguous().view(2, 8, 1)
+        kv_len = torch.full((2,), p + 1, dtype=torch.int32, device=DEV)
+        d_r, d_s = gqe.decode(dims_of(cfg), 1, inp["q"][:, p:p + 1].contiguous(), inp["k"], inp["v"],
+                              kv_len, idx_p)
+        assert_close(d_r[:, 0], f64(o_r[:, p]), "bf16", f"decode vs prefill p={p}")
+        assert_close(d_s[:, 0], f64(o_s[:, p]), "bf16", f"decode vs prefill shared p={p}")
+
+
+def test_decode_workload_sampled():
+    cfg = synth.workload("decode_kv64k")
+    inp = synth.make_decode_inputs(cfg)
+    idx = synth.random_selection(cfg.B, cfg.q_len, cfg.G, cfg.M, cfg.k, cfg.seed)
+    g = to_dev(inp)
+    o_r, o_s = gqe.decode(dims_of(cfg), cfg.q_len, g["q"], g["k"], g["v"], g["kv_len"], idx.to(DEV))
+    torch.cuda.synchronize()
+    idx4 = idx.numpy().reshape(cfg.B, cfg.q_len, cfg.G, cfg.k)
+    for b in (0, 7, cfg.B - 1):
+        ref_r, ref_s = oracle.decode(f64(inp["q"][b:b + 1]), f64(inp["k"][b:b + 1]), f64(inp["v"][b:b + 1]),
+                                     inp["kv_len"].numpy()[b:b + 1], idx4[b:b + 1], cfg.M)
+        assert_close(o_r[b:b + 1], ref_r, cfg.dtype, f"decode b={b} O_routed")
+        assert_close(o_s[b:b + 1], ref_s, cfg.dtype, f"decode b={b} O_shared")
+
+
+# ---------------------------------------------------------------------------
+# Slot assembly + W_O
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,G,k,d,D,dtype", [(1, 2, 1, 32, 256, "f32"), (130, 2, 2, 64, 72, "f32"),
+                                             (1, 8, 1, 64, 1024, "bf16"), (300, 8, 1, 64, 1024, "bf16"),
+                                             (257, 8, 2, 128, 136, "bf16"), (64, 1, 1, 32, 8, "bf16"),
+                                             (129, 4, 3, 32, 264, "bf16")])
+def test_out_proj_small(T, G, k, d, D, dtype):
+    s = synth.make_slot_inputs(T, G, k, d, D, dtype, seed=T)
+    g = to_dev(s)
+    dims = gqe.gqe_dims.make(1, T, D, G * k, G, k, d, dtype)
+    y = gqe.out_proj(dims, T, g["o_r"], g["w"], g["o_s"], g["w_o"])
+    torch.cuda.synchronize()
+    ref = oracle.out_proj(f64(s["o_r"]), f64(s["w"]), f64(s["o_s"]), f64(s["w_o"]))
+    assert_close(y, ref, dtype, f"out_proj T={T}")
+
+
+@pytest.mark.parametrize("name", ["main_s2k", "long_s128k", "llama_s8k_skew", "decode_kv64k"])
+def test_out_proj_workloads_sampled(name):
+    cfg = synth.workload(name)
+    T = cfg.T
+    s = synth.make_slot_inputs(T, cfg.G, cfg.k, cfg.d, cfg.D, cfg.dtype, seed=1)
+    g = to_dev(s)
+    y = gqe.out_proj(dims_of(cfg), T, g["o_r"], g["w"], g["o_s"], g["w_o"])
+    torch.cuda.synchronize()
+    rows = _sample_positions(T, 512, seed=2)
+    ref = oracle.out_proj(f64(s["o_r"][rows]), f64(s["w"][rows]), f64(s["o_s"][rows]), f64(s["w_o"]))
+    assert_close(y[rows], ref, cfg.dtype, f"{name} y (sampled rows)")
+
+
+# ---------------------------------------------------------------------------
+# Whole layer: route -> prefill -> slot assembly + W_O, all on the GPU
+# ---------------------------------------------------------------------------
+
+def _layer_gpu(cfg, inp):
+    g = to_dev(inp)
+    dims = dims_of(cfg)
+    r = gqe.route(dims, g["x"], g["w_r"], g["b_r"])
+    o_r, o_s = gqe.prefill(dims, g["q"], g["k"], g["v"], r["topk_idx"])
+    y = gqe.out_proj(dims, cfg.T, o_r, r["topk_w"], o_s, g["w_o"])
+    torch.cuda.synchronize()
+    return r, o_r, o_s, y
+
+
+@pytest.mark.parametrize("cfg", [synth.workload("tiny_f32"),
+                                 small_cfg(2, 300, 256, 16, 8, 1, 64),
+                                 small_cfg(1, 333, 512, 32, 8, 2, 128, skew=True),
+                                 small_cfg(1, 97, 64, 8, 2, 4, 32)], ids=lambda c: f"{c.dtype}-S{c.S}-N{c.N}-k{c.k}")
+def test_layer_full(cfg):
+    inp = synth.make_prefill_inputs(cfg)
+    r, o_r, o_s, y = _layer_gpu(cfg, inp)
+    ref = oracle.layer(f64(inp["x"]), f64(inp["w_r"]), f64(inp["q"]), f64(inp["k"]), f64(inp["v"]),
+                       f64(inp["w_o"]), cfg.G, cfg.k, None if inp["b_r"] is None else f64(inp["b_r"]))
+    assert np.array_equal(r["topk_idx"].cpu().numpy(), ref["idx"]), "routing differs"
+    assert_close(o_r, ref["O_r"], cfg.dtype, "layer O_routed")
+    assert_close(o_s, ref["O_s"], cfg.dtype, "layer O_shared")
+    assert_close(y, ref["y"], cfg.dtype, "layer y")
+
+
+def test_layer_main_sampled():
+    cfg = synth.workload("main_s2k")
+    inp = synth.make_prefill_inputs(cfg)
+    r, o_r, o_s, y = _layer_gpu(cfg, inp)
+    b = 3
+    pos = _sample_positions(cfg.S, 128, seed=3)
+    z, p, idx, w = oracle.route(f64(inp["x"][b * cfg.S:(b + 1) * cfg.S]), f64(inp["w_r"]), cfg.G, cfg.M, cfg.k)
+    gidx = r["topk_idx"].cpu().numpy()[b * cfg.S:(b + 1) * cfg.S]
+    assert np.array_equal(gidx, idx)
+    ref_r, ref_s = oracle.prefill(f64(inp["q"][b:b + 1]), f64(inp["k"][b:b + 1]), f64(inp["v"][b:b + 1]),
+                                  idx.reshape(1, cfg.S, cfg.G, cfg.k), cfg.M, positions=pos)
+    yref = oracle.out_proj(ref_r[0].reshape(-1, cfg.G, cfg.k, cfg.d), w[pos], ref_s[0], f64(inp["w_o"]))
+    assert_close(y[b * cfg.S + pos], yref, cfg.dtype, "main layer y (sampled)")
