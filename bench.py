@@ -129,7 +129,7 @@ def main():
     ap.add_argument("--workload", default="long_s128k")
     ap.add_argument("--decode-workload", default="decode_kv64k")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=1536)
+    ap.add_argument("--cpu-rows", type=int, default=3072)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()

@@ -26,6 +26,7 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-variable", "-Wno-unused-but-set-variable",
+    "-fno-honor-nans",  # no NaN canonicalisation around min/max; infinities still honoured
     "-I", os.path.join(ROOT, "include"),
 ]
 

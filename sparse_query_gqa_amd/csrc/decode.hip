@@ -10,8 +10,11 @@
 //
 // Split-sequence: block (split c, group g, sequence b) reads keys
 // [c*chunk, min((c+1)*chunk, kv_len)) with coalesced 16-byte loads (a key row
-// is spread over d*elem/16 lanes), keeps an fp32 running (max, sum, o) per
-// row, and writes one partial per row. A combine kernel merges the partials.
+// is spread over d*elem/16 lanes; a wavefront load covers whole rows), keeps
+// an fp32 running (max, sum, o) per row, and writes one partial per row. The
+// inner loop is branch-free per lane: q.k uses v_dot2_f32_bf16 on packed
+// pairs, the row reduction uses DPP lane permutes, keys past the split are
+// loaded clamped and masked. A combine kernel merges the partials.
 #include "gqe_internal.h"
 
 namespace gqe {
@@ -31,38 +34,104 @@ DecodeSplit decode_split(int B, int G, int Smax, int k, int q_len) {
   return s;
 }
 
-template <typename T>
-struct Vec16;
-template <>
-struct Vec16<__bf16> {
-  typedef bf16x8 type;
-  static constexpr int n = 8;
-};
-template <>
-struct Vec16<float> {
-  typedef f32x4 type;
-  static constexpr int n = 4;
-};
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Merge running softmax state (m, l, o) with another one; m in raw score
-// units, exponentials exp2((s - m) * c).
+// Merge running softmax state (m, l, o) with another one; m is in log2 units
+// (scores already multiplied by scale*log2(e)).
 __device__ __forceinline__ void merge_state(float& m, float& l, float* o, float m2, float l2,
-                                            const float* o2, int n, float c) {
+                                            const float* o2, int n) {
   const float mn = fmaxf(m, m2);
-  const float a1 = (m == -INFINITY) ? 0.f : exp2f((m - mn) * c);
-  const float a2 = (m2 == -INFINITY) ? 0.f : exp2f((m2 - mn) * c);
+  const float a1 = (m == -INFINITY) ? 0.f : exp2f(m - mn);
+  const float a2 = (m2 == -INFINITY) ? 0.f : exp2f(m2 - mn);
   l = l * a1 + l2 * a2;
   for (int i = 0; i < n; ++i) o[i] = o[i] * a1 + o2[i] * a2;
   m = mn;
 }
 
+// Sum over each aligned group of TPK lanes, left in every lane of the group:
+// quad permutes (xor 1, xor 2), then the half-row and row mirrors, all as
+// DPP moves (no LDS traffic); groups wider than a 16-lane row add shuffles.
+__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
+  int x = __builtin_bit_cast(int, v), y;
+  switch (ctrl_sel) {
+    case 0: y = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true); break;   // quad_perm [1,0,3,2]
+    case 1: y = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true); break;   // quad_perm [2,3,0,1]
+    case 2: y = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true); break;  // row_half_mirror
+    default: y = __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, true); break; // row_mirror
+  }
+  return v + __builtin_bit_cast(float, y);
+}
+template <int TPK>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (TPK >= 2) v = dpp_add(v, 0);
+  if constexpr (TPK >= 4) v = dpp_add(v, 1);
+  if constexpr (TPK >= 8) v = dpp_add(v, 2);
+  if constexpr (TPK >= 16) v = dpp_add(v, 3);
+  if constexpr (TPK >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (TPK >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// Element i of a 4-dword vector, reinterpreted. The element is copied to a
+// scalar first: bit-casting a vector subscript directly reads element 0 with
+// this compiler.
+__device__ __forceinline__ bf16x2 pair_at(const u32x4& v, int i) {
+  const uint32_t w = v[i];
+  return __builtin_bit_cast(bf16x2, w);
+}
+__device__ __forceinline__ float f32_at(const u32x4& v, int i) {
+  const uint32_t w = v[i];
+  return __builtin_bit_cast(float, w);
+}
+
+// Unpack a 16-byte key/value slice to fp32.
+template <typename T>
+__device__ __forceinline__ void to_f32(const u32x4& w, float* f);
+template <>
+__device__ __forceinline__ void to_f32<__bf16>(const u32x4& w, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = w[i];
+    f[2 * i] = __builtin_bit_cast(float, x << 16);
+    f[2 * i + 1] = __builtin_bit_cast(float, x & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void to_f32<float>(const u32x4& w, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[i] = f32_at(w, i);
+}
+
+// Partial q.k over this lane's 16-byte slice: bf16 pairs through
+// v_dot2_f32_bf16 (exact products, fp32 sums), fp32 through FMAs.
+template <typename T>
+__device__ __forceinline__ float slice_dot(const u32x4& q, const u32x4& k);
+template <>
+__device__ __forceinline__ float slice_dot<__bf16>(const u32x4& q, const u32x4& k) {
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pair_at(q, i), pair_at(k, i), acc, false);
+  return acc;
+}
+template <>
+__device__ __forceinline__ float slice_dot<float>(const u32x4& q, const u32x4& k) {
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    acc = fmaf(f32_at(q, i), f32_at(k, i), acc);
+  return acc;
+}
+
+constexpr float kDecodeRescaleLog2 = 8.0f;
+
 template <typename T, int D, int RM>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
-  using V = typename Vec16<T>::type;
-  constexpr int VEC = Vec16<T>::n;   // elements per lane per key
-  constexpr int TPK = D / VEC;       // lanes per key row
-  constexpr int KPB = 256 / TPK;     // keys per block-wide pass
-  constexpr int U = 4;               // passes in flight
+  constexpr int VEC = 16 / (int)sizeof(T);  // elements per lane per key row
+  constexpr int TPK = D / VEC;              // lanes per key row
+  constexpr int KPB = 256 / TPK;            // keys per block-wide pass
+  constexpr int U = 4;                      // passes per iteration
   static_assert(TPK <= 64 && (64 % TPK) == 0, "key row must fit a wavefront");
 
   const int c_split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -71,20 +140,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   if (k_begin >= kvl) return;  // the combine reads only the splits below kv_len
   const int k_end = min(k_begin + p.chunk, kvl);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int part = tid % TPK;        // which VEC-slice of d
-  const int kl = tid / TPK;          // key lane within a pass
+  const int part = tid % TPK;  // which 16-byte slice of the row
+  const int kl = tid / TPK;    // key lane within a pass
   const float c = p.scale * 1.44269504088896340736f;
 
   // rows of (b, g): K*L routed rows (token t = r / K, slot r % K), then L
   // shared rows on group 0
   const int nrows = p.K * p.L + (g == 0 ? p.L : 0);
-  float q[RM][VEC];
+  u32x4 q[RM];
   int rpos[RM];
 #pragma unroll
   for (int r = 0; r < RM; ++r) {
     rpos[r] = -1;
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) q[r][i] = 0.f;
+    q[r] = u32x4{0u, 0u, 0u, 0u};
     if (r < nrows) {
       int t, head;
       if (r < p.K * p.L) {
@@ -95,10 +163,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         head = p.N;
       }
       rpos[r] = kvl - p.L + t;
-      const T* qp = (const T*)p.q + (((int64_t)b * p.L + t) * (p.N + 1) + head) * D + part * VEC;
-      const V qv = *(const V*)qp;
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) q[r][i] = (float)qv[i];
+      q[r] = *(const u32x4*)((const T*)p.q + (((int64_t)b * p.L + t) * (p.N + 1) + head) * D + part * VEC);
     }
   }
 
@@ -115,53 +180,54 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   const T* vb = (const T*)p.v + ((int64_t)b * p.G + g) * (int64_t)p.Smax * D + part * VEC;
 
   for (int j0 = k_begin; j0 < k_end; j0 += U * KPB) {
-    V kv[U], vv[U];
+    // keys past the split are loaded from its last key (always valid) and masked
+    u32x4 kw[U], vw[U];
     int key[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       key[u] = j0 + u * KPB + kl;
-      if (key[u] < k_end) {
-        kv[u] = *(const V*)(kb + (int64_t)key[u] * D);
-        vv[u] = *(const V*)(vb + (int64_t)key[u] * D);
-      }
+      const int64_t kk = min(key[u], k_end - 1);
+      kw[u] = *(const u32x4*)(kb + kk * D);
+      vw[u] = *(const u32x4*)(vb + kk * D);
     }
+    float vf[U][VEC];
+#pragma unroll
+    for (int u = 0; u < U; ++u) to_f32<T>(vw[u], vf[u]);
 #pragma unroll
     for (int r = 0; r < RM; ++r) {
-      if (r < nrows) {
+      if (r < nrows) {  // uniform
         float s[U];
+        float bm = -INFINITY;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          float acc = 0.f;
-          if (key[u] < k_end) {
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) acc = fmaf(q[r][i], (float)kv[u][i], acc);
-          }
-#pragma unroll
-          for (int o2 = 1; o2 < TPK; o2 <<= 1) acc += __shfl_xor(acc, o2, 64);
-          s[u] = (key[u] < k_end && key[u] <= rpos[r]) ? acc : -INFINITY;
+          const float dot = group_sum<TPK>(slice_dot<T>(q[r], kw[u]));
+          s[u] = (key[u] < k_end && key[u] <= rpos[r]) ? dot * c : -INFINITY;
+          bm = fmaxf(bm, s[u]);
         }
-        float mx = m[r];
-#pragma unroll
-        for (int u = 0; u < U; ++u) mx = fmaxf(mx, s[u]);
-        if (mx != -INFINITY) {  // else nothing visible yet for this row here
-          const float alpha = (m[r] == -INFINITY) ? 0.f : exp2f((m[r] - mx) * c);
+        // lazy rescale: move the reference max only when it grows by more
+        // than 2^8 (or is still -inf), so most iterations skip the rescale
+        const float mn = fmaxf(m[r], bm);
+        const bool move = mn - m[r] > kDecodeRescaleLog2;  // NaN (both -inf) -> false
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+          const float alpha = move ? ((m[r] == -INFINITY) ? 0.f : exp2f(m[r] - mn)) : 1.f;
+          if (move) m[r] = mn;
           l[r] *= alpha;
 #pragma unroll
           for (int i = 0; i < VEC; ++i) o[r][i] *= alpha;
+        }
 #pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const float e = (s[u] == -INFINITY) ? 0.f : exp2f((s[u] - mx) * c);
-            l[r] += e;
+        for (int u = 0; u < U; ++u) {
+          // s finite implies m finite (it moved to at least s - 2^8)
+          const float e = (s[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[u] - m[r]);
+          l[r] += e;
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) o[r][i] = fmaf(e, (key[u] < k_end) ? (float)vv[u][i] : 0.f, o[r][i]);
-          }
-          m[r] = mx;
+          for (int i = 0; i < VEC; ++i) o[r][i] = fmaf(e, vf[u][i], o[r][i]);
         }
       }
     }
   }
 
-  // merge key lanes inside the wavefront (lanes with equal `part`)
+  // merge the key lanes of the wavefront (lanes with equal `part`)
 #pragma unroll
   for (int r = 0; r < RM; ++r) {
     if (r < nrows) {
@@ -172,7 +238,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         float o2[VEC];
 #pragma unroll
         for (int i = 0; i < VEC; ++i) o2[i] = __shfl_xor(o[r][i], off, 64);
-        merge_state(m[r], l[r], o[r], m2, l2, o2, VEC, c);
+        merge_state(m[r], l[r], o[r], m2, l2, o2, VEC);
       }
     }
   }
@@ -198,7 +264,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     float mm = -INFINITY, ll = 0.f, oo = 0.f;
     for (int w = 0; w < 4; ++w) {
       const float m2 = sm[w][r][0], l2 = sm[w][r][1], o2 = so[w][r][e];
-      merge_state(mm, ll, &oo, m2, l2, &o2, 1, c);
+      merge_state(mm, ll, &oo, m2, l2, &o2, 1);
     }
     p.ws_o[(rec + r) * D + e] = oo;
     if (e == 0) {
@@ -215,16 +281,36 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   const int kvl = p.kv_len[b];
   const int ns = min(p.nsplit, (kvl + p.chunk - 1) / p.chunk);
   const int nrows = p.K * p.L + (g == 0 ? p.L : 0);
-  const float c = p.scale * 1.44269504088896340736f;
   const int64_t rec0 = ((int64_t)b * p.G + g) * p.nsplit;
   for (int idx = threadIdx.x; idx < nrows * D; idx += blockDim.x) {
     const int r = idx / D, e = idx % D;
-    float mm = -INFINITY, ll = 0.f, oo = 0.f;
-    for (int cs = 0; cs < ns; ++cs) {
+    // pass 1: the largest split max; pass 2: rescaled sums (8 splits per step)
+    float mm = -INFINITY;
+    for (int cs = 0; cs < ns; ++cs) mm = fmaxf(mm, p.ws_ml[((rec0 + cs) * p.R + r) * 2]);
+    float ll = 0.f, oo = 0.f;
+    int cs = 0;
+    for (; cs + 8 <= ns; cs += 8) {
+      float m8[8], l8[8], o8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t rr = (rec0 + cs + u) * p.R + r;
+        m8[u] = p.ws_ml[rr * 2 + 0];
+        l8[u] = p.ws_ml[rr * 2 + 1];
+        o8[u] = p.ws_o[rr * D + e];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float a = (m8[u] == -INFINITY) ? 0.f : exp2f(m8[u] - mm);
+        ll = fmaf(l8[u], a, ll);
+        oo = fmaf(o8[u], a, oo);
+      }
+    }
+    for (; cs < ns; ++cs) {
       const int64_t rr = (rec0 + cs) * p.R + r;
-      const float m2 = p.ws_ml[rr * 2 + 0], l2 = p.ws_ml[rr * 2 + 1];
-      const float o2 = p.ws_o[rr * D + e];
-      merge_state(mm, ll, &oo, m2, l2, &o2, 1, c);
+      const float m2 = p.ws_ml[rr * 2 + 0];
+      const float a = (m2 == -INFINITY) ? 0.f : exp2f(m2 - mm);
+      ll = fmaf(p.ws_ml[rr * 2 + 1], a, ll);
+      oo = fmaf(p.ws_o[rr * D + e], a, oo);
     }
     const float val = oo / ll;
     T* out;

@@ -19,56 +19,70 @@
 // lane owns one query row in both products (row max, row sum and rescale are
 // per-lane scalars; the two lane halves are combined with one exchange).
 // Online softmax in fp32 with exp2 and scale*log2(e) folded into one FMA.
+#include <type_traits>
+
 #include "gqe_internal.h"
 
 namespace gqe {
 
-constexpr int kRowsPerWave = 32;
 constexpr int kWaves = 4;
-constexpr int kTileRows = kRowsPerWave * kWaves;  // 128
 constexpr int kKeyBlock = 64;
 constexpr int kKPad = 8;  // bf16 elements of padding per K row in LDS
-constexpr int kVPad = 8;  // per V^T row
+constexpr int kVPad = 4;  // per V^T row: a 34-dword stride keeps 16 lanes' 8-byte reads on distinct banks
+// Lazy rescaling: the running max used for the exponentials is only moved
+// when a row's max grows by more than this many powers of two, so the
+// un-normalised probabilities stay below 2^8 and most key blocks skip the
+// rescale of the output accumulators.
+constexpr float kRescaleLog2 = 8.0f;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 32-row blocks per wavefront for each head dim (64 rows halve the LDS
+// bytes per MFMA FLOP; d=128 keeps 32 rows to stay within 256 VGPRs).
+template <int D>
+struct PrefillShape {
+  static constexpr int RB = (D <= 64) ? 2 : 1;
+  static constexpr int kTileRows = kWaves * 32 * RB;
+};
 
 struct TileCoord {
-  int b, v, tile;  // tile index within (b, v): rows [tile*128, tile*128+128)
+  int b, v, tile;  // tile index within (b, v)
   bool valid;
 };
 
 // Block -> tile. Blocks are spread round-robin over the 8 XCDs, so block w
 // is re-mapped to a logical tile index such that each XCD walks a contiguous
-// range of the (b, v, tile) order: its concurrently running workgroups read
+// range of the (v, b, tile) order: its concurrently running workgroups read
 // the same KV head and share it in that XCD's L2. Within a (b, v) tiles run
 // from the longest causal extent to the shortest.
 __device__ __forceinline__ TileCoord tile_of_block(const PrefillParams& p, int tiles_r,
                                                   int tiles_s) {
   const int per_b = p.G * tiles_r + tiles_s;
   const int total = p.B * per_b;
-  const int nblk = gridDim.x;
-  const int per_xcd = nblk / 8;
+  const int per_xcd = gridDim.x / 8;
   const int w = blockIdx.x;
   const int logical = (w % 8) * per_xcd + (w / 8);
   TileCoord c;
   c.valid = logical < total;
   int rem = c.valid ? logical : 0;
-  // order: v-major over (v, b) so groups sharing a KV head sit together
-  // (the shared head, v == G, reads KV head 0 and follows group 0).
-  int vslot = rem / (p.B * tiles_r);
-  if (vslot < 1) {  // group 0
+  // order: group 0, then the shared head (it also reads KV head 0), then
+  // groups 1..G-1; sequences inside each.
+  if (rem < p.B * tiles_r) {
     c.v = 0;
     c.b = rem / tiles_r;
     c.tile = tiles_r - 1 - rem % tiles_r;
   } else {
     rem -= p.B * tiles_r;
-    if (rem < p.B * tiles_s) {  // shared head next to group 0
+    if (rem < p.B * tiles_s) {
       c.v = p.G;
       c.b = rem / tiles_s;
       c.tile = tiles_s - 1 - rem % tiles_s;
     } else {
       rem -= p.B * tiles_s;
-      const int vv = 1 + rem / (p.B * tiles_r);
+      c.v = 1 + rem / (p.B * tiles_r);
       rem %= (p.B * tiles_r);
-      c.v = vv;
       c.b = rem / tiles_r;
       c.tile = tiles_r - 1 - rem % tiles_r;
     }
@@ -94,11 +108,15 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, int tiles_r,
                                                               int tiles_s) {
   static_assert(D == 32 || D == 64 || D == 128, "head dim");
-  constexpr int KS = D / 16;                       // MFMA k-steps over d
-  constexpr int DB = D / 32;                       // 32-wide d blocks of O^T
-  constexpr int LD_PASSES = kKeyBlock * D / (256 * 8);  // 16-byte loads per thread
-  __shared__ __bf16 Ks[kKeyBlock][D + kKPad];
-  __shared__ __bf16 Vt[D][kKeyBlock + kVPad];
+  constexpr int RB = PrefillShape<D>::RB;                // 32-row blocks per wave
+  constexpr int kTileRows = PrefillShape<D>::kTileRows;
+  constexpr int KS = D / 16;                             // MFMA k-steps over d
+  constexpr int DB = D / 32;                             // 32-wide d blocks of O^T
+  constexpr int DCH = D / 8;                             // 8-element chunks per key row
+  constexpr int LD_PASSES = (kKeyBlock / 2) * DCH / 256 > 0 ? (kKeyBlock / 2) * DCH / 256 : 1;
+  constexpr int LD_THREADS = (kKeyBlock / 2) * DCH / LD_PASSES;  // threads that load
+  __shared__ __bf16 Ks[2][kKeyBlock][D + kKPad];
+  __shared__ __bf16 Vt[2][D][kKeyBlock + kVPad];
 
   const TileCoord tc = tile_of_block(p, tiles_r, tiles_s);
   if (!tc.valid) return;
@@ -110,119 +128,152 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, i
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
 
-  // this lane's query row
-  const int my_r = r0 + wave * kRowsPerWave + l32;
   const int last_r = min(r0 + kTileRows, nrows) - 1;
-  const bool row_ok = my_r < nrows;
-  int pos, slot, head;
-  row_info(p, b, v, row_ok ? my_r : last_r, pos, slot, head);
-  int pos_last, s_, h_;
+  int pos_last, pos_first, s_, h_;
   row_info(p, b, v, last_r, pos_last, s_, h_);
-  int pos_first;
   row_info(p, b, v, r0, pos_first, s_, h_);
 
-  // Q^T fragments (B operand of S^T = K Q^T): d = 16*s + 8*half + [0,8)
-  const __bf16* qrow = (const __bf16*)p.q + (((int64_t)b * p.S + pos) * (p.N + 1) + head) * D;
-  bf16x8 qf[KS];
+  // this lane's query rows (one per 32-row block), Q^T fragments for the B
+  // operand of S^T = K Q^T: d = 16*s + 8*half + [0,8)
+  int pos[RB], slot[RB];
+  bool row_ok[RB];
+  bf16x8 qf[RB][KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) qf[s] = *(const bf16x8*)(qrow + 16 * s + 8 * half);
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = r0 + wave * 32 * RB + rb * 32 + l32;
+    row_ok[rb] = r < nrows;
+    int head;
+    row_info(p, b, v, row_ok[rb] ? r : last_r, pos[rb], slot[rb], head);
+    const __bf16* qrow = (const __bf16*)p.q + (((int64_t)b * p.S + pos[rb]) * (p.N + 1) + head) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[rb][s] = *(const bf16x8*)(qrow + 16 * s + 8 * half);
+  }
 
   const __bf16* kbase = (const __bf16*)p.k + ((int64_t)b * p.G + kvh) * (int64_t)p.S * D;
   const __bf16* vbase = (const __bf16*)p.v + ((int64_t)b * p.G + kvh) * (int64_t)p.S * D;
 
-  f32x16 oacc[DB];
+  f32x16 oacc[RB][DB];
 #pragma unroll
-  for (int i = 0; i < DB; ++i)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) oacc[i][j] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) oacc[rb][i][j] = 0.f;
+  float m_run[RB], l_run[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.f;
+  }
   const float c = p.scale * 1.44269504088896340736f;  // scale * log2(e)
 
   const int nblocks = pos_last / kKeyBlock + 1;
-  bf16x8 kreg[LD_PASSES], vreg[LD_PASSES];
+  // K/V loader: thread -> key pair (2*kp, 2*kp+1) and an 8-wide d chunk; V is
+  // written transposed as packed pairs of keys (4-byte LDS stores).
+  const int ld_kp = tid / DCH, ld_d0 = (tid % DCH) * 8;
+  const bool ld_on = tid < LD_THREADS;
+  bf16x8 kreg[LD_PASSES][2], vreg[LD_PASSES][2];
   const bf16x8 zero8 = {};
 
   auto gload = [&](int kb) {
 #pragma unroll
-    for (int ps = 0; ps < LD_PASSES; ++ps) {
-      const int e = (ps * 256 + tid) * 8;
-      const int key = e / D, col = e % D;
-      const int gk = kb * kKeyBlock + key;
-      if (gk < p.S) {
-        kreg[ps] = *(const bf16x8*)(kbase + (int64_t)gk * D + col);
-        vreg[ps] = *(const bf16x8*)(vbase + (int64_t)gk * D + col);
-      } else {
-        kreg[ps] = zero8;
-        vreg[ps] = zero8;
+    for (int ps = 0; ps < LD_PASSES; ++ps)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int gk = kb * kKeyBlock + 2 * (ld_kp + ps * (LD_THREADS / DCH)) + e;
+        if (ld_on && gk < p.S) {
+          kreg[ps][e] = *(const bf16x8*)(kbase + (int64_t)gk * D + ld_d0);
+          vreg[ps][e] = *(const bf16x8*)(vbase + (int64_t)gk * D + ld_d0);
+        } else {
+          kreg[ps][e] = zero8;
+          vreg[ps][e] = zero8;
+        }
       }
-    }
   };
-  auto lstore = [&]() {
+  auto lstore = [&](int buf) {
+    if (!ld_on) return;
 #pragma unroll
     for (int ps = 0; ps < LD_PASSES; ++ps) {
-      const int e = (ps * 256 + tid) * 8;
-      const int key = e / D, col = e % D;
-      *(bf16x8*)&Ks[key][col] = kreg[ps];
+      const int key = 2 * (ld_kp + ps * (LD_THREADS / DCH));
+      *(bf16x8*)&Ks[buf][key][ld_d0] = kreg[ps][0];
+      *(bf16x8*)&Ks[buf][key + 1][ld_d0] = kreg[ps][1];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) Vt[col + i][key] = vreg[ps][i];
+      for (int i = 0; i < 8; ++i) {
+        const bf16x2 pr = {vreg[ps][0][i], vreg[ps][1][i]};
+        *(bf16x2*)&Vt[buf][ld_d0 + i][key] = pr;
+      }
     }
   };
 
   gload(0);
-  lstore();
+  lstore(0);
   __syncthreads();
 
-  for (int kb = 0; kb < nblocks; ++kb) {
-    if (kb + 1 < nblocks) gload(kb + 1);
-
-    // S^T for two 32-key halves of the block
-    f32x16 sacc[2];
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // One key block: S^T = K Q^T, (causal mask), online softmax, O^T += V^T P^T.
+  // MASK is a compile-time flag: only the diagonal blocks of the tile pay
+  // for the causal mask.
+  auto block = [&](const int kb, const int buf, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    // S^T for the two 32-key halves of the block; each K fragment read from
+    // LDS feeds every row block of the wave.
+    f32x16 sacc[RB][2];
+    const f32x16 zero16 = {};
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sacc[sb][j] = 0.f;
+      for (int sb = 0; sb < 2; ++sb) {
+        const bf16x8 kf = *(const bf16x8*)&Ks[buf][sb * 32 + l32][16 * s + 8 * half];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf = *(const bf16x8*)&Ks[sb * 32 + l32][16 * s + 8 * half];
-        sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[sb], 0, 0, 0);
+        for (int rb = 0; rb < RB; ++rb)
+          sacc[rb][sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[rb][s], s == 0 ? zero16 : sacc[rb][sb], 0, 0, 0);
+      }
+    if constexpr (MASK) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        // key = kb*64 + sb*32 + 8*(j/4) + 4*half + j%4 is visible iff key <= pos
+        const int lim = pos[rb] - kb * kKeyBlock - 4 * half;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (sb * 32 + 8 * (j >> 2) + (j & 3) > lim) sacc[rb][sb][j] = -INFINITY;
       }
     }
-    // causal mask only on blocks that reach past the tile's first position
-    if (kb * kKeyBlock + kKeyBlock - 1 > pos_first) {
+    u32x4 pf[RB][2][2];  // bf16 P^T fragments, two probabilities per dword
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float bmax = fmaxf(sacc[rb][0][0], sacc[rb][1][0]);
+#pragma unroll
+      for (int j = 1; j < 16; ++j) bmax = fmaxf(bmax, fmaxf(sacc[rb][0][j], sacc[rb][1][j]));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+      // key 0 is in the first block and visible to every row, so m_run is
+      // finite from the first block on; later fully masked rows keep it.
+      const float m_new = fmaxf(m_run[rb], bmax);
+      const bool move = (m_new - m_run[rb]) * c > kRescaleLog2;  // -inf m_run moves
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        __asm__ volatile("" ::: "memory");  // keep this a real branch
+        const float alpha = move ? __builtin_amdgcn_exp2f((m_run[rb] - m_new) * c) : 1.f;
+        if (move) m_run[rb] = m_new;
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) oacc[rb][i][j] *= alpha;
+      }
+      const float mc = m_run[rb] * c;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = kb * kKeyBlock + sb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-          if (key > pos) sacc[sb][j] = -INFINITY;
+        for (int j = 0; j < 16; j += 2) {
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[rb][sb][j], c, -mc));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[rb][sb][j + 1], c, -mc));
+          const bf16x2 pr = {f2bf(e0), f2bf(e1)};
+          pf[rb][sb][j >> 3][(j & 7) >> 1] = __builtin_bit_cast(uint32_t, pr);
+          // row sum of the bf16 probabilities actually used in P V
+          l_run[rb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run[rb], false);
         }
     }
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) bmax = fmaxf(bmax, sacc[sb][j]);
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-    const float m_new = fmaxf(m_run, bmax);  // finite: key 0 is visible to every row
-    const float alpha = exp2f((m_run - m_new) * c);
-    const float mc = m_new * c;
-    float psum = 0.f;
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float e = exp2f(fmaf(sacc[sb][j], c, -mc));
-        psum += e;
-        pf[sb][j >> 3][j & 7] = f2bf(e);
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) oacc[i][j] *= alpha;
-
     // O^T += V^T P^T. Contraction index of step st of key half sb, lane half h,
     // element t <-> key sb*32 + 16*st + 8*(t/4) + 4*h + t%4 (the S^T layout).
 #pragma unroll
@@ -232,36 +283,59 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, i
         const int kc = sb * 32 + 16 * st + 4 * half;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const __bf16* vr = &Vt[db * 32 + l32][kc];
-          const bf16x4 lo = *(const bf16x4*)vr;
-          const bf16x4 hi = *(const bf16x4*)(vr + 8);
-          const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[sb][st], oacc[db], 0, 0, 0);
+          const __bf16* vr = &Vt[buf][db * 32 + l32][kc];
+          const u32x2 lo = *(const u32x2*)vr;
+          const u32x2 hi = *(const u32x2*)(vr + 8);
+          const u32x4 vw = {lo[0], lo[1], hi[0], hi[1]};
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, vw);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                vf, __builtin_bit_cast(bf16x8, pf[rb][sb][st]), oacc[rb][db], 0, 0, 0);
         }
       }
+  };
 
+  // Blocks entirely at or below the tile's first position need no mask; the
+  // few diagonal blocks after them do, and load their K/V without register
+  // prefetch to keep the second copy of the body within the register budget.
+  const int nfull = min((pos_first + 1) / kKeyBlock, nblocks);
+  int kb = 0;
+  for (; kb < nfull; ++kb) {
+    const int buf = kb & 1;
+    if (kb + 1 < nblocks) gload(kb + 1);
+    block(kb, buf, std::integral_constant<bool, false>());
+    if (kb + 1 < nblocks) lstore(buf ^ 1);  // the other buffer: last read before the previous barrier
+    __syncthreads();
+  }
+  for (; kb < nblocks; ++kb) {
+    const int buf = kb & 1;
+    block(kb, buf, std::integral_constant<bool, true>());
     if (kb + 1 < nblocks) {
-      __syncthreads();
-      lstore();
-      __syncthreads();
+      gload(kb + 1);
+      lstore(buf ^ 1);
     }
+    __syncthreads();
   }
 
-  if (!row_ok) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.f / l_tot;
-  __bf16* out = (v == p.G)
-                    ? (__bf16*)p.o_s + ((int64_t)b * p.S + pos) * D
-                    : (__bf16*)p.o_r + ((((int64_t)b * p.S + pos) * p.G + v) * p.K + slot) * D;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int rb = 0; rb < RB; ++rb) {
+    const float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 32, 64);
+    if (!row_ok[rb]) continue;
+    const float inv = 1.f / l_tot;
+    __bf16* out = (v == p.G)
+                      ? (__bf16*)p.o_s + ((int64_t)b * p.S + pos[rb]) * D
+                      : (__bf16*)p.o_r + ((((int64_t)b * p.S + pos[rb]) * p.G + v) * p.K + slot[rb]) * D;
 #pragma unroll
-    for (int jq = 0; jq < 4; ++jq) {
-      bf16x4 o4;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o4[i] = f2bf(oacc[db][4 * jq + i] * inv);
-      *(bf16x4*)(out + db * 32 + 8 * jq + 4 * half) = o4;
-    }
+      for (int jq = 0; jq < 4; ++jq) {
+        bf16x4 o4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = f2bf(oacc[rb][db][4 * jq + i] * inv);
+        *(bf16x4*)(out + db * 32 + 8 * jq + 4 * half) = o4;
+      }
+  }
 }
 
 // fp32 path: one wavefront per query row; lanes over keys for the scores,
@@ -321,16 +395,22 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillParams p) {
   }
 }
 
+template <int D>
+static void launch_prefill_bf16(const PrefillParams& p, hipStream_t s) {
+  constexpr int TR = PrefillShape<D>::kTileRows;
+  const int tiles_r = (p.S * p.K + TR - 1) / TR;
+  const int tiles_s = (p.S + TR - 1) / TR;
+  const int total = p.B * (p.G * tiles_r + tiles_s);
+  const int nblk = ((total + 7) / 8) * 8;
+  hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3(nblk), dim3(256), 0, s, p, tiles_r, tiles_s);
+}
+
 hipError_t launch_prefill(const PrefillParams& p, int d, bool bf16, hipStream_t s) {
   if (bf16) {
-    const int tiles_r = (p.S * p.K + kTileRows - 1) / kTileRows;
-    const int tiles_s = (p.S + kTileRows - 1) / kTileRows;
-    const int total = p.B * (p.G * tiles_r + tiles_s);
-    const int nblk = ((total + 7) / 8) * 8;
     switch (d) {
-      case 32: hipLaunchKernelGGL(prefill_bf16_kernel<32>, dim3(nblk), dim3(256), 0, s, p, tiles_r, tiles_s); break;
-      case 64: hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3(nblk), dim3(256), 0, s, p, tiles_r, tiles_s); break;
-      case 128: hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3(nblk), dim3(256), 0, s, p, tiles_r, tiles_s); break;
+      case 32: launch_prefill_bf16<32>(p, s); break;
+      case 64: launch_prefill_bf16<64>(p, s); break;
+      case 128: launch_prefill_bf16<128>(p, s); break;
       default: return hipErrorInvalidValue;
     }
   } else {

@@ -5,16 +5,17 @@
 // weights w_m = p_m / sum_{m' in K_g} p_{m'}.
 //
 // Router scores are a skinny product z[T, G*M] = x[T, D] W_r^T. For bf16 it
-// runs on MFMA (16x16x32 bf16 -> fp32): one wavefront owns 16 tokens and all
-// G*M experts, streaming x once from HBM with 16-byte loads; W_r (at most
-// 256 x D bf16) stays hot in L2. The fp32 path is a plain VALU dot product.
+// runs on MFMA (16x16x32 bf16 -> fp32): a workgroup owns 16 tokens and all
+// G*M experts, its wavefronts splitting the features, streaming x once from
+// HBM with 16-byte loads; W_r (at most 256 x D bf16) stays hot in L2. The
+// fp32 path is a plain VALU dot product.
 // The reduction order is fixed, so the emitted logits - and therefore the
 // selection, which is a pure function of them - are deterministic.
 #include "gqe_internal.h"
 
 namespace gqe {
 
-constexpr int kRouteTok = 16;  // tokens per wavefront / workgroup
+constexpr int kRouteTok = 16;  // tokens per workgroup
 
 // Selection epilogue: z for kRouteTok tokens in LDS ([tok][G*M], bias
 // included). One thread per (token, group): TopK by repeated first-maximum
@@ -57,60 +58,70 @@ __device__ void route_select_store(const float* zs, int ntok, int64_t tok0,
   }
 }
 
-// bf16 router scores on MFMA. Block = one wavefront, 16 tokens.
+// bf16 router scores on MFMA. Block = W wavefronts and 16 tokens; wavefront
+// w owns a contiguous slice of the 32-wide feature steps, and the W partial
+// score tiles are summed in LDS in wavefront order (fixed, so the logits are
+// deterministic). Many wavefronts per block keep many 16-byte loads in
+// flight even when there are few tokens (decode).
 // 16x16x32 operand layout: lane l holds A[l%16][8*(l/16) .. +8] (token row,
 // 8 consecutive features) and B[8*(l/16) .. +8][l%16] (expert column); the
 // result D[4*(l/16)+i][l%16] lands in register i.
-__global__ __launch_bounds__(64) void route_bf16_kernel(RouteParams p) {
-  __shared__ float zs[kRouteTok * kMaxRouterCols];
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(1024) void route_bf16_kernel(RouteParams p) {
+  extern __shared__ float zpart[];  // [W][16][GM]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, W = blockDim.x >> 6;
   const int64_t tok0 = (int64_t)blockIdx.x * kRouteTok;
   const int ntok = (int)((p.T - tok0) < kRouteTok ? (p.T - tok0) : kRouteTok);
   const int GM = p.G * p.M;
   const int ntiles = (GM + 15) / 16;
   const int D = p.D;
   const __bf16* x = (const __bf16*)p.x;
-  const __bf16* w = (const __bf16*)p.w;
+  const __bf16* wr = (const __bf16*)p.w;
 
   const int row = lane & 15;
   const int kof = 8 * (lane >> 4);
   const bool tok_ok = row < ntok;
   const __bf16* xrow = x + (tok0 + (tok_ok ? row : 0)) * (int64_t)D;
+  const int nsteps = (D + 31) / 32;
+  const int st0 = (int)((int64_t)w * nsteps / W), st1 = (int)((int64_t)(w + 1) * nsteps / W);
 
   f32x4 acc[kMaxRouterCols / 16];
 #pragma unroll
   for (int e = 0; e < kMaxRouterCols / 16; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const bf16x8 zero8 = {};
-  for (int c0 = 0; c0 < D; c0 += 32) {
+  for (int st = st0; st < st1; ++st) {
     // D is a multiple of 8; a 32-wide step may run past D only in its tail.
-    const int c = c0 + kof;
+    const int c = st * 32 + kof;
     bf16x8 a = (tok_ok && c < D) ? *(const bf16x8*)(xrow + c) : zero8;
 #pragma unroll
     for (int e = 0; e < kMaxRouterCols / 16; ++e) {
       if (e < ntiles) {
         const int ex = e * 16 + row;
-        bf16x8 b = (ex < GM && c < D) ? *(const bf16x8*)(w + (int64_t)ex * D + c) : zero8;
+        bf16x8 b = (ex < GM && c < D) ? *(const bf16x8*)(wr + (int64_t)ex * D + c) : zero8;
         acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[e], 0, 0, 0);
       }
     }
   }
+  float* zw = zpart + (size_t)w * kRouteTok * GM;
 #pragma unroll
   for (int e = 0; e < kMaxRouterCols / 16; ++e) {
     if (e < ntiles) {
       const int ex = e * 16 + row;  // output column = expert
       if (ex < GM) {
-        const float bias = p.bias ? p.bias[ex] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 4 * (lane >> 4) + i;
-          zs[t * GM + ex] = acc[e][i] + bias;
-        }
+        for (int i = 0; i < 4; ++i) zw[(4 * (lane >> 4) + i) * GM + ex] = acc[e][i];
       }
     }
   }
   __syncthreads();
-  route_select_store(zs, ntok, tok0, p);
+  // sum the wavefront partials in order, add the bias; result in slice 0
+  for (int idx = threadIdx.x; idx < kRouteTok * GM; idx += blockDim.x) {
+    float z = zpart[idx];
+    for (int ww = 1; ww < W; ++ww) z += zpart[(size_t)ww * kRouteTok * GM + idx];
+    zpart[idx] = z + (p.bias ? p.bias[idx % GM] : 0.f);
+  }
+  __syncthreads();
+  route_select_store(zpart, ntok, tok0, p);
 }
 
 // fp32 router scores: one thread per (token, expert), sequential fp32 FMAs.
@@ -217,10 +228,17 @@ __global__ __launch_bounds__(64) void list_scatter_kernel(ListParams p) {
 
 hipError_t launch_route(const RouteParams& p, bool bf16, hipStream_t s) {
   const unsigned nblk = (unsigned)((p.T + kRouteTok - 1) / kRouteTok);
-  if (bf16)
-    hipLaunchKernelGGL(route_bf16_kernel, dim3(nblk), dim3(64), 0, s, p);
-  else
+  if (bf16) {
+    // wavefronts per block: about 256 features each, at most 16, and the
+    // [W][16][G*M] fp32 partials within 64 KB of LDS
+    const int GM = p.G * p.M;
+    int W = 1;
+    while (W < 16 && W * 2 * 256 <= p.D && W * 2 * kRouteTok * GM * 4 <= 65536) W *= 2;
+    const size_t lds = (size_t)W * kRouteTok * GM * sizeof(float);
+    hipLaunchKernelGGL(route_bf16_kernel, dim3(nblk), dim3(64 * W), lds, s, p);
+  } else {
     hipLaunchKernelGGL(route_f32_kernel, dim3(nblk), dim3(64), 0, s, p);
+  }
   return hipGetLastError();
 }
 
