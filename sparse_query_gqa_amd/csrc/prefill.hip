@@ -9,16 +9,18 @@
 // group v in 0..G (v == G is the shared head, which reads KV head 0) the rows
 // are the selected (token, slot) pairs, token-major: row r of a routed group
 // is token r/k, slot r%k; row r of the shared group is token r. A workgroup
-// owns 128 consecutive rows, so every tile holds exactly k rows per token
-// whatever the routing skew, and all of them read the same KV head: each
-// K/V tile is staged once in LDS and used by every selected head of the
-// group.
+// owns a tile of consecutive rows (256 for d <= 64, 128 for d = 128), so
+// every tile holds exactly k rows per token whatever the routing skew, and
+// all of them read the same KV head: each K/V block is staged once in LDS and
+// used by every selected head of the group.
 //
-// bf16 path: 4 wavefronts x 32 rows. Per 64-key block each wavefront computes
-// S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16, so that every
-// lane owns one query row in both products (row max, row sum and rescale are
-// per-lane scalars; the two lane halves are combined with one exchange).
-// Online softmax in fp32 with exp2 and scale*log2(e) folded into one FMA.
+// bf16 path: 4 wavefronts x (64 or 32) rows. Per 64-key block each wavefront
+// computes S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16, so
+// that every lane owns one query row in both products (row max, row sum and
+// rescale are per-lane scalars; the two lane halves are combined with one
+// exchange). Online softmax in fp32 with exp2 and scale*log2(e) folded into
+// one FMA; the running max is moved lazily (2^8 headroom); the causal mask
+// only runs on the tile's diagonal blocks.
 #include <type_traits>
 
 #include "gqe_internal.h"
