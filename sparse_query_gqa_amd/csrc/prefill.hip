@@ -19,7 +19,8 @@
 // that every lane owns one query row in both products (row max, row sum and
 // rescale are per-lane scalars; the two lane halves are combined with one
 // exchange). Online softmax in fp32 with exp2 and scale*log2(e) folded into
-// one FMA; the running max is moved lazily (2^8 headroom); the causal mask
+// one FMA; the running max is moved lazily (2^64 headroom, checked through
+// the row sums, so most blocks need no max at all); the causal mask
 // only runs on the tile's diagonal blocks.
 #include <type_traits>
 
@@ -31,11 +32,11 @@ constexpr int kWaves = 4;
 constexpr int kKeyBlock = 64;
 constexpr int kKPad = 8;  // bf16 elements of padding per K row in LDS
 constexpr int kVPad = 4;  // per V^T row: a 34-dword stride keeps 16 lanes' 8-byte reads on distinct banks
-// Lazy rescaling: the running max used for the exponentials is only moved
-// when a row's max grows by more than this many powers of two, so the
-// un-normalised probabilities stay below 2^8 and most key blocks skip the
-// rescale of the output accumulators.
-constexpr float kRescaleLog2 = 8.0f;
+// The reference max used for the exponentials is only moved when a row's
+// partial sum in a block reaches this value (no element can then exceed it),
+// which keeps the fp32 accumulators far from overflow while most key blocks
+// skip both the block max and the rescale of the output accumulators.
+constexpr float kSumLimit = 18446744073709551616.0f;  // 2^64
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -242,28 +243,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, i
             if (sb * 32 + 8 * (j >> 2) + (j & 3) > lim) sacc[rb][sb][j] = -INFINITY;
       }
     }
+    // Exponentials against the reference max m_run, without a per-block max:
+    // probabilities above 1 are fine as long as nothing can overflow fp32
+    // (values below 2^64 keep l and O below 2^64 * 2^17 keys * |v|). A row
+    // whose partial sum reaches 2^64 - or the first block, which sets the
+    // reference - takes the exact path: block max, rescale, recompute.
     u32x4 pf[RB][2][2];  // bf16 P^T fragments, two probabilities per dword
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float bmax = fmaxf(sacc[rb][0][0], sacc[rb][1][0]);
-#pragma unroll
-      for (int j = 1; j < 16; ++j) bmax = fmaxf(bmax, fmaxf(sacc[rb][0][j], sacc[rb][1][j]));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-      // key 0 is in the first block and visible to every row, so m_run is
-      // finite from the first block on; later fully masked rows keep it.
-      const float m_new = fmaxf(m_run[rb], bmax);
-      const bool move = (m_new - m_run[rb]) * c > kRescaleLog2;  // -inf m_run moves
-      if (__builtin_amdgcn_ballot_w64(move) != 0) {
-        __asm__ volatile("" ::: "memory");  // keep this a real branch
-        const float alpha = move ? __builtin_amdgcn_exp2f((m_run[rb] - m_new) * c) : 1.f;
-        if (move) m_run[rb] = m_new;
-        l_run[rb] *= alpha;
-#pragma unroll
-        for (int i = 0; i < DB; ++i)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) oacc[rb][i][j] *= alpha;
-      }
+    float lsum[RB];
+    auto exps = [&](const int rb) __attribute__((always_inline)) {
       const float mc = m_run[rb] * c;
+      float ls = 0.f;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -273,9 +262,39 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, i
           const bf16x2 pr = {f2bf(e0), f2bf(e1)};
           pf[rb][sb][j >> 3][(j & 7) >> 1] = __builtin_bit_cast(uint32_t, pr);
           // row sum of the bf16 probabilities actually used in P V
-          l_run[rb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run[rb], false);
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls, false);
         }
+      lsum[rb] = ls;
+    };
+    bool big = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      exps(rb);
+      big = big || lsum[rb] > kSumLimit;
     }
+    if (kb == 0 || __builtin_amdgcn_ballot_w64(big) != 0) {
+      __asm__ volatile("" ::: "memory");  // keep this a real branch
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float bmax = fmaxf(sacc[rb][0][0], sacc[rb][1][0]);
+#pragma unroll
+        for (int j = 1; j < 16; ++j) bmax = fmaxf(bmax, fmaxf(sacc[rb][0][j], sacc[rb][1][j]));
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+        // key 0 is in the first block and visible to every row, so the
+        // reference is finite from the first block on
+        const float m_new = fmaxf(m_run[rb], bmax);
+        const float alpha = (m_run[rb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run[rb] - m_new) * c);
+        m_run[rb] = m_new;
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) oacc[rb][i][j] *= alpha;
+        exps(rb);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) l_run[rb] += lsum[rb];
     // O^T += V^T P^T. Contraction index of step st of key half sb, lane half h,
     // element t <-> key sb*32 + 16*st + 8*(t/4) + 4*h + t%4 (the S^T layout).
 #pragma unroll
