@@ -18,10 +18,12 @@
 // computes S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16, so
 // that every lane owns one query row in both products (row max, row sum and
 // rescale are per-lane scalars; the two lane halves are combined with one
-// exchange). Online softmax in fp32 with exp2 and scale*log2(e) folded into
-// one FMA; the running max is moved lazily (2^64 headroom, checked through
-// the row sums, so most blocks need no max at all); the causal mask
-// only runs on the tile's diagonal blocks.
+// exchange). Online softmax in fp32 with exp2; the running max is moved
+// lazily (2^64 headroom, checked through the row sums, so most blocks need no
+// max at all); the causal mask only runs on the tile's diagonal blocks. For
+// d <= 64 the softmax is the bottleneck next to the MFMAs, so Q is taken
+// pre-scaled by scale*log2(e) and the reference max enters as the MFMA's
+// initial accumulator: the scores come out of the MFMA as exp2 arguments.
 #include <type_traits>
 
 #include "gqe_internal.h"
@@ -138,6 +140,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, i
 
   // this lane's query rows (one per 32-row block), Q^T fragments for the B
   // operand of S^T = K Q^T: d = 16*s + 8*half + [0,8)
+  const float c = p.scale * 1.44269504088896340736f;  // scale * log2(e)
   int pos[RB], slot[RB];
   bool row_ok[RB];
   bf16x8 qf[RB][KS];
@@ -149,7 +152,15 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, i
     row_info(p, b, v, row_ok[rb] ? r : last_r, pos[rb], slot[rb], head);
     const __bf16* qrow = (const __bf16*)p.q + (((int64_t)b * p.S + pos[rb]) * (p.N + 1) + head) * D;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[rb][s] = *(const bf16x8*)(qrow + 16 * s + 8 * half);
+    for (int s = 0; s < KS; ++s) {
+      qf[rb][s] = *(const bf16x8*)(qrow + 16 * s + 8 * half);
+      if constexpr (RB == 2) {
+        // the two-row-block form takes q * scale * log2(e), rounded to bf16,
+        // so the S^T MFMA yields exp2 arguments directly
+#pragma unroll
+        for (int t = 0; t < 8; ++t) qf[rb][s][t] = f2bf((float)qf[rb][s][t] * c);
+      }
+    }
   }
 
   const __bf16* kbase = (const __bf16*)p.k + ((int64_t)b * p.G + kvh) * (int64_t)p.S * D;
@@ -168,7 +179,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, i
     m_run[rb] = -INFINITY;
     l_run[rb] = 0.f;
   }
-  const float c = p.scale * 1.44269504088896340736f;  // scale * log2(e)
 
   const int nblocks = pos_last / kKeyBlock + 1;
   // K/V loader: thread -> key pair (2*kp, 2*kp+1) and an 8-wide d chunk; V is
@@ -317,21 +327,191 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, i
       }
   };
 
-  // Blocks entirely at or below the tile's first position need no mask; the
+  // Two-row-block form (d <= 64). The two 32-row halves of the wavefront are
+  // software-pipelined within a key block: the S^T MFMAs of half 1 run while
+  // half 0 does its softmax, and the P V MFMAs of half 0 run while half 1
+  // does its softmax. sched_group_barrier fixes the MFMA / VALU interleave.
+  // Scores are kept in log2 units relative to a per-row reference mr: Q is
+  // pre-scaled by scale*log2(e) and the S^T accumulator starts at -mr, so the
+  // MFMA output is the exp2 argument and the softmax needs no FMA per score.
+  // The reference is checked per half, so each half's P is final before its
+  // P V product.
+  float mr[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) mr[rb] = 0.f;
+  auto mask_half = [&](const int kb, const int rb, f32x16 (&sh)[2]) __attribute__((always_inline)) {
+    const int lim = pos[rb] - kb * kKeyBlock - 4 * half;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (sb * 32 + 8 * (j >> 2) + (j & 3) > lim) sh[sb][j] = -INFINITY;
+  };
+  auto exps_half = [&](f32x16 (&sh)[2], u32x4 (&ph)[2][2], float& lsum) __attribute__((always_inline)) {
+    float ls = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        const bf16x2 pr = {f2bf(__builtin_amdgcn_exp2f(sh[sb][j])), f2bf(__builtin_amdgcn_exp2f(sh[sb][j + 1]))};
+        ph[sb][j >> 3][(j & 7) >> 1] = __builtin_bit_cast(uint32_t, pr);
+        ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls, false);  // row sum of the bf16 P used in P V
+      }
+    lsum = ls;
+  };
+  // Exact path of one half: move the reference up to the block max (the first
+  // block sets it), rescale O and l, recompute P.
+  auto exact_half = [&](const int rb, f32x16 (&sh)[2], u32x4 (&ph)[2][2], float& lsum, auto first_tag)
+                        __attribute__((always_inline)) {
+    constexpr bool FIRST = decltype(first_tag)::value;
+    float bmax = fmaxf(sh[0][0], sh[1][0]);
+#pragma unroll
+    for (int j = 1; j < 16; ++j) bmax = fmaxf(bmax, fmaxf(sh[0][j], sh[1][j]));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+    // key 0 is in the first block and visible to every row: bmax is finite there
+    const float delta = FIRST ? bmax : fmaxf(bmax, 0.f);
+    mr[rb] += delta;
+    if constexpr (!FIRST) {
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      l_run[rb] *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[rb][i][j] *= alpha;
+    }
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sh[sb][j] -= delta;
+    exps_half(sh, ph, lsum);
+  };
+  auto block2 = [&](const int kb, const int buf, auto mask_tag, auto first_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool FIRST = decltype(first_tag)::value;
+    constexpr int NS = 2 * KS;   // S^T MFMAs per half
+    constexpr int NPV = 4 * DB;  // P V MFMAs per half
+    constexpr int VS = 8;        // VALU slots after each MFMA
+    f32x16 sh0[2], sh1[2];
+    u32x4 ph0[2][2], ph1[2][2];
+    float ls0, ls1;
+    f32x16 init0, init1;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      init0[j] = FIRST ? 0.f : -mr[0];
+      init1[j] = FIRST ? 0.f : -mr[RB - 1];
+    }
+    bf16x8 kf[2][KS];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kf[sb][s] = *(const bf16x8*)&Ks[buf][sb * 32 + l32][16 * s + 8 * half];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        sh0[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sb][s], qf[0][s], s == 0 ? init0 : sh0[sb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // region: S^T of half 1 || softmax of half 0
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        sh1[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sb][s], qf[RB - 1][s], s == 0 ? init1 : sh1[sb], 0, 0, 0);
+    if constexpr (MASK) mask_half(kb, 0, sh0);
+    if constexpr (FIRST) {
+      exact_half(0, sh0, ph0, ls0, first_tag);
+    } else {
+      exps_half(sh0, ph0, ls0);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, VS, 0);
+      }
+      if (__builtin_amdgcn_ballot_w64(ls0 > kSumLimit) != 0) {
+        __asm__ volatile("" ::: "memory");
+        exact_half(0, sh0, ph0, ls0, first_tag);
+      }
+    }
+    l_run[0] += ls0;
+    // region: P V of half 0 || softmax of half 1. Contraction index of step st
+    // of key half sb, lane half h, element t <-> key sb*32 + 16*st + 8*(t/4) +
+    // 4*h + t%4 (the S^T output layout).
+    bf16x8 vf[2][2][DB];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const __bf16* vr = &Vt[buf][db * 32 + l32][sb * 32 + 16 * st + 4 * half];
+          const u32x2 lo = *(const u32x2*)vr;
+          const u32x2 hi = *(const u32x2*)(vr + 8);
+          const u32x4 vw = {lo[0], lo[1], hi[0], hi[1]};
+          vf[sb][st][db] = __builtin_bit_cast(bf16x8, vw);
+        }
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          oacc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[sb][st][db], __builtin_bit_cast(bf16x8, ph0[sb][st]),
+                                                                oacc[0][db], 0, 0, 0);
+    if constexpr (MASK) mask_half(kb, RB - 1, sh1);
+    if constexpr (FIRST) {
+      exact_half(RB - 1, sh1, ph1, ls1, first_tag);
+    } else {
+      exps_half(sh1, ph1, ls1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8 * DB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2 * VS, 0);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, VS, 0);
+      }
+      if (__builtin_amdgcn_ballot_w64(ls1 > kSumLimit) != 0) {
+        __asm__ volatile("" ::: "memory");
+        exact_half(RB - 1, sh1, ph1, ls1, first_tag);
+      }
+    }
+    l_run[RB - 1] += ls1;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          oacc[RB - 1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              vf[sb][st][db], __builtin_bit_cast(bf16x8, ph1[sb][st]), oacc[RB - 1][db], 0, 0, 0);
+  };
+  auto body = [&](const int kb, const int buf, auto mask_tag, auto first_tag) __attribute__((always_inline)) {
+    if constexpr (RB == 2) block2(kb, buf, mask_tag, first_tag);
+    else block(kb, buf, mask_tag);
+  };
+
+  // The first block sets the reference max, through the exact path; it runs
+  // with the mask, which it needs only in a sequence's first tile. Later
+  // blocks entirely at or below the tile's first position need no mask; the
   // few diagonal blocks after them do, and load their K/V without register
   // prefetch to keep the second copy of the body within the register budget.
+  using kNo = std::integral_constant<bool, false>;
+  using kYes = std::integral_constant<bool, true>;
   const int nfull = min((pos_first + 1) / kKeyBlock, nblocks);
-  int kb = 0;
+  if (1 < nblocks) gload(1);
+  body(0, 0, kYes(), kYes());
+  if (1 < nblocks) lstore(1);
+  __syncthreads();
+  int kb = 1;
   for (; kb < nfull; ++kb) {
     const int buf = kb & 1;
     if (kb + 1 < nblocks) gload(kb + 1);
-    block(kb, buf, std::integral_constant<bool, false>());
+    body(kb, buf, kNo(), kNo());
     if (kb + 1 < nblocks) lstore(buf ^ 1);  // the other buffer: last read before the previous barrier
     __syncthreads();
   }
   for (; kb < nblocks; ++kb) {
     const int buf = kb & 1;
-    block(kb, buf, std::integral_constant<bool, true>());
+    body(kb, buf, kYes(), kNo());
     if (kb + 1 < nblocks) {
       gload(kb + 1);
       lstore(buf ^ 1);
