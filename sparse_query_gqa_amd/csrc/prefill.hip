@@ -43,6 +43,7 @@ constexpr float kSumLimit = 18446744073709551616.0f;  // 2^64
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // 32-row blocks per wavefront for each head dim (64 rows halve the LDS
 // bytes per MFMA FLOP; d=128 keeps 32 rows to stay within 256 VGPRs).
@@ -539,6 +540,353 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, i
   }
 }
 
+// Quarter-pipelined form (d <= 64). A wavefront owns 64 query rows (two
+// 32-row halves h) and each 64-key block splits into two 32-key halves sb,
+// so a block is four 32x32 quarters, taken in the order (sb, h) = (0,0),
+// (0,1), (1,0), (1,1). Quarter t goes through S^T (KS MFMAs), softmax (VALU)
+// and P V (2*DB MFMAs). The steps are software-pipelined across quarters and
+// key blocks: step t issues the S^T MFMAs of quarter t+1, the softmax of
+// quarter t and the P V MFMAs of quarter t-1, so every MFMA has a share of
+// the exponentials beside it. Consecutive quarters belong to different row
+// halves, so a softmax that moves its half's reference only has to rescale
+// an accumulator whose P V products are all issued.
+//
+// K/V blocks go from HBM straight into LDS (global_load_lds_dwordx4, no
+// staging registers), row-major with the 16-byte chunks of each row
+// XOR-swizzled so that neither read pattern has bank conflicts. K fragments are plain 16-byte reads; V^T fragments come from
+// ds_read_b64_tr_b16, which hands each lane one d column of four keys. Blocks
+// rotate through three buffers: block j+2 is loaded while blocks j and j+1
+// are read, with one barrier per block.
+template <int D>
+__global__ __launch_bounds__(256, 2) void prefill_qp_kernel(PrefillParams p, int tiles_r, int tiles_s) {
+  static_assert(D == 32 || D == 64, "head dim");
+  constexpr int kTileRows = 256;
+  constexpr int KS = D / 16;   // MFMA k-steps over d
+  constexpr int DB = D / 32;   // 32-wide d blocks of O^T
+  constexpr int CPR = D / 8;   // 16-byte chunks per key row
+  constexpr int ROWB = 2 * D;  // bytes per key row
+  constexpr int MATB = kKeyBlock * ROWB;  // bytes of one K or V block
+  constexpr int NPW = MATB / 1024 / 4;    // 1 KiB LDS-DMA chunks per wavefront per matrix
+  static_assert(NPW >= 1, "block too small for the LDS-DMA split");
+  constexpr int NBUF = 3;
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF][2][MATB];  // [buffer][K, V]
+
+  const TileCoord tc = tile_of_block(p, tiles_r, tiles_s);
+  if (!tc.valid) return;
+  const int b = tc.b, v = tc.v;
+  const int kvh = (v == p.G) ? 0 : v;
+  const int nrows = (v == p.G) ? p.S : p.S * p.K;
+  const int r0 = tc.tile * kTileRows;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int last_r = min(r0 + kTileRows, nrows) - 1;
+  int pos_last, pos_first, s_, h_;
+  row_info(p, b, v, last_r, pos_last, s_, h_);
+  row_info(p, b, v, r0, pos_first, s_, h_);
+
+  // Q^T fragments (B operand of S^T = K Q^T), pre-scaled by scale*log2(e) and
+  // rounded to bf16, so that S^T comes out in log2 units.
+  const float c = p.scale * 1.44269504088896340736f;
+  int pos[2], slot[2];
+  bool row_ok[2];
+  bf16x8 qf[2][KS];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = r0 + wave * 64 + h * 32 + l32;
+    row_ok[h] = r < nrows;
+    int head;
+    row_info(p, b, v, row_ok[h] ? r : last_r, pos[h], slot[h], head);
+    const __bf16* qrow = (const __bf16*)p.q + (((int64_t)b * p.S + pos[h]) * (p.N + 1) + head) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qf[h][s] = *(const bf16x8*)(qrow + 16 * s + 8 * half);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) qf[h][s][t] = f2bf((float)qf[h][s][t] * c);
+    }
+  }
+  const __bf16* kbase = (const __bf16*)p.k + ((int64_t)b * p.G + kvh) * (int64_t)p.S * D;
+  const __bf16* vbase = (const __bf16*)p.v + ((int64_t)b * p.G + kvh) * (int64_t)p.S * D;
+
+  f32x16 oacc[2][DB];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) oacc[h][i][j] = 0.f;
+  // per row: running sum of P and the reference (log2 units) the scores are taken against
+  float l_run[2] = {0.f, 0.f}, mr[2] = {0.f, 0.f};
+  // -mr of half 0 as a 16-register MFMA accumulator, kept for its S^T
+  // MFMAs; the moves are asm so that the compiler keeps the tuple instead of
+  // re-creating it (16 moves) before every S^T product. It changes only when
+  // the reference moves. Half 1's initial accumulator is built per product:
+  // a second kept tuple would not fit the register budget.
+  f32x16 bias0;
+  auto set_bias = [&](const int h) __attribute__((always_inline)) {
+    const float nm = -mr[h];
+    if (h == 0)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) __asm__("v_mov_b32 %0, %1" : "=v"(bias0[j]) : "v"(nm));
+  };
+  const int nblocks = pos_last / kKeyBlock + 1;
+
+  // Layout of a block in LDS: key row r at r*ROWB, its 16-byte chunk c at
+  // chunk position c ^ swz(r). With 64 four-byte banks two 128-byte rows
+  // share a bank cycle, so swz takes row bits 1..3: the 16 rows of a 16-byte
+  // K read land on distinct (row parity, chunk) pairs, and the 8 rows x 64
+  // bytes of a transposing V read fill each bank exactly twice (bit 1 of the
+  // row flips the 64-byte half). Row offsets that are multiples of 16 leave
+  // swz unchanged, so they fold into instruction offsets.
+  //
+  // Block kb of K and V into buffer bf: lane l of 1 KiB chunk n writes LDS
+  // bytes [1024 n + 16 l, +16), i.e. row 1024 n / ROWB + (16 l) / ROWB,
+  // chunk position (16 l % ROWB) / 16; it loads the source chunk the swizzle
+  // puts there. Keys past the sequence re-read its last key (finite data;
+  // those keys are masked).
+  auto swz = [](int r) { return (((r >> 1) & 7) ^ ((r & 2) << 1)) & (CPR - 1); };
+  constexpr int RPC = 1024 / ROWB;  // key rows per 1 KiB chunk
+  const int dma_r = (16 * lane) / ROWB;
+  const int dma_p = ((16 * lane) % ROWB) / 16;  // chunk position
+  auto dma = [&](const int kb, const int bf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+      const int n = wave * NPW + i;
+      const int rb = n * RPC + dma_r;  // row in the block
+      const int row = min(kb * kKeyBlock + rb, p.S - 1);
+      const int64_t g = (int64_t)row * D + 8 * (dma_p ^ swz(rb));
+      __builtin_amdgcn_global_load_lds(kbase + g, (__attribute__((address_space(3))) void*)(lds[bf][0] + n * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vbase + g, (__attribute__((address_space(3))) void*)(lds[bf][1] + n * 1024), 16, 0, 0);
+    }
+  };
+
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  f32x16 sh[4];        // S^T per quarter (log2 units, relative to mr of its half)
+  u32x4 ph[4][2];      // bf16 P^T fragments per quarter, one per 16-key step
+  float ls[4];         // row sums of the bf16 P per quarter
+  bf16x8 kf[2][KS];    // K fragments by key half
+  bf16x8 vf[2][2][DB]; // V^T fragments by key half, 16-key step and d block
+
+  // K fragment s of key half sb: row sb*32 + l32, chunk 2s + half
+  int k_off[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) k_off[s] = l32 * ROWB + 16 * ((2 * s + half) ^ swz(l32));
+  auto read_k = [&](const int buf, const int sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kf[sb][s] = *(const bf16x8*)(lds[buf][0] + sb * 32 * ROWB + k_off[s]);
+  };
+  // V^T fragment for key half sb, step st, d block db: lane (half, l32) holds
+  // d = db*32 + l32 and contraction element t <-> key sb*32 + 16*st + 8*(t/4) +
+  // 4*half + t%4, the S^T output layout. In a 16-lane group of the transposing
+  // read, source lane i points at key K0 + i/4, d D0 + 4*(i%4), and output
+  // lane i receives keys K0..K0+3 of d D0 + i.
+  const int tr_key = 4 * half + ((lane & 15) >> 2);
+  const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int v_off[2][DB];  // by the 8-key step tt (it changes row bit 3) and d block
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      v_off[tt][db] = (8 * tt + tr_key) * ROWB + 16 * ((4 * db + (tr_d >> 3)) ^ swz(8 * tt + tr_key)) + 2 * (tr_d & 7);
+  auto read_v = [&](const int buf, const int sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        u32x4 vw;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const char* a = lds[buf][1] + (sb * 32 + 16 * st) * ROWB + v_off[tt][db];
+          const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a);
+          const u32x2 w = __builtin_bit_cast(u32x2, x);
+          vw[2 * tt] = w[0];
+          vw[2 * tt + 1] = w[1];
+        }
+        vf[sb][st][db] = __builtin_bit_cast(bf16x8, vw);
+      }
+  };
+  // S^T of quarter q: the accumulator starts at -mr of the quarter's half
+  // (0 for the first block, which sets the reference).
+  auto s_mfma = [&](const int q, auto first_tag) __attribute__((always_inline)) {
+    const int sb = q >> 1, h = q & 1;
+    const f32x16 zero16 = {};
+    f32x16 bias1;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) bias1[j] = -mr[1];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      sh[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          kf[sb][s], qf[h][s], s == 0 ? (decltype(first_tag)::value ? zero16 : (h == 0 ? bias0 : bias1)) : sh[q],
+          0, 0, 0);
+  };
+  auto pv_mfma = [&](const int q) __attribute__((always_inline)) {
+    const int sb = q >> 1, h = q & 1;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        oacc[h][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[sb][st][db], __builtin_bit_cast(bf16x8, ph[q][st]),
+                                                              oacc[h][db], 0, 0, 0);
+  };
+  auto exps = [&](const int q) __attribute__((always_inline)) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+      const bf16x2 pr = {f2bf(__builtin_amdgcn_exp2f(sh[q][j])), f2bf(__builtin_amdgcn_exp2f(sh[q][j + 1]))};
+      ph[q][j >> 3][(j & 7) >> 1] = __builtin_bit_cast(uint32_t, pr);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);  // row sum of the bf16 P used in P V
+    }
+    ls[q] = acc;
+  };
+  // Exact path: move the half's reference up to this quarter's max (the first
+  // block sets it), rescale O and l of that half, recompute P.
+  auto exact = [&](const int q, auto first_tag) __attribute__((always_inline)) {
+    constexpr bool FIRST = decltype(first_tag)::value;
+    const int h = q & 1;
+    float bmax = sh[q][0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) bmax = fmaxf(bmax, sh[q][j]);
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+    // key 0 is visible to every row, so bmax is finite in the first block
+    const float delta = FIRST ? bmax : fmaxf(bmax, 0.f);
+    mr[h] += delta;
+    set_bias(h);
+    if constexpr (!FIRST) {
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      l_run[h] *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[h][i][j] *= alpha;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sh[q][j] -= delta;
+    exps(q);
+  };
+  // Causal mask of quarter q of block kb, only on the tile's diagonal blocks
+  // (a uniform branch kept out of the interleaved region).
+  auto mask = [&](const int q, const int kb, const bool on) __attribute__((always_inline)) {
+    if (on) {
+      __asm__ volatile("" ::: "memory");  // keep this a real branch
+      // key kb*64 + sb*32 + 8*(j/4) + 4*half + j%4 is visible iff key <= pos
+      const int lim = pos[q & 1] - kb * kKeyBlock - (q >> 1) * 32 - 4 * half;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (8 * (j >> 2) + (j & 3) > lim) sh[q][j] = -INFINITY;
+    }
+  };
+  auto softmax = [&](const int q, auto first_tag) __attribute__((always_inline)) {
+    if constexpr (decltype(first_tag)::value) exact(q, first_tag);
+    else exps(q);
+  };
+  // Overflow check of a lazy softmax, then the half's row sum. Ends the step.
+  auto settle = [&](const int q, auto first_tag) __attribute__((always_inline)) {
+    if constexpr (!decltype(first_tag)::value) {
+      if (__builtin_amdgcn_ballot_w64(ls[q] > kSumLimit) != 0) {
+        __asm__ volatile("" ::: "memory");  // keep this a real branch
+        exact(q, first_tag);
+      }
+    }
+    l_run[q & 1] += ls[q];
+  };
+  // MFMA / VALU interleave of one step's region: the LDS reads for the next
+  // step, then one MFMA per VALU group.
+  auto interleave = [&](auto n_mfma) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+    for (int i = 0; i < decltype(n_mfma)::value; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+  };
+  using kNo = std::integral_constant<bool, false>;
+  using kYes = std::integral_constant<bool, true>;
+  using kNS = std::integral_constant<int, KS>;
+  using kNSPV = std::integral_constant<int, KS + 2 * DB>;
+
+  // One key block j (in LDS buffer buf; its quarter 0 S^T is already in sh[0]
+  // and its K fragments of key half 0 in kf[0]). Fragments are read one step
+  // before their first use, into registers whose previous contents died a
+  // step earlier.
+  auto iteration = [&](const int j, const int buf, const int nbuf, const bool masked, auto first_tag,
+                       auto prev_tag) __attribute__((always_inline)) {
+    // step 0: P V(q3 of block j-1) | S^T(q1) | softmax(q0)
+    mask(0, j, masked);
+    read_k(buf, 1);
+    read_v(buf, 0);
+    if constexpr (decltype(prev_tag)::value) pv_mfma(3);
+    s_mfma(1, first_tag);
+    softmax(0, first_tag);
+    if constexpr (decltype(prev_tag)::value) interleave(kNSPV());
+    else interleave(kNS());
+    settle(0, first_tag);
+    // step 1: P V(q0) | S^T(q2) | softmax(q1)
+    mask(1, j, masked);
+    pv_mfma(0);
+    s_mfma(2, kNo());
+    softmax(1, first_tag);
+    interleave(kNSPV());
+    settle(1, first_tag);
+    // step 2: P V(q1) | S^T(q3) | softmax(q2)
+    mask(2, j, masked);
+    read_v(buf, 1);
+    pv_mfma(1);
+    s_mfma(3, kNo());
+    softmax(2, kNo());
+    interleave(kNSPV());
+    settle(2, kNo());
+    // block j+1 (loaded during the previous block) is complete and visible
+    // after the wait and the barrier; block j+2 then goes into the buffer of
+    // block j-1, whose last reader was step 0
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j + 2 < nblocks) dma(j + 2, nbuf == NBUF - 1 ? 0 : nbuf + 1);
+    read_k(nbuf, 0);  // past the last block this reads a stale buffer; the result is unused
+    // step 3: P V(q2) | S^T(q0 of block j+1) | softmax(q3)
+    mask(3, j, masked);
+    pv_mfma(2);
+    s_mfma(0, kNo());
+    softmax(3, kNo());
+    interleave(kNSPV());
+    settle(3, kNo());
+  };
+
+  dma(0, 0);
+  if (1 < nblocks) dma(1, 1);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  read_k(0, 0);
+  s_mfma(0, kYes());
+  // Blocks at or below the tile's first position need no mask. The first
+  // block sets the references.
+  const int nfull = min((pos_first + 1) / kKeyBlock, nblocks);
+  iteration(0, 0, 1, nfull < 1, kYes(), kNo());
+  for (int j = 1, buf = 1; j < nblocks; ++j) {
+    const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;
+    iteration(j, buf, nbuf, j >= nfull, kNo(), kYes());
+    buf = nbuf;
+  }
+  pv_mfma(3);
+
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float l_tot = l_run[h] + __shfl_xor(l_run[h], 32, 64);
+    if (!row_ok[h]) continue;
+    const float inv = 1.f / l_tot;
+    __bf16* out = (v == p.G)
+                      ? (__bf16*)p.o_s + ((int64_t)b * p.S + pos[h]) * D
+                      : (__bf16*)p.o_r + ((((int64_t)b * p.S + pos[h]) * p.G + v) * p.K + slot[h]) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        bf16x4 o4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = f2bf(oacc[h][db][4 * jq + i] * inv);
+        *(bf16x4*)(out + db * 32 + 8 * jq + 4 * half) = o4;
+      }
+  }
+}
+
 // fp32 path: one wavefront per query row; lanes over keys for the scores,
 // lanes over d for P V. Plain fp32 arithmetic throughout.
 template <int D>
@@ -603,7 +951,12 @@ static void launch_prefill_bf16(const PrefillParams& p, hipStream_t s) {
   const int tiles_s = (p.S + TR - 1) / TR;
   const int total = p.B * (p.G * tiles_r + tiles_s);
   const int nblk = ((total + 7) / 8) * 8;
-  hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3(nblk), dim3(256), 0, s, p, tiles_r, tiles_s);
+  if constexpr (D <= 64) {
+    static_assert(PrefillShape<D>::kTileRows == 256, "quarter-pipelined tiles are 256 rows");
+    hipLaunchKernelGGL(prefill_qp_kernel<D>, dim3(nblk), dim3(256), 0, s, p, tiles_r, tiles_s);
+  } else {
+    hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3(nblk), dim3(256), 0, s, p, tiles_r, tiles_s);
+  }
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int d, bool bf16, hipStream_t s) {
