@@ -9,31 +9,30 @@
 // group v in 0..G (v == G is the shared head, which reads KV head 0) the rows
 // are the selected (token, slot) pairs, token-major: row r of a routed group
 // is token r/k, slot r%k; row r of the shared group is token r. A workgroup
-// owns a tile of consecutive rows (256 for d <= 64, 128 for d = 128), so
-// every tile holds exactly k rows per token whatever the routing skew, and
-// all of them read the same KV head: each K/V block is staged once in LDS and
-// used by every selected head of the group.
+// owns a tile of 256 consecutive rows, so every tile holds exactly k rows per
+// token whatever the routing skew, and all of them read the same KV head:
+// each K/V block is staged once in LDS and used by every selected head of the
+// group.
 //
-// bf16 path: 4 wavefronts x (64 or 32) rows. Per 64-key block each wavefront
-// computes S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16, so
-// that every lane owns one query row in both products (row max, row sum and
-// rescale are per-lane scalars; the two lane halves are combined with one
-// exchange). Online softmax in fp32 with exp2; the running max is moved
-// lazily (2^64 headroom, checked through the row sums, so most blocks need no
-// max at all); the causal mask only runs on the tile's diagonal blocks. For
-// d <= 64 the softmax is the bottleneck next to the MFMAs, so Q is taken
-// pre-scaled by scale*log2(e) and the reference max enters as the MFMA's
-// initial accumulator: the scores come out of the MFMA as exp2 arguments.
+// bf16 path. Per 64-key block a wavefront computes S^T = K Q^T and
+// O^T += V^T P^T with v_mfma_f32_32x32x16_bf16, so that every lane owns one
+// query row in both products (row max, row sum and rescale are per-lane
+// scalars; the two lane halves are combined with one exchange). Q is taken
+// pre-scaled by scale*log2(e) and the row's reference max enters as the S^T
+// MFMA's initial accumulator, so the scores come out of the MFMA as exp2
+// arguments. The online softmax (fp32, exp2) moves the reference lazily: 2^64
+// of headroom, checked through the row sums, so most blocks need no max at
+// all. The causal mask only runs on the tile's diagonal blocks. Two kernels:
+// 64 rows per wavefront for d <= 64 and 32 rows per wavefront for d = 128,
+// both software-pipelined so that MFMAs and the softmax of neighbouring
+// 32x32 score tiles overlap.
 #include <type_traits>
 
 #include "gqe_internal.h"
 
 namespace gqe {
 
-constexpr int kWaves = 4;
 constexpr int kKeyBlock = 64;
-constexpr int kKPad = 8;  // bf16 elements of padding per K row in LDS
-constexpr int kVPad = 4;  // per V^T row: a 34-dword stride keeps 16 lanes' 8-byte reads on distinct banks
 // The reference max used for the exponentials is only moved when a row's
 // partial sum in a block reaches this value (no element can then exceed it),
 // which keeps the fp32 accumulators far from overflow while most key blocks
@@ -44,14 +43,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// 32-row blocks per wavefront for each head dim (64 rows halve the LDS
-// bytes per MFMA FLOP; d=128 keeps 32 rows to stay within 256 VGPRs).
-template <int D>
-struct PrefillShape {
-  static constexpr int RB = (D <= 64) ? 2 : 1;
-  static constexpr int kTileRows = kWaves * 32 * RB;
-};
 
 struct TileCoord {
   int b, v, tile;  // tile index within (b, v)
@@ -110,436 +101,6 @@ __device__ __forceinline__ void row_info(const PrefillParams& p, int b, int v, i
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, int tiles_r,
-                                                              int tiles_s) {
-  static_assert(D == 32 || D == 64 || D == 128, "head dim");
-  constexpr int RB = PrefillShape<D>::RB;                // 32-row blocks per wave
-  constexpr int kTileRows = PrefillShape<D>::kTileRows;
-  constexpr int KS = D / 16;                             // MFMA k-steps over d
-  constexpr int DB = D / 32;                             // 32-wide d blocks of O^T
-  constexpr int DCH = D / 8;                             // 8-element chunks per key row
-  constexpr int LD_PASSES = (kKeyBlock / 2) * DCH / 256 > 0 ? (kKeyBlock / 2) * DCH / 256 : 1;
-  constexpr int LD_THREADS = (kKeyBlock / 2) * DCH / LD_PASSES;  // threads that load
-  __shared__ __bf16 Ks[2][kKeyBlock][D + kKPad];
-  __shared__ __bf16 Vt[2][D][kKeyBlock + kVPad];
-
-  const TileCoord tc = tile_of_block(p, tiles_r, tiles_s);
-  if (!tc.valid) return;
-  const int b = tc.b, v = tc.v;
-  const int kvh = (v == p.G) ? 0 : v;
-  const int nrows = (v == p.G) ? p.S : p.S * p.K;
-  const int r0 = tc.tile * kTileRows;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int half = lane >> 5, l32 = lane & 31;
-
-  const int last_r = min(r0 + kTileRows, nrows) - 1;
-  int pos_last, pos_first, s_, h_;
-  row_info(p, b, v, last_r, pos_last, s_, h_);
-  row_info(p, b, v, r0, pos_first, s_, h_);
-
-  // this lane's query rows (one per 32-row block), Q^T fragments for the B
-  // operand of S^T = K Q^T: d = 16*s + 8*half + [0,8)
-  const float c = p.scale * 1.44269504088896340736f;  // scale * log2(e)
-  int pos[RB], slot[RB];
-  bool row_ok[RB];
-  bf16x8 qf[RB][KS];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = r0 + wave * 32 * RB + rb * 32 + l32;
-    row_ok[rb] = r < nrows;
-    int head;
-    row_info(p, b, v, row_ok[rb] ? r : last_r, pos[rb], slot[rb], head);
-    const __bf16* qrow = (const __bf16*)p.q + (((int64_t)b * p.S + pos[rb]) * (p.N + 1) + head) * D;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      qf[rb][s] = *(const bf16x8*)(qrow + 16 * s + 8 * half);
-      if constexpr (RB == 2) {
-        // the two-row-block form takes q * scale * log2(e), rounded to bf16,
-        // so the S^T MFMA yields exp2 arguments directly
-#pragma unroll
-        for (int t = 0; t < 8; ++t) qf[rb][s][t] = f2bf((float)qf[rb][s][t] * c);
-      }
-    }
-  }
-
-  const __bf16* kbase = (const __bf16*)p.k + ((int64_t)b * p.G + kvh) * (int64_t)p.S * D;
-  const __bf16* vbase = (const __bf16*)p.v + ((int64_t)b * p.G + kvh) * (int64_t)p.S * D;
-
-  f32x16 oacc[RB][DB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) oacc[rb][i][j] = 0.f;
-  float m_run[RB], l_run[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = -INFINITY;
-    l_run[rb] = 0.f;
-  }
-
-  const int nblocks = pos_last / kKeyBlock + 1;
-  // K/V loader: thread -> key pair (2*kp, 2*kp+1) and an 8-wide d chunk; V is
-  // written transposed as packed pairs of keys (4-byte LDS stores).
-  const int ld_kp = tid / DCH, ld_d0 = (tid % DCH) * 8;
-  const bool ld_on = tid < LD_THREADS;
-  bf16x8 kreg[LD_PASSES][2], vreg[LD_PASSES][2];
-  const bf16x8 zero8 = {};
-
-  auto gload = [&](int kb) {
-#pragma unroll
-    for (int ps = 0; ps < LD_PASSES; ++ps)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int gk = kb * kKeyBlock + 2 * (ld_kp + ps * (LD_THREADS / DCH)) + e;
-        if (ld_on && gk < p.S) {
-          kreg[ps][e] = *(const bf16x8*)(kbase + (int64_t)gk * D + ld_d0);
-          vreg[ps][e] = *(const bf16x8*)(vbase + (int64_t)gk * D + ld_d0);
-        } else {
-          kreg[ps][e] = zero8;
-          vreg[ps][e] = zero8;
-        }
-      }
-  };
-  auto lstore = [&](int buf) {
-    if (!ld_on) return;
-#pragma unroll
-    for (int ps = 0; ps < LD_PASSES; ++ps) {
-      const int key = 2 * (ld_kp + ps * (LD_THREADS / DCH));
-      *(bf16x8*)&Ks[buf][key][ld_d0] = kreg[ps][0];
-      *(bf16x8*)&Ks[buf][key + 1][ld_d0] = kreg[ps][1];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bf16x2 pr = {vreg[ps][0][i], vreg[ps][1][i]};
-        *(bf16x2*)&Vt[buf][ld_d0 + i][key] = pr;
-      }
-    }
-  };
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  // One key block: S^T = K Q^T, (causal mask), online softmax, O^T += V^T P^T.
-  // MASK is a compile-time flag: only the diagonal blocks of the tile pay
-  // for the causal mask.
-  auto block = [&](const int kb, const int buf, auto mask_tag) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    // S^T for the two 32-key halves of the block; each K fragment read from
-    // LDS feeds every row block of the wave.
-    f32x16 sacc[RB][2];
-    const f32x16 zero16 = {};
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const bf16x8 kf = *(const bf16x8*)&Ks[buf][sb * 32 + l32][16 * s + 8 * half];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          sacc[rb][sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[rb][s], s == 0 ? zero16 : sacc[rb][sb], 0, 0, 0);
-      }
-    if constexpr (MASK) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        // key = kb*64 + sb*32 + 8*(j/4) + 4*half + j%4 is visible iff key <= pos
-        const int lim = pos[rb] - kb * kKeyBlock - 4 * half;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j)
-            if (sb * 32 + 8 * (j >> 2) + (j & 3) > lim) sacc[rb][sb][j] = -INFINITY;
-      }
-    }
-    // Exponentials against the reference max m_run, without a per-block max:
-    // probabilities above 1 are fine as long as nothing can overflow fp32
-    // (values below 2^64 keep l and O below 2^64 * 2^17 keys * |v|). A row
-    // whose partial sum reaches 2^64 - or the first block, which sets the
-    // reference - takes the exact path: block max, rescale, recompute.
-    u32x4 pf[RB][2][2];  // bf16 P^T fragments, two probabilities per dword
-    float lsum[RB];
-    auto exps = [&](const int rb) __attribute__((always_inline)) {
-      const float mc = m_run[rb] * c;
-      float ls = 0.f;
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) {
-          const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[rb][sb][j], c, -mc));
-          const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[rb][sb][j + 1], c, -mc));
-          const bf16x2 pr = {f2bf(e0), f2bf(e1)};
-          pf[rb][sb][j >> 3][(j & 7) >> 1] = __builtin_bit_cast(uint32_t, pr);
-          // row sum of the bf16 probabilities actually used in P V
-          ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls, false);
-        }
-      lsum[rb] = ls;
-    };
-    bool big = false;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      exps(rb);
-      big = big || lsum[rb] > kSumLimit;
-    }
-    if (kb == 0 || __builtin_amdgcn_ballot_w64(big) != 0) {
-      __asm__ volatile("" ::: "memory");  // keep this a real branch
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        float bmax = fmaxf(sacc[rb][0][0], sacc[rb][1][0]);
-#pragma unroll
-        for (int j = 1; j < 16; ++j) bmax = fmaxf(bmax, fmaxf(sacc[rb][0][j], sacc[rb][1][j]));
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-        // key 0 is in the first block and visible to every row, so the
-        // reference is finite from the first block on
-        const float m_new = fmaxf(m_run[rb], bmax);
-        const float alpha = (m_run[rb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run[rb] - m_new) * c);
-        m_run[rb] = m_new;
-        l_run[rb] *= alpha;
-#pragma unroll
-        for (int i = 0; i < DB; ++i)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) oacc[rb][i][j] *= alpha;
-        exps(rb);
-      }
-    }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) l_run[rb] += lsum[rb];
-    // O^T += V^T P^T. Contraction index of step st of key half sb, lane half h,
-    // element t <-> key sb*32 + 16*st + 8*(t/4) + 4*h + t%4 (the S^T layout).
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int kc = sb * 32 + 16 * st + 4 * half;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const __bf16* vr = &Vt[buf][db * 32 + l32][kc];
-          const u32x2 lo = *(const u32x2*)vr;
-          const u32x2 hi = *(const u32x2*)(vr + 8);
-          const u32x4 vw = {lo[0], lo[1], hi[0], hi[1]};
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, vw);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                vf, __builtin_bit_cast(bf16x8, pf[rb][sb][st]), oacc[rb][db], 0, 0, 0);
-        }
-      }
-  };
-
-  // Two-row-block form (d <= 64). The two 32-row halves of the wavefront are
-  // software-pipelined within a key block: the S^T MFMAs of half 1 run while
-  // half 0 does its softmax, and the P V MFMAs of half 0 run while half 1
-  // does its softmax. sched_group_barrier fixes the MFMA / VALU interleave.
-  // Scores are kept in log2 units relative to a per-row reference mr: Q is
-  // pre-scaled by scale*log2(e) and the S^T accumulator starts at -mr, so the
-  // MFMA output is the exp2 argument and the softmax needs no FMA per score.
-  // The reference is checked per half, so each half's P is final before its
-  // P V product.
-  float mr[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) mr[rb] = 0.f;
-  auto mask_half = [&](const int kb, const int rb, f32x16 (&sh)[2]) __attribute__((always_inline)) {
-    const int lim = pos[rb] - kb * kKeyBlock - 4 * half;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (sb * 32 + 8 * (j >> 2) + (j & 3) > lim) sh[sb][j] = -INFINITY;
-  };
-  auto exps_half = [&](f32x16 (&sh)[2], u32x4 (&ph)[2][2], float& lsum) __attribute__((always_inline)) {
-    float ls = 0.f;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) {
-        const bf16x2 pr = {f2bf(__builtin_amdgcn_exp2f(sh[sb][j])), f2bf(__builtin_amdgcn_exp2f(sh[sb][j + 1]))};
-        ph[sb][j >> 3][(j & 7) >> 1] = __builtin_bit_cast(uint32_t, pr);
-        ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls, false);  // row sum of the bf16 P used in P V
-      }
-    lsum = ls;
-  };
-  // Exact path of one half: move the reference up to the block max (the first
-  // block sets it), rescale O and l, recompute P.
-  auto exact_half = [&](const int rb, f32x16 (&sh)[2], u32x4 (&ph)[2][2], float& lsum, auto first_tag)
-                        __attribute__((always_inline)) {
-    constexpr bool FIRST = decltype(first_tag)::value;
-    float bmax = fmaxf(sh[0][0], sh[1][0]);
-#pragma unroll
-    for (int j = 1; j < 16; ++j) bmax = fmaxf(bmax, fmaxf(sh[0][j], sh[1][j]));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-    // key 0 is in the first block and visible to every row: bmax is finite there
-    const float delta = FIRST ? bmax : fmaxf(bmax, 0.f);
-    mr[rb] += delta;
-    if constexpr (!FIRST) {
-      const float alpha = __builtin_amdgcn_exp2f(-delta);
-      l_run[rb] *= alpha;
-#pragma unroll
-      for (int i = 0; i < DB; ++i)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[rb][i][j] *= alpha;
-    }
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sh[sb][j] -= delta;
-    exps_half(sh, ph, lsum);
-  };
-  auto block2 = [&](const int kb, const int buf, auto mask_tag, auto first_tag) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr bool FIRST = decltype(first_tag)::value;
-    constexpr int NS = 2 * KS;   // S^T MFMAs per half
-    constexpr int NPV = 4 * DB;  // P V MFMAs per half
-    constexpr int VS = 8;        // VALU slots after each MFMA
-    f32x16 sh0[2], sh1[2];
-    u32x4 ph0[2][2], ph1[2][2];
-    float ls0, ls1;
-    f32x16 init0, init1;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      init0[j] = FIRST ? 0.f : -mr[0];
-      init1[j] = FIRST ? 0.f : -mr[RB - 1];
-    }
-    bf16x8 kf[2][KS];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int s = 0; s < KS; ++s) kf[sb][s] = *(const bf16x8*)&Ks[buf][sb * 32 + l32][16 * s + 8 * half];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        sh0[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sb][s], qf[0][s], s == 0 ? init0 : sh0[sb], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    // region: S^T of half 1 || softmax of half 0
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        sh1[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sb][s], qf[RB - 1][s], s == 0 ? init1 : sh1[sb], 0, 0, 0);
-    if constexpr (MASK) mask_half(kb, 0, sh0);
-    if constexpr (FIRST) {
-      exact_half(0, sh0, ph0, ls0, first_tag);
-    } else {
-      exps_half(sh0, ph0, ls0);
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, VS, 0);
-      }
-      if (__builtin_amdgcn_ballot_w64(ls0 > kSumLimit) != 0) {
-        __asm__ volatile("" ::: "memory");
-        exact_half(0, sh0, ph0, ls0, first_tag);
-      }
-    }
-    l_run[0] += ls0;
-    // region: P V of half 0 || softmax of half 1. Contraction index of step st
-    // of key half sb, lane half h, element t <-> key sb*32 + 16*st + 8*(t/4) +
-    // 4*h + t%4 (the S^T output layout).
-    bf16x8 vf[2][2][DB];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const __bf16* vr = &Vt[buf][db * 32 + l32][sb * 32 + 16 * st + 4 * half];
-          const u32x2 lo = *(const u32x2*)vr;
-          const u32x2 hi = *(const u32x2*)(vr + 8);
-          const u32x4 vw = {lo[0], lo[1], hi[0], hi[1]};
-          vf[sb][st][db] = __builtin_bit_cast(bf16x8, vw);
-        }
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          oacc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[sb][st][db], __builtin_bit_cast(bf16x8, ph0[sb][st]),
-                                                                oacc[0][db], 0, 0, 0);
-    if constexpr (MASK) mask_half(kb, RB - 1, sh1);
-    if constexpr (FIRST) {
-      exact_half(RB - 1, sh1, ph1, ls1, first_tag);
-    } else {
-      exps_half(sh1, ph1, ls1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 8 * DB, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2 * VS, 0);
-#pragma unroll
-      for (int i = 0; i < NPV; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, VS, 0);
-      }
-      if (__builtin_amdgcn_ballot_w64(ls1 > kSumLimit) != 0) {
-        __asm__ volatile("" ::: "memory");
-        exact_half(RB - 1, sh1, ph1, ls1, first_tag);
-      }
-    }
-    l_run[RB - 1] += ls1;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          oacc[RB - 1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              vf[sb][st][db], __builtin_bit_cast(bf16x8, ph1[sb][st]), oacc[RB - 1][db], 0, 0, 0);
-  };
-  auto body = [&](const int kb, const int buf, auto mask_tag, auto first_tag) __attribute__((always_inline)) {
-    if constexpr (RB == 2) block2(kb, buf, mask_tag, first_tag);
-    else block(kb, buf, mask_tag);
-  };
-
-  // The first block sets the reference max, through the exact path; it runs
-  // with the mask, which it needs only in a sequence's first tile. Later
-  // blocks entirely at or below the tile's first position need no mask; the
-  // few diagonal blocks after them do, and load their K/V without register
-  // prefetch to keep the second copy of the body within the register budget.
-  using kNo = std::integral_constant<bool, false>;
-  using kYes = std::integral_constant<bool, true>;
-  const int nfull = min((pos_first + 1) / kKeyBlock, nblocks);
-  if (1 < nblocks) gload(1);
-  body(0, 0, kYes(), kYes());
-  if (1 < nblocks) lstore(1);
-  __syncthreads();
-  int kb = 1;
-  for (; kb < nfull; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nblocks) gload(kb + 1);
-    body(kb, buf, kNo(), kNo());
-    if (kb + 1 < nblocks) lstore(buf ^ 1);  // the other buffer: last read before the previous barrier
-    __syncthreads();
-  }
-  for (; kb < nblocks; ++kb) {
-    const int buf = kb & 1;
-    body(kb, buf, kYes(), kNo());
-    if (kb + 1 < nblocks) {
-      gload(kb + 1);
-      lstore(buf ^ 1);
-    }
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 32, 64);
-    if (!row_ok[rb]) continue;
-    const float inv = 1.f / l_tot;
-    __bf16* out = (v == p.G)
-                      ? (__bf16*)p.o_s + ((int64_t)b * p.S + pos[rb]) * D
-                      : (__bf16*)p.o_r + ((((int64_t)b * p.S + pos[rb]) * p.G + v) * p.K + slot[rb]) * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        bf16x4 o4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o4[i] = f2bf(oacc[rb][db][4 * jq + i] * inv);
-        *(bf16x4*)(out + db * 32 + 8 * jq + 4 * half) = o4;
-      }
-  }
-}
-
 // Quarter-pipelined form (d <= 64). A wavefront owns 64 query rows (two
 // 32-row halves h) and each 64-key block splits into two 32-key halves sb,
 // so a block is four 32x32 quarters, taken in the order (sb, h) = (0,0),
@@ -553,7 +114,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillParams p, i
 //
 // K/V blocks go from HBM straight into LDS (global_load_lds_dwordx4, no
 // staging registers), row-major with the 16-byte chunks of each row
-// XOR-swizzled so that neither read pattern has bank conflicts. K fragments are plain 16-byte reads; V^T fragments come from
+// XOR-swizzled so that neither read pattern has bank conflicts. K fragments
+// are plain 16-byte reads; V^T fragments come from
 // ds_read_b64_tr_b16, which hands each lane one d column of four keys. Blocks
 // rotate through three buffers: block j+2 is loaded while blocks j and j+1
 // are read, with one barrier per block.
@@ -887,6 +449,282 @@ __global__ __launch_bounds__(256, 2) void prefill_qp_kernel(PrefillParams p, int
   }
 }
 
+// Head dim 128. A wavefront owns 32 query rows and a workgroup of 8
+// wavefronts owns a 256-row tile. Each 64-key block is two 32-key halves;
+// half t (block t/2, key half t%2) goes through S^T (8 MFMAs), softmax and
+// P V (8 MFMAs), pipelined as in the quarter form: step t issues the P V
+// MFMAs of half t-1, the S^T MFMAs of half t+1 and the softmax of half t.
+// Consecutive halves belong to the same rows, so a reference move in step t
+// also shifts the S^T of half t+1, which that step already computed.
+//
+// K/V go through LDS-DMA into three 32 KiB buffers (one workgroup per CU).
+// Rows are 256 bytes, so every row covers all 64 banks; the chunk swizzle
+// swaps the two 2-bit fields of the row's low 4 bits, which makes a 16-byte
+// K read over 16 rows and a transposing V read over 8 rows x 64 bytes both
+// conflict-free.
+template <int D>
+__global__ __launch_bounds__(512, 1) void prefill_d128_kernel(PrefillParams p, int tiles_r, int tiles_s) {
+  static_assert(D == 128, "head dim");
+  constexpr int kWaves8 = 8;
+  constexpr int kTileRows = 32 * kWaves8;
+  constexpr int KS = D / 16;   // MFMA k-steps over d
+  constexpr int DB = D / 32;   // 32-wide d blocks of O^T
+  constexpr int ROWB = 2 * D;  // bytes per key row
+  constexpr int MATB = kKeyBlock * ROWB;        // bytes of one K or V block
+  constexpr int NPW = MATB / 1024 / kWaves8;    // 1 KiB LDS-DMA chunks per wavefront per matrix
+  static_assert(NPW >= 1, "block too small for the LDS-DMA split");
+  constexpr int NBUF = 3;
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF][2][MATB];  // [buffer][K, V]
+
+  const TileCoord tc = tile_of_block(p, tiles_r, tiles_s);
+  if (!tc.valid) return;
+  const int b = tc.b, v = tc.v;
+  const int kvh = (v == p.G) ? 0 : v;
+  const int nrows = (v == p.G) ? p.S : p.S * p.K;
+  const int r0 = tc.tile * kTileRows;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int last_r = min(r0 + kTileRows, nrows) - 1;
+  int pos_last, pos_first, s_, h_;
+  row_info(p, b, v, last_r, pos_last, s_, h_);
+  row_info(p, b, v, r0, pos_first, s_, h_);
+
+  // Q^T fragments, pre-scaled by scale*log2(e) and rounded to bf16
+  const float c = p.scale * 1.44269504088896340736f;
+  int pos, slot, head;
+  const int r = r0 + wave * 32 + l32;
+  const bool row_ok = r < nrows;
+  row_info(p, b, v, row_ok ? r : last_r, pos, slot, head);
+  bf16x8 qf[KS];
+  {
+    const __bf16* qrow = (const __bf16*)p.q + (((int64_t)b * p.S + pos) * (p.N + 1) + head) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qf[s] = *(const bf16x8*)(qrow + 16 * s + 8 * half);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) qf[s][t] = f2bf((float)qf[s][t] * c);
+    }
+  }
+  const __bf16* kbase = (const __bf16*)p.k + ((int64_t)b * p.G + kvh) * (int64_t)p.S * D;
+  const __bf16* vbase = (const __bf16*)p.v + ((int64_t)b * p.G + kvh) * (int64_t)p.S * D;
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) oacc[i][j] = 0.f;
+  float l_run = 0.f, mr = 0.f;  // running sum of P and the reference (log2 units)
+  const int nblocks = pos_last / kKeyBlock + 1;
+
+  // chunk position of 16-byte chunk c in row r is c ^ swz(r)
+  auto swz = [](int rr) { return ((rr & 3) << 2) | ((rr >> 2) & 3); };
+  constexpr int RPC = 1024 / ROWB;  // key rows per 1 KiB chunk
+  const int dma_r = (16 * lane) / ROWB;
+  const int dma_p = ((16 * lane) % ROWB) / 16;
+  auto dma = [&](const int kb, const int bf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+      const int n = wave * NPW + i;
+      const int rb = n * RPC + dma_r;
+      const int row = min(kb * kKeyBlock + rb, p.S - 1);  // past the sequence: its last key (masked)
+      const int64_t g = (int64_t)row * D + 8 * (dma_p ^ swz(rb));
+      __builtin_amdgcn_global_load_lds(kbase + g, (__attribute__((address_space(3))) void*)(lds[bf][0] + n * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vbase + g, (__attribute__((address_space(3))) void*)(lds[bf][1] + n * 1024), 16, 0, 0);
+    }
+  };
+
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  f32x16 sh[2];      // S^T of the current and the next key half (log2 units, relative to mr)
+  u32x4 ph[2][2];    // bf16 P^T fragments of a key half, one per 16-key step
+  float ls[2];       // row sums of the bf16 P of a key half
+  bf16x8 kf[KS];     // K fragments of one key half
+  bf16x8 vf[2][DB];  // V^T fragments of one key half, by 16-key step and d block
+
+  // K fragment s of key half sb: row sb*32 + l32, chunk 2s + half
+  int k_off[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) k_off[s] = l32 * ROWB + 16 * ((2 * s + half) ^ swz(l32));
+  auto read_k = [&](const int buf, const int sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kf[s] = *(const bf16x8*)(lds[buf][0] + sb * 32 * ROWB + k_off[s]);
+  };
+  // V^T fragments: as in the quarter form (lane (half, l32) holds d = db*32 +
+  // l32, contraction element t <-> key sb*32 + 16*st + 8*(t/4) + 4*half + t%4)
+  const int tr_key = 4 * half + ((lane & 15) >> 2);
+  const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int v_off[2][DB];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      v_off[tt][db] = (8 * tt + tr_key) * ROWB + 16 * ((4 * db + (tr_d >> 3)) ^ swz(8 * tt + tr_key)) + 2 * (tr_d & 7);
+  auto read_v = [&](const int buf, const int sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        u32x4 vw;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const char* a = lds[buf][1] + (sb * 32 + 16 * st) * ROWB + v_off[tt][db];
+          const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a);
+          const u32x2 w = __builtin_bit_cast(u32x2, x);
+          vw[2 * tt] = w[0];
+          vw[2 * tt + 1] = w[1];
+        }
+        vf[st][db] = __builtin_bit_cast(bf16x8, vw);
+      }
+  };
+  // S^T of a key half into slot i; the accumulator starts at -mr (0 in the
+  // first block, which sets the reference)
+  auto s_mfma = [&](const int i, auto first_tag) __attribute__((always_inline)) {
+    f32x16 init;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) init[j] = decltype(first_tag)::value ? 0.f : -mr;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      sh[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], s == 0 ? init : sh[i], 0, 0, 0);
+  };
+  auto pv_mfma = [&](const int i) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st][db], __builtin_bit_cast(bf16x8, ph[i][st]),
+                                                           oacc[db], 0, 0, 0);
+  };
+  auto exps = [&](const int i) __attribute__((always_inline)) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+      const bf16x2 pr = {f2bf(__builtin_amdgcn_exp2f(sh[i][j])), f2bf(__builtin_amdgcn_exp2f(sh[i][j + 1]))};
+      ph[i][j >> 3][(j & 7) >> 1] = __builtin_bit_cast(uint32_t, pr);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);  // row sum of the bf16 P used in P V
+    }
+    ls[i] = acc;
+  };
+  // Exact path: move the reference up to this half's max (the first block
+  // sets it), rescale O and l, shift the next half's S^T, recompute P.
+  auto exact = [&](const int i, auto first_tag) __attribute__((always_inline)) {
+    constexpr bool FIRST = decltype(first_tag)::value;
+    float bmax = sh[i][0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) bmax = fmaxf(bmax, sh[i][j]);
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+    // key 0 is visible to every row, so bmax is finite in the first block
+    const float delta = FIRST ? bmax : fmaxf(bmax, 0.f);
+    mr += delta;
+    if constexpr (!FIRST) {
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      sh[i][j] -= delta;
+      sh[i ^ 1][j] -= delta;
+    }
+    exps(i);
+  };
+  auto mask = [&](const int i, const int kb, const bool on) __attribute__((always_inline)) {
+    if (on) {
+      __asm__ volatile("" ::: "memory");  // keep this a real branch
+      // key kb*64 + sb*32 + 8*(j/4) + 4*half + j%4 is visible iff key <= pos
+      const int lim = pos - kb * kKeyBlock - i * 32 - 4 * half;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (8 * (j >> 2) + (j & 3) > lim) sh[i][j] = -INFINITY;
+    }
+  };
+  auto settle = [&](const int i, auto first_tag) __attribute__((always_inline)) {
+    if constexpr (decltype(first_tag)::value) {
+      exact(i, first_tag);
+    } else if (__builtin_amdgcn_ballot_w64(ls[i] > kSumLimit) != 0) {
+      __asm__ volatile("" ::: "memory");  // keep this a real branch
+      exact(i, first_tag);
+    }
+    l_run += ls[i];
+  };
+  auto interleave = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+#pragma unroll
+    for (int i = 0; i < KS + 2 * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+  };
+  using kNo = std::integral_constant<bool, false>;
+  using kYes = std::integral_constant<bool, true>;
+
+  // One key block j in buffer buf. On entry sh[0] holds S^T of its key half
+  // 0, kf its K fragments of key half 1 and vf block j-1's V^T fragments of
+  // key half 1. Fragments are read at the end of a step, after the last MFMA
+  // that uses the ones they replace.
+  auto iteration = [&](const int j, const int buf, const int nbuf, const bool masked, auto first_tag,
+                       auto prev_tag) __attribute__((always_inline)) {
+    // step 0: P V(key half 1 of block j-1) | S^T(key half 1) | softmax(key half 0)
+    mask(0, j, masked);
+    if constexpr (decltype(prev_tag)::value) pv_mfma(1);
+    s_mfma(1, first_tag);
+    if constexpr (!decltype(first_tag)::value) exps(0);
+    interleave();
+    settle(0, first_tag);
+    read_v(buf, 0);
+    // block j+1 (loaded during the previous block) is complete and visible
+    // after the wait and the barrier; block j+2 then goes into the buffer of
+    // block j-1, whose last reader was step 0
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j + 2 < nblocks) dma(j + 2, nbuf == NBUF - 1 ? 0 : nbuf + 1);
+    read_k(nbuf, 0);  // past the last block this reads a stale buffer; the result is unused
+    // step 1: P V(key half 0) | S^T(key half 0 of block j+1) | softmax(key half 1)
+    mask(1, j, masked);
+    pv_mfma(0);
+    s_mfma(0, kNo());
+    exps(1);
+    interleave();
+    settle(1, kNo());
+    read_v(buf, 1);
+    read_k(nbuf, 1);
+  };
+
+  dma(0, 0);
+  if (1 < nblocks) dma(1, 1);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  read_k(0, 0);
+  s_mfma(0, kYes());
+  read_k(0, 1);
+  // Blocks at or below the tile's first position need no mask. The first
+  // block sets the reference (and shifts its key half 1 to it).
+  const int nfull = min((pos_first + 1) / kKeyBlock, nblocks);
+  iteration(0, 0, 1, nfull < 1, kYes(), kNo());
+  for (int j = 1, buf = 1; j < nblocks; ++j) {
+    const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;
+    iteration(j, buf, nbuf, j >= nfull, kNo(), kYes());
+    buf = nbuf;
+  }
+  pv_mfma(1);
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (!row_ok) return;
+  const float inv = 1.f / l_tot;
+  __bf16* out = (v == p.G) ? (__bf16*)p.o_s + ((int64_t)b * p.S + pos) * D
+                           : (__bf16*)p.o_r + ((((int64_t)b * p.S + pos) * p.G + v) * p.K + slot) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      bf16x4 o4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o4[i] = f2bf(oacc[db][4 * jq + i] * inv);
+      *(bf16x4*)(out + db * 32 + 8 * jq + 4 * half) = o4;
+    }
+}
+
 // fp32 path: one wavefront per query row; lanes over keys for the scores,
 // lanes over d for P V. Plain fp32 arithmetic throughout.
 template <int D>
@@ -946,17 +784,15 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillParams p) {
 
 template <int D>
 static void launch_prefill_bf16(const PrefillParams& p, hipStream_t s) {
-  constexpr int TR = PrefillShape<D>::kTileRows;
+  constexpr int TR = 256;  // rows per tile (workgroup)
   const int tiles_r = (p.S * p.K + TR - 1) / TR;
   const int tiles_s = (p.S + TR - 1) / TR;
   const int total = p.B * (p.G * tiles_r + tiles_s);
   const int nblk = ((total + 7) / 8) * 8;
-  if constexpr (D <= 64) {
-    static_assert(PrefillShape<D>::kTileRows == 256, "quarter-pipelined tiles are 256 rows");
+  if constexpr (D <= 64)
     hipLaunchKernelGGL(prefill_qp_kernel<D>, dim3(nblk), dim3(256), 0, s, p, tiles_r, tiles_s);
-  } else {
-    hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3(nblk), dim3(256), 0, s, p, tiles_r, tiles_s);
-  }
+  else
+    hipLaunchKernelGGL(prefill_d128_kernel<D>, dim3(nblk), dim3(512), 0, s, p, tiles_r, tiles_s);
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int d, bool bf16, hipStream_t s) {

@@ -205,6 +205,42 @@ def test_prefill_small(case):
     assert_close(o_s, ref_s, dtype, "O_shared")
 
 
+# Scores that rise (or fall) steeply along the sequence: the kernels' reference
+# max must move many times after the first key block (rising), or stay far
+# above most later scores (falling). Keys are a ramp a_j along one direction u
+# plus noise; every query is u plus noise, so the log2-domain scores
+# log2(e) * q.k / sqrt(d) span about 1500 over the sequence.
+RAMP_CASES = [
+    # B, S, D, N, G, k, d, rising
+    (3, 200, 64, 8, 4, 2, 32, True),
+    (2, 300, 128, 16, 8, 1, 64, True),
+    (2, 300, 128, 16, 8, 1, 64, False),
+    (1, 517, 128, 32, 8, 2, 128, True),
+    (1, 517, 128, 32, 8, 2, 128, False),
+]
+
+
+@pytest.mark.parametrize("case", RAMP_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_reference_moves(case):
+    B, S, D, N, G, k, d, rising = case
+    cfg = small_cfg(B, S, D, N, G, k, d)
+    inp = _prefill_inputs(cfg, False)
+    gen = torch.Generator().manual_seed(11)
+    u = torch.ones(d)
+    q = u + 0.1 * torch.randn(B, S, N + 1, d, generator=gen)
+    j = torch.arange(S, dtype=torch.float32)
+    a = 1500.0 * (j if rising else (S - 1 - j)) / (S * 1.4426950408889634 * d ** 0.5)
+    kk = a.view(1, 1, S, 1) * u + 0.5 * torch.randn(B, G, S, d, generator=gen)
+    inp["q"], inp["k"] = q.to(cfg.torch_dtype), kk.to(cfg.torch_dtype)
+    g = to_dev(inp)
+    o_r, o_s = gqe.prefill(dims_of(cfg), g["q"], g["k"], g["v"], g["idx"])
+    torch.cuda.synchronize()
+    idx = inp["idx"].numpy().reshape(B, S, G, k)
+    ref_r, ref_s = oracle.prefill(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), idx, cfg.M)
+    assert_close(o_r, ref_r, "bf16", "O_routed")
+    assert_close(o_s, ref_s, "bf16", "O_shared")
+
+
 def _sample_positions(S, n=256, seed=1):
     if S <= n:
         return np.arange(S)
