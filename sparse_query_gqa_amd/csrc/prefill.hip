@@ -49,41 +49,45 @@ struct TileCoord {
   bool valid;
 };
 
-// Block -> tile. Blocks are spread round-robin over the 8 XCDs, so block w
-// is re-mapped to a logical tile index such that each XCD walks a contiguous
-// range of the (v, b, tile) order: its concurrently running workgroups read
-// the same KV head and share it in that XCD's L2. Within a (b, v) tiles run
-// from the longest causal extent to the shortest.
-__device__ __forceinline__ TileCoord tile_of_block(const PrefillParams& p, int tiles_r,
-                                                  int tiles_s) {
-  const int per_b = p.G * tiles_r + tiles_s;
-  const int total = p.B * per_b;
-  const int per_xcd = gridDim.x / 8;
-  const int w = blockIdx.x;
-  const int logical = (w % 8) * per_xcd + (w / 8);
+// Block -> tile, longest causal extent first. Routed tile t of a group covers
+// rows [256t, 256t+255], i.e. tokens up to (256t+255)/k; shared tile t covers
+// tokens up to 256t+255, the same extent as routed tile k*t+k-1. Blocks run
+// through the tiles in rounds of equal extent, from the last tiles of the
+// sequences to the first: the routed tiles t = k*ts+k-1 of every (sequence,
+// group) with the shared tiles ts of every sequence, then routed tiles
+// t = k*ts+k-2, ..., k*ts. Workgroups are dispatched in block order and
+// spread round-robin over the XCDs, so every XCD gets an even share of each
+// round and the long tiles start first (longest-processing-time order). The
+// routed index t can pass the last routed tile when S*k is not a multiple of
+// 256; those blocks exit at once.
+__device__ __forceinline__ TileCoord tile_of_block(const PrefillParams& p, int tiles_r, int tiles_s) {
+  const int BG = p.B * p.G;
+  const int per_round = p.K * BG + p.B;
+  const int i = blockIdx.x;
   TileCoord c;
-  c.valid = logical < total;
-  int rem = c.valid ? logical : 0;
-  // order: group 0, then the shared head (it also reads KV head 0), then
-  // groups 1..G-1; sequences inside each.
-  if (rem < p.B * tiles_r) {
-    c.v = 0;
-    c.b = rem / tiles_r;
-    c.tile = tiles_r - 1 - rem % tiles_r;
-  } else {
-    rem -= p.B * tiles_r;
-    if (rem < p.B * tiles_s) {
-      c.v = p.G;
-      c.b = rem / tiles_s;
-      c.tile = tiles_s - 1 - rem % tiles_s;
+  const int sr = i / per_round;
+  int rem = i - sr * per_round;
+  const int ts = tiles_s - 1 - sr;
+  c.valid = sr < tiles_s;
+  if (rem < BG + p.B) {
+    if (rem < BG) {
+      c.b = rem / p.G;
+      c.v = rem - c.b * p.G;
+      c.tile = p.K * ts + p.K - 1;
     } else {
-      rem -= p.B * tiles_s;
-      c.v = 1 + rem / (p.B * tiles_r);
-      rem %= (p.B * tiles_r);
-      c.b = rem / tiles_r;
-      c.tile = tiles_r - 1 - rem % tiles_r;
+      c.b = rem - BG;
+      c.v = p.G;
+      c.tile = ts;
     }
+  } else {
+    rem -= BG + p.B;
+    const int step = rem / BG;
+    rem -= step * BG;
+    c.b = rem / p.G;
+    c.v = rem - c.b * p.G;
+    c.tile = p.K * ts + p.K - 2 - step;
   }
+  if (c.v < p.G && c.tile >= tiles_r) c.valid = false;
   return c;
 }
 
@@ -787,8 +791,7 @@ static void launch_prefill_bf16(const PrefillParams& p, hipStream_t s) {
   constexpr int TR = 256;  // rows per tile (workgroup)
   const int tiles_r = (p.S * p.K + TR - 1) / TR;
   const int tiles_s = (p.S + TR - 1) / TR;
-  const int total = p.B * (p.G * tiles_r + tiles_s);
-  const int nblk = ((total + 7) / 8) * 8;
+  const int nblk = tiles_s * (p.K * p.B * p.G + p.B);  // rounds of equal extent; see tile_of_block
   if constexpr (D <= 64)
     hipLaunchKernelGGL(prefill_qp_kernel<D>, dim3(nblk), dim3(256), 0, s, p, tiles_r, tiles_s);
   else
