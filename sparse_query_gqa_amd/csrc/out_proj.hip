@@ -9,13 +9,17 @@
 // columns [G*k*d, G*k*d + d) are obar computed in fp32 from the G*k stored
 // slots and the fp32 weights; the last d columns are o_shared[t].
 //
-// bf16: 128x128 output tile per 256-thread workgroup, K step 32, four
-// wavefronts of 64x64 each on v_mfma_f32_32x32x16_bf16. W_O is row-major
-// [K, D] (the natural y = A W_O layout), so its tile is transposed into LDS
-// to give the B operand k-contiguous lanes.
+// Two bf16 kernels: a pipelined GEMM for T >= 256 (below) and, for fewer
+// tokens, a plain 128x128-tile kernel: four wavefronts of 64x64 each on
+// v_mfma_f32_32x32x16_bf16, W_O's tile transposed into LDS to give the B
+// operand k-contiguous lanes.
 #include "gqe_internal.h"
 
 namespace gqe {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 128, kBN = 128, kBK = 32, kPadK = 8;
 
@@ -133,6 +137,197 @@ __global__ __launch_bounds__(256) void out_proj_bf16_kernel(OutProjParams p) {
     }
 }
 
+// bf16 GEMM form. Computed as y^T = W_O^T A^T with v_mfma_f32_32x32x16_bf16:
+// the W_O tile sits in LDS row-major ([k][n], as stored) and its fragments
+// come from ds_read_b64_tr_b16 (four consecutive k of one n per lane); the A
+// tile sits token-major ([t][k]) and is read with 16-byte loads. Each lane
+// then holds four consecutive output columns of one token. A workgroup of 8
+// wavefronts computes 128 tokens x 256 columns (64 x 64 per wavefront), k in
+// steps of 32 through a four-stage LDS ring filled by LDS-DMA
+// (global_load_lds_dwordx4): the hard-slot and shared-head columns of A come
+// straight from o_routed / o_shared, obar is computed once per tile into its
+// own LDS region at the start. Every step issues the same three DMA loads
+// per thread (dummies for obar steps and past the end), so one fixed vmcnt
+// wait before the barrier makes the current step's tile complete. The output
+// tile is staged through LDS and written as whole rows.
+constexpr int kGT = 128;      // tokens per tile
+constexpr int kGN = 256;      // output columns per tile
+constexpr int kGK = 32;       // k per step
+constexpr int kGStages = 4;
+
+template <int DH>
+__global__ __launch_bounds__(512, 1) void out_proj_gemm_kernel(OutProjParams p) {
+  constexpr int AB = kGT * kGK * 2;  // A tile: 128 token rows x 64 bytes
+  constexpr int BB = kGK * kGN * 2;  // W_O tile: 32 k rows x 512 bytes
+  constexpr int SB = AB + BB;
+  constexpr int OPAD = DH + 8;       // obar row stride: 16 bytes of padding keep 16 rows on distinct banks
+  constexpr int YPAD = kGN + 8;      // output staging row stride
+  static_assert(kGT * YPAD * 2 <= kGStages * SB, "output staging must fit the stage ring");
+  __shared__ __attribute__((aligned(1024))) char lds[kGStages * SB];
+  __shared__ __attribute__((aligned(16))) __bf16 obar[kGT][OPAD];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int wm = wave & 1, wn = wave >> 1;  // token half, column quarter
+  const int64_t m0 = (int64_t)blockIdx.x * kGT;
+  const int n0 = blockIdx.y * kGN;
+  const int hard = p.Gk * DH;
+  const int nk = (hard + 2 * DH) / kGK;
+  const __bf16* orr = (const __bf16*)p.o_r;
+  const __bf16* os = (const __bf16*)p.o_s;
+  const __bf16* wo = (const __bf16*)p.w_o;
+  const int64_t tmax = p.T - 1;
+
+  // obar = sum over the G*k slots of w * o, in fp32, rounded to bf16; one
+  // 8-column piece of one token per work item
+  for (int it = tid; it < kGT * (DH / 8); it += 512) {
+    const int row = it / (DH / 8), e = (it % (DH / 8)) * 8;
+    const int64_t t = min(m0 + row, tmax);
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < p.Gk; ++j) {
+      const float wj = p.w[t * p.Gk + j];
+      const bf16x8 ov = *(const bf16x8*)(orr + t * hard + j * DH + e);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] = fmaf(wj, (float)ov[i], s[i]);
+    }
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = f2bf(s[i]);
+    *(bf16x8*)&obar[row][e] = r;
+  }
+
+  // LDS-DMA of step kt into stage st. A: chunk `wave` = token rows
+  // 16*wave + lane/4, 16-byte chunk position lane%4, holding logical chunk
+  // position ^ ((row >> 2) & 3). W_O: chunks 2*wave + i = k rows 2n + lane/32,
+  // position lane%32 holding logical chunk position ^ ((row & 3) << 2).
+  const int a_row = 16 * wave + (lane >> 2);
+  const int a_c = (lane & 3) ^ ((a_row >> 2) & 3);
+  const int64_t a_t = min(m0 + a_row, tmax);
+  auto dma = [&](const int kt, const int st) __attribute__((always_inline)) {
+    const int k0 = min(kt, nk - 1) * kGK;
+    char* sbase = lds + st * SB;
+    const __bf16* asrc;
+    if (k0 < hard) asrc = orr + a_t * hard + k0 + 8 * a_c;
+    else if (k0 >= hard + DH) asrc = os + a_t * DH + (k0 - hard - DH) + 8 * a_c;
+    else asrc = orr + a_t * hard + 8 * a_c;  // obar step: a dummy load, the tile is not read
+    __builtin_amdgcn_global_load_lds(asrc, (__attribute__((address_space(3))) void*)(sbase + wave * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int n = 2 * wave + i;
+      const int row = 2 * n + (lane >> 5);
+      const int c = (lane & 31) ^ ((row & 3) << 2);
+      const int col = min(n0 + 8 * c, p.Dout - 8);
+      __builtin_amdgcn_global_load_lds(wo + (int64_t)(k0 + row) * p.Dout + col,
+                                       (__attribute__((address_space(3))) void*)(sbase + AB + n * 1024), 16, 0, 0);
+    }
+  };
+
+  // fragment addresses. A^T (B operand): token row t = wm*64 + tb*32 + l32,
+  // chunk 2*kk + half. W^T (A operand): transposing read; in a 16-lane group
+  // source lane i points at k row K0 + i/4, column N0 + 4*(i%4), and output
+  // lane i receives k rows K0..K0+3 of column N0 + i.
+  int a_off[2][2];  // [tb][kk]
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int t = wm * 64 + tb * 32 + l32;
+      a_off[tb][kk] = t * 64 + 16 * ((2 * kk + half) ^ ((t >> 2) & 3));
+    }
+  const int tr_row = 8 * half + ((lane & 15) >> 2);  // + 16*kk + 4*tt
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + wn*64 + nb*32
+  int w_off[2][2];  // [nb][tt] at kk = 0; kk adds 16 rows (same swizzle)
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int row = tr_row + 4 * tt;
+      const int col = wn * 64 + nb * 32 + tr_col;
+      w_off[nb][tt] = row * 512 + 16 * ((col >> 3) ^ ((row & 3) << 2)) + 2 * (col & 7);
+    }
+
+  f32x16 acc[2][2];  // [nb][tb]: 32 columns x 32 tokens
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+#pragma unroll
+  for (int kt = 0; kt < kGStages - 1; ++kt) dma(kt, kt);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt % kGStages;
+    // step kt's tile is complete when at most the two later tiles' loads are
+    // outstanding; the barrier makes it (and obar) visible and frees the
+    // stage read in step kt-1 for step kt+3
+    __asm__ volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    __syncthreads();
+    dma(kt + kGStages - 1, (kt + kGStages - 1) % kGStages);
+    const char* sbase = lds + st * SB;
+    const int k0 = kt * kGK;
+    const bool ob = k0 >= hard && k0 < hard + DH;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 af[2], wf[2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        if (ob) {
+          const int t = wm * 64 + tb * 32 + l32;
+          af[tb] = *(const bf16x8*)&obar[t][k0 - hard + 16 * kk + 8 * half];
+        } else {
+          af[tb] = *(const bf16x8*)(sbase + a_off[tb][kk]);
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        u32x4 w4;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const char* a = sbase + AB + kk * 16 * 512 + w_off[nb][tt];
+          const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a);
+          const u32x2 w2 = __builtin_bit_cast(u32x2, x);
+          w4[2 * tt] = w2[0];
+          w4[2 * tt + 1] = w2[1];
+        }
+        wf[nb] = __builtin_bit_cast(bf16x8, w4);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+          acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], af[tb], acc[nb][tb], 0, 0, 0);
+    }
+  }
+
+  // output tile through LDS: lane (half, l32) of tile (nb, tb) holds token
+  // wm*64 + tb*32 + l32 and columns wn*64 + nb*32 + 8*(r/4) + 4*half + r%4
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  __bf16* ys = (__bf16*)lds;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int t = wm * 64 + tb * 32 + l32;
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        bf16x4 o4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = f2bf(acc[nb][tb][4 * rq + i]);
+        *(bf16x4*)&ys[t * YPAD + wn * 64 + nb * 32 + 8 * rq + 4 * half] = o4;
+      }
+    }
+  __syncthreads();
+  __bf16* y = (__bf16*)p.y;
+  for (int it = tid; it < kGT * (kGN / 8); it += 512) {
+    const int row = it / (kGN / 8), c8 = (it % (kGN / 8)) * 8;
+    const int64_t t = m0 + row;
+    const int n = n0 + c8;
+    if (t < p.T && n < p.Dout) *(bf16x8*)(y + t * p.Dout + n) = *(const bf16x8*)&ys[row * YPAD + c8];
+  }
+}
+
 // fp32: one thread per output element, sequential fp32 accumulation.
 __global__ __launch_bounds__(256) void out_proj_f32_kernel(OutProjParams p) {
   const int n = blockIdx.y * 64 + (threadIdx.x & 63);
@@ -147,7 +342,16 @@ __global__ __launch_bounds__(256) void out_proj_f32_kernel(OutProjParams p) {
 }
 
 hipError_t launch_out_proj(const OutProjParams& p, bool bf16, hipStream_t s) {
-  if (bf16) {
+  if (p.T == 0) return hipSuccess;
+  if (bf16 && p.T >= kGT * 2) {
+    const dim3 grid((unsigned)((p.T + kGT - 1) / kGT), (p.Dout + kGN - 1) / kGN);
+    switch (p.d) {
+      case 32: hipLaunchKernelGGL(out_proj_gemm_kernel<32>, grid, dim3(512), 0, s, p); break;
+      case 64: hipLaunchKernelGGL(out_proj_gemm_kernel<64>, grid, dim3(512), 0, s, p); break;
+      case 128: hipLaunchKernelGGL(out_proj_gemm_kernel<128>, grid, dim3(512), 0, s, p); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (bf16) {
     const dim3 grid((unsigned)((p.T + kBM - 1) / kBM), (p.Dout + kBN - 1) / kBN);
     hipLaunchKernelGGL(out_proj_bf16_kernel, grid, dim3(256), 0, s, p);
   } else {
