@@ -328,6 +328,114 @@ __global__ __launch_bounds__(512, 1) void out_proj_gemm_kernel(OutProjParams p) 
   }
 }
 
+// Few-token form (T <= 16, decode): y^T = W_O^T A^T on v_mfma_f32_16x16x32_bf16
+// with 16 output columns per workgroup, so that the W_O stream is spread over
+// Dout/16 workgroups. The 8 wavefronts split K; each copies its K slice of
+// the 16 columns (32 k rows x 32 bytes per step) into a private LDS region by
+// LDS-DMA and reads the W_O^T fragments from it with ds_read_b64_tr_b16. The
+// A^T operand needs no transpose: lane l takes token l%16 and 8 consecutive
+// k, which are contiguous in o_routed / o_shared; obar is computed once for
+// the 16 tokens into LDS. A pass first issues all its loads, then its MFMAs.
+// The partial 16x16 tiles of the 8 wavefronts are added in LDS in a fixed
+// order.
+constexpr int kSmallT = 16;
+constexpr int kSmallSteps = 16;  // 32-k steps per wavefront per pass (16 KiB of LDS)
+
+template <int DH>
+__global__ __launch_bounds__(512, 1) void out_proj_small_kernel(OutProjParams p) {
+  __shared__ __attribute__((aligned(1024))) char wl[8][kSmallSteps][1024];
+  __shared__ float part[8][16][17];
+  __shared__ __attribute__((aligned(16))) __bf16 obar_s[16][DH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Workgroups go round-robin to the 8 XCDs. Four 16-column slices share each
+  // 128-byte line of a W_O row, so when the slice count allows, the four
+  // slices of a line are given to consecutive workgroups of one XCD: the line
+  // then comes from HBM once, into that XCD's L2.
+  int slice = blockIdx.x;
+  if (gridDim.x % 32 == 0) {
+    const int x = blockIdx.x % 8, i = blockIdx.x / 8;
+    slice = (i / 4) * 32 + x * 4 + i % 4;
+  }
+  const int n0 = slice * 16;
+  const int hard = p.Gk * DH;
+  const int nsteps = (hard + 2 * DH) / 32;
+  const int s_lo = wave * nsteps / 8, s_hi = (wave + 1) * nsteps / 8;
+  const __bf16* orr = (const __bf16*)p.o_r;
+  const __bf16* os = (const __bf16*)p.o_s;
+  const __bf16* wo = (const __bf16*)p.w_o;
+
+  // obar of the 16 tokens (tokens past T repeat token T-1), fp32 sums rounded to bf16
+  for (int it = tid; it < 16 * (DH / 8); it += 512) {
+    const int t = min(it / (DH / 8), (int)p.T - 1), e = (it % (DH / 8)) * 8;
+    float sacc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 16
+    for (int j = 0; j < p.Gk; ++j) {
+      const float wj = p.w[(int64_t)t * p.Gk + j];
+      const bf16x8 ov = *(const bf16x8*)(orr + (int64_t)t * hard + j * DH + e);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sacc[i] = fmaf(wj, (float)ov[i], sacc[i]);
+    }
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = f2bf(sacc[i]);
+    *(bf16x8*)&obar_s[it / (DH / 8)][e] = r;
+  }
+  __syncthreads();
+
+  // B operand: token t = lane%16 (tokens past T read token T-1; their
+  // outputs are not stored), k = 8*(lane/16) + 0..7 of the step
+  const int bt = min(lane & 15, (int)p.T - 1), bk = 8 * (lane >> 4);
+  // W_O DMA: lane l copies k row l/2, columns 8*(l%2) + 0..7 (clamped to the
+  // last full 8 columns past Dout; those outputs are not stored)
+  const int d_row = lane >> 1, d_col = min(n0 + 8 * (lane & 1), p.Dout - 8);
+  // transposing read: source lane i of a 16-lane group points at k row
+  // K0 + i/4, column 4*(i%4); output lane i gets k rows K0..K0+3 of column i
+  const int tr_off = (((lane & 15) >> 2) + 8 * (lane >> 4)) * 32 + 8 * (lane & 3);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = s_lo; s0 < s_hi; s0 += kSmallSteps) {
+    const int ns = min(kSmallSteps, s_hi - s0);
+    bf16x8 bq[kSmallSteps];
+#pragma unroll
+    for (int i = 0; i < kSmallSteps; ++i) {
+      if (i < ns) {
+        __builtin_amdgcn_global_load_lds(wo + (int64_t)((s0 + i) * 32 + d_row) * p.Dout + d_col,
+                                         (__attribute__((address_space(3))) void*)wl[wave][i], 16, 0, 0);
+        const int k = (s0 + i) * 32 + bk;
+        if (k < hard) bq[i] = *(const bf16x8*)(orr + (int64_t)bt * hard + k);
+        else if (k < hard + DH) bq[i] = *(const bf16x8*)&obar_s[lane & 15][k - hard];
+        else bq[i] = *(const bf16x8*)(os + (int64_t)bt * DH + (k - hard - DH));
+      }
+    }
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < kSmallSteps; ++i) {
+      if (i < ns) {
+        u32x4 w4;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(wl[wave][i] + tr_off + tt * 4 * 32));
+          const u32x2 w2 = __builtin_bit_cast(u32x2, x);
+          w4[2 * tt] = w2[0];
+          w4[2 * tt + 1] = w2[1];
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w4), bq[i], acc, 0, 0, 0);
+      }
+    }
+  }
+  // lane l holds columns 4*(l/16) + 0..3 of token l%16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part[wave][lane & 15][4 * (lane >> 4) + i] = acc[i];
+  __syncthreads();
+  if (tid < 256) {
+    const int t = tid >> 4, c = tid & 15;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) sum += part[w][t][c];
+    if (t < p.T && n0 + c < p.Dout) ((__bf16*)p.y)[(int64_t)t * p.Dout + n0 + c] = f2bf(sum);
+  }
+}
+
 // fp32: one thread per output element, sequential fp32 accumulation.
 __global__ __launch_bounds__(256) void out_proj_f32_kernel(OutProjParams p) {
   const int n = blockIdx.y * 64 + (threadIdx.x & 63);
@@ -349,6 +457,14 @@ hipError_t launch_out_proj(const OutProjParams& p, bool bf16, hipStream_t s) {
       case 32: hipLaunchKernelGGL(out_proj_gemm_kernel<32>, grid, dim3(512), 0, s, p); break;
       case 64: hipLaunchKernelGGL(out_proj_gemm_kernel<64>, grid, dim3(512), 0, s, p); break;
       case 128: hipLaunchKernelGGL(out_proj_gemm_kernel<128>, grid, dim3(512), 0, s, p); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (bf16 && p.T <= kSmallT) {
+    const dim3 grid((p.Dout + 15) / 16);
+    switch (p.d) {
+      case 32: hipLaunchKernelGGL(out_proj_small_kernel<32>, grid, dim3(512), 0, s, p); break;
+      case 64: hipLaunchKernelGGL(out_proj_small_kernel<64>, grid, dim3(512), 0, s, p); break;
+      case 128: hipLaunchKernelGGL(out_proj_small_kernel<128>, grid, dim3(512), 0, s, p); break;
       default: return hipErrorInvalidValue;
     }
   } else if (bf16) {

@@ -358,7 +358,13 @@ def test_decode_workload_sampled():
 @pytest.mark.parametrize("T,G,k,d,D,dtype", [(1, 2, 1, 32, 256, "f32"), (130, 2, 2, 64, 72, "f32"),
                                              (1, 8, 1, 64, 1024, "bf16"), (300, 8, 1, 64, 1024, "bf16"),
                                              (257, 8, 2, 128, 136, "bf16"), (64, 1, 1, 32, 8, "bf16"),
-                                             (129, 4, 3, 32, 264, "bf16")])
+                                             (129, 4, 3, 32, 264, "bf16"),
+                                             # few-token kernel: ragged column tiles, several DMA passes
+                                             (16, 8, 2, 128, 4096, "bf16"), (7, 2, 3, 32, 72, "bf16"),
+                                             (16, 1, 1, 32, 8, "bf16"), (5, 4, 2, 64, 136, "bf16"),
+                                             (11, 32, 4, 128, 264, "bf16"),
+                                             # GEMM kernel: d=32, ragged columns and tokens
+                                             (256, 2, 3, 32, 264, "bf16"), (1000, 4, 2, 128, 8, "bf16")])
 def test_out_proj_small(T, G, k, d, D, dtype):
     s = synth.make_slot_inputs(T, G, k, d, D, dtype, seed=T)
     g = to_dev(s)
