@@ -15,7 +15,8 @@
 
 namespace gqe {
 
-constexpr int kRouteTok = 16;  // tokens per workgroup
+constexpr int kRouteTok = 16;       // tokens per workgroup (fp32)
+constexpr int kRouteBlockTok = 64;  // tokens per workgroup (bf16)
 
 // Selection epilogue: z for kRouteTok tokens in LDS ([tok][G*M], bias
 // included). One thread per (token, group): TopK by repeated first-maximum
@@ -58,66 +59,86 @@ __device__ void route_select_store(const float* zs, int ntok, int64_t tok0,
   }
 }
 
-// bf16 router scores on MFMA. Block = W wavefronts and 16 tokens; wavefront
-// w owns a contiguous slice of the 32-wide feature steps, and the W partial
-// score tiles are summed in LDS in wavefront order (fixed, so the logits are
-// deterministic). Many wavefronts per block keep many 16-byte loads in
-// flight even when there are few tokens (decode).
+// bf16 router scores on MFMA. A block takes 64 tokens (four 16-token tiles)
+// and all G*M experts; its W wavefronts split the 32-wide feature steps, and
+// the W partial score tiles are summed in LDS in wavefront order (fixed, so
+// the logits are deterministic). Each wavefront loads a batch of SB steps -
+// x fragments of its four token tiles and W_r fragments of its NT expert
+// tiles - before the batch's MFMAs, so the loads of a batch are in flight
+// together; each W_r fragment feeds four MFMAs.
 // 16x16x32 operand layout: lane l holds A[l%16][8*(l/16) .. +8] (token row,
 // 8 consecutive features) and B[8*(l/16) .. +8][l%16] (expert column); the
 // result D[4*(l/16)+i][l%16] lands in register i.
-__global__ __launch_bounds__(1024) void route_bf16_kernel(RouteParams p) {
-  extern __shared__ float zpart[];  // [W][16][GM]
+constexpr int kRouteTT = kRouteBlockTok / 16;  // token tiles per block
+
+template <int NT, int SB, int MAXW>
+__global__ __launch_bounds__(64 * MAXW) void route_bf16_kernel(RouteParams p) {
+  extern __shared__ float zpart[];  // [W][64][GM]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, W = blockDim.x >> 6;
-  const int64_t tok0 = (int64_t)blockIdx.x * kRouteTok;
-  const int ntok = (int)((p.T - tok0) < kRouteTok ? (p.T - tok0) : kRouteTok);
+  const int64_t tok0 = (int64_t)blockIdx.x * kRouteBlockTok;
+  const int ntok = (int)((p.T - tok0) < kRouteBlockTok ? (p.T - tok0) : kRouteBlockTok);
   const int GM = p.G * p.M;
-  const int ntiles = (GM + 15) / 16;
   const int D = p.D;
   const __bf16* x = (const __bf16*)p.x;
   const __bf16* wr = (const __bf16*)p.w;
 
   const int row = lane & 15;
   const int kof = 8 * (lane >> 4);
-  const bool tok_ok = row < ntok;
-  const __bf16* xrow = x + (tok0 + (tok_ok ? row : 0)) * (int64_t)D;
+  // token rows past T read row T-1; their scores are not used
+  const __bf16* xrow[kRouteTT];
+#pragma unroll
+  for (int tt = 0; tt < kRouteTT; ++tt)
+    xrow[tt] = x + min(tok0 + tt * 16 + row, p.T - 1) * (int64_t)D;
+  // expert rows past G*M read row G*M-1; their scores are not stored
+  const __bf16* wrow[NT];
+#pragma unroll
+  for (int e = 0; e < NT; ++e) wrow[e] = wr + (int64_t)min(e * 16 + row, GM - 1) * D;
   const int nsteps = (D + 31) / 32;
   const int st0 = (int)((int64_t)w * nsteps / W), st1 = (int)((int64_t)(w + 1) * nsteps / W);
 
-  f32x4 acc[kMaxRouterCols / 16];
+  f32x4 acc[kRouteTT][NT];
 #pragma unroll
-  for (int e = 0; e < kMaxRouterCols / 16; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int tt = 0; tt < kRouteTT; ++tt)
+#pragma unroll
+    for (int e = 0; e < NT; ++e) acc[tt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const bf16x8 zero8 = {};
-  for (int st = st0; st < st1; ++st) {
-    // D is a multiple of 8; a 32-wide step may run past D only in its tail.
-    const int c = st * 32 + kof;
-    bf16x8 a = (tok_ok && c < D) ? *(const bf16x8*)(xrow + c) : zero8;
+  for (int sb = st0; sb < st1; sb += SB) {
+    bf16x8 a[SB][kRouteTT], bw[SB][NT];
 #pragma unroll
-    for (int e = 0; e < kMaxRouterCols / 16; ++e) {
-      if (e < ntiles) {
-        const int ex = e * 16 + row;
-        bf16x8 b = (ex < GM && c < D) ? *(const bf16x8*)(wr + (int64_t)ex * D + c) : zero8;
-        acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[e], 0, 0, 0);
-      }
+    for (int i = 0; i < SB; ++i) {
+      // D is a multiple of 8; a 32-wide step may run past D only in its tail
+      const int c = (sb + i) * 32 + kof;
+      const bool ok = sb + i < st1 && c < D;
+#pragma unroll
+      for (int tt = 0; tt < kRouteTT; ++tt) a[i][tt] = ok ? *(const bf16x8*)(xrow[tt] + c) : zero8;
+#pragma unroll
+      for (int e = 0; e < NT; ++e) bw[i][e] = ok ? *(const bf16x8*)(wrow[e] + c) : zero8;
     }
-  }
-  float* zw = zpart + (size_t)w * kRouteTok * GM;
 #pragma unroll
-  for (int e = 0; e < kMaxRouterCols / 16; ++e) {
-    if (e < ntiles) {
+    for (int i = 0; i < SB; ++i)
+#pragma unroll
+      for (int tt = 0; tt < kRouteTT; ++tt)
+#pragma unroll
+        for (int e = 0; e < NT; ++e)
+          acc[tt][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][tt], bw[i][e], acc[tt][e], 0, 0, 0);
+  }
+  float* zw = zpart + (size_t)w * kRouteBlockTok * GM;
+#pragma unroll
+  for (int tt = 0; tt < kRouteTT; ++tt)
+#pragma unroll
+    for (int e = 0; e < NT; ++e) {
       const int ex = e * 16 + row;  // output column = expert
       if (ex < GM) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) zw[(4 * (lane >> 4) + i) * GM + ex] = acc[e][i];
+        for (int i = 0; i < 4; ++i) zw[(tt * 16 + 4 * (lane >> 4) + i) * GM + ex] = acc[tt][e][i];
       }
     }
-  }
   __syncthreads();
   // sum the wavefront partials in order, add the bias; result in slice 0
-  for (int idx = threadIdx.x; idx < kRouteTok * GM; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < kRouteBlockTok * GM; idx += blockDim.x) {
     float z = zpart[idx];
-    for (int ww = 1; ww < W; ++ww) z += zpart[(size_t)ww * kRouteTok * GM + idx];
+    for (int ww = 1; ww < W; ++ww) z += zpart[(size_t)ww * kRouteBlockTok * GM + idx];
     zpart[idx] = z + (p.bias ? p.bias[idx % GM] : 0.f);
   }
   __syncthreads();
@@ -226,17 +247,30 @@ __global__ __launch_bounds__(64) void list_scatter_kernel(ListParams p) {
   }
 }
 
+template <int NT, int SB, int MAXW>
+static void launch_route_bf16(const RouteParams& p, hipStream_t s) {
+  // wavefronts per block: about 256 features each, at most MAXW, and the
+  // [W][64][G*M] fp32 partials within 64 KB of LDS
+  const int GM = p.G * p.M;
+  int W = 1;
+  while (W < MAXW && W * 2 * 256 <= p.D && W * 2 * kRouteBlockTok * GM * 4 <= 65536) W *= 2;
+  const size_t lds = (size_t)W * kRouteBlockTok * GM * sizeof(float);
+  const unsigned nblk = (unsigned)((p.T + kRouteBlockTok - 1) / kRouteBlockTok);
+  hipLaunchKernelGGL((route_bf16_kernel<NT, SB, MAXW>), dim3(nblk), dim3(64 * W), lds, s, p);
+}
+
 hipError_t launch_route(const RouteParams& p, bool bf16, hipStream_t s) {
-  const unsigned nblk = (unsigned)((p.T + kRouteTok - 1) / kRouteTok);
   if (bf16) {
-    // wavefronts per block: about 256 features each, at most 16, and the
-    // [W][16][G*M] fp32 partials within 64 KB of LDS
-    const int GM = p.G * p.M;
-    int W = 1;
-    while (W < 16 && W * 2 * 256 <= p.D && W * 2 * kRouteTok * GM * 4 <= 65536) W *= 2;
-    const size_t lds = (size_t)W * kRouteTok * GM * sizeof(float);
-    hipLaunchKernelGGL(route_bf16_kernel, dim3(nblk), dim3(64 * W), lds, s, p);
+    const int nt = (p.G * p.M + 15) / 16;  // 16-expert tiles
+    // batch size and block size keep the fragments and accumulators within
+    // the register budget of the block size
+    if (nt <= 1) launch_route_bf16<1, 4, 16>(p, s);
+    else if (nt <= 2) launch_route_bf16<2, 2, 16>(p, s);
+    else if (nt <= 4) launch_route_bf16<4, 1, 16>(p, s);
+    else if (nt <= 8) launch_route_bf16<8, 1, 4>(p, s);
+    else launch_route_bf16<16, 1, 4>(p, s);
   } else {
+    const unsigned nblk = (unsigned)((p.T + kRouteTok - 1) / kRouteTok);
     hipLaunchKernelGGL(route_f32_kernel, dim3(nblk), dim3(64), 0, s, p);
   }
   return hipGetLastError();
