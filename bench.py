@@ -257,7 +257,7 @@ def main():
                        "G": dcfg.G, "M": dcfg.M, "k": dcfg.k, "head_dim": dcfg.d},
         },
         "roofline": {
-            "kernel": "prefill_bf16_kernel<64> (gqe_attn_prefill)",
+            "kernel": "prefill_qp_kernel<64> (gqe_attn_prefill)",
             "bound": "mfma",
             "achieved": round(attn_tflops, 2),
             "peak": PEAK_BF16_FLOPS / 1e12,

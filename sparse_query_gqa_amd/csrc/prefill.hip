@@ -51,43 +51,76 @@ struct TileCoord {
 
 // Block -> tile, longest causal extent first. Routed tile t of a group covers
 // rows [256t, 256t+255], i.e. tokens up to (256t+255)/k; shared tile t covers
-// tokens up to 256t+255, the same extent as routed tile k*t+k-1. Blocks run
-// through the tiles in rounds of equal extent, from the last tiles of the
-// sequences to the first: the routed tiles t = k*ts+k-1 of every (sequence,
-// group) with the shared tiles ts of every sequence, then routed tiles
-// t = k*ts+k-2, ..., k*ts. Workgroups are dispatched in block order and
-// spread round-robin over the XCDs, so every XCD gets an even share of each
-// round and the long tiles start first (longest-processing-time order). The
-// routed index t can pass the last routed tile when S*k is not a multiple of
-// 256; those blocks exit at once.
+// tokens up to 256t+255, the same extent as routed tile k*t+k-1. Tiles are
+// taken in "super-rounds" sr of decreasing extent (shared tile ts =
+// tiles_s-1-sr): the shared tiles ts with the routed tiles t = k*ts+k-1 of
+// the same extent, then routed tiles t = k*ts+k-2, ..., k*ts. Workgroups are
+// dispatched in block order and go round-robin to the 8 XCDs (block i to XCD
+// i % 8), so each XCD works through its own list, longest first.
+//
+// When G is a multiple of 8, XCD x's list holds the routed tiles of groups
+// x, x+8, ... of every sequence, plus the shared tiles (sr, b) with
+// (sr + b) % 8 == x: each XCD then streams K/V of one KV head (and now and
+// then head 0) through its L2, and every 8 consecutive super-rounds give
+// each XCD the same work. Otherwise the super-rounds are striped over all
+// XCDs. A routed index past the last routed tile (S*k not a multiple of
+// 256) and the unused tail of a shorter XCD list are invalid blocks, which
+// exit at once.
 __device__ __forceinline__ TileCoord tile_of_block(const PrefillParams& p, int tiles_r, int tiles_s) {
-  const int BG = p.B * p.G;
-  const int per_round = p.K * BG + p.B;
-  const int i = blockIdx.x;
   TileCoord c;
-  const int sr = i / per_round;
-  int rem = i - sr * per_round;
-  const int ts = tiles_s - 1 - sr;
-  c.valid = sr < tiles_s;
-  if (rem < BG + p.B) {
-    if (rem < BG) {
-      c.b = rem / p.G;
-      c.v = rem - c.b * p.G;
-      c.tile = p.K * ts + p.K - 1;
-    } else {
-      c.b = rem - BG;
-      c.v = p.G;
-      c.tile = ts;
-    }
+  const int i = blockIdx.x;
+  int sr, rem;
+  int nsh, sh_b0, sh_bstep;   // shared tiles first in rem: b = sh_b0 + sh_bstep*r, r < nsh
+  int gsel, gstride, gcount;  // routed groups of this list: gsel + gstride*j, j < gcount
+  if (p.G % 8 == 0) {
+    const int x = i % 8, j = i / 8;
+    const int gx = p.G / 8;
+    const int per = p.K * p.B * gx;  // routed entries per super-round
+    // shared tiles of XCD x in super-round r: b = (x - r) mod 8, +8, ... < B
+    auto cnt = [&](int r) { return (p.B + 7 - ((x - r) & 7)) / 8; };
+    // start(r) = r*per + shared tiles of super-rounds < r (B per 8 of them)
+    auto start = [&](int r) {
+      int n = r * per + p.B * (r / 8);
+      for (int q = r & ~7; q < r; ++q) n += cnt(q);
+      return n;
+    };
+    sr = (8 * j) / (8 * per + p.B);
+    while (sr > 0 && start(sr) > j) --sr;
+    while (start(sr + 1) <= j) ++sr;
+    rem = j - start(sr);
+    nsh = cnt(sr);
+    sh_b0 = (x - sr) & 7;
+    sh_bstep = 8;
+    gsel = x;
+    gstride = 8;
+    gcount = gx;
   } else {
-    rem -= BG + p.B;
-    const int step = rem / BG;
-    rem -= step * BG;
-    c.b = rem / p.G;
-    c.v = rem - c.b * p.G;
-    c.tile = p.K * ts + p.K - 2 - step;
+    const int per_round = p.K * p.B * p.G + p.B;
+    sr = i / per_round;
+    rem = i - sr * per_round;
+    nsh = p.B;
+    sh_b0 = 0;
+    sh_bstep = 1;
+    gsel = 0;
+    gstride = 1;
+    gcount = p.G;
   }
-  if (c.v < p.G && c.tile >= tiles_r) c.valid = false;
+  const int ts = tiles_s - 1 - sr;
+  c.valid = ts >= 0;
+  if (rem < nsh) {
+    c.b = sh_b0 + sh_bstep * rem;
+    c.v = p.G;
+    c.tile = ts;
+  } else {
+    rem -= nsh;
+    const int per_step = p.B * gcount;
+    const int step = rem / per_step;
+    rem -= step * per_step;
+    c.b = rem / gcount;
+    c.v = gsel + gstride * (rem - c.b * gcount);
+    c.tile = p.K * ts + p.K - 1 - step;
+    if (step >= p.K || c.tile >= tiles_r) c.valid = false;
+  }
   return c;
 }
 
@@ -791,7 +824,9 @@ static void launch_prefill_bf16(const PrefillParams& p, hipStream_t s) {
   constexpr int TR = 256;  // rows per tile (workgroup)
   const int tiles_r = (p.S * p.K + TR - 1) / TR;
   const int tiles_s = (p.S + TR - 1) / TR;
-  const int nblk = tiles_s * (p.K * p.B * p.G + p.B);  // rounds of equal extent; see tile_of_block
+  // see tile_of_block: 8 lists of tiles_s super-rounds, or striped super-rounds
+  const int nblk = (p.G % 8 == 0) ? 8 * (tiles_s * p.K * p.B * (p.G / 8) + p.B * ((tiles_s + 7) / 8))
+                                  : tiles_s * (p.K * p.B * p.G + p.B);  // (8 lists are at most this long)
   if constexpr (D <= 64)
     hipLaunchKernelGGL(prefill_qp_kernel<D>, dim3(nblk), dim3(256), 0, s, p, tiles_r, tiles_s);
   else
