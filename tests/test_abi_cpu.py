@@ -143,9 +143,12 @@ def test_out_proj_validation():
 def test_workspace_sizes_closed_form():
     lib = _lib()
     d = _dims(B=16, S=65536, N=32, G=8, k=2, d=128)
-    # split geometry: ~8192 blocks over B*G = 128 pairs -> 64 splits of 1024 keys
-    recs = 16 * 8 * 64 * 3
+    # split geometry: ~4096 blocks over B*G = 128 pairs -> 32 splits of 2048 keys
+    recs = 16 * 8 * 32 * 3
     assert lib.gqe_decode_workspace_bytes(ctypes.byref(d), 1) == recs * (128 + 2) * 4
+    # small cache: splits are at least 512 keys -> 2 splits of 1000 keys; q_len=2 -> (k+1)*2 rows
+    d3 = _dims(B=1, S=1000, N=4, G=2, k=1, d=64)
+    assert lib.gqe_decode_workspace_bytes(ctypes.byref(d3), 2) == (1 * 2 * 2 * 4) * (64 + 2) * 4
     d2 = _dims(B=1, S=131072, N=16, G=8, k=1)
     assert lib.gqe_route_workspace_bytes(ctypes.byref(d2)) == 1 * 8 * 2 * 2048 * 4
     assert lib.gqe_route_workspace_bytes(ctypes.byref(_dims(N=8, G=3))) == 0
