@@ -176,6 +176,9 @@ PREFILL_CASES = [
     (3, 200, 64, 8, 4, 2, 32, "bf16", True),
     (1, 129, 64, 8, 8, 1, 64, "bf16", False),
     (1, 64, 64, 16, 4, 4, 64, "bf16", False),
+    # MHA (M = 1) and dense MQA (G = 1, k = M) at d = 128
+    (2, 100, 64, 8, 8, 1, 128, "bf16", False),
+    (1, 300, 64, 4, 1, 4, 128, "bf16", True),
 ]
 
 
@@ -319,6 +322,30 @@ def test_decode_boundary_matrix(dtype, G, q_len):
     ref_r, ref_s = oracle.decode(f64(q), f64(kc), f64(vc), kv_len, idx.numpy().reshape(B, q_len, G, k), M)
     assert_close(o_r, ref_r, dtype, f"decode G={G} q_len={q_len} O_routed")
     assert_close(o_s, ref_s, dtype, f"decode G={G} q_len={q_len} O_shared")
+
+
+# Decode with many query rows per (sequence, group): (k+1)*q_len up to the
+# 16-row limit, which selects the 8- and 16-row kernel instantiations.
+@pytest.mark.parametrize("dtype,d,H,G,k,q_len", [("bf16", 64, 16, 2, 3, 2), ("bf16", 128, 16, 2, 7, 2),
+                                                 ("bf16", 32, 8, 2, 3, 4), ("f32", 64, 16, 2, 7, 2),
+                                                 ("f32", 128, 8, 1, 3, 3), ("bf16", 128, 32, 4, 5, 2)])
+def test_decode_many_rows(dtype, d, H, G, k, q_len):
+    M = H // G
+    B, Smax = 2, 700
+    rng = np.random.default_rng(d + 7 * k + q_len)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = torch.from_numpy(rng.standard_normal((B, q_len, H + 1, d), dtype=np.float32)).to(tdt)
+    kc = torch.from_numpy(rng.standard_normal((B, G, Smax, d), dtype=np.float32)).to(tdt)
+    vc = torch.from_numpy((rng.standard_normal((B, G, Smax, d)) + 0.25 * np.arange(G)[None, :, None, None]).astype(np.float32)).to(tdt)
+    kv_len = np.array([q_len + 3, 651], dtype=np.int32)
+    idx = synth.random_selection(B, q_len, G, M, k, 9)
+    dims = gqe.gqe_dims.make(B, Smax, 64, H, G, k, d, dtype)
+    o_r, o_s = gqe.decode(dims, q_len, q.to(DEV), kc.to(DEV), vc.to(DEV), torch.from_numpy(kv_len).to(DEV),
+                          idx.to(DEV))
+    torch.cuda.synchronize()
+    ref_r, ref_s = oracle.decode(f64(q), f64(kc), f64(vc), kv_len, idx.numpy().reshape(B, q_len, G, k), M)
+    assert_close(o_r, ref_r, dtype, f"decode rows={(k + 1) * q_len} d={d} O_routed")
+    assert_close(o_s, ref_s, dtype, f"decode rows={(k + 1) * q_len} d={d} O_shared")
 
 
 def test_decode_matches_prefill_rows():
