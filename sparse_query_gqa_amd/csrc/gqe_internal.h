@@ -95,6 +95,30 @@ hipError_t launch_out_proj(const OutProjParams& p, bool bf16, hipStream_t s);
 __device__ __forceinline__ float bf2f(__bf16 h) { return (float)h; }
 __device__ __forceinline__ __bf16 f2bf(float f) { return (__bf16)f; }  // round to nearest even
 
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane l writes LDS bytes [lds + 16 l, +16), lds a
+// wavefront-uniform LDS byte address, which the instruction takes from m0. It
+// is issued from asm so that the compiler does not track it as a pending LDS
+// store: it would otherwise wait for every such load (vmcnt(0)) before any
+// LDS read it cannot prove disjoint, the transposing reads among them, which
+// leaves no load in flight across a step. The caller waits on vmcnt itself
+// before the barrier that publishes the data. The instruction writes no
+// register; the nop is the wait state an m0 write needs before it.
+__device__ __forceinline__ uint32_t lds_addr(const void* lds) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds);
+}
+__device__ __forceinline__ void lds_dma16(const void* gptr, const void* lds) {
+  __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_addr(lds)) : "memory");
+}
+
+// The same with a wavefront-uniform base address and a 32-bit per-lane byte
+// offset (the saddr form): moving the base to the next block is scalar work.
+// Five wait states cover a base that a VALU op (readfirstlane) wrote.
+__device__ __forceinline__ void lds_dma16_s(const void* base, uint32_t off, const void* lds) {
+  __asm__ volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_addr(lds))
+                   : "memory");
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -145,7 +145,9 @@ __device__ __forceinline__ void row_info(const PrefillParams& p, int b, int v, i
 // and P V (2*DB MFMAs). The steps are software-pipelined across quarters and
 // key blocks: step t issues the S^T MFMAs of quarter t+1, the softmax of
 // quarter t and the P V MFMAs of quarter t-1, so every MFMA has a share of
-// the exponentials beside it. Consecutive quarters belong to different row
+// the exponentials beside it. The S^T MFMAs go first, so that the scores the
+// next step exponentiates are complete long before it starts; nothing reads
+// the P V results until the step after. Consecutive quarters belong to different row
 // halves, so a softmax that moves its half's reference only has to rescale
 // an accumulator whose P V products are all issued.
 //
@@ -154,8 +156,8 @@ __device__ __forceinline__ void row_info(const PrefillParams& p, int b, int v, i
 // XOR-swizzled so that neither read pattern has bank conflicts. K fragments
 // are plain 16-byte reads; V^T fragments come from
 // ds_read_b64_tr_b16, which hands each lane one d column of four keys. Blocks
-// rotate through three buffers: block j+2 is loaded while blocks j and j+1
-// are read, with one barrier per block.
+// rotate through four buffers: block j+3 is loaded while blocks j+2 and j+1
+// are in flight and block j is read, with one barrier per block.
 template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_qp_kernel(PrefillParams p, int tiles_r, int tiles_s) {
   static_assert(D == 32 || D == 64, "head dim");
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(256, 2) void prefill_qp_kernel(PrefillParams p, int
   constexpr int MATB = kKeyBlock * ROWB;  // bytes of one K or V block
   constexpr int NPW = MATB / 1024 / 4;    // 1 KiB LDS-DMA chunks per wavefront per matrix
   static_assert(NPW >= 1, "block too small for the LDS-DMA split");
-  constexpr int NBUF = 3;
+  constexpr int NBUF = 4;
   __shared__ __attribute__((aligned(1024))) char lds[NBUF][2][MATB];  // [buffer][K, V]
 
   const TileCoord tc = tile_of_block(p, tiles_r, tiles_s);
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(256, 2) void prefill_qp_kernel(PrefillParams p, int
   const int kvh = (v == p.G) ? 0 : v;
   const int nrows = (v == p.G) ? p.S : p.S * p.K;
   const int r0 = tc.tile * kTileRows;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int last_r = min(r0 + kTileRows, nrows) - 1;
   int pos_last, pos_first, s_, h_;
@@ -215,17 +217,15 @@ __global__ __launch_bounds__(256, 2) void prefill_qp_kernel(PrefillParams p, int
       for (int j = 0; j < 16; ++j) oacc[h][i][j] = 0.f;
   // per row: running sum of P and the reference (log2 units) the scores are taken against
   float l_run[2] = {0.f, 0.f}, mr[2] = {0.f, 0.f};
-  // -mr of half 0 as a 16-register MFMA accumulator, kept for its S^T
-  // MFMAs; the moves are asm so that the compiler keeps the tuple instead of
-  // re-creating it (16 moves) before every S^T product. It changes only when
-  // the reference moves. Half 1's initial accumulator is built per product:
-  // a second kept tuple would not fit the register budget.
-  f32x16 bias0;
+  // -mr of each half as a 16-register MFMA accumulator, kept for its S^T
+  // MFMAs; the moves are asm so that the compiler keeps the tuples instead of
+  // re-creating them (16 moves) before every S^T product. They change only
+  // when the reference moves.
+  f32x16 bias[2] = {};
   auto set_bias = [&](const int h) __attribute__((always_inline)) {
     const float nm = -mr[h];
-    if (h == 0)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) __asm__("v_mov_b32 %0, %1" : "=v"(bias0[j]) : "v"(nm));
+    for (int j = 0; j < 16; ++j) __asm__("v_mov_b32 %0, %1" : "+v"(bias[h][j]) : "v"(nm));
   };
   const int nblocks = pos_last / kKeyBlock + 1;
 
@@ -240,21 +240,40 @@ __global__ __launch_bounds__(256, 2) void prefill_qp_kernel(PrefillParams p, int
   // Block kb of K and V into buffer bf: lane l of 1 KiB chunk n writes LDS
   // bytes [1024 n + 16 l, +16), i.e. row 1024 n / ROWB + (16 l) / ROWB,
   // chunk position (16 l % ROWB) / 16; it loads the source chunk the swizzle
-  // puts there. Keys past the sequence re-read its last key (finite data;
-  // those keys are masked).
+  // puts there. That lane offset is the same in every block, so a whole block
+  // moves with the scalar base address. Only a block that runs past the
+  // sequence takes per-lane addresses: its keys past the end re-read the
+  // last key (finite data; those keys are masked).
   auto swz = [](int r) { return (((r >> 1) & 7) ^ ((r & 2) << 1)) & (CPR - 1); };
   constexpr int RPC = 1024 / ROWB;  // key rows per 1 KiB chunk
   const int dma_r = (16 * lane) / ROWB;
   const int dma_p = ((16 * lane) % ROWB) / 16;  // chunk position
-  auto dma = [&](const int kb, const int bf) __attribute__((always_inline)) {
+  uint32_t dma_off[NPW];
 #pragma unroll
-    for (int i = 0; i < NPW; ++i) {
-      const int n = wave * NPW + i;
-      const int rb = n * RPC + dma_r;  // row in the block
-      const int row = min(kb * kKeyBlock + rb, p.S - 1);
-      const int64_t g = (int64_t)row * D + 8 * (dma_p ^ swz(rb));
-      __builtin_amdgcn_global_load_lds(kbase + g, (__attribute__((address_space(3))) void*)(lds[bf][0] + n * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vbase + g, (__attribute__((address_space(3))) void*)(lds[bf][1] + n * 1024), 16, 0, 0);
+  for (int i = 0; i < NPW; ++i) {
+    const int rb = (wave * NPW + i) * RPC + dma_r;  // row in the block
+    dma_off[i] = rb * ROWB + 16 * (dma_p ^ swz(rb));
+  }
+  auto dma = [&](const int kb, const int bf) __attribute__((always_inline)) {
+    if ((kb + 1) * kKeyBlock <= p.S) {
+      const __bf16* kblk = kbase + (int64_t)kb * kKeyBlock * D;
+      const __bf16* vblk = vbase + (int64_t)kb * kKeyBlock * D;
+#pragma unroll
+      for (int i = 0; i < NPW; ++i) {
+        const int n = wave * NPW + i;
+        lds_dma16_s(kblk, dma_off[i], lds[bf][0] + n * 1024);
+        lds_dma16_s(vblk, dma_off[i], lds[bf][1] + n * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NPW; ++i) {
+        const int n = wave * NPW + i;
+        const int rb = n * RPC + dma_r;
+        const int row = min(kb * kKeyBlock + rb, p.S - 1);
+        const int64_t g = (int64_t)row * D + 8 * (dma_p ^ swz(rb));
+        lds_dma16(kbase + g, lds[bf][0] + n * 1024);
+        lds_dma16(vbase + g, lds[bf][1] + n * 1024);
+      }
     }
   };
 
@@ -308,13 +327,10 @@ __global__ __launch_bounds__(256, 2) void prefill_qp_kernel(PrefillParams p, int
   auto s_mfma = [&](const int q, auto first_tag) __attribute__((always_inline)) {
     const int sb = q >> 1, h = q & 1;
     const f32x16 zero16 = {};
-    f32x16 bias1;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) bias1[j] = -mr[1];
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       sh[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          kf[sb][s], qf[h][s], s == 0 ? (decltype(first_tag)::value ? zero16 : (h == 0 ? bias0 : bias1)) : sh[q],
+          kf[sb][s], qf[h][s], s == 0 ? (decltype(first_tag)::value ? zero16 : bias[h]) : sh[q],
           0, 0, 0);
   };
   auto pv_mfma = [&](const int q) __attribute__((always_inline)) {
@@ -388,11 +404,11 @@ __global__ __launch_bounds__(256, 2) void prefill_qp_kernel(PrefillParams p, int
     l_run[q & 1] += ls[q];
   };
   // MFMA / VALU interleave of one step's region: the LDS reads for the next
-  // step, then one MFMA per VALU group.
+  // step spread two per MFMA, and four VALU ops beside each MFMA.
   auto interleave = [&](auto n_mfma) __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
 #pragma unroll
     for (int i = 0; i < decltype(n_mfma)::value; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
@@ -412,59 +428,63 @@ __global__ __launch_bounds__(256, 2) void prefill_qp_kernel(PrefillParams p, int
     mask(0, j, masked);
     read_k(buf, 1);
     read_v(buf, 0);
-    if constexpr (decltype(prev_tag)::value) pv_mfma(3);
     s_mfma(1, first_tag);
+    if constexpr (decltype(prev_tag)::value) pv_mfma(3);
     softmax(0, first_tag);
     if constexpr (decltype(prev_tag)::value) interleave(kNSPV());
     else interleave(kNS());
     settle(0, first_tag);
     // step 1: P V(q0) | S^T(q2) | softmax(q1)
     mask(1, j, masked);
-    pv_mfma(0);
     s_mfma(2, kNo());
+    pv_mfma(0);
     softmax(1, first_tag);
     interleave(kNSPV());
     settle(1, first_tag);
     // step 2: P V(q1) | S^T(q3) | softmax(q2)
     mask(2, j, masked);
     read_v(buf, 1);
-    pv_mfma(1);
     s_mfma(3, kNo());
+    pv_mfma(1);
     softmax(2, kNo());
     interleave(kNSPV());
     settle(2, kNo());
-    // block j+1 (loaded during the previous block) is complete and visible
-    // after the wait and the barrier; block j+2 then goes into the buffer of
-    // block j-1, whose last reader was step 0
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // block j+1 (loaded two blocks ago) is complete and visible after the
+    // wait, which leaves block j+2's loads in flight, and the barrier; block
+    // j+3 then goes into the buffer of block j-1, whose last reads were
+    // issued in its step 2. Every block issues the same loads (past the last
+    // block it re-loads that one), so the wait count is fixed.
+    __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NPW) : "memory");
     __syncthreads();
-    if (j + 2 < nblocks) dma(j + 2, nbuf == NBUF - 1 ? 0 : nbuf + 1);
+    dma(min(j + 3, nblocks - 1), (buf + 3) % NBUF);
     read_k(nbuf, 0);  // past the last block this reads a stale buffer; the result is unused
     // step 3: P V(q2) | S^T(q0 of block j+1) | softmax(q3)
     mask(3, j, masked);
-    pv_mfma(2);
     s_mfma(0, kNo());
+    pv_mfma(2);
     softmax(3, kNo());
     interleave(kNSPV());
     settle(3, kNo());
   };
 
   dma(0, 0);
-  if (1 < nblocks) dma(1, 1);
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  dma(min(1, nblocks - 1), 1);
+  dma(min(2, nblocks - 1), 2);
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NPW) : "memory");
   __syncthreads();
   read_k(0, 0);
   s_mfma(0, kYes());
   // Blocks at or below the tile's first position need no mask. The first
-  // block sets the references.
+  // block sets the references. Block j sits in buffer j % 4.
   const int nfull = min((pos_first + 1) / kKeyBlock, nblocks);
   iteration(0, 0, 1, nfull < 1, kYes(), kNo());
   for (int j = 1, buf = 1; j < nblocks; ++j) {
-    const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;
+    const int nbuf = (buf + 1) % NBUF;
     iteration(j, buf, nbuf, j >= nfull, kNo(), kYes());
     buf = nbuf;
   }
   pv_mfma(3);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS-DMA may outlive the workgroup
 
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -494,7 +514,7 @@ __global__ __launch_bounds__(256, 2) void prefill_qp_kernel(PrefillParams p, int
 // Consecutive halves belong to the same rows, so a reference move in step t
 // also shifts the S^T of half t+1, which that step already computed.
 //
-// K/V go through LDS-DMA into three 32 KiB buffers (one workgroup per CU).
+// K/V go through LDS-DMA into four 32 KiB buffers (one workgroup per CU).
 // Rows are 256 bytes, so every row covers all 64 banks; the chunk swizzle
 // swaps the two 2-bit fields of the row's low 4 bits, which makes a 16-byte
 // K read over 16 rows and a transposing V read over 8 rows x 64 bytes both
@@ -510,7 +530,7 @@ __global__ __launch_bounds__(512, 1) void prefill_d128_kernel(PrefillParams p, i
   constexpr int MATB = kKeyBlock * ROWB;        // bytes of one K or V block
   constexpr int NPW = MATB / 1024 / kWaves8;    // 1 KiB LDS-DMA chunks per wavefront per matrix
   static_assert(NPW >= 1, "block too small for the LDS-DMA split");
-  constexpr int NBUF = 3;
+  constexpr int NBUF = 4;
   __shared__ __attribute__((aligned(1024))) char lds[NBUF][2][MATB];  // [buffer][K, V]
 
   const TileCoord tc = tile_of_block(p, tiles_r, tiles_s);
@@ -519,7 +539,7 @@ __global__ __launch_bounds__(512, 1) void prefill_d128_kernel(PrefillParams p, i
   const int kvh = (v == p.G) ? 0 : v;
   const int nrows = (v == p.G) ? p.S : p.S * p.K;
   const int r0 = tc.tile * kTileRows;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int last_r = min(r0 + kTileRows, nrows) - 1;
   int pos_last, pos_first, s_, h_;
@@ -558,15 +578,34 @@ __global__ __launch_bounds__(512, 1) void prefill_d128_kernel(PrefillParams p, i
   constexpr int RPC = 1024 / ROWB;  // key rows per 1 KiB chunk
   const int dma_r = (16 * lane) / ROWB;
   const int dma_p = ((16 * lane) % ROWB) / 16;
-  auto dma = [&](const int kb, const int bf) __attribute__((always_inline)) {
+  // as in the d <= 64 form: a fixed per-lane offset and a scalar block base,
+  // per-lane clamped addresses only for a block that runs past the sequence
+  uint32_t dma_off[NPW];
 #pragma unroll
-    for (int i = 0; i < NPW; ++i) {
-      const int n = wave * NPW + i;
-      const int rb = n * RPC + dma_r;
-      const int row = min(kb * kKeyBlock + rb, p.S - 1);  // past the sequence: its last key (masked)
-      const int64_t g = (int64_t)row * D + 8 * (dma_p ^ swz(rb));
-      __builtin_amdgcn_global_load_lds(kbase + g, (__attribute__((address_space(3))) void*)(lds[bf][0] + n * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vbase + g, (__attribute__((address_space(3))) void*)(lds[bf][1] + n * 1024), 16, 0, 0);
+  for (int i = 0; i < NPW; ++i) {
+    const int rb = (wave * NPW + i) * RPC + dma_r;
+    dma_off[i] = rb * ROWB + 16 * (dma_p ^ swz(rb));
+  }
+  auto dma = [&](const int kb, const int bf) __attribute__((always_inline)) {
+    if ((kb + 1) * kKeyBlock <= p.S) {
+      const __bf16* kblk = kbase + (int64_t)kb * kKeyBlock * D;
+      const __bf16* vblk = vbase + (int64_t)kb * kKeyBlock * D;
+#pragma unroll
+      for (int i = 0; i < NPW; ++i) {
+        const int n = wave * NPW + i;
+        lds_dma16_s(kblk, dma_off[i], lds[bf][0] + n * 1024);
+        lds_dma16_s(vblk, dma_off[i], lds[bf][1] + n * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NPW; ++i) {
+        const int n = wave * NPW + i;
+        const int rb = n * RPC + dma_r;
+        const int row = min(kb * kKeyBlock + rb, p.S - 1);  // past the sequence: its last key (masked)
+        const int64_t g = (int64_t)row * D + 8 * (dma_p ^ swz(rb));
+        lds_dma16(kbase + g, lds[bf][0] + n * 1024);
+        lds_dma16(vbase + g, lds[bf][1] + n * 1024);
+      }
     }
   };
 
@@ -686,7 +725,6 @@ __global__ __launch_bounds__(512, 1) void prefill_d128_kernel(PrefillParams p, i
     l_run += ls[i];
   };
   auto interleave = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
 #pragma unroll
     for (int i = 0; i < KS + 2 * DB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -702,25 +740,27 @@ __global__ __launch_bounds__(512, 1) void prefill_d128_kernel(PrefillParams p, i
   // that uses the ones they replace.
   auto iteration = [&](const int j, const int buf, const int nbuf, const bool masked, auto first_tag,
                        auto prev_tag) __attribute__((always_inline)) {
-    // step 0: P V(key half 1 of block j-1) | S^T(key half 1) | softmax(key half 0)
+    // step 0: S^T(key half 1) | P V(key half 1 of block j-1) | softmax(key half 0)
     mask(0, j, masked);
-    if constexpr (decltype(prev_tag)::value) pv_mfma(1);
     s_mfma(1, first_tag);
+    if constexpr (decltype(prev_tag)::value) pv_mfma(1);
     if constexpr (!decltype(first_tag)::value) exps(0);
     interleave();
     settle(0, first_tag);
     read_v(buf, 0);
-    // block j+1 (loaded during the previous block) is complete and visible
-    // after the wait and the barrier; block j+2 then goes into the buffer of
-    // block j-1, whose last reader was step 0
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // block j+1 (loaded two blocks ago) is complete and visible after the
+    // wait, which leaves block j+2's loads in flight, and the barrier; block
+    // j+3 then goes into the buffer of block j-1, whose last reads were
+    // issued in its step 1. Every block issues the same loads (past the last
+    // block it re-loads that one), so the wait count is fixed.
+    __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NPW) : "memory");
     __syncthreads();
-    if (j + 2 < nblocks) dma(j + 2, nbuf == NBUF - 1 ? 0 : nbuf + 1);
+    dma(min(j + 3, nblocks - 1), (buf + 3) % NBUF);
     read_k(nbuf, 0);  // past the last block this reads a stale buffer; the result is unused
-    // step 1: P V(key half 0) | S^T(key half 0 of block j+1) | softmax(key half 1)
+    // step 1: S^T(key half 0 of block j+1) | P V(key half 0) | softmax(key half 1)
     mask(1, j, masked);
-    pv_mfma(0);
     s_mfma(0, kNo());
+    pv_mfma(0);
     exps(1);
     interleave();
     settle(1, kNo());
@@ -729,8 +769,9 @@ __global__ __launch_bounds__(512, 1) void prefill_d128_kernel(PrefillParams p, i
   };
 
   dma(0, 0);
-  if (1 < nblocks) dma(1, 1);
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  dma(min(1, nblocks - 1), 1);
+  dma(min(2, nblocks - 1), 2);
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NPW) : "memory");
   __syncthreads();
   read_k(0, 0);
   s_mfma(0, kYes());
@@ -740,11 +781,12 @@ __global__ __launch_bounds__(512, 1) void prefill_d128_kernel(PrefillParams p, i
   const int nfull = min((pos_first + 1) / kKeyBlock, nblocks);
   iteration(0, 0, 1, nfull < 1, kYes(), kNo());
   for (int j = 1, buf = 1; j < nblocks; ++j) {
-    const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;
+    const int nbuf = (buf + 1) % NBUF;
     iteration(j, buf, nbuf, j >= nfull, kNo(), kYes());
     buf = nbuf;
   }
   pv_mfma(1);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS-DMA may outlive the workgroup
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!row_ok) return;
