@@ -166,7 +166,7 @@ __global__ __launch_bounds__(512, 1) void out_proj_gemm_kernel(OutProjParams p) 
   __shared__ __attribute__((aligned(1024))) char lds[kGStages * SB];
   __shared__ __attribute__((aligned(16))) __bf16 obar[kGT][OPAD];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int wm = wave & 1, wn = wave >> 1;  // token half, column quarter
   const int64_t m0 = (int64_t)blockIdx.x * kGT;
@@ -210,15 +210,14 @@ __global__ __launch_bounds__(512, 1) void out_proj_gemm_kernel(OutProjParams p) 
     if (k0 < hard) asrc = orr + a_t * hard + k0 + 8 * a_c;
     else if (k0 >= hard + DH) asrc = os + a_t * DH + (k0 - hard - DH) + 8 * a_c;
     else asrc = orr + a_t * hard + 8 * a_c;  // obar step: a dummy load, the tile is not read
-    __builtin_amdgcn_global_load_lds(asrc, (__attribute__((address_space(3))) void*)(sbase + wave * 1024), 16, 0, 0);
+    lds_dma16(asrc, sbase + wave * 1024);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int n = 2 * wave + i;
       const int row = 2 * n + (lane >> 5);
       const int c = (lane & 31) ^ ((row & 3) << 2);
       const int col = min(n0 + 8 * c, p.Dout - 8);
-      __builtin_amdgcn_global_load_lds(wo + (int64_t)(k0 + row) * p.Dout + col,
-                                       (__attribute__((address_space(3))) void*)(sbase + AB + n * 1024), 16, 0, 0);
+      lds_dma16(wo + (int64_t)(k0 + row) * p.Dout + col, sbase + AB + n * 1024);
     }
   };
 
