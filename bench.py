@@ -58,8 +58,13 @@ def decode_kv_bytes(cfg) -> int:
 
 
 def source_sha(name: str) -> str:
-    with open(os.path.join(ROOT, "sparse_query_gqa_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source together with the internal header it includes
+    (shared device helpers), so that a change to either retires old counters."""
+    h = hashlib.sha256()
+    for n in (name, "gqe_internal.h"):
+        with open(os.path.join(ROOT, "sparse_query_gqa_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel_file: str, summary: str):
