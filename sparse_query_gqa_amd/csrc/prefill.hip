@@ -653,13 +653,20 @@ __global__ __launch_bounds__(512, 1) void prefill_d128_kernel(PrefillParams p, i
   };
   // S^T of a key half into slot i; the accumulator starts at -mr (0 in the
   // first block, which sets the reference)
-  auto s_mfma = [&](const int i, auto first_tag) __attribute__((always_inline)) {
-    f32x16 init;
+  // -mr as a kept 16-register MFMA accumulator, rewritten (asm moves tied to
+  // the old value, so it stays in place) only when the reference moves
+  f32x16 bias = {};
+  auto set_bias = [&]() __attribute__((always_inline)) {
+    const float nm = -mr;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) init[j] = decltype(first_tag)::value ? 0.f : -mr;
+    for (int j = 0; j < 16; ++j) __asm__("v_mov_b32 %0, %1" : "+v"(bias[j]) : "v"(nm));
+  };
+  auto s_mfma = [&](const int i, auto first_tag) __attribute__((always_inline)) {
+    const f32x16 zero16 = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      sh[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], s == 0 ? init : sh[i], 0, 0, 0);
+      sh[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          kf[s], qf[s], s == 0 ? (decltype(first_tag)::value ? zero16 : bias) : sh[i], 0, 0, 0);
   };
   auto pv_mfma = [&](const int i) __attribute__((always_inline)) {
 #pragma unroll
@@ -690,6 +697,7 @@ __global__ __launch_bounds__(512, 1) void prefill_d128_kernel(PrefillParams p, i
     // key 0 is visible to every row, so bmax is finite in the first block
     const float delta = FIRST ? bmax : fmaxf(bmax, 0.f);
     mr += delta;
+    set_bias();
     if constexpr (!FIRST) {
       const float alpha = __builtin_amdgcn_exp2f(-delta);
       l_run *= alpha;
