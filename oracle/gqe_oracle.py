@@ -49,7 +49,8 @@ import numpy as np
 __all__ = [
     "softmax", "topk_select", "route_logits", "route_select", "route",
     "build_lists", "attend_rows", "prefill", "decode", "assemble", "out_proj",
-    "layer", "kv_bytes", "prefill_flops", "check_dims",
+    "layer", "kv_bytes", "prefill_flops", "check_dims", "project",
+    "project_decode", "project_flops",
 ]
 
 
@@ -272,6 +273,72 @@ def layer(x, w_r, Q, K, V, W_O, G: int, k: int, b_r=None):
     T = B * S
     y = out_proj(O_r.reshape(T, G, k, d), w, O_s.reshape(T, d), W_O)
     return dict(z=z, p=p, idx=idx, w=w, O_r=O_r, O_s=O_s, y=y)
+
+
+def project(x, W_Q, W_K, W_V, idx, N: int, G: int):
+    """Query, key and value projections of a prefill, Q compacted to the
+    heads that are used.
+
+    [GQE-review] §二: only the selected query heads take part in attention and
+    the rest are skipped, so only their query rows are computed; the shared
+    head s(x_i) is computed for every token. [GQA-zone] §4.3: queries carry H
+    heads and keys/values G heads (stored here as [B, G, S, d]).
+    The projections are linear without bias (a reading: the pages give no
+    other form): q_{i,h} = W_Q[h] x_i, where W_Q[h] is rows h*d .. h*d+d-1 of
+    W_Q and block N is the shared head; k_{i,g} = W_K[g] x_i, v_{i,g} =
+    W_V[g] x_i with G blocks of d rows each.
+    x: [B, S, D]; W_Q: [(N+1)*d, D]; W_K, W_V: [G*d, D]; idx: [B, S, G, k].
+    Returns (Q [B, S, N+1, d], NaN in every row that is not computed,
+    K [B, G, S, d], V [B, G, S, d]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    idx = np.asarray(idx)
+    B, S, D = x.shape
+    M = check_dims(N, G, idx.shape[-1])
+    W_Q = np.asarray(W_Q, dtype=np.float64)
+    d = W_Q.shape[0] // (N + 1)
+    Wq = W_Q.reshape(N + 1, d, D)
+    Q = np.full((B, S, N + 1, d), np.nan)
+    for h in range(N):
+        g, m = divmod(h, M)
+        chose = np.any(idx[:, :, g, :] == m, axis=-1)  # [B, S]: tokens whose group g picked m
+        Q[chose, h] = x[chose] @ Wq[h].T
+    Q[:, :, N] = x @ Wq[N].T
+    K = (x @ np.asarray(W_K, dtype=np.float64).T).reshape(B, S, G, d).transpose(0, 2, 1, 3)
+    V = (x @ np.asarray(W_V, dtype=np.float64).T).reshape(B, S, G, d).transpose(0, 2, 1, 3)
+    return Q, K, V
+
+
+def project_decode(x, W_Q, W_K, W_V, idx, N: int, G: int, kv_len, K_cache, V_cache):
+    """The projections of q_len new tokens per sequence, with their key and
+    value rows written into the caches.
+
+    New token t of sequence b sits at absolute position kv_len[b]-q_len+t
+    ([GQA-zone] §技术深化: a decode query's absolute position), which is the
+    cache row that receives its key and value; no other row changes.
+    x: [B, q_len, D]; idx: [B, q_len, G, k]; kv_len: [B];
+    K_cache, V_cache: [B, G, S_max, d].
+    Returns (Q [B, q_len, N+1, d] with NaN rows as in project, the new K cache,
+    the new V cache).
+    """
+    Q, K, V = project(x, W_Q, W_K, W_V, idx, N, G)
+    Kc = np.array(K_cache, dtype=np.float64, copy=True)
+    Vc = np.array(V_cache, dtype=np.float64, copy=True)
+    L = Q.shape[1]
+    for b in range(Q.shape[0]):
+        n = int(kv_len[b])
+        if n < L or n > Kc.shape[2]:
+            raise ValueError("kv_len must satisfy q_len <= kv_len <= S_max")
+        Kc[b, :, n - L:n] = K[b]
+        Vc[b, :, n - L:n] = V[b]
+    return Q, Kc, Vc
+
+
+def project_flops(T: int, D: int, G: int, k: int, d: int) -> int:
+    """Matmul FLOP of the projections: 2*D per output element, with
+    (G*k+1)*d query columns (the selected heads and the shared head) and
+    2*G*d key/value columns per token."""
+    return 2 * T * D * ((G * k + 1) * d + 2 * G * d)
 
 
 def kv_bytes(B: int, L: int, G: int, d: int, S: int, b: int) -> int:

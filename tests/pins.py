@@ -361,4 +361,122 @@ def pin_flop_count(O):
         assert O.prefill_flops(B, S, G, k, d) == 4 * d * pairs
 
 
+# --------------------------------------------------------------------------
+# Projections: token-compacted Q, dense K/V, decode append
+# --------------------------------------------------------------------------
+
+def _selector_weights(N, G, d, D):
+    """W_Q block h copies coordinates h*d..h*d+d-1 of x (the shared block N
+    included); W_K block g copies the G*d coordinates after those, and W_V
+    block g twice the G*d coordinates after the keys'."""
+    W_Q = np.zeros(((N + 1) * d, D))
+    W_K = np.zeros((G * d, D))
+    W_V = np.zeros((G * d, D))
+    for r in range((N + 1) * d):
+        W_Q[r, r] = 1.0
+    for r in range(G * d):
+        W_K[r, (N + 1) * d + r] = 1.0
+        W_V[r, (N + 1 + G) * d + r] = 2.0
+    return W_Q, W_K, W_V
+
+
+def _random_idx(rng, B, S, G, M, k):
+    return np.sort(rng.permuted(np.tile(np.arange(M), (B, S, G, 1)), axis=-1)[..., :k], -1)
+
+
+def pin_projection_closed_form(O):
+    """With coordinate-selecting weights every projected row is a slice of x:
+    the selected heads' and the shared head's query rows, every key and value
+    row; the rows of heads a token did not select are not computed."""
+    rng = np.random.default_rng(11)
+    B, S, N, G, k, d = 2, 7, 6, 2, 2, 3
+    M = N // G
+    D = (N + 1 + 2 * G) * d + 5
+    x = rng.standard_normal((B, S, D))
+    W_Q, W_K, W_V = _selector_weights(N, G, d, D)
+    idx = _random_idx(rng, B, S, G, M, k)
+    Q, K, V = O.project(x, W_Q, W_K, W_V, idx, N, G)
+    assert Q.shape == (B, S, N + 1, d) and K.shape == (B, G, S, d) and V.shape == (B, G, S, d)
+    kb, vb = (N + 1) * d, (N + 1 + G) * d
+    for b in range(B):
+        for i in range(S):
+            chosen = {g * M + int(m) for g in range(G) for m in idx[b, i, g]} | {N}
+            for h in range(N + 1):
+                if h in chosen:
+                    _close(Q[b, i, h], x[b, i, h * d:(h + 1) * d], what=f"q of head {h}")
+                else:
+                    assert np.all(np.isnan(Q[b, i, h])), f"unselected head {h} of token {i} computed"
+            for g in range(G):
+                _close(K[b, g, i], x[b, i, kb + g * d:kb + (g + 1) * d], what=f"k of group {g}")
+                _close(V[b, g, i], 2 * x[b, i, vb + g * d:vb + (g + 1) * d], what=f"v of group {g}")
+
+
+def pin_projection_dense_reduction(O):
+    """k = M selects every head, so the compacted projection equals the dense
+    linear layer torch.nn.functional.linear(x, W) = x W^T: all N+1 query
+    heads, and K and V laid out [B, G, S, d]."""
+    rng = np.random.default_rng(12)
+    B, S, N, G, d, D = 2, 9, 8, 2, 4, 24
+    M = N // G
+    x = rng.standard_normal((B, S, D))
+    W_Q, W_K, W_V = (rng.standard_normal((r, D)) for r in ((N + 1) * d, G * d, G * d))
+    idx = np.broadcast_to(np.arange(M), (B, S, G, M)).copy()
+    Q, K, V = O.project(x, W_Q, W_K, W_V, idx, N, G)
+
+    def lin(w):
+        return torch.nn.functional.linear(torch.from_numpy(x), torch.from_numpy(w)).numpy()
+
+    _close(Q, lin(W_Q).reshape(B, S, N + 1, d), 1e-10, "dense Q")
+    _close(K, lin(W_K).reshape(B, S, G, d).transpose(0, 2, 1, 3), 1e-10, "dense K")
+    _close(V, lin(W_V).reshape(B, S, G, d).transpose(0, 2, 1, 3), 1e-10, "dense V")
+
+
+def pin_projection_row_count(O):
+    """Every token computes exactly G*k routed query rows plus the shared one:
+    9 of 17 heads at N = 16, G = 8, k = 1 ([GQE-review] §二: 8 routed heads
+    plus the shared head per token). The FLOP count is 2*D per computed
+    output value."""
+    rng = np.random.default_rng(13)
+    B, S, N, G, k, d, D = 2, 6, 16, 8, 1, 2, 8
+    x = rng.standard_normal((B, S, D))
+    W_Q, W_K, W_V = (rng.standard_normal((r, D)) for r in ((N + 1) * d, G * d, G * d))
+    idx = _random_idx(rng, B, S, G, N // G, k)
+    Q, K, V = O.project(x, W_Q, W_K, W_V, idx, N, G)
+    computed = ~np.all(np.isnan(Q), axis=-1)  # [B, S, N+1]
+    assert np.all(computed.sum(axis=-1) == 9) and np.all(computed[..., N])
+    n_out = int(computed.sum()) * d + K.size + V.size
+    assert O.project_flops(B * S, D, G, k, d) == 2 * D * n_out
+
+
+def pin_decode_append(O):
+    """The new tokens' keys and values land in cache rows kv_len-q_len+t and
+    nowhere else; their queries are the prefill projection of the same
+    tokens."""
+    rng = np.random.default_rng(14)
+    B, L, N, G, k, d, Smax = 3, 2, 4, 2, 1, 2, 9
+    D = (N + 1 + 2 * G) * d
+    x = rng.standard_normal((B, L, D))
+    W_Q, W_K, W_V = _selector_weights(N, G, d, D)
+    idx = _random_idx(rng, B, L, G, N // G, k)
+    kv_len = np.array([2, 5, 9])
+    Kc0 = rng.standard_normal((B, G, Smax, d))
+    Vc0 = rng.standard_normal((B, G, Smax, d))
+    Q, Kc, Vc = O.project_decode(x, W_Q, W_K, W_V, idx, N, G, kv_len, Kc0, Vc0)
+    kb, vb = (N + 1) * d, (N + 1 + G) * d
+    for b in range(B):
+        n = int(kv_len[b])
+        for j in range(Smax):
+            t = j - (n - L)
+            if 0 <= t < L:
+                for g in range(G):
+                    _close(Kc[b, g, j], x[b, t, kb + g * d:kb + (g + 1) * d], what="appended k")
+                    _close(Vc[b, g, j], 2 * x[b, t, vb + g * d:vb + (g + 1) * d], what="appended v")
+            else:
+                assert np.array_equal(Kc[b, :, j], Kc0[b, :, j]), f"cache row {j} of sequence {b} changed"
+                assert np.array_equal(Vc[b, :, j], Vc0[b, :, j]), f"cache row {j} of sequence {b} changed"
+    Qp, _, _ = O.project(x, W_Q, W_K, W_V, idx, N, G)
+    assert np.array_equal(np.isnan(Q), np.isnan(Qp))
+    _close(np.nan_to_num(Q), np.nan_to_num(Qp), what="decode queries")
+
+
 ALL_PINS = [v for kname, v in sorted(globals().items()) if kname.startswith("pin_")]

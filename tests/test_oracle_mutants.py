@@ -72,6 +72,21 @@ MUTANTS = {
         "tok[b, g, pos:pos + rows.size] = rows", "tok[b, g, pos:pos + rows.size] = rows[::-1]"),
     "reject_nothing": (
         "if G <= 0 or N <= 0 or N % G != 0:", "if G <= 0 or N <= 0:"),
+    "proj_head_mapping_transposed": (
+        "        g, m = divmod(h, M)", "        m, g = divmod(h, G)"),
+    "proj_shared_head_from_block0": (
+        "    Q[:, :, N] = x @ Wq[N].T", "    Q[:, :, N] = x @ Wq[0].T"),
+    "proj_every_head_computed": (
+        "        Q[chose, h] = x[chose] @ Wq[h].T", "        Q[:, :, h] = x @ Wq[h].T"),
+    "proj_k_layout_token_major": (
+        "K = (x @ np.asarray(W_K, dtype=np.float64).T).reshape(B, S, G, d).transpose(0, 2, 1, 3)",
+        "K = (x @ np.asarray(W_K, dtype=np.float64).T).reshape(B, G, S, d)"),
+    "proj_v_from_key_weights": (
+        "V = (x @ np.asarray(W_V, dtype=np.float64).T)", "V = (x @ np.asarray(W_K, dtype=np.float64).T)"),
+    "decode_append_at_cache_start": (
+        "        Kc[b, :, n - L:n] = K[b]", "        Kc[b, :, 0:L] = K[b]"),
+    "proj_flops_without_shared_head": (
+        "return 2 * T * D * ((G * k + 1) * d + 2 * G * d)", "return 2 * T * D * (G * k * d + 2 * G * d)"),
     "flops_strict_triangle": (
         "return 4 * d * (G * k + 1) * B * S * (S + 1) // 2", "return 4 * d * (G * k + 1) * B * S * (S - 1) // 2"),
 }
