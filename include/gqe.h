@@ -150,6 +150,44 @@ int gqe_out_proj(const gqe_dims* dims, int64_t T, const void* o_routed,
                  const float* topk_w, const void* o_shared, const void* w_o,
                  void* y, void* stream);
 
+/* Query, key and value projections of a prefill with token-compacted
+ * queries. GQE review, section 二: only the selected query heads take part in
+ * attention, the others are skipped, so only their query rows are projected;
+ * GQA tutorial, 4.3: queries carry N heads, keys and values G heads.
+ *   q_{i,h} = W_Q[h] x_i for the G*k heads token i selected and for the shared
+ *   head h = N; k_{i,g} = W_K[g] x_i and v_{i,g} = W_V[g] x_i for every token
+ *   and group, where W[h] is rows h*d .. h*d+d-1 of W (no bias).
+ *   x        [B, S, D]       dtype
+ *   w_q      [(N+1)*d, D]    dtype (block N projects the shared head)
+ *   w_k, w_v [G*d, D]        dtype
+ *   topk_idx [B*S, G, k]     int32, list_off [B, G, M+1], list_tok [B, G, k*S]
+ *            int32, all as written by gqe_route (the lists must match topk_idx)
+ *   q        [B, S, N+1, d]  dtype out: the rows of the selected heads and of
+ *            the shared head are written; rows of unselected heads keep their
+ *            previous contents
+ *   k, v     [B, G, S, d]    dtype out
+ * bf16 needs D % 64 == 0 (else GQE_ERR_UNSUPPORTED). */
+int gqe_qkv_proj(const gqe_dims* dims, const void* x, const void* w_q,
+                 const void* w_k, const void* w_v, const int32_t* topk_idx,
+                 const int32_t* list_off, const int32_t* list_tok, void* q,
+                 void* k, void* v, void* stream);
+
+/* The same projections for q_len new tokens per sequence in decode, with the
+ * new keys and values written into the cache: token t of sequence b goes to
+ * cache row kv_len[b] - q_len + t, its absolute position (GQA tutorial,
+ * 技术深化). No other cache row is touched.
+ *   x        [B, q_len, D]   dtype; topk_idx [B*q_len, G, k] int32
+ *   kv_len   [B] int32 device, q_len <= kv_len[b] <= S_max = dims->S (not
+ *            checkable without a device sync; a violating entry makes that
+ *            sequence's writes land in unspecified rows of its own cache)
+ *   q        [B, q_len, N+1, d] dtype out (selected heads and shared head)
+ *   k_cache, v_cache [B, G, S_max, d] dtype, updated in place
+ * bf16 needs D % 64 == 0. */
+int gqe_qkv_proj_decode(const gqe_dims* dims, int32_t q_len, const void* x,
+                        const void* w_q, const void* w_k, const void* w_v,
+                        const int32_t* topk_idx, const int32_t* kv_len,
+                        void* q, void* k_cache, void* v_cache, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

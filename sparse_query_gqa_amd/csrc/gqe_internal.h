@@ -75,6 +75,21 @@ struct OutProjParams {
   int Gk, d, Dout;
 };
 
+struct ProjParams {
+  const void* x;           // [T, D], T = B*L
+  const void* w_q;         // [(N+1)*d, D]
+  const void* w_k;         // [G*d, D]
+  const void* w_v;         // [G*d, D]
+  const int32_t* topk;     // [T, G, k]
+  const int32_t* list_off; // [B, G, M+1] (prefill)
+  const int32_t* list_tok; // [B, G, k*L] (prefill)
+  const int32_t* kv_len;   // [B] (decode) or null (prefill)
+  void* q;                 // [T, N+1, d]
+  void* k;                 // [B, G, Smax, d]
+  void* v;                 // [B, G, Smax, d]
+  int T, B, L, D, N, G, M, K, d, Smax;
+};
+
 // Decode split geometry shared by the workspace query and the launcher.
 struct DecodeSplit {
   int rows;    // (k+1)*q_len
@@ -88,6 +103,7 @@ hipError_t launch_lists(const ListParams& p, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int d, bool bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s);
 hipError_t launch_out_proj(const OutProjParams& p, bool bf16, hipStream_t s);
+hipError_t launch_proj(const ProjParams& p, bool bf16, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Small device helpers

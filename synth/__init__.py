@@ -13,7 +13,9 @@ float32 ``standard_normal``):
 * decode: x [B,q_len,D] ~ N(0,1); then W_Q, W_r, W_O as above. The KV cache
   K,V [B,G,S_max,d] ~ N(0,1) is drawn per (b, g) block from
   ``default_rng([seed, b, g, t])`` with t=0 for K and t=1 for V, so blocks can
-  be drawn in parallel threads.
+  be drawn in parallel threads. The decode layer's W_K and W_V (used only
+  to project and append the new tokens' keys and values) come from
+  ``default_rng([seed, 303])``, so the draws above are unchanged.
 * bf16 workloads round x and every weight to bfloat16 (round to nearest even).
   Q, K and V are the fp32 products x @ W^T of those rounded values, then
   rounded to bfloat16. The projections are input preparation, not part of the
@@ -138,8 +140,10 @@ def _proj(x: torch.Tensor, w: torch.Tensor, cfg: GQEConfig) -> torch.Tensor:
     return y.to(cfg.torch_dtype)
 
 
-def make_prefill_inputs(cfg: GQEConfig) -> dict:
-    """CPU tensors for one prefill invocation (see the module docstring)."""
+def make_prefill_inputs(cfg: GQEConfig, project: bool = True) -> dict:
+    """CPU tensors for one prefill invocation (see the module docstring).
+    With ``project`` False the prepared q, k, v are left out (the draws are
+    the same)."""
     assert cfg.mode == "prefill"
     B, S, D, N, G, k, d, M = cfg.B, cfg.S, cfg.D, cfg.N, cfg.G, cfg.k, cfg.d, cfg.M
     rng = np.random.default_rng(cfg.seed)
@@ -149,10 +153,12 @@ def make_prefill_inputs(cfg: GQEConfig) -> dict:
     w_v = _store(rng.standard_normal((G * d, D), dtype=np.float32) * np.float32(0.02), cfg)
     w_r = _store(rng.standard_normal((G * M, D), dtype=np.float32) * np.float32(0.02), cfg)
     w_o = _store(rng.standard_normal(((G * k + 2) * d, D), dtype=np.float32) * np.float32(0.02), cfg)
-    q = _proj(x, w_q, cfg).reshape(B, S, N + 1, d).contiguous()
-    kk = _proj(x, w_k, cfg).reshape(B, S, G, d).permute(0, 2, 1, 3).contiguous()
-    vv = _proj(x, w_v, cfg).reshape(B, S, G, d).permute(0, 2, 1, 3).contiguous()
-    return dict(x=x, w_r=w_r, b_r=_router_bias(cfg), q=q, k=kk, v=vv, w_o=w_o)
+    q = kk = vv = None
+    if project:
+        q = _proj(x, w_q, cfg).reshape(B, S, N + 1, d).contiguous()
+        kk = _proj(x, w_k, cfg).reshape(B, S, G, d).permute(0, 2, 1, 3).contiguous()
+        vv = _proj(x, w_v, cfg).reshape(B, S, G, d).permute(0, 2, 1, 3).contiguous()
+    return dict(x=x, w_r=w_r, b_r=_router_bias(cfg), q=q, k=kk, v=vv, w_o=w_o, w_q=w_q, w_k=w_k, w_v=w_v)
 
 
 def _cache_block(seed: int, b: int, g: int, t: int, S: int, d: int, bf16: bool):
@@ -184,7 +190,11 @@ def make_decode_inputs(cfg: GQEConfig, threads: Optional[int] = None) -> dict:
         list(ex.map(fill, jobs))
     kv_len = cfg.kv_len if cfg.kv_len is not None else S
     kvl = torch.full((B,), kv_len, dtype=torch.int32)
-    return dict(x=x, w_r=w_r, b_r=_router_bias(cfg), q=q, k=kc, v=vc, kv_len=kvl, w_o=w_o)
+    rng_kv = np.random.default_rng([cfg.seed, 303])
+    w_k = _store(rng_kv.standard_normal((G * d, D), dtype=np.float32) * np.float32(0.02), cfg)
+    w_v = _store(rng_kv.standard_normal((G * d, D), dtype=np.float32) * np.float32(0.02), cfg)
+    return dict(x=x, w_r=w_r, b_r=_router_bias(cfg), q=q, k=kc, v=vc, kv_len=kvl, w_o=w_o, w_q=w_q,
+                w_k=w_k, w_v=w_v)
 
 
 def random_selection(B: int, S: int, G: int, M: int, k: int, seed: int,

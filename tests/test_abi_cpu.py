@@ -140,6 +140,41 @@ def test_out_proj_validation():
     assert call(_dims(), T=0) == gqe.GQE_OK
 
 
+def test_qkv_proj_validation():
+    lib = _lib()
+
+    def call(dims, x=A, lo=A, q=A, k=A):
+        return lib.gqe_qkv_proj(ctypes.byref(dims), P(x), P(A), P(A), P(A), P(A), P(lo), P(A), P(q),
+                                P(k), P(A), None)
+
+    assert call(_dims(N=8, G=3)) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(d=96)) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(D=96)) == gqe.GQE_ERR_UNSUPPORTED            # bf16 needs D % 64 == 0
+    assert call(_dims(), x=0) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), lo=0) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), q=MIS) == gqe.GQE_ERR_ALIGNMENT
+    assert call(_dims(B=0)) == gqe.GQE_OK
+    assert call(_dims(S=0)) == gqe.GQE_OK
+    assert call(_dims(B=0, D=96, dtype=gqe.GQE_F32)) == gqe.GQE_OK  # fp32 takes any D % 8
+
+
+def test_qkv_proj_decode_validation():
+    lib = _lib()
+
+    def call(dims, L=1, kv=A, kc=A):
+        return lib.gqe_qkv_proj_decode(ctypes.byref(dims), L, P(A), P(A), P(A), P(A), P(A), P(kv), P(A),
+                                       P(kc), P(A), None)
+
+    assert call(_dims(), L=-1) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), kv=0) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), kc=MIS) == gqe.GQE_ERR_ALIGNMENT
+    assert call(_dims(S=4), L=5) == gqe.GQE_ERR_INVALID_ARG          # q_len > S_max
+    assert call(_dims(D=96)) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(N=8, G=3)) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(B=0)) == gqe.GQE_OK
+    assert call(_dims(), L=0) == gqe.GQE_OK
+
+
 def test_workspace_sizes_closed_form():
     lib = _lib()
     d = _dims(B=16, S=65536, N=32, G=8, k=2, d=128)
