@@ -160,8 +160,9 @@ int gqe_out_proj(const gqe_dims* dims, int64_t T, const void* o_routed,
  *   x        [B, S, D]       dtype
  *   w_q      [(N+1)*d, D]    dtype (block N projects the shared head)
  *   w_k, w_v [G*d, D]        dtype
- *   topk_idx [B*S, G, k]     int32, list_off [B, G, M+1], list_tok [B, G, k*S]
- *            int32, all as written by gqe_route (the lists must match topk_idx)
+ *   topk_idx [B*S, G, k]     int32 (as written by gqe_route); a routed head's
+ *            rows are the tokens whose top-k holds it, the rows of its
+ *            expert-major token list
  *   q        [B, S, N+1, d]  dtype out: the rows of the selected heads and of
  *            the shared head are written; rows of unselected heads keep their
  *            previous contents
@@ -169,8 +170,7 @@ int gqe_out_proj(const gqe_dims* dims, int64_t T, const void* o_routed,
  * bf16 needs D % 64 == 0 (else GQE_ERR_UNSUPPORTED). */
 int gqe_qkv_proj(const gqe_dims* dims, const void* x, const void* w_q,
                  const void* w_k, const void* w_v, const int32_t* topk_idx,
-                 const int32_t* list_off, const int32_t* list_tok, void* q,
-                 void* k, void* v, void* stream);
+                 void* q, void* k, void* v, void* stream);
 
 /* The same projections for q_len new tokens per sequence in decode, with the
  * new keys and values written into the cache: token t of sequence b goes to

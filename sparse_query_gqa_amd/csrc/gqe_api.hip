@@ -181,19 +181,18 @@ int gqe_out_proj(const gqe_dims* d, int64_t T, const void* o_routed, const float
 }
 
 int gqe_qkv_proj(const gqe_dims* d, const void* x, const void* w_q, const void* w_k,
-                 const void* w_v, const int32_t* topk_idx, const int32_t* list_off,
-                 const int32_t* list_tok, void* q, void* k, void* v, void* stream) {
+                 const void* w_v, const int32_t* topk_idx, void* q, void* k, void* v,
+                 void* stream) {
   int st = check_dims(d);
   if (st) return st;
-  if (!x || !w_q || !w_k || !w_v || !topk_idx || !list_off || !list_tok || !q || !k || !v)
-    return GQE_ERR_INVALID_ARG;
-  const void* ptrs[] = {x, w_q, w_k, w_v, topk_idx, list_off, list_tok, q, k, v};
+  if (!x || !w_q || !w_k || !w_v || !topk_idx || !q || !k || !v) return GQE_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, w_q, w_k, w_v, topk_idx, q, k, v};
   for (const void* p : ptrs)
     if (!aligned16(p)) return GQE_ERR_ALIGNMENT;
   if (d->dtype == GQE_BF16 && d->D % 64 != 0) return GQE_ERR_UNSUPPORTED;
   if ((int64_t)d->S * d->k > (int64_t)INT32_MAX / 2) return GQE_ERR_UNSUPPORTED;
   if (d->B == 0 || d->S == 0) return GQE_OK;
-  ProjParams pp{x, w_q, w_k, w_v, topk_idx, list_off, list_tok, nullptr, q, k, v,
+  ProjParams pp{x, w_q, w_k, w_v, topk_idx, nullptr, q, k, v,
                 d->B * d->S, d->B, d->S, d->D, d->N, d->G, d->N / d->G, d->k, d->d, d->S};
   if (trace_on())
     fprintf(stderr, "[gqe] qkv_proj B=%d S=%d D=%d N=%d G=%d k=%d d=%d\n", d->B, d->S, d->D, d->N,
@@ -217,7 +216,7 @@ int gqe_qkv_proj_decode(const gqe_dims* d, int32_t q_len, const void* x, const v
   if (d->dtype == GQE_BF16 && d->D % 64 != 0) return GQE_ERR_UNSUPPORTED;
   if ((int64_t)d->B * q_len > (int64_t)INT32_MAX / 2) return GQE_ERR_UNSUPPORTED;
   if (d->B == 0 || q_len == 0) return GQE_OK;
-  ProjParams pp{x, w_q, w_k, w_v, topk_idx, nullptr, nullptr, kv_len, q, k_cache, v_cache,
+  ProjParams pp{x, w_q, w_k, w_v, topk_idx, kv_len, q, k_cache, v_cache,
                 d->B * q_len, d->B, q_len, d->D, d->N, d->G, d->N / d->G, d->k, d->d, d->S};
   if (trace_on())
     fprintf(stderr, "[gqe] qkv_proj_decode B=%d L=%d Smax=%d D=%d N=%d G=%d k=%d d=%d\n", d->B,

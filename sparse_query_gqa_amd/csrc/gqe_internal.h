@@ -81,8 +81,6 @@ struct ProjParams {
   const void* w_k;         // [G*d, D]
   const void* w_v;         // [G*d, D]
   const int32_t* topk;     // [T, G, k]
-  const int32_t* list_off; // [B, G, M+1] (prefill)
-  const int32_t* list_tok; // [B, G, k*L] (prefill)
   const int32_t* kv_len;   // [B] (decode) or null (prefill)
   void* q;                 // [T, N+1, d]
   void* k;                 // [B, G, Smax, d]

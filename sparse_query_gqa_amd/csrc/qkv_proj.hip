@@ -8,14 +8,15 @@
 // rows h*d .. h*d+d-1 of W_Q (block N is the shared head), k_{i,g} =
 // W_K[g] x_i, v_{i,g} = W_V[g] x_i.
 //
-// Work is split into tiles of one head's d output columns by a set of token
-// rows. A routed query head takes its rows from the token list of its
-// (sequence, group, expert), which the router builds, so no row of an
-// unselected head is ever computed; the shared head, K and V take
-// contiguous token ranges. Tile kinds:
-//   * prefill (large T): 256-row tiles on v_mfma_f32_32x32x16_bf16, x rows
-//     gathered straight into LDS by LDS-DMA, k in steps of 32 through a
-//     four-stage ring;
+// Work is split into tiles of output columns by a set of token rows. A
+// routed query head takes only the tokens whose top-k holds it, compacted in
+// token order (the order of the router's expert-major token lists), so no
+// row of an unselected head is ever computed; the shared head, K and V take
+// every token. Tile kinds:
+//   * prefill (large T): windows of 256 tokens, each with 128-column dense
+//     tiles and one routed tile per query head, on v_mfma_f32_32x32x16_bf16;
+//     x rows go straight into LDS by LDS-DMA, k in steps of 32 through a
+//     three-stage ring;
 //   * decode (few tokens, bound by reading the weights): 32-row tiles whose
 //     routed rows are found by scanning the tokens' top-k, the model width
 //     split over the four wavefronts, fragments loaded from global memory,
@@ -30,7 +31,7 @@ namespace {
 
 constexpr int kPRows = 256;  // token rows per prefill tile (4 wavefronts x 64)
 constexpr int kPK = 32;      // k per stage
-constexpr int kPStages = 4;
+constexpr int kPStages = 3;
 constexpr int kDRows = 32;   // token rows per decode tile
 
 // Output row of token ft for head slot `which` (0..N query heads, then K
@@ -60,78 +61,95 @@ __device__ __forceinline__ void* out_base(const ProjParams& p, int kind) {
 }
 
 // ---------------------------------------------------------------------------
-// Prefill tiles. Blocks are laid out per XCD (block i runs on XCD i % 8):
-// logical tile j = (i % 8) * per + i / 8, so consecutive logical tiles share
-// an XCD and its L2. Logical tiles are the contiguous-row tiles first, the
-// 2G+1 heads of one token range next to each other (x read once into that
-// L2), then the routed-query tiles, per (sequence, group) an upper bound of
-// ceil(k*S/256) + M tiles of which the tiles past the lists' real count exit.
+// Prefill tiles, by window of 256 consecutive tokens (flat index b*S + s).
+// A window has ceil((2G+1)*d / 128) dense tiles over the columns [shared
+// query head | G key heads | G value heads], 128 columns each, and N routed
+// tiles, one per query head h = g*M + m, whose rows are the window's tokens
+// with m in their group-g top-k: a ballot over the window in token order,
+// which is the order of the expert-major token lists. Wavefronts skip the
+// 32-row blocks past a routed tile's row count, so the work follows the
+// selected rows. The tiles of a window are consecutive logical tiles, and
+// consecutive logical tiles run on one XCD (block i on XCD i % 8, logical
+// tile (i % 8) * per + i / 8), so the window's x rows come from HBM once and
+// then from that XCD's L2.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void proj_prefill_kernel(ProjParams p, int n_row_tiles,
-                                                                            int e_per_bg, int per) {
-  constexpr int CB = D / 32;              // 32-column blocks of the head
+__global__ __launch_bounds__(256, 2) void proj_prefill_kernel(ProjParams p, int tiles_pw, int n_dense, int per) {
+  constexpr int TC = 128;                 // columns of a dense tile
+  constexpr int CB = TC / 32;             // 32-column blocks (a routed tile uses D / 32)
   constexpr int XB = kPRows * kPK * 2;    // x stage: 256 rows x 64 bytes
-  constexpr int WB = D * kPK * 2;         // W stage: d rows x 64 bytes
+  constexpr int WB = TC * kPK * 2;        // W stage: 128 rows x 64 bytes
   constexpr int SB = XB + WB;
   constexpr int XCH = XB / 1024 / 4;      // 1 KiB x chunks per wavefront per stage
-  constexpr int WCH = WB / 1024;          // 1 KiB W chunks per stage (2, 4 or 8)
-  constexpr int WPW = WCH >= 4 ? WCH / 4 : 1;  // W chunks per wavefront (re-loaded when WCH < 4)
+  constexpr int WCH = WB / 1024 / 4;      // 1 KiB W chunks per wavefront per stage
   __shared__ __attribute__((aligned(1024))) char lds[kPStages * SB];
   __shared__ int rows[kPRows];
+  __shared__ int wcount[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int j = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  const int heads_r = 2 * p.G + 1;  // shared query head, G key heads, G value heads
-  int which, nrows;
-  if (j < n_row_tiles * heads_r) {
-    const int rt = j / heads_r, hs = j - rt * heads_r;
-    which = hs == 0 ? p.N : p.N + hs;
-    const int t0 = rt * kPRows;
-    nrows = min(kPRows, p.T - t0);
-    rows[tid] = t0 + min(tid, nrows - 1);
+  const int win = j / tiles_pw, kt = j - win * tiles_pw;
+  const int t0 = win * kPRows;
+  if (t0 >= p.T) return;
+  const int nwin = min(kPRows, p.T - t0);
+  const int ncols = (2 * p.G + 1) * D;  // dense columns
+  int c0 = 0, qhead = -1, ncb, nrows;
+  if (kt < n_dense) {
+    c0 = kt * TC;
+    ncb = min(CB, (ncols - c0) / 32);
+    nrows = nwin;
+    rows[tid] = t0 + min(tid, nwin - 1);
   } else {
-    const int e = j - n_row_tiles * heads_r;
-    const int bg = e / e_per_bg;
-    if (bg >= p.B * p.G) return;
-    int r = e - bg * e_per_bg;
-    const int b = bg / p.G, g = bg - b * p.G;
-    const int32_t* off = p.list_off + (int64_t)bg * (p.M + 1);
-    int m = 0, n = 0;
-    for (; m < p.M; ++m) {
-      n = off[m + 1] - off[m];
-      const int tiles = (n + kPRows - 1) / kPRows;
-      if (r < tiles) break;
-      r -= tiles;
+    qhead = kt - n_dense;
+    ncb = D / 32;
+    const int g = qhead / p.M, m = qhead - g * p.M;
+    const int ft = t0 + tid;
+    bool keep = tid < nwin;
+    if (keep) {
+      bool chose = false;
+      for (int s = 0; s < p.K; ++s) chose |= p.topk[((int64_t)ft * p.G + g) * p.K + s] == m;
+      keep = chose;
     }
-    if (m == p.M) return;  // past this (sequence, group)'s real tile count
-    which = g * p.M + m;
-    nrows = min(kPRows, n - r * kPRows);
-    const int32_t* lt = p.list_tok + (int64_t)bg * p.K * p.L + off[m] + r * kPRows;
-    rows[tid] = b * p.L + lt[min(tid, nrows - 1)];
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+    if (lane == 0) wcount[wave] = __builtin_popcountll(bal);
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < wave; ++i) base += wcount[i];
+    nrows = wcount[0] + wcount[1] + wcount[2] + wcount[3];
+    if (keep) rows[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0))] = ft;
+    if (nrows == 0) return;  // uniform: no token of the window picked this head
   }
   __syncthreads();
 
-  const __bf16* xg = (const __bf16*)p.x;
-  const __bf16* wh = head_weights(p, which);
   // LDS layout per stage: row r at r*64 bytes, 16-byte chunk c at position
   // c ^ ((r >> 2) & 3), so the 16 rows of a 16-byte fragment read fall on
   // distinct bank groups. DMA: lane l of a 1 KiB chunk writes row l/4,
-  // position l%4, loading the chunk the swizzle puts there.
+  // position l%4, loading the chunk the swizzle puts there. Rows past the
+  // tile's count re-load its last row (not stored); so do W rows past the
+  // tile's columns.
   const int dr = lane >> 2, dp = lane & 3;
   const __bf16* xsrc[XCH];
 #pragma unroll
   for (int i = 0; i < XCH; ++i) {
     const int r = (wave * XCH + i) * 16 + dr;
-    xsrc[i] = xg + (int64_t)rows[r] * p.D + 8 * (dp ^ ((r >> 2) & 3));
+    xsrc[i] = (const __bf16*)p.x + (int64_t)rows[min(r, nrows - 1)] * p.D + 8 * (dp ^ ((r >> 2) & 3));
   }
-  uint32_t woff[WPW];
+  const __bf16* wsrc[WCH];
 #pragma unroll
-  for (int i = 0; i < WPW; ++i) {
-    const int n = (wave * WPW + i) % WCH;
-    const int r = n * 16 + dr;
-    woff[i] = (uint32_t)(r * p.D + 8 * (dp ^ ((r >> 2) & 3))) * 2;
+  for (int i = 0; i < WCH; ++i) {
+    const int r = (wave * WCH + i) * 16 + dr;
+    const int chunk = 8 * (dp ^ ((r >> 2) & 3));
+    const __bf16* row;
+    if (qhead >= 0) {
+      row = (const __bf16*)p.w_q + ((int64_t)qhead * D + min(r, D - 1)) * p.D;
+    } else {
+      const int c = min(c0 + r, ncols - 1);
+      if (c < D) row = (const __bf16*)p.w_q + ((int64_t)p.N * D + c) * p.D;
+      else if (c < D + p.G * D) row = (const __bf16*)p.w_k + (int64_t)(c - D) * p.D;
+      else row = (const __bf16*)p.w_v + (int64_t)(c - D - p.G * D) * p.D;
+    }
+    wsrc[i] = row + chunk;
   }
   const int nk = p.D / kPK;
   auto dma = [&](const int ks, const int st) __attribute__((always_inline)) {
@@ -140,21 +158,22 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void proj_prefill_kernel(Pro
 #pragma unroll
     for (int i = 0; i < XCH; ++i) lds_dma16(xsrc[i] + kk, sb + (wave * XCH + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < WPW; ++i) lds_dma16_s(wh + kk, woff[i], sb + XB + ((wave * WPW + i) % WCH) * 1024);
+    for (int i = 0; i < WCH; ++i) lds_dma16(wsrc[i] + kk, sb + XB + (wave * WCH + i) * 1024);
   };
 
-  // fragments: W rows 32*cb + l32 (A operand), x rows 64*wave + 32*rb + l32
-  // (B operand), chunk 2*ks + half of the stage
+  // fragments: W rows 32*cb + l32 (A operand), x rows 32*(wave + 4*rb) + l32
+  // (B operand: row blocks interleaved over the wavefronts, so a routed tile
+  // that is half full still keeps all four busy), chunk 2*kq + half
+  const int sw = (l32 >> 2) & 3;
   int w_off[2], x_off[2][2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    w_off[ks] = l32 * 64 + 16 * ((2 * ks + half) ^ ((l32 >> 2) & 3));
+  for (int kq = 0; kq < 2; ++kq) {
+    w_off[kq] = l32 * 64 + 16 * ((2 * kq + half) ^ sw);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int r = 64 * wave + 32 * rb + l32;
-      x_off[rb][ks] = r * 64 + 16 * ((2 * ks + half) ^ ((r >> 2) & 3));
-    }
+    for (int rb = 0; rb < 2; ++rb) x_off[rb][kq] = (32 * (wave + 4 * rb) + l32) * 64 + 16 * ((2 * kq + half) ^ sw);
   }
+  // 32-row blocks of this wavefront that hold selected rows (uniform)
+  const bool rb_on0 = 32 * wave < nrows, rb_on1 = 32 * (wave + 4) < nrows;
   f32x16 acc[CB][2];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
@@ -167,47 +186,60 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void proj_prefill_kernel(Pro
   for (int s = 0; s < kPStages - 1; ++s) dma(s, s);
   for (int ks = 0; ks < nk; ++ks) {
     const int st = ks % kPStages;
-    // stage ks is complete when at most the two later stages' loads are
+    // stage ks is complete when at most the next stage's loads are
     // outstanding; the barrier publishes it and frees the stage read in step
-    // ks-1 for step ks+3
-    __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (XCH + WPW)) : "memory");
+    // ks-1 for step ks+2
+    __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(XCH + WCH) : "memory");
     __syncthreads();
     dma(ks + kPStages - 1, (ks + kPStages - 1) % kPStages);
+    if (!rb_on0) continue;
     const char* sb = lds + st * SB;
 #pragma unroll
     for (int kq = 0; kq < 2; ++kq) {
       bf16x8 wf[CB], xf[2];
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) wf[cb] = *(const bf16x8*)(sb + XB + cb * 32 * 64 + w_off[kq]);
-#pragma unroll
       for (int rb = 0; rb < 2; ++rb) xf[rb] = *(const bf16x8*)(sb + x_off[rb][kq]);
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          acc[cb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb], xf[rb], acc[cb][rb], 0, 0, 0);
+      for (int cb = 0; cb < CB; ++cb) {
+        if (cb >= ncb) break;
+        wf[cb] = *(const bf16x8*)(sb + XB + cb * 32 * 64 + w_off[kq]);
+        acc[cb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb], xf[0], acc[cb][0], 0, 0, 0);
+        if (rb_on1) acc[cb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb], xf[1], acc[cb][1], 0, 0, 0);
+      }
     }
   }
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS-DMA may outlive the workgroup
 
-  // lane (half, l32) of tile (cb, rb) holds token row 64*wave + 32*rb + l32
+  // lane (half, l32) of tile (cb, rb) holds token row 32*(wave + 4*rb) + l32
   // and columns 32*cb + 8*(e/4) + 4*half + e%4
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const int r = 64 * wave + 32 * rb + l32;
+    const int r = 32 * (wave + 4 * rb) + l32;
     if (r >= nrows) continue;
-    int kind;
-    const int64_t o = out_row(p, which, rows[r], kind);
-    __bf16* out = (__bf16*)out_base(p, kind) + o;
+    const int ft = rows[r];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+    for (int cb = 0; cb < CB; ++cb) {
+      if (cb >= ncb) break;
+      int which, col;
+      if (qhead >= 0) {
+        which = qhead;
+        col = 32 * cb;
+      } else {
+        const int c = c0 + 32 * cb;
+        which = c < D ? p.N : p.N + 1 + (c - D) / D;
+        col = c < D ? c : (c - D) % D;
+      }
+      int kind;
+      const int64_t o = out_row(p, which, ft, kind);
+      __bf16* out = (__bf16*)out_base(p, kind) + o + col;
 #pragma unroll
       for (int jq = 0; jq < 4; ++jq) {
         bf16x4 o4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o4[e] = f2bf(acc[cb][rb][4 * jq + e]);
-        *(bf16x4*)(out + 32 * cb + 8 * jq + 4 * half) = o4;
+        *(bf16x4*)(out + 8 * jq + 4 * half) = o4;
       }
+    }
   }
 }
 
@@ -239,16 +271,17 @@ __global__ __launch_bounds__(256) void proj_f32_kernel(ProjParams p) {
   ((float*)out_base(p, kind))[o + c] = s;
 }
 
-// Decode tiles: head slot blockIdx.y, chunk blockIdx.x of 32 tokens (flat
-// index b*q_len + t). A routed head keeps the chunk's tokens whose top-k
-// holds it (a ballot, in token order); other slots keep every token. The
-// four wavefronts each take a quarter of the model width; fragments come
-// straight from global memory (the weights are read once, x stays in L2),
-// and the partial tiles are summed in LDS in a fixed order.
-template <int D>
+// Decode tiles: head slot blockIdx.y, 32-column block blockIdx.z of that
+// head, chunk blockIdx.x of 32 tokens (flat index b*q_len + t). A routed head
+// keeps the chunk's tokens whose top-k holds it (a ballot, in token order);
+// other slots keep every token. Splitting the head's columns over blocks
+// spreads the weight reads, which bound this shape, over more CUs. The four
+// wavefronts each take a quarter of the model width; fragments come straight
+// from global memory (the weights are read once, x stays in L2), and the
+// partial tiles are summed in LDS in a fixed order.
 __global__ __launch_bounds__(256) void proj_decode_kernel(ProjParams p) {
-  constexpr int CB = D / 32;
-  constexpr int U = 4;  // k-steps of loads in flight per wavefront
+  constexpr int CB = 1;
+  constexpr int U = 8;  // k-steps of loads in flight per wavefront
   __shared__ int rows[kDRows];
   __shared__ int nrows_s;
   __shared__ float red[4][CB][16][64];
@@ -273,7 +306,8 @@ __global__ __launch_bounds__(256) void proj_decode_kernel(ProjParams p) {
   if (nrows == 0) return;
 
   const __bf16* xr = (const __bf16*)p.x + (int64_t)rows[min(l32, nrows - 1)] * p.D + 8 * half;
-  const __bf16* wh = head_weights(p, which) + (int64_t)l32 * p.D + 8 * half;
+  const int col0 = 32 * blockIdx.z;  // first column of this block within the head
+  const __bf16* wh = head_weights(p, which) + (int64_t)(col0 + l32) * p.D + 8 * half;
   const int kq = p.D / 4;  // model-width quarter of this wavefront
   const int k0 = wave * kq;
   f32x16 acc[CB];
@@ -312,7 +346,7 @@ __global__ __launch_bounds__(256) void proj_decode_kernel(ProjParams p) {
     if (l32 >= nrows) continue;
     int kind;
     const int64_t o = out_row(p, which, rows[l32], kind);
-    __bf16* out = (__bf16*)out_base(p, kind) + o;
+    __bf16* out = (__bf16*)out_base(p, kind) + o + col0;
 #pragma unroll
     for (int jq = 0; jq < 4; ++jq) {
       bf16x4 o4;
@@ -336,24 +370,19 @@ hipError_t launch_proj(const ProjParams& p, bool bf16, hipStream_t s) {
     return hipGetLastError();
   }
   if (p.kv_len) {  // decode: few tokens, (chunk of 32 tokens) x head slot
-    const dim3 grid((unsigned)((p.T + kDRows - 1) / kDRows), (unsigned)heads);
-    switch (p.d) {
-      case 32: hipLaunchKernelGGL(proj_decode_kernel<32>, grid, dim3(256), 0, s, p); break;
-      case 64: hipLaunchKernelGGL(proj_decode_kernel<64>, grid, dim3(256), 0, s, p); break;
-      case 128: hipLaunchKernelGGL(proj_decode_kernel<128>, grid, dim3(256), 0, s, p); break;
-      default: return hipErrorInvalidValue;
-    }
+    const dim3 grid((unsigned)((p.T + kDRows - 1) / kDRows), (unsigned)heads, (unsigned)(p.d / 32));
+    hipLaunchKernelGGL(proj_decode_kernel, grid, dim3(256), 0, s, p);
     return hipGetLastError();
   }
-  const int n_row_tiles = (p.T + kPRows - 1) / kPRows;
-  const int e_per_bg = (p.K * p.L + kPRows - 1) / kPRows + p.M;
-  const int64_t total = (int64_t)n_row_tiles * (2 * p.G + 1) + (int64_t)p.B * p.G * e_per_bg;
+  const int n_dense = ((2 * p.G + 1) * p.d + 127) / 128;
+  const int tiles_pw = n_dense + p.N;
+  const int64_t total = (int64_t)((p.T + kPRows - 1) / kPRows) * tiles_pw;
   const int per = (int)((total + 7) / 8);
   const unsigned nblk = (unsigned)(8 * per);
   switch (p.d) {
-    case 32: hipLaunchKernelGGL(proj_prefill_kernel<32>, dim3(nblk), dim3(256), 0, s, p, n_row_tiles, e_per_bg, per); break;
-    case 64: hipLaunchKernelGGL(proj_prefill_kernel<64>, dim3(nblk), dim3(256), 0, s, p, n_row_tiles, e_per_bg, per); break;
-    case 128: hipLaunchKernelGGL(proj_prefill_kernel<128>, dim3(nblk), dim3(256), 0, s, p, n_row_tiles, e_per_bg, per); break;
+    case 32: hipLaunchKernelGGL(proj_prefill_kernel<32>, dim3(nblk), dim3(256), 0, s, p, tiles_pw, n_dense, per); break;
+    case 64: hipLaunchKernelGGL(proj_prefill_kernel<64>, dim3(nblk), dim3(256), 0, s, p, tiles_pw, n_dense, per); break;
+    case 128: hipLaunchKernelGGL(proj_prefill_kernel<128>, dim3(nblk), dim3(256), 0, s, p, tiles_pw, n_dense, per); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

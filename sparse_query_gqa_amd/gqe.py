@@ -84,7 +84,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gqe_decode_workspace_bytes": (SZ, [D, I32]),
         "gqe_attn_decode": (ctypes.c_int, [D, I32, P, P, P, P, P, P, P, P, SZ, P]),
         "gqe_out_proj": (ctypes.c_int, [D, I64, P, P, P, P, P, P]),
-        "gqe_qkv_proj": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P, P]),
+        "gqe_qkv_proj": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P]),
         "gqe_qkv_proj_decode": (ctypes.c_int, [D, I32, P, P, P, P, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -201,21 +201,18 @@ def gqe_out_proj(dims, T, o_routed, topk_w, o_shared, w_o, y, stream=None):
     _raise(st, "gqe_out_proj")
 
 
-def gqe_qkv_proj(dims, x, w_q, w_k, w_v, topk_idx, list_off, list_tok, q, k, v, stream=None):
+def gqe_qkv_proj(dims, x, w_q, w_k, w_v, topk_idx, q, k, v, stream=None):
     B, S, D, N, G, kk, d, dt = dims.B, dims.S, dims.D, dims.N, dims.G, dims.k, dims.d, dims.torch_dtype
     _check(x, "x", (B, S, D), dt)
     _check(w_q, "w_q", ((N + 1) * d, D), dt)
     _check(w_k, "w_k", (G * d, D), dt)
     _check(w_v, "w_v", (G * d, D), dt)
     _check(topk_idx, "topk_idx", (B * S, G, kk), torch.int32)
-    _check(list_off, "list_off", (B, G, dims.M + 1), torch.int32)
-    _check(list_tok, "list_tok", (B, G, kk * S), torch.int32)
     _check(q, "q", (B, S, N + 1, d), dt)
     _check(k, "k", (B, G, S, d), dt)
     _check(v, "v", (B, G, S, d), dt)
     st = load_library().gqe_qkv_proj(ctypes.byref(dims), _ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v),
-                                     _ptr(topk_idx), _ptr(list_off), _ptr(list_tok), _ptr(q), _ptr(k),
-                                     _ptr(v), _stream(stream))
+                                     _ptr(topk_idx), _ptr(q), _ptr(k), _ptr(v), _stream(stream))
     _raise(st, "gqe_qkv_proj")
 
 
@@ -281,14 +278,14 @@ def decode(dims, q_len, q, k_cache, v_cache, kv_len, topk_idx, workspace=None, s
     return o_r, o_s
 
 
-def qkv_proj(dims, x, w_q, w_k, w_v, topk_idx, list_off, list_tok, q=None, stream=None):
+def qkv_proj(dims, x, w_q, w_k, w_v, topk_idx, q=None, stream=None):
     """Prefill projections; q (if given) keeps the rows of unselected heads."""
     dev, dt = x.device, x.dtype
     if q is None:
         q = torch.zeros((dims.B, dims.S, dims.N + 1, dims.d), dtype=dt, device=dev)
     k = torch.empty((dims.B, dims.G, dims.S, dims.d), dtype=dt, device=dev)
     v = torch.empty((dims.B, dims.G, dims.S, dims.d), dtype=dt, device=dev)
-    gqe_qkv_proj(dims, x, w_q, w_k, w_v, topk_idx, list_off, list_tok, q, k, v, stream)
+    gqe_qkv_proj(dims, x, w_q, w_k, w_v, topk_idx, q, k, v, stream)
     return q, k, v
 
 

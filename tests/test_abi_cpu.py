@@ -143,15 +143,14 @@ def test_out_proj_validation():
 def test_qkv_proj_validation():
     lib = _lib()
 
-    def call(dims, x=A, lo=A, q=A, k=A):
-        return lib.gqe_qkv_proj(ctypes.byref(dims), P(x), P(A), P(A), P(A), P(A), P(lo), P(A), P(q),
-                                P(k), P(A), None)
+    def call(dims, x=A, idx=A, q=A, k=A):
+        return lib.gqe_qkv_proj(ctypes.byref(dims), P(x), P(A), P(A), P(A), P(idx), P(q), P(k), P(A), None)
 
     assert call(_dims(N=8, G=3)) == gqe.GQE_ERR_UNSUPPORTED
     assert call(_dims(d=96)) == gqe.GQE_ERR_UNSUPPORTED
     assert call(_dims(D=96)) == gqe.GQE_ERR_UNSUPPORTED            # bf16 needs D % 64 == 0
     assert call(_dims(), x=0) == gqe.GQE_ERR_INVALID_ARG
-    assert call(_dims(), lo=0) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), idx=0) == gqe.GQE_ERR_INVALID_ARG
     assert call(_dims(), q=MIS) == gqe.GQE_ERR_ALIGNMENT
     assert call(_dims(B=0)) == gqe.GQE_OK
     assert call(_dims(S=0)) == gqe.GQE_OK

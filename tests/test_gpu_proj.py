@@ -5,8 +5,7 @@ max |error| <= 2e-2 and relative Frobenius error <= 1e-2; fp32: 1e-5), with
 the bf16 bound scaled by max(1, |ref|) for outputs that exceed 8.
 Query rows of unselected heads and cache rows outside the appended ones must
 be left bit for bit as they were. The selection comes from the seeded input
-generator and the token lists from the oracle, so nothing the oracle sees
-comes from the HIP path.
+generator, so nothing the oracle sees comes from the HIP path.
 """
 import numpy as np
 import pytest
@@ -43,11 +42,6 @@ def _weights(rng, N, G, d, D, tdt, scale):
     return w((N + 1) * d), w(G * d), w(G * d)
 
 
-def _lists(idx, B, S, G, k, M):
-    off, tok = oracle.build_lists(idx.numpy().reshape(B, S, G, k), M)
-    return torch.from_numpy(off.astype(np.int32)), torch.from_numpy(tok.astype(np.int32))
-
-
 def _check_q(q_gpu, Q_ref, dtype, what):
     """Computed rows against the oracle; the rest must still hold the sentinel."""
     got = f64(q_gpu)
@@ -78,12 +72,10 @@ def test_qkv_proj_matches_oracle(B, S, D, N, G, k, d, dtype, skew):
     x = torch.from_numpy(rng.standard_normal((B, S, D), dtype=np.float32)).to(tdt)
     w_q, w_k, w_v = _weights(rng, N, G, d, D, tdt, 1.0 / np.sqrt(D))
     idx = synth.random_selection(B, S, G, M, k, 5, skew=skew)
-    off, tok = _lists(idx, B, S, G, k, M)
     dims = gqe.gqe_dims.make(B, S, D, N, G, k, d, dtype)
     q = torch.full((B, S, N + 1, d), SENTINEL, dtype=tdt, device=DEV)
     print(f"case B={B} S={S} D={D} N={N} G={G} k={k} d={d} {dtype}", flush=True)
-    _, kk, vv = gqe.qkv_proj(dims, x.to(DEV), w_q.to(DEV), w_k.to(DEV), w_v.to(DEV), idx.to(DEV),
-                             off.to(DEV), tok.to(DEV), q=q)
+    _, kk, vv = gqe.qkv_proj(dims, x.to(DEV), w_q.to(DEV), w_k.to(DEV), w_v.to(DEV), idx.to(DEV), q=q)
     torch.cuda.synchronize()
     Q, K, V = oracle.project(f64(x), f64(w_q), f64(w_k), f64(w_v), idx.numpy().reshape(B, S, G, k), N, G)
     _check_q(q, Q, dtype, "q")
@@ -142,13 +134,12 @@ def test_qkv_proj_full_size_sampled(wl, n_sample):
     B, S, D, N, G, k, d, M = cfg.B, cfg.S, cfg.D, cfg.N, cfg.G, cfg.k, cfg.d, cfg.M
     inp = synth.make_prefill_inputs(cfg, project=False)
     idx = synth.random_selection(B, S, G, M, k, 0, skew=cfg.skew)
-    off, tok = _lists(idx, B, S, G, k, M)
     dims = gqe.gqe_dims.from_config(cfg)
     q = torch.full((B, S, N + 1, d), SENTINEL, dtype=torch.bfloat16, device=DEV)
     print(f"workload {wl}", flush=True)
     x = inp["x"].view(B, S, D)
     _, kk, vv = gqe.qkv_proj(dims, x.to(DEV), inp["w_q"].to(DEV), inp["w_k"].to(DEV), inp["w_v"].to(DEV),
-                             idx.to(DEV), off.to(DEV), tok.to(DEV), q=q)
+                             idx.to(DEV), q=q)
     torch.cuda.synchronize()
     rng = np.random.default_rng(1)
     flat = np.unique(np.concatenate([[0, B * S - 1], rng.choice(B * S, n_sample - 2, replace=False)]))
