@@ -206,7 +206,7 @@ def prefill(Q, K, V, idx, M: int, positions=None):
     return O_r, O_s
 
 
-def decode(q, K, V, kv_len, idx, M: int):
+def decode(q, K, V, kv_len, idx, M: int, kv_start=None):
     """Sparse-query attention of q_len new tokens per sequence against a cache.
 
     q: [B, q_len, N+1, d]; K, V: [B, G, S_max, d]; kv_len: [B] valid cache
@@ -215,6 +215,9 @@ def decode(q, K, V, kv_len, idx, M: int):
     sees keys j <= that position ([GQA-zone] §技术深化 and §工程实操: in decode
     Sq is small and Sk is the full history, so the causal mask must use the
     query's absolute position, not a top-left triangle).
+    kv_start: optional [B]; keys j < kv_start[b] are padding and visible to
+    no query (visibility = causal and key-valid, [GQA-zone] §工程实操 on
+    padding masks).
     Returns (O_r [B, q_len, G, k, d], O_s [B, q_len, d]).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -231,13 +234,16 @@ def decode(q, K, V, kv_len, idx, M: int):
         n = int(kv_len[b])
         if n < L or n > K.shape[2]:
             raise ValueError("kv_len must satisfy q_len <= kv_len <= S_max")
-        pos = n - L + np.arange(L)
+        s0 = 0 if kv_start is None else int(kv_start[b])
+        if s0 < 0 or s0 > n - L:
+            raise ValueError("kv_start must satisfy 0 <= kv_start <= kv_len - q_len")
+        pos = n - L + np.arange(L) - s0  # positions within the valid keys s0 .. n-1
         for g in range(G):
             for j in range(k):
                 heads = g * M + idx[b, :, g, j]
                 O_r[b, :, g, j] = attend_rows(q[b, np.arange(L), heads, :], pos,
-                                              K[b, g, :n], V[b, g, :n])
-        O_s[b] = attend_rows(q[b, :, N, :], pos, K[b, 0, :n], V[b, 0, :n])
+                                              K[b, g, s0:n], V[b, g, s0:n])
+        O_s[b] = attend_rows(q[b, :, N, :], pos, K[b, 0, s0:n], V[b, 0, s0:n])
     return O_r, O_s
 
 

@@ -119,6 +119,28 @@ def pin_nonsquare_causal(O):
         assert h // M == kv
 
 
+def pin_decode_left_padding(O):
+    """Keys before kv_start are padding: with K = 0 (uniform weights) and
+    V_j = j, a query at position p sees the mean of kv_start..p, i.e.
+    (kv_start + p) / 2; without the padding mask it would be p / 2."""
+    G, H, L, n, d = 2, 4, 2, 9, 3
+    M = H // G
+    K = np.zeros((2, G, n, d))
+    V = np.broadcast_to(np.arange(n, dtype=float)[None, None, :, None], (2, G, n, d)).copy()
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((2, L, H + 1, d))
+    idx = np.tile(np.arange(M), (2, L, G, 1))
+    kv_len, kv_start = np.array([9, 6]), np.array([3, 0])
+    O_r, O_s = O.decode(q, K, V, kv_len, idx, M, kv_start=kv_start)
+    for b in range(2):
+        pos = kv_len[b] - L + np.arange(L)
+        want = (kv_start[b] + pos) / 2.0
+        for g in range(G):
+            for j in range(M):
+                _close(O_r[b, :, g, j, 0], want, 1e-12, f"left padding b={b}")
+        _close(O_s[b, :, 0], want, 1e-12, f"left padding shared b={b}")
+
+
 # --------------------------------------------------------------------------
 # Closed forms
 # --------------------------------------------------------------------------

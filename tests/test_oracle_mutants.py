@@ -50,8 +50,10 @@ MUTANTS = {
     "decode_top_left_mask": (
         "pos = n - L + np.arange(L)", "pos = np.arange(L)"),
     "decode_shared_head_on_last_group": (
-        "O_s[b] = attend_rows(q[b, :, N, :], pos, K[b, 0, :n], V[b, 0, :n])",
-        "O_s[b] = attend_rows(q[b, :, N, :], pos, K[b, G - 1, :n], V[b, G - 1, :n])"),
+        "O_s[b] = attend_rows(q[b, :, N, :], pos, K[b, 0, s0:n], V[b, 0, s0:n])",
+        "O_s[b] = attend_rows(q[b, :, N, :], pos, K[b, G - 1, s0:n], V[b, G - 1, s0:n])"),
+    "decode_padding_ignored": (
+        "        s0 = 0 if kv_start is None else int(kv_start[b])", "        s0 = 0"),
     "obar_mean_over_groups": (
         "obar = np.sum(np.asarray(w, dtype=np.float64)[..., None] * O_r, axis=(1, 2))",
         "obar = np.sum(np.asarray(w, dtype=np.float64)[..., None] * O_r, axis=(1, 2)) / G"),
