@@ -138,6 +138,28 @@ int gqe_attn_decode(const gqe_dims* dims, int32_t q_len, const void* q,
                     void* o_routed, void* o_shared, void* workspace,
                     size_t ws_bytes, void* stream);
 
+/* gqe_attn_decode against a paged KV cache, with optional left padding.
+ * The cache of every sequence is a list of pages of page_size consecutive
+ * keys for all G heads; key j of sequence b is row j % page_size of head g in
+ * page block_table[b, j / page_size]. Keys j < kv_start[b] are padding and
+ * visible to no query: visibility = causal and key-valid (GQA tutorial,
+ * 工程实操). Everything else is as for gqe_attn_decode, with S_max =
+ * dims->S = max_pages * page_size.
+ *   k_pages, v_pages [n_pages, G, page_size, d] dtype
+ *   block_table [B, max_pages] int32 device; the entries of the pages that
+ *            hold keys below kv_len[b] must be valid page indices (others are
+ *            not read)
+ *   page_size  a power of two, >= 64 (else GQE_ERR_UNSUPPORTED); dims->S must
+ *            be a multiple of it (else GQE_ERR_INVALID_ARG)
+ *   kv_start_or_null [B] int32 device, 0 <= kv_start[b] <= kv_len[b] - q_len
+ *   workspace >= gqe_decode_workspace_bytes(dims, q_len) device bytes. */
+int gqe_attn_decode_paged(const gqe_dims* dims, int32_t q_len, const void* q,
+                          const void* k_pages, const void* v_pages,
+                          const int32_t* block_table, int32_t page_size,
+                          const int32_t* kv_start_or_null, const int32_t* kv_len,
+                          const int32_t* topk_idx, void* o_routed, void* o_shared,
+                          void* workspace, size_t ws_bytes, void* stream);
+
 /* Slot assembly and output projection for T tokens (GQE review, section 二,
  * the y equation): A_t = [o_routed[t] (G*k*d values, group-major, slots as
  * stored), obar_t, o_shared[t]] with obar_t = sum_{g,j} topk_w[t,g,j] *

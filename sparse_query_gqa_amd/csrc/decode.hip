@@ -128,7 +128,7 @@ __device__ __forceinline__ float slice_dot<float>(const u32x4& q, const u32x4& k
 
 constexpr float kDecodeRescaleLog2 = 8.0f;
 
-template <typename T, int D, int RM>
+template <typename T, int D, int RM, bool PAGED>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   constexpr int VEC = 16 / (int)sizeof(T);  // elements per lane per key row
   constexpr int TPK = D / VEC;              // lanes per key row
@@ -141,6 +141,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   const int k_begin = c_split * p.chunk;
   if (k_begin >= kvl) return;  // the combine reads only the splits below kv_len
   const int k_end = min(k_begin + p.chunk, kvl);
+  const int k_lo = p.kv_start ? p.kv_start[b] : 0;  // keys below are padding
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int part = tid % TPK;  // which 16-byte slice of the row
   const int kl = tid / TPK;    // key lane within a pass
@@ -178,8 +179,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     for (int i = 0; i < VEC; ++i) o[r][i] = 0.f;
   }
 
-  const T* kb = (const T*)p.k + ((int64_t)b * p.G + g) * (int64_t)p.Smax * D + part * VEC;
-  const T* vb = (const T*)p.v + ((int64_t)b * p.G + g) * (int64_t)p.Smax * D + part * VEC;
+  // contiguous: the (b, g) slice of the cache; paged: the pool (the page
+  // offset locates the row)
+  const int64_t slice = PAGED ? 0 : ((int64_t)b * p.G + g) * (int64_t)p.Smax * D;
+  const T* kb = (const T*)p.k + slice + part * VEC;
+  const T* vb = (const T*)p.v + slice + part * VEC;
+  // Paged: a pass covers KPB <= 64 consecutive keys and pages hold a power of
+  // two >= 64 of them, so a pass lies in one page (one block-table entry per
+  // pass); lanes clamped to the split's last key use that key's page.
+  const int32_t* bt = PAGED ? p.block_table + (int64_t)b * p.max_pages : nullptr;
+  const int pmask = (1 << p.page_shift) - 1;
+  const int64_t pstride = (int64_t)p.G << p.page_shift;  // rows per page across the G heads
+  const int64_t goff = (int64_t)g << p.page_shift;
+  int64_t last_row = 0;
+  if constexpr (PAGED) last_row = ((int64_t)bt[(k_end - 1) >> p.page_shift] * pstride + goff + ((k_end - 1) & pmask)) * D;
 
   for (int j0 = k_begin; j0 < k_end; j0 += U * KPB) {
     // keys past the split are loaded from its last key (always valid) and masked
@@ -188,10 +201,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       key[u] = j0 + u * KPB + kl;
-      const int64_t kk = min(key[u], k_end - 1);
+      int64_t off;
+      if constexpr (PAGED) {
+        const int key0 = min(j0 + u * KPB, k_end - 1);  // uniform: first key of the pass
+        const int64_t page = bt[key0 >> p.page_shift];
+        off = key[u] < k_end ? (page * pstride + goff + (key[u] & pmask)) * D : last_row;
+      } else {
+        off = (int64_t)min(key[u], k_end - 1) * D;
+      }
       // the cache is read once per call: non-temporal loads stream it
-      kw[u] = __builtin_nontemporal_load((const u32x4*)(kb + kk * D));
-      vw[u] = __builtin_nontemporal_load((const u32x4*)(vb + kk * D));
+      kw[u] = __builtin_nontemporal_load((const u32x4*)(kb + off));
+      vw[u] = __builtin_nontemporal_load((const u32x4*)(vb + off));
     }
     float vf[U][VEC];
 #pragma unroll
@@ -204,7 +224,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const float dot = group_sum<TPK>(slice_dot<T>(q[r], kw[u]));
-          s[u] = (key[u] < k_end && key[u] <= rpos[r]) ? dot * c : -INFINITY;
+          s[u] = (key[u] < k_end && key[u] <= rpos[r] && key[u] >= k_lo) ? dot * c : -INFINITY;
           bm = fmaxf(bm, s[u]);
         }
         // lazy rescale: move the reference max only when it grows by more
@@ -329,12 +349,17 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
 template <typename T, int D>
 static void launch_decode_t(const DecodeParams& p, hipStream_t s) {
   const dim3 grid(p.nsplit, p.G, p.B);
-  if (p.R <= 4)
-    hipLaunchKernelGGL((decode_split_kernel<T, D, 4>), grid, dim3(256), 0, s, p);
-  else if (p.R <= 8)
-    hipLaunchKernelGGL((decode_split_kernel<T, D, 8>), grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<T, D, kMaxDecodeRows>), grid, dim3(256), 0, s, p);
+  const bool paged = p.block_table != nullptr;
+  if (p.R <= 4) {
+    if (paged) hipLaunchKernelGGL((decode_split_kernel<T, D, 4, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((decode_split_kernel<T, D, 4, false>), grid, dim3(256), 0, s, p);
+  } else if (p.R <= 8) {
+    if (paged) hipLaunchKernelGGL((decode_split_kernel<T, D, 8, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((decode_split_kernel<T, D, 8, false>), grid, dim3(256), 0, s, p);
+  } else {
+    if (paged) hipLaunchKernelGGL((decode_split_kernel<T, D, kMaxDecodeRows, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((decode_split_kernel<T, D, kMaxDecodeRows, false>), grid, dim3(256), 0, s, p);
+  }
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(p.R, p.G, p.B), dim3(D), 0, s, p);
 }
 

@@ -162,6 +162,43 @@ int gqe_attn_decode(const gqe_dims* d, int32_t q_len, const void* q, const void*
   return hip_status(launch_decode(dp, d->d, d->dtype == GQE_BF16, (hipStream_t)stream));
 }
 
+int gqe_attn_decode_paged(const gqe_dims* d, int32_t q_len, const void* q, const void* k_pages,
+                          const void* v_pages, const int32_t* block_table, int32_t page_size,
+                          const int32_t* kv_start, const int32_t* kv_len, const int32_t* topk_idx,
+                          void* o_routed, void* o_shared, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  int st = check_dims(d, false);
+  if (st) return st;
+  if (q_len < 0) return GQE_ERR_INVALID_ARG;
+  if (!q || !k_pages || !v_pages || !block_table || !kv_len || !topk_idx || !o_routed || !o_shared)
+    return GQE_ERR_INVALID_ARG;
+  if (page_size < 64 || (page_size & (page_size - 1)) != 0) return GQE_ERR_UNSUPPORTED;
+  if (d->S % page_size != 0) return GQE_ERR_INVALID_ARG;
+  if (q_len > d->S && d->B > 0) return GQE_ERR_INVALID_ARG;
+  if ((int64_t)(d->k + 1) * q_len > kMaxDecodeRows) return GQE_ERR_UNSUPPORTED;
+  const void* ptrs[] = {q, k_pages, v_pages, block_table, kv_len, topk_idx, o_routed, o_shared};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GQE_ERR_ALIGNMENT;
+  if (kv_start && !aligned16(kv_start)) return GQE_ERR_ALIGNMENT;
+  if (d->B == 0 || q_len == 0) return GQE_OK;
+  const size_t need = gqe_decode_workspace_bytes(d, q_len);
+  if (!workspace || ws_bytes < need) return GQE_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GQE_ERR_ALIGNMENT;
+  const DecodeSplit sp = decode_split(d->B, d->G, d->S, d->k, q_len);
+  const size_t recs = (size_t)d->B * d->G * sp.nsplit * sp.rows;
+  float* ws_o = (float*)workspace;
+  float* ws_ml = ws_o + recs * d->d;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  DecodeParams dp{q, k_pages, v_pages, kv_len, topk_idx, o_routed, o_shared, ws_o, ws_ml,
+                  d->B, q_len, d->S, d->N, d->G, d->N / d->G, d->k, sp.rows, sp.nsplit, sp.chunk,
+                  (float)(1.0 / sqrt((double)d->d)), block_table, shift, d->S / page_size, kv_start};
+  if (trace_on())
+    fprintf(stderr, "[gqe] decode_paged B=%d L=%d Smax=%d page=%d G=%d k=%d d=%d nsplit=%d\n", d->B,
+            q_len, d->S, page_size, d->G, d->k, d->d, sp.nsplit);
+  return hip_status(launch_decode(dp, d->d, d->dtype == GQE_BF16, (hipStream_t)stream));
+}
+
 int gqe_out_proj(const gqe_dims* d, int64_t T, const void* o_routed, const float* topk_w,
                  const void* o_shared, const void* w_o, void* y, void* stream) {
   int st = check_dims(d);

@@ -63,6 +63,12 @@ struct DecodeParams {
   float* ws_ml;           // [B, G, nsplit, R, 2]
   int B, L, Smax, N, G, M, K, R, nsplit, chunk;
   float scale;
+  // paged cache (block_table non-null): k, v are page pools [n_pages, G, P, d]
+  // with P = 1 << page_shift; key j of sequence b is row j % P of page
+  // block_table[b * max_pages + j / P]
+  const int32_t* block_table;
+  int page_shift, max_pages;
+  const int32_t* kv_start;  // [B] first valid key (left padding) or null
 };
 
 struct OutProjParams {

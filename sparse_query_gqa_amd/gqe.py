@@ -29,7 +29,7 @@ GQE_F32 = 1
 EXPORTED = [
     "gqe_status_string", "gqe_version", "gqe_route_workspace_bytes", "gqe_route",
     "gqe_attn_prefill", "gqe_decode_workspace_bytes", "gqe_attn_decode", "gqe_out_proj",
-    "gqe_qkv_proj", "gqe_qkv_proj_decode",
+    "gqe_qkv_proj", "gqe_qkv_proj_decode", "gqe_attn_decode_paged",
 ]
 
 
@@ -86,6 +86,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gqe_out_proj": (ctypes.c_int, [D, I64, P, P, P, P, P, P]),
         "gqe_qkv_proj": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P]),
         "gqe_qkv_proj_decode": (ctypes.c_int, [D, I32, P, P, P, P, P, P, P, P, P, P]),
+        "gqe_attn_decode_paged": (ctypes.c_int, [D, I32, P, P, P, P, I32, P, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -189,6 +190,28 @@ def gqe_attn_decode(dims, q_len, q, k_cache, v_cache, kv_len, topk_idx, o_routed
     _raise(st, "gqe_attn_decode")
 
 
+def gqe_attn_decode_paged(dims, q_len, q, k_pages, v_pages, block_table, page_size, kv_start, kv_len,
+                          topk_idx, o_routed, o_shared, workspace, stream=None):
+    B, S, N, G, kk, d, dt = dims.B, dims.S, dims.N, dims.G, dims.k, dims.d, dims.torch_dtype
+    _check(q, "q", (B, q_len, N + 1, d), dt)
+    if k_pages.dim() != 4 or tuple(k_pages.shape[1:]) != (G, page_size, d):
+        raise ValueError(f"k_pages has shape {tuple(k_pages.shape)}, expected (n_pages, {G}, {page_size}, {d})")
+    _check(k_pages, "k_pages", tuple(k_pages.shape), dt)
+    _check(v_pages, "v_pages", tuple(k_pages.shape), dt)
+    _check(block_table, "block_table", (B, S // page_size), torch.int32)
+    _check(kv_start, "kv_start", (B,), torch.int32, optional=True)
+    _check(kv_len, "kv_len", (B,), torch.int32)
+    _check(topk_idx, "topk_idx", (B * q_len, G, kk), torch.int32)
+    _check(o_routed, "o_routed", (B, q_len, G, kk, d), dt)
+    _check(o_shared, "o_shared", (B, q_len, d), dt)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().gqe_attn_decode_paged(ctypes.byref(dims), q_len, _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                              _ptr(block_table), page_size, _ptr(kv_start), _ptr(kv_len),
+                                              _ptr(topk_idx), _ptr(o_routed), _ptr(o_shared), _ptr(workspace),
+                                              ws_bytes, _stream(stream))
+    _raise(st, "gqe_attn_decode_paged")
+
+
 def gqe_out_proj(dims, T, o_routed, topk_w, o_shared, w_o, y, stream=None):
     G, kk, d, D, dt = dims.G, dims.k, dims.d, dims.D, dims.torch_dtype
     _check(o_routed, "o_routed", (T, G, kk, d), dt)
@@ -287,6 +310,17 @@ def qkv_proj(dims, x, w_q, w_k, w_v, topk_idx, q=None, stream=None):
     v = torch.empty((dims.B, dims.G, dims.S, dims.d), dtype=dt, device=dev)
     gqe_qkv_proj(dims, x, w_q, w_k, w_v, topk_idx, q, k, v, stream)
     return q, k, v
+
+
+def decode_paged(dims, q_len, q, k_pages, v_pages, block_table, page_size, kv_len, topk_idx, kv_start=None,
+                 workspace=None, stream=None):
+    if workspace is None:
+        workspace = decode_workspace(dims, q_len, q.device)
+    o_r = torch.empty((dims.B, q_len, dims.G, dims.k, dims.d), dtype=q.dtype, device=q.device)
+    o_s = torch.empty((dims.B, q_len, dims.d), dtype=q.dtype, device=q.device)
+    gqe_attn_decode_paged(dims, q_len, q, k_pages, v_pages, block_table, page_size, kv_start, kv_len,
+                          topk_idx, o_r, o_s, workspace, stream)
+    return o_r, o_s
 
 
 def out_proj(dims, T, o_routed, topk_w, o_shared, w_o, stream=None):

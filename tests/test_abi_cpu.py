@@ -174,6 +174,27 @@ def test_qkv_proj_decode_validation():
     assert call(_dims(), L=0) == gqe.GQE_OK
 
 
+def test_decode_paged_validation():
+    lib = _lib()
+
+    def call(dims, L=1, page=64, bt=A, kvs=None, ws=A, nws=1 << 30):
+        return lib.gqe_attn_decode_paged(ctypes.byref(dims), L, P(A), P(A), P(A), P(bt), page,
+                                         None if kvs is None else P(kvs), P(A), P(A), P(A), P(A),
+                                         None if ws is None else P(ws), nws, None)
+
+    d = _dims(S=4096, N=32, G=8, k=2, d=128)
+    assert call(d, page=48) == gqe.GQE_ERR_UNSUPPORTED    # not a power of two
+    assert call(d, page=32) == gqe.GQE_ERR_UNSUPPORTED    # below 64
+    assert call(_dims(S=4000), page=64) == gqe.GQE_ERR_INVALID_ARG  # S not a multiple of the page
+    assert call(d, bt=0) == gqe.GQE_ERR_INVALID_ARG
+    assert call(d, kvs=MIS) == gqe.GQE_ERR_ALIGNMENT
+    assert call(d, ws=None) == gqe.GQE_ERR_WORKSPACE
+    assert call(d, L=-1) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(S=128, k=2), L=6, page=64) == gqe.GQE_ERR_UNSUPPORTED  # (k+1)*q_len > 16
+    assert call(_dims(B=0, S=128), page=64) == gqe.GQE_OK
+    assert call(d, L=0) == gqe.GQE_OK
+
+
 def test_workspace_sizes_closed_form():
     lib = _lib()
     d = _dims(B=16, S=65536, N=32, G=8, k=2, d=128)
