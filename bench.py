@@ -52,6 +52,13 @@ def prefill_path_flops(cfg) -> dict:
     return dict(attention=attn, router=router, out_proj=proj, total=attn + router + proj)
 
 
+def projection_flops(T: int, D: int, G: int, k: int, d: int) -> int:
+    """Matmul FLOP of the token-compacted projections: 2*D per output value,
+    (G*k+1)*d query columns (selected heads + shared head) and 2*G*d
+    key/value columns per token."""
+    return 2 * T * D * ((G * k + 1) * d + 2 * G * d)
+
+
 def decode_kv_bytes(cfg) -> int:
     """KV-cache bytes one decode call must read: 2*B*G*kv_len*d*b (one layer)."""
     return 2 * cfg.B * cfg.G * cfg.kv_len * cfg.d * 2
@@ -239,6 +246,69 @@ def main():
     kv = decode_kv_bytes(dcfg)
     dec_gbps = kv / t_dec.mean() / 1e9
 
+    # The Q/K/V projections (token-compacted Q) precede the path; they are
+    # timed on their own after the steps and reported beside the step, not
+    # inside it.
+    q_p = torch.zeros((cfg.B, cfg.S, cfg.N + 1, d), dtype=torch.bfloat16, device=dev)
+    k_p = torch.empty((cfg.B, G, cfg.S, d), dtype=torch.bfloat16, device=dev)
+    v_p = torch.empty_like(k_p)
+    x3 = g["x"].view(cfg.B, cfg.S, cfg.D)
+    dq_p = torch.empty((dcfg.B, dcfg.q_len, dcfg.N + 1, dcfg.d), dtype=torch.bfloat16, device=dev)
+    dx3 = dg["x"].view(dcfg.B, dcfg.q_len, dcfg.D)
+
+    def proj_call():
+        gqe.gqe_qkv_proj(dims, x3, g["w_q"], g["w_k"], g["w_v"], r_out["topk_idx"], q_p, k_p, v_p)
+
+    def dproj_call():
+        gqe.gqe_qkv_proj_decode(ddims, dcfg.q_len, dx3, dg["w_q"], dg["w_k"], dg["w_v"], d_idx,
+                                dg["kv_len"], dq_p, dg["k"], dg["v"])
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        es = [(ev(), ev()) for _ in range(n)]
+        for a, b in es:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in es]) * 1e-3
+
+    t_qkv = timed(proj_call, args.steps)
+    t_dqkv = timed(dproj_call, args.steps)
+    qkv_flop = projection_flops(T, cfg.D, G, k, d)
+    sel = np.unique(d_idx.view(dT, dcfg.G, dcfg.k).cpu().numpy()
+                    + dcfg.M * np.arange(dcfg.G)[None, :, None])
+    dqkv_bytes = (sel.size + 1 + 2 * dcfg.G) * dcfg.d * dcfg.D * 2  # weights of the heads in use
+    qkv = {
+        "prefill_ms": round(t_qkv.mean() * 1e3, 4),
+        "prefill_tflops": round(qkv_flop / t_qkv.mean() / 1e12, 2),
+        "prefill_frac": round(qkv_flop / t_qkv.mean() / PEAK_BF16_FLOPS, 4),
+        "prefill_flop": qkv_flop,
+        "decode_us": round(t_dqkv.mean() * 1e6, 2),
+        "decode_weight_gbps": round(dqkv_bytes / t_dqkv.mean() / 1e9, 1),
+        "decode_weight_bytes": int(dqkv_bytes),
+    }
+
+    # The same decode against a paged cache: 256-key pages in a seeded random
+    # order (gqe_attn_decode_paged), timed after the steps.
+    page = 256
+    mp = dcfg.S // page
+    perm = torch.randperm(dcfg.B * mp, generator=torch.Generator().manual_seed(1)).to(dev)
+    kp = torch.empty((dcfg.B * mp, dcfg.G, page, dcfg.d), dtype=torch.bfloat16, device=dev)
+    vp = torch.empty_like(kp)
+    kp[perm] = dg["k"].view(dcfg.B, dcfg.G, mp, page, dcfg.d).permute(0, 2, 1, 3, 4).reshape(kp.shape)
+    vp[perm] = dg["v"].view(dcfg.B, dcfg.G, mp, page, dcfg.d).permute(0, 2, 1, 3, 4).reshape(vp.shape)
+    bt = perm.to(torch.int32).view(dcfg.B, mp)
+
+    def paged_call():
+        gqe.gqe_attn_decode_paged(ddims, dcfg.q_len, dg["q"], kp, vp, bt, page, None, dg["kv_len"], d_idx,
+                                  d_or, d_os, d_ws)
+
+    t_paged = timed(paged_call, args.steps)
+    del kp, vp
+    paged_gbps = kv / t_paged.mean() / 1e9
+
     traffic = measured_traffic("prefill.hip", "prefill_long_s128k_pmc.txt")
     dtraffic = measured_traffic("decode.hip", "decode_kv64k_pmc.txt")
     result = {
@@ -284,6 +354,9 @@ def main():
             },
             "ms_per_call": round(t_dec.mean() * 1e3, 4),
             "path_ms": round(t_decode.mean() * 1e3, 4),
+            "paged": {"page_size": page, "order": "shuffled", "value": round(paged_gbps, 1), "unit": "GB/s",
+                      "frac": round(paged_gbps * 1e9 / PEAK_HBM_BPS, 4),
+                      "ms_per_call": round(t_paged.mean() * 1e3, 4)},
         },
         "breakdown_ms": {
             "prefill_route": round(t_route.mean() * 1e3, 4),
@@ -295,6 +368,7 @@ def main():
             "attention_min_ms": round(t_attn.min() * 1e3, 4),
             "attention_max_ms": round(t_attn.max() * 1e3, 4),
         },
+        "qkv_proj": qkv,
         "flop_per_step": fl,
         "wall_s": round(wall, 3),
     }
