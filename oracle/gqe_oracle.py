@@ -247,25 +247,40 @@ def decode(q, K, V, kv_len, idx, M: int, kv_start=None):
     return O_r, O_s
 
 
-def assemble(O_r, w, O_s) -> np.ndarray:
+def assemble(O_r, w, O_s, mode: str = "full") -> np.ndarray:
     """Slot vector A_i = Concat(O_i, ō_i, s(x_i)) for every token.
 
     [GQE-review] §二 输出怎么拼起来: hard-selected slot O_i (the selected heads'
     outputs, concatenated), renormalised weighted-sum slot
     ō_i = sum w_{i,g,m} o_{i,g,m} (summed over all groups), and the shared
     head's output s(x_i).
-    O_r: [T, G, k, d]; w: [T, G, k]; O_s: [T, d]. Returns [T, (G*k+2)*d].
+    The ablation variants of [GQE-review] §四 (Table 2) drop the ō slot:
+    mode "hard" is [O_i, s(x_i)] (hard concatenation only) and mode
+    "weighted" is [w ⊙ O_i, s(x_i)] (weighted concatenation: each hard slot
+    times its renormalised weight). Keeping the shared head in both is a
+    reading; the table does not say.
+    O_r: [T, G, k, d]; w: [T, G, k]; O_s: [T, d]. Returns [T, (G*k+2)*d]
+    (full) or [T, (G*k+1)*d].
     """
     O_r = np.asarray(O_r, dtype=np.float64)
     T, G, k, d = O_r.shape
-    hard = O_r.reshape(T, G * k * d)
-    obar = np.sum(np.asarray(w, dtype=np.float64)[..., None] * O_r, axis=(1, 2))
-    return np.concatenate([hard, obar, np.asarray(O_s, dtype=np.float64)], axis=1)
+    w = np.asarray(w, dtype=np.float64)
+    shared = np.asarray(O_s, dtype=np.float64)
+    if mode == "full":
+        hard = O_r.reshape(T, G * k * d)
+        obar = np.sum(w[..., None] * O_r, axis=(1, 2))
+        return np.concatenate([hard, obar, shared], axis=1)
+    if mode == "hard":
+        return np.concatenate([O_r.reshape(T, G * k * d), shared], axis=1)
+    if mode == "weighted":
+        return np.concatenate([(w[..., None] * O_r).reshape(T, G * k * d), shared], axis=1)
+    raise ValueError(f"unknown slot mode {mode!r}")
 
 
-def out_proj(O_r, w, O_s, W_O) -> np.ndarray:
-    """y_i = Concat(O_i, ō_i, s(x_i)) W_O  ([GQE-review] §二, the y equation)."""
-    return assemble(O_r, w, O_s) @ np.asarray(W_O, dtype=np.float64)
+def out_proj(O_r, w, O_s, W_O, mode: str = "full") -> np.ndarray:
+    """y_i = Concat(O_i, ō_i, s(x_i)) W_O  ([GQE-review] §二, the y equation),
+    or the same product with an ablation variant's slot vector."""
+    return assemble(O_r, w, O_s, mode) @ np.asarray(W_O, dtype=np.float64)
 
 
 def layer(x, w_r, Q, K, V, W_O, G: int, k: int, b_r=None):

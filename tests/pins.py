@@ -383,6 +383,30 @@ def pin_flop_count(O):
         assert O.prefill_flops(B, S, G, k, d) == 4 * d * pairs
 
 
+def pin_ablation_slot_variants(O):
+    """The two ablation layouts: hard concatenation is the hard slots then the
+    shared head (no ō); weighted concatenation scales slot (g, j) by w[g, j]
+    (checked on integer values, exactly); with k = 1 every w is 1, so the two
+    variants coincide."""
+    O_r = np.arange(2 * 2 * 2 * 3, dtype=float).reshape(2, 2, 2, 3)  # T=2, G=2, k=2, d=3
+    w = np.array([[[0.25, 0.75], [0.5, 0.5]], [[1.0, 0.0], [0.125, 0.875]]])
+    O_s = -np.ones((2, 3))
+    A_h = O.assemble(O_r, w, O_s, "hard")
+    A_w = O.assemble(O_r, w, O_s, "weighted")
+    assert A_h.shape == (2, 5 * 3) and A_w.shape == (2, 5 * 3)
+    for t in range(2):
+        for g in range(2):
+            for j in range(2):
+                c = (g * 2 + j) * 3
+                _close(A_h[t, c:c + 3], O_r[t, g, j], what="hard slot")
+                _close(A_w[t, c:c + 3], w[t, g, j] * O_r[t, g, j], what="weighted slot")
+        _close(A_h[t, 12:], O_s[t], what="shared after the hard slots")
+        _close(A_w[t, 12:], O_s[t], what="shared after the weighted slots")
+    w1 = np.ones((2, 2, 1))
+    _close(O.assemble(O_r[:, :, :1], w1, O_s, "weighted"), O.assemble(O_r[:, :, :1], w1, O_s, "hard"),
+           what="k = 1")
+
+
 # --------------------------------------------------------------------------
 # Projections: token-compacted Q, dense K/V, decode append
 # --------------------------------------------------------------------------

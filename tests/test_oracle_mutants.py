@@ -54,20 +54,26 @@ MUTANTS = {
         "O_s[b] = attend_rows(q[b, :, N, :], pos, K[b, G - 1, s0:n], V[b, G - 1, s0:n])"),
     "decode_padding_ignored": (
         "        s0 = 0 if kv_start is None else int(kv_start[b])", "        s0 = 0"),
+    "weighted_variant_unscaled": (
+        "        return np.concatenate([(w[..., None] * O_r).reshape(T, G * k * d), shared], axis=1)",
+        "        return np.concatenate([O_r.reshape(T, G * k * d), shared], axis=1)"),
+    "hard_variant_without_shared": (
+        "        return np.concatenate([O_r.reshape(T, G * k * d), shared], axis=1)",
+        "        return O_r.reshape(T, G * k * d)"),
     "obar_mean_over_groups": (
-        "obar = np.sum(np.asarray(w, dtype=np.float64)[..., None] * O_r, axis=(1, 2))",
-        "obar = np.sum(np.asarray(w, dtype=np.float64)[..., None] * O_r, axis=(1, 2)) / G"),
+        "        obar = np.sum(w[..., None] * O_r, axis=(1, 2))",
+        "        obar = np.sum(w[..., None] * O_r, axis=(1, 2)) / G"),
     "obar_group0_only": (
-        "obar = np.sum(np.asarray(w, dtype=np.float64)[..., None] * O_r, axis=(1, 2))",
-        "obar = np.sum(np.asarray(w, dtype=np.float64)[:, 0, :, None] * O_r[:, 0], axis=1)"),
+        "        obar = np.sum(w[..., None] * O_r, axis=(1, 2))",
+        "        obar = np.sum(w[:, 0, :, None] * O_r[:, 0], axis=1)"),
     "obar_unweighted": (
-        "obar = np.sum(np.asarray(w, dtype=np.float64)[..., None] * O_r, axis=(1, 2))",
-        "obar = np.sum(O_r, axis=(1, 2))"),
+        "        obar = np.sum(w[..., None] * O_r, axis=(1, 2))",
+        "        obar = np.sum(O_r, axis=(1, 2))"),
     "hard_slots_slot_major": (
         "hard = O_r.reshape(T, G * k * d)", "hard = O_r.transpose(0, 2, 1, 3).reshape(T, G * k * d)"),
     "slot_parts_swapped": (
-        "return np.concatenate([hard, obar, np.asarray(O_s, dtype=np.float64)], axis=1)",
-        "return np.concatenate([hard, np.asarray(O_s, dtype=np.float64), obar], axis=1)"),
+        "return np.concatenate([hard, obar, shared], axis=1)",
+        "return np.concatenate([hard, shared, obar], axis=1)"),
     "kv_bytes_without_factor_2": (
         "return 2 * B * L * G * S * d * b", "return B * L * G * S * d * b"),
     "lists_descending": (
