@@ -56,6 +56,15 @@ typedef enum {
 
 typedef enum { GQE_BF16 = 0, GQE_F32 = 1 } gqe_dtype;
 
+/* Slot layouts of the output projection: the method's [O, obar, s] and the
+ * two ablation variants of GQE review, section 四, Table 2. */
+typedef enum {
+  GQE_SLOTS_FULL = 0,     /* [O_i, obar_i, s_i], W_O has (G*k+2)*d rows */
+  GQE_SLOTS_HARD = 1,     /* hard concatenation only: [O_i, s_i], (G*k+1)*d rows */
+  GQE_SLOTS_WEIGHTED = 2  /* weighted concatenation: [w * O_i, s_i], each hard
+                             slot scaled by its renormalised weight; (G*k+1)*d rows */
+} gqe_slot_mode;
+
 /* Layer shape. B sequences of S tokens, model width D, N routed query heads,
  * G KV heads (= groups), top-k per group, head_dim d; M = N/G. The shared
  * head is always present. For decode, S is the cache capacity S_max. */
@@ -171,6 +180,16 @@ int gqe_attn_decode_paged(const gqe_dims* dims, int32_t q_len, const void* q,
 int gqe_out_proj(const gqe_dims* dims, int64_t T, const void* o_routed,
                  const float* topk_w, const void* o_shared, const void* w_o,
                  void* y, void* stream);
+
+/* gqe_out_proj with another slot layout (gqe_slot_mode). The ablation
+ * variants drop the obar slot (the pages' "仅硬拼接" and "仅加权拼接" rows);
+ * both keep the always-on shared head, a reading: the table does not say.
+ *   w_o [(G*k+2)*d, D] for GQE_SLOTS_FULL, else [(G*k+1)*d, D]; any other
+ *   mode returns GQE_ERR_UNSUPPORTED. */
+int gqe_out_proj_variant(const gqe_dims* dims, int32_t mode, int64_t T,
+                         const void* o_routed, const float* topk_w,
+                         const void* o_shared, const void* w_o, void* y,
+                         void* stream);
 
 /* Query, key and value projections of a prefill with token-compacted
  * queries. GQE review, section 二: only the selected query heads take part in

@@ -199,11 +199,14 @@ int gqe_attn_decode_paged(const gqe_dims* d, int32_t q_len, const void* q, const
   return hip_status(launch_decode(dp, d->d, d->dtype == GQE_BF16, (hipStream_t)stream));
 }
 
-int gqe_out_proj(const gqe_dims* d, int64_t T, const void* o_routed, const float* topk_w,
-                 const void* o_shared, const void* w_o, void* y, void* stream) {
+static int out_proj_mode(const gqe_dims* d, int32_t mode, int64_t T, const void* o_routed,
+                         const float* topk_w, const void* o_shared, const void* w_o, void* y,
+                         void* stream) {
   int st = check_dims(d);
   if (st) return st;
   if (T < 0) return GQE_ERR_INVALID_ARG;
+  if (mode != GQE_SLOTS_FULL && mode != GQE_SLOTS_HARD && mode != GQE_SLOTS_WEIGHTED)
+    return GQE_ERR_UNSUPPORTED;
   if (!o_routed || !topk_w || !o_shared || !w_o || !y) return GQE_ERR_INVALID_ARG;
   const void* ptrs[] = {o_routed, topk_w, o_shared, w_o, y};
   for (const void* p : ptrs)
@@ -211,10 +214,23 @@ int gqe_out_proj(const gqe_dims* d, int64_t T, const void* o_routed, const float
   if ((T + 127) / 128 > (int64_t)UINT32_MAX) return GQE_ERR_UNSUPPORTED;
   if (T == 0) return GQE_OK;
   OutProjParams op{o_routed, topk_w, o_shared, w_o, y, T, d->G * d->k, d->d, d->D};
+  op.nob = mode == GQE_SLOTS_FULL ? d->d : 0;
+  op.weighted = mode == GQE_SLOTS_WEIGHTED ? 1 : 0;
   if (trace_on())
-    fprintf(stderr, "[gqe] out_proj T=%lld K=%d D=%d\n", (long long)T, (d->G * d->k + 2) * d->d,
-            d->D);
+    fprintf(stderr, "[gqe] out_proj mode=%d T=%lld K=%d D=%d\n", mode, (long long)T,
+            d->G * d->k * d->d + op.nob + d->d, d->D);
   return hip_status(launch_out_proj(op, d->dtype == GQE_BF16, (hipStream_t)stream));
+}
+
+int gqe_out_proj(const gqe_dims* d, int64_t T, const void* o_routed, const float* topk_w,
+                 const void* o_shared, const void* w_o, void* y, void* stream) {
+  return out_proj_mode(d, GQE_SLOTS_FULL, T, o_routed, topk_w, o_shared, w_o, y, stream);
+}
+
+int gqe_out_proj_variant(const gqe_dims* d, int32_t mode, int64_t T, const void* o_routed,
+                         const float* topk_w, const void* o_shared, const void* w_o, void* y,
+                         void* stream) {
+  return out_proj_mode(d, mode, T, o_routed, topk_w, o_shared, w_o, y, stream);
 }
 
 int gqe_qkv_proj(const gqe_dims* d, const void* x, const void* w_q, const void* w_k,

@@ -79,6 +79,9 @@ struct OutProjParams {
   void* y;                // [T, Dout]
   int64_t T;
   int Gk, d, Dout;
+  // slot layout: [hard slots | obar (nob = d columns, or 0) | shared]; with
+  // `weighted` each hard slot is scaled by its renormalised weight
+  int nob, weighted;
 };
 
 struct ProjParams {

@@ -9,6 +9,11 @@
 // columns [G*k*d, G*k*d + d) are obar computed in fp32 from the G*k stored
 // slots and the fp32 weights; the last d columns are o_shared[t].
 //
+// Two further slot layouts serve the ablation variants (GQE review, section
+// 四, Table 2): hard slots only, [O_t, s_t], and weighted concatenation,
+// [w * O_t, s_t], where each hard slot is scaled by its renormalised weight;
+// neither has the obar slot, and W_O has (G*k+1)*d rows.
+//
 // Two bf16 kernels: a pipelined GEMM for T >= 256 (below) and, for fewer
 // tokens, a plain 128x128-tile kernel: four wavefronts of 64x64 each on
 // v_mfma_f32_32x32x16_bf16, W_O's tile transposed into LDS to give the B
@@ -23,18 +28,27 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 128, kBN = 128, kBK = 32, kPadK = 8;
 
+__device__ __forceinline__ bf16x8 scale8(bf16x8 v, float s) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = f2bf((float)v[i] * s);
+  return v;
+}
+
 template <typename T>
 __device__ __forceinline__ float slot_value(const OutProjParams& p, int64_t t, int col) {
   const int hard = p.Gk * p.d;
-  if (col < hard) return (float)((const T*)p.o_r)[t * hard + col];
-  if (col < hard + p.d) {
+  if (col < hard) {
+    const float v = (float)((const T*)p.o_r)[t * hard + col];
+    return p.weighted ? v * p.w[t * p.Gk + col / p.d] : v;
+  }
+  if (col < hard + p.nob) {
     const int e = col - hard;
     float s = 0.f;
     for (int j = 0; j < p.Gk; ++j)
       s = fmaf(p.w[t * p.Gk + j], (float)((const T*)p.o_r)[t * hard + j * p.d + e], s);
     return s;
   }
-  return (float)((const T*)p.o_s)[t * p.d + (col - hard - p.d)];
+  return (float)((const T*)p.o_s)[t * p.d + (col - hard - p.nob)];
 }
 
 __global__ __launch_bounds__(256) void out_proj_bf16_kernel(OutProjParams p) {
@@ -46,7 +60,7 @@ __global__ __launch_bounds__(256) void out_proj_bf16_kernel(OutProjParams p) {
   const int64_t m0 = (int64_t)blockIdx.x * kBM;
   const int n0 = blockIdx.y * kBN;
   const int hard = p.Gk * p.d;
-  const int Kd = hard + 2 * p.d;
+  const int Kd = hard + p.nob + p.d;
   const __bf16* orr = (const __bf16*)p.o_r;
   const __bf16* os = (const __bf16*)p.o_s;
   const __bf16* wo = (const __bf16*)p.w_o;
@@ -76,7 +90,8 @@ __global__ __launch_bounds__(256) void out_proj_bf16_kernel(OutProjParams p) {
         a[h] = zero8;
       } else if (col < hard) {
         a[h] = *(const bf16x8*)(orr + at * hard + col);
-      } else if (col < hard + p.d) {
+        if (p.weighted) a[h] = scale8(a[h], p.w[at * p.Gk + col / p.d]);
+      } else if (col < hard + p.nob) {
         const int e = col - hard;
         float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int j = 0; j < p.Gk; ++j) {
@@ -88,7 +103,7 @@ __global__ __launch_bounds__(256) void out_proj_bf16_kernel(OutProjParams p) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) a[h][i] = f2bf(s[i]);
       } else {
-        a[h] = *(const bf16x8*)(os + at * p.d + (col - hard - p.d));
+        a[h] = *(const bf16x8*)(os + at * p.d + (col - hard - p.nob));
       }
     }
     bf16x8 bw[2];
@@ -155,7 +170,7 @@ constexpr int kGN = 256;      // output columns per tile
 constexpr int kGK = 32;       // k per step
 constexpr int kGStages = 4;
 
-template <int DH>
+template <int DH, int MODE>  // MODE: 0 [O, obar, s], 1 [O, s], 2 [w*O, s]
 __global__ __launch_bounds__(512, 1) void out_proj_gemm_kernel(OutProjParams p) {
   constexpr int AB = kGT * kGK * 2;  // A tile: 128 token rows x 64 bytes
   constexpr int BB = kGK * kGN * 2;  // W_O tile: 32 k rows x 512 bytes
@@ -172,7 +187,9 @@ __global__ __launch_bounds__(512, 1) void out_proj_gemm_kernel(OutProjParams p) 
   const int64_t m0 = (int64_t)blockIdx.x * kGT;
   const int n0 = blockIdx.y * kGN;
   const int hard = p.Gk * DH;
-  const int nk = (hard + 2 * DH) / kGK;
+  constexpr int nob = MODE == 0 ? DH : 0;
+  constexpr bool weighted = MODE == 2;
+  const int nk = (hard + nob + DH) / kGK;
   const __bf16* orr = (const __bf16*)p.o_r;
   const __bf16* os = (const __bf16*)p.o_s;
   const __bf16* wo = (const __bf16*)p.w_o;
@@ -180,7 +197,7 @@ __global__ __launch_bounds__(512, 1) void out_proj_gemm_kernel(OutProjParams p) 
 
   // obar = sum over the G*k slots of w * o, in fp32, rounded to bf16; one
   // 8-column piece of one token per work item
-  for (int it = tid; it < kGT * (DH / 8); it += 512) {
+  for (int it = tid; nob && it < kGT * (DH / 8); it += 512) {
     const int row = it / (DH / 8), e = (it % (DH / 8)) * 8;
     const int64_t t = min(m0 + row, tmax);
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -208,7 +225,7 @@ __global__ __launch_bounds__(512, 1) void out_proj_gemm_kernel(OutProjParams p) 
     char* sbase = lds + st * SB;
     const __bf16* asrc;
     if (k0 < hard) asrc = orr + a_t * hard + k0 + 8 * a_c;
-    else if (k0 >= hard + DH) asrc = os + a_t * DH + (k0 - hard - DH) + 8 * a_c;
+    else if (k0 >= hard + nob) asrc = os + a_t * DH + (k0 - hard - nob) + 8 * a_c;
     else asrc = orr + a_t * hard + 8 * a_c;  // obar step: a dummy load, the tile is not read
     lds_dma16(asrc, sbase + wave * 1024);
 #pragma unroll
@@ -265,7 +282,14 @@ __global__ __launch_bounds__(512, 1) void out_proj_gemm_kernel(OutProjParams p) 
     dma(kt + kGStages - 1, (kt + kGStages - 1) % kGStages);
     const char* sbase = lds + st * SB;
     const int k0 = kt * kGK;
-    const bool ob = k0 >= hard && k0 < hard + DH;
+    const bool ob = k0 >= hard && k0 < hard + nob;
+    // weighted concatenation: this step's hard slot k0 / DH, one weight per token
+    float wsc[2] = {1.f, 1.f};
+    if (weighted && k0 < hard) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        wsc[tb] = p.w[min(m0 + wm * 64 + tb * 32 + l32, tmax) * p.Gk + k0 / DH];
+    }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       bf16x8 af[2], wf[2];
@@ -276,6 +300,7 @@ __global__ __launch_bounds__(512, 1) void out_proj_gemm_kernel(OutProjParams p) 
           af[tb] = *(const bf16x8*)&obar[t][k0 - hard + 16 * kk + 8 * half];
         } else {
           af[tb] = *(const bf16x8*)(sbase + a_off[tb][kk]);
+          if (weighted && k0 < hard) af[tb] = scale8(af[tb], wsc[tb]);
         }
       }
 #pragma unroll
@@ -357,14 +382,15 @@ __global__ __launch_bounds__(512, 1) void out_proj_small_kernel(OutProjParams p)
   }
   const int n0 = slice * 16;
   const int hard = p.Gk * DH;
-  const int nsteps = (hard + 2 * DH) / 32;
+  const int nob = p.nob;
+  const int nsteps = (hard + nob + DH) / 32;
   const int s_lo = wave * nsteps / 8, s_hi = (wave + 1) * nsteps / 8;
   const __bf16* orr = (const __bf16*)p.o_r;
   const __bf16* os = (const __bf16*)p.o_s;
   const __bf16* wo = (const __bf16*)p.w_o;
 
   // obar of the 16 tokens (tokens past T repeat token T-1), fp32 sums rounded to bf16
-  for (int it = tid; it < 16 * (DH / 8); it += 512) {
+  for (int it = tid; nob && it < 16 * (DH / 8); it += 512) {
     const int t = min(it / (DH / 8), (int)p.T - 1), e = (it % (DH / 8)) * 8;
     float sacc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll 16
@@ -400,9 +426,14 @@ __global__ __launch_bounds__(512, 1) void out_proj_small_kernel(OutProjParams p)
         __builtin_amdgcn_global_load_lds(wo + (int64_t)((s0 + i) * 32 + d_row) * p.Dout + d_col,
                                          (__attribute__((address_space(3))) void*)wl[wave][i], 16, 0, 0);
         const int k = (s0 + i) * 32 + bk;
-        if (k < hard) bq[i] = *(const bf16x8*)(orr + (int64_t)bt * hard + k);
-        else if (k < hard + DH) bq[i] = *(const bf16x8*)&obar_s[lane & 15][k - hard];
-        else bq[i] = *(const bf16x8*)(os + (int64_t)bt * DH + (k - hard - DH));
+        if (k < hard) {
+          bq[i] = *(const bf16x8*)(orr + (int64_t)bt * hard + k);
+          if (p.weighted) bq[i] = scale8(bq[i], p.w[(int64_t)bt * p.Gk + k / DH]);
+        } else if (k < hard + nob) {
+          bq[i] = *(const bf16x8*)&obar_s[lane & 15][k - hard];
+        } else {
+          bq[i] = *(const bf16x8*)(os + (int64_t)bt * DH + (k - hard - nob));
+        }
       }
     }
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -440,7 +471,7 @@ __global__ __launch_bounds__(256) void out_proj_f32_kernel(OutProjParams p) {
   const int n = blockIdx.y * 64 + (threadIdx.x & 63);
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= p.Dout || t >= p.T) return;
-  const int Kd = p.Gk * p.d + 2 * p.d;
+  const int Kd = p.Gk * p.d + p.nob + p.d;
   const float* wo = (const float*)p.w_o;
   float acc = 0.f;
   for (int col = 0; col < Kd; ++col)
@@ -452,12 +483,18 @@ hipError_t launch_out_proj(const OutProjParams& p, bool bf16, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
   if (bf16 && p.T >= kGT * 2) {
     const dim3 grid((unsigned)((p.T + kGT - 1) / kGT), (p.Dout + kGN - 1) / kGN);
+    const int mode = p.nob ? 0 : (p.weighted ? 2 : 1);
+#define GQE_OUT_PROJ_GEMM(DH)                                                                    \
+  if (mode == 0) hipLaunchKernelGGL((out_proj_gemm_kernel<DH, 0>), grid, dim3(512), 0, s, p);    \
+  else if (mode == 1) hipLaunchKernelGGL((out_proj_gemm_kernel<DH, 1>), grid, dim3(512), 0, s, p); \
+  else hipLaunchKernelGGL((out_proj_gemm_kernel<DH, 2>), grid, dim3(512), 0, s, p);
     switch (p.d) {
-      case 32: hipLaunchKernelGGL(out_proj_gemm_kernel<32>, grid, dim3(512), 0, s, p); break;
-      case 64: hipLaunchKernelGGL(out_proj_gemm_kernel<64>, grid, dim3(512), 0, s, p); break;
-      case 128: hipLaunchKernelGGL(out_proj_gemm_kernel<128>, grid, dim3(512), 0, s, p); break;
+      case 32: GQE_OUT_PROJ_GEMM(32) break;
+      case 64: GQE_OUT_PROJ_GEMM(64) break;
+      case 128: GQE_OUT_PROJ_GEMM(128) break;
       default: return hipErrorInvalidValue;
     }
+#undef GQE_OUT_PROJ_GEMM
   } else if (bf16 && p.T <= kSmallT) {
     const dim3 grid((p.Dout + 15) / 16);
     switch (p.d) {

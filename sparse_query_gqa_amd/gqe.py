@@ -25,11 +25,14 @@ GQE_ERR_WORKSPACE = -4
 GQE_ERR_HIP = -5
 GQE_BF16 = 0
 GQE_F32 = 1
+GQE_SLOTS_FULL = 0
+GQE_SLOTS_HARD = 1
+GQE_SLOTS_WEIGHTED = 2
 
 EXPORTED = [
     "gqe_status_string", "gqe_version", "gqe_route_workspace_bytes", "gqe_route",
     "gqe_attn_prefill", "gqe_decode_workspace_bytes", "gqe_attn_decode", "gqe_out_proj",
-    "gqe_qkv_proj", "gqe_qkv_proj_decode", "gqe_attn_decode_paged",
+    "gqe_qkv_proj", "gqe_qkv_proj_decode", "gqe_attn_decode_paged", "gqe_out_proj_variant",
 ]
 
 
@@ -87,6 +90,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gqe_qkv_proj": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P]),
         "gqe_qkv_proj_decode": (ctypes.c_int, [D, I32, P, P, P, P, P, P, P, P, P, P]),
         "gqe_attn_decode_paged": (ctypes.c_int, [D, I32, P, P, P, P, I32, P, P, P, P, P, P, SZ, P]),
+        "gqe_out_proj_variant": (ctypes.c_int, [D, I32, I64, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -210,6 +214,18 @@ def gqe_attn_decode_paged(dims, q_len, q, k_pages, v_pages, block_table, page_si
                                               _ptr(topk_idx), _ptr(o_routed), _ptr(o_shared), _ptr(workspace),
                                               ws_bytes, _stream(stream))
     _raise(st, "gqe_attn_decode_paged")
+
+
+def gqe_out_proj_variant(dims, mode, T, o_routed, topk_w, o_shared, w_o, y, stream=None):
+    G, kk, d, D, dt = dims.G, dims.k, dims.d, dims.D, dims.torch_dtype
+    _check(o_routed, "o_routed", (T, G, kk, d), dt)
+    _check(topk_w, "topk_w", (T, G, kk), torch.float32)
+    _check(o_shared, "o_shared", (T, d), dt)
+    _check(w_o, "w_o", ((G * kk + (2 if mode == GQE_SLOTS_FULL else 1)) * d, D), dt)
+    _check(y, "y", (T, D), dt)
+    st = load_library().gqe_out_proj_variant(ctypes.byref(dims), mode, T, _ptr(o_routed), _ptr(topk_w),
+                                             _ptr(o_shared), _ptr(w_o), _ptr(y), _stream(stream))
+    _raise(st, "gqe_out_proj_variant")
 
 
 def gqe_out_proj(dims, T, o_routed, topk_w, o_shared, w_o, y, stream=None):

@@ -140,6 +140,20 @@ def test_out_proj_validation():
     assert call(_dims(), T=0) == gqe.GQE_OK
 
 
+def test_out_proj_variant_validation():
+    lib = _lib()
+
+    def call(dims, mode, T=10, y=A):
+        return lib.gqe_out_proj_variant(ctypes.byref(dims), mode, T, P(A), P(A), P(A), P(A), P(y), None)
+
+    assert call(_dims(), 3) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(), -1) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(), gqe.GQE_SLOTS_HARD, y=0) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), gqe.GQE_SLOTS_WEIGHTED, T=-1) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), gqe.GQE_SLOTS_WEIGHTED, y=MIS) == gqe.GQE_ERR_ALIGNMENT
+    assert call(_dims(), gqe.GQE_SLOTS_HARD, T=0) == gqe.GQE_OK
+
+
 def test_qkv_proj_validation():
     lib = _lib()
 

@@ -402,6 +402,30 @@ def test_out_proj_small(T, G, k, d, D, dtype):
     assert_close(y, ref, dtype, f"out_proj T={T}")
 
 
+@pytest.mark.parametrize("mode", ["hard", "weighted"])
+@pytest.mark.parametrize("T,G,k,d,D,dtype", [(5, 4, 2, 64, 136, "bf16"), (16, 8, 2, 128, 4096, "bf16"),
+                                             (100, 8, 2, 64, 264, "bf16"), (300, 8, 1, 64, 1024, "bf16"),
+                                             (1000, 4, 2, 128, 8, "bf16"), (130, 2, 2, 64, 72, "f32")])
+def test_out_proj_ablation_variants(mode, T, G, k, d, D, dtype):
+    """The two slot layouts of the ablation table through every kernel path
+    (few-token, 128x128-tile, pipelined GEMM, fp32); W_O has (G*k+1)*d rows.
+    The full layout through the same entry point equals gqe_out_proj bit for
+    bit."""
+    s = synth.make_slot_inputs(T, G, k, d, D, dtype, seed=T + 17)
+    g = to_dev(s)
+    dims = gqe.gqe_dims.make(1, T, D, G * k, G, k, d, dtype)
+    code = {"hard": gqe.GQE_SLOTS_HARD, "weighted": gqe.GQE_SLOTS_WEIGHTED}[mode]
+    w_o = g["w_o"][:(G * k + 1) * d].contiguous()
+    y = torch.empty((T, D), dtype=w_o.dtype, device=DEV)
+    gqe.gqe_out_proj_variant(dims, code, T, g["o_r"], g["w"], g["o_s"], w_o, y)
+    y_full = torch.empty_like(y)
+    gqe.gqe_out_proj_variant(dims, gqe.GQE_SLOTS_FULL, T, g["o_r"], g["w"], g["o_s"], g["w_o"], y_full)
+    torch.cuda.synchronize()
+    ref = oracle.out_proj(f64(s["o_r"]), f64(s["w"]), f64(s["o_s"]), f64(w_o), mode=mode)
+    assert_close(y, ref, dtype, f"out_proj {mode} T={T}")
+    assert torch.equal(y_full, gqe.out_proj(dims, T, g["o_r"], g["w"], g["o_s"], g["w_o"]))
+
+
 @pytest.mark.parametrize("name", ["main_s2k", "long_s128k", "llama_s8k_skew", "decode_kv64k"])
 def test_out_proj_workloads_sampled(name):
     cfg = synth.workload(name)
