@@ -50,7 +50,8 @@ __all__ = [
     "softmax", "topk_select", "route_logits", "route_select", "route",
     "build_lists", "attend_rows", "prefill", "decode", "assemble", "out_proj",
     "layer", "kv_bytes", "prefill_flops", "check_dims", "project",
-    "project_decode", "project_flops",
+    "project_decode", "project_flops", "attend_rows_bwd", "prefill_bwd",
+    "out_proj_bwd", "route_bwd",
 ]
 
 
@@ -360,6 +361,140 @@ def project_flops(T: int, D: int, G: int, k: int, d: int) -> int:
     (G*k+1)*d query columns (the selected heads and the shared head) and
     2*G*d key/value columns per token."""
     return 2 * T * D * ((G * k + 1) * d + 2 * G * d)
+
+
+# --------------------------------------------------------------------------
+# Backward pass: gradients of the scalar loss sum(dy * y) (the reverse-mode
+# derivatives of the functions above, written out)
+# --------------------------------------------------------------------------
+
+def attend_rows_bwd(q, pos, K, V, dO):
+    """Gradients of causal attention of query rows against one KV head.
+
+    With s_j = q.k_j/sqrt(d) over visible keys j <= pos, P = softmax(s) and
+    o = sum_j P_j v_j: dv_j = P_j dO, dP_j = dO.v_j, ds_j = P_j (dP_j - dO.o),
+    dq = sum_j ds_j k_j / sqrt(d), dk_j = ds_j q / sqrt(d).
+    q: [n, d]; pos: [n]; K, V: [S, d]; dO: [n, d]. Returns (dq [n, d],
+    dK [S, d], dV [S, d]), dK and dV summed over the rows.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    n, d = q.shape
+    S = K.shape[0]
+    dq = np.zeros((n, d))
+    dK = np.zeros((S, d))
+    dV = np.zeros((S, d))
+    if n == 0:
+        return dq, dK, dV
+    L = int(pos.max()) + 1
+    s = (q @ K[:L].T) / np.sqrt(d)
+    s = s + np.where(np.arange(L)[None, :] <= pos[:, None], 0.0, -np.inf)
+    s = s - np.max(s, axis=1, keepdims=True)
+    P = np.exp(s)
+    P = P / np.sum(P, axis=1, keepdims=True)
+    o = P @ V[:L]
+    dV[:L] = P.T @ dO
+    dP = dO @ V[:L].T
+    dS = P * (dP - np.sum(dO * o, axis=1, keepdims=True))
+    dq = (dS @ K[:L]) / np.sqrt(d)
+    dK[:L] = (dS.T @ q) / np.sqrt(d)
+    return dq, dK, dV
+
+
+def prefill_bwd(Q, K, V, idx, M: int, dO_r, dO_s):
+    """Gradients of prefill (the function above) given dO_r [B, S, G, k, d]
+    and dO_s [B, S, d]. A KV head's dK and dV are summed over every row that
+    reads it: the selected heads of its group and, for head 0, the shared
+    head ([GQA-zone] 训练与部署: shared keys/values gather the gradients of
+    all their query heads). Returns (dQ [B, S, N+1, d], zero in the rows of
+    unselected heads, dK [B, G, S, d], dV [B, G, S, d]).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, S, H1, d = Q.shape
+    G = K.shape[1]
+    k = idx.shape[-1]
+    N = H1 - 1
+    check_dims(N, G, k)
+    pos = np.arange(S)
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    for b in range(B):
+        for g in range(G):
+            for j in range(k):
+                heads = g * M + idx[b, :, g, j]
+                dq, dk, dv = attend_rows_bwd(Q[b, pos, heads, :], pos, K[b, g], V[b, g], dO_r[b, :, g, j])
+                dQ[b, pos, heads, :] += dq
+                dK[b, g] += dk
+                dV[b, g] += dv
+        dq, dk, dv = attend_rows_bwd(Q[b, :, N, :], pos, K[b, 0], V[b, 0], dO_s[b])
+        dQ[b, :, N, :] += dq
+        dK[b, 0] += dk
+        dV[b, 0] += dv
+    return dQ, dK, dV
+
+
+def out_proj_bwd(O_r, w, O_s, W_O, dy, mode: str = "full"):
+    """Gradients of out_proj given dy [T, D]: with A the slot vector and
+    y = A W_O, dW_O = A^T dy and dA = dy W_O^T; dA splits into the hard
+    slots, ō and s, and ō = sum w o feeds back into the hard slots (w dō)
+    and into the routing weights (dw = o . dō), which is how the router
+    receives a gradient ([GQE-review] §二: the renormalised slot).
+    Returns (dO_r [T, G, k, d], dw [T, G, k], dO_s [T, d], dW_O).
+    """
+    O_r = np.asarray(O_r, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    T, G, k, d = O_r.shape
+    A = assemble(O_r, w, O_s, mode)
+    dW_O = A.T @ dy
+    dA = dy @ np.asarray(W_O, dtype=np.float64).T
+    hard = dA[:, :G * k * d].reshape(T, G, k, d)
+    if mode == "full":
+        dobar = dA[:, G * k * d:G * k * d + d]
+        dO_r = hard + w[..., None] * dobar[:, None, None, :]
+        dw = np.einsum("tgkd,td->tgk", O_r, dobar)
+        dO_s = dA[:, G * k * d + d:]
+    elif mode == "hard":
+        dO_r, dw, dO_s = hard, np.zeros_like(w), dA[:, G * k * d:]
+    elif mode == "weighted":
+        dO_r = w[..., None] * hard
+        dw = np.einsum("tgkd,tgkd->tgk", O_r, hard)
+        dO_s = dA[:, G * k * d:]
+    else:
+        raise ValueError(f"unknown slot mode {mode!r}")
+    return dO_r, dw, dO_s, dW_O
+
+
+def route_bwd(x, w_r, z, idx, dw, G: int, M: int):
+    """Gradients of the router given dw [T, G, k] (the gradient of the
+    renormalised weights). p = softmax(z), w_j = p_{m_j} / sum_{j'} p_{m_j'}
+    over the selected experts ([GQE-review] §二, the w equation); the
+    selection itself is piecewise constant. dp_{m_j} = (dw_j - sum_j' dw_j'
+    w_j') / sum_j' p_{m_j'} on the selected experts, 0 elsewhere;
+    dz = p * (dp - p . dp); dW_r = dz^T x, db_r = sum_t dz, dx = dz W_r.
+    x: [T, D]; w_r: [G*M, D]; z: [T, G, M]; idx: [T, G, k].
+    Returns (dz [T, G, M], dW_r [G*M, D], db_r [G*M], dx [T, D]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    dw = np.asarray(dw, dtype=np.float64)
+    T = x.shape[0]
+    p = softmax(z, axis=-1)
+    idx = np.asarray(idx)
+    p_sel = np.take_along_axis(p, idx, -1)
+    ssum = np.sum(p_sel, axis=-1, keepdims=True)
+    wsel = p_sel / ssum
+    dp_sel = (dw - np.sum(dw * wsel, axis=-1, keepdims=True)) / ssum
+    dp = np.zeros_like(p)
+    np.put_along_axis(dp, idx, dp_sel, axis=-1)
+    dz = p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
+    dz2 = dz.reshape(T, G * M)
+    w_r = np.asarray(w_r, dtype=np.float64)
+    return dz, dz2.T @ x, dz2.sum(axis=0), dz2 @ w_r
 
 
 def kv_bytes(B: int, L: int, G: int, d: int, S: int, b: int) -> int:

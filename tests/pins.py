@@ -408,6 +408,107 @@ def pin_ablation_slot_variants(O):
 
 
 # --------------------------------------------------------------------------
+# Backward: analytic gradients against central differences of the forward
+# --------------------------------------------------------------------------
+
+def _central(f, x, eps=1e-6):
+    """Numerical gradient of the scalar f at x (every element), float64."""
+    g = np.zeros_like(x)
+    flat, gflat = x.reshape(-1), g.reshape(-1)
+    for i in range(flat.size):
+        old = flat[i]
+        flat[i] = old + eps
+        fp = f()
+        flat[i] = old - eps
+        fm = f()
+        flat[i] = old
+        gflat[i] = (fp - fm) / (2 * eps)
+    return g
+
+
+def pin_prefill_bwd_central_differences(O):
+    """dQ, dK, dV of the sparse causal prefill against central differences of
+    sum(dO_r * O_r) + sum(dO_s * O_s); rows of unselected heads get zero."""
+    rng = np.random.default_rng(21)
+    B, S, N, G, k, d = 1, 5, 4, 2, 1, 3
+    M = N // G
+    Q = rng.standard_normal((B, S, N + 1, d))
+    K = rng.standard_normal((B, G, S, d))
+    V = rng.standard_normal((B, G, S, d))
+    idx = _random_idx(rng, B, S, G, M, k)
+    dO_r = rng.standard_normal((B, S, G, k, d))
+    dO_s = rng.standard_normal((B, S, d))
+
+    def loss():
+        o_r, o_s = O.prefill(Q, K, V, idx, M)
+        return float(np.sum(dO_r * o_r) + np.sum(dO_s * o_s))
+
+    dQ, dK, dV = O.prefill_bwd(Q, K, V, idx, M, dO_r, dO_s)
+    _close(dQ, _central(loss, Q), 1e-6, "dQ")
+    _close(dK, _central(loss, K), 1e-6, "dK")
+    _close(dV, _central(loss, V), 1e-6, "dV")
+
+
+def pin_single_key_backward(O):
+    """One visible key: o = v_0 whatever q is, so dq = 0, dk_0 = 0 and
+    dv_0 = dO (closed form)."""
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((1, 4))
+    K = rng.standard_normal((3, 4))
+    V = rng.standard_normal((3, 4))
+    dO = rng.standard_normal((1, 4))
+    dq, dK, dV = O.attend_rows_bwd(q, np.array([0]), K, V, dO)
+    _close(dq, np.zeros((1, 4)), 1e-12, "single key dq")
+    _close(dK, np.zeros((3, 4)), 1e-12, "single key dK")
+    _close(dV[0], dO[0], 1e-12, "single key dV")
+    _close(dV[1:], np.zeros((2, 4)), 1e-12, "invisible keys dV")
+
+
+def pin_out_proj_bwd_central_differences(O):
+    """dO_r, dw, dO_s, dW_O of y = A W_O (all three slot layouts) against
+    central differences of sum(dy * y)."""
+    rng = np.random.default_rng(23)
+    T, G, k, d, D = 3, 2, 2, 2, 5
+    O_r = rng.standard_normal((T, G, k, d))
+    w = rng.random((T, G, k))
+    O_s = rng.standard_normal((T, d))
+    dy = rng.standard_normal((T, D))
+    for mode, rows in (("full", (G * k + 2) * d), ("hard", (G * k + 1) * d), ("weighted", (G * k + 1) * d)):
+        W_O = rng.standard_normal((rows, D))
+
+        def loss():
+            return float(np.sum(dy * O.out_proj(O_r, w, O_s, W_O, mode=mode)))
+
+        dO_r, dw, dO_s, dW_O = O.out_proj_bwd(O_r, w, O_s, W_O, dy, mode=mode)
+        _close(dO_r, _central(loss, O_r), 1e-6, f"{mode} dO_r")
+        _close(dw, _central(loss, w), 1e-6, f"{mode} dw")
+        _close(dO_s, _central(loss, O_s), 1e-6, f"{mode} dO_s")
+        _close(dW_O, _central(loss, W_O), 1e-6, f"{mode} dW_O")
+
+
+def pin_route_bwd_central_differences(O):
+    """dW_r, db_r, dx of the renormalised top-k weights against central
+    differences of sum(dw * w(x, W_r, b_r)); the logits are far apart, so
+    the perturbations never change the selection."""
+    rng = np.random.default_rng(24)
+    T, D, G, M, k = 4, 6, 2, 4, 2
+    x = rng.standard_normal((T, D))
+    w_r = rng.standard_normal((G * M, D))
+    b_r = rng.standard_normal(G * M) * 3.0
+    dw = rng.standard_normal((T, G, k))
+
+    def loss():
+        _, _, _, ww = O.route(x, w_r, G, M, k, b_r)
+        return float(np.sum(dw * ww))
+
+    z, _, idx, _ = O.route(x, w_r, G, M, k, b_r)
+    dz, dW_r, db_r, dx = O.route_bwd(x, w_r, z, idx, dw, G, M)
+    _close(dW_r, _central(loss, w_r), 1e-6, "dW_r")
+    _close(db_r, _central(loss, b_r), 1e-6, "db_r")
+    _close(dx, _central(loss, x), 1e-6, "dx")
+
+
+# --------------------------------------------------------------------------
 # Projections: token-compacted Q, dense K/V, decode append
 # --------------------------------------------------------------------------
 

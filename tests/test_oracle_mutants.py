@@ -60,6 +60,16 @@ MUTANTS = {
     "hard_variant_without_shared": (
         "        return np.concatenate([O_r.reshape(T, G * k * d), shared], axis=1)",
         "        return O_r.reshape(T, G * k * d)"),
+    "bwd_softmax_without_delta": (
+        "    dS = P * (dP - np.sum(dO * o, axis=1, keepdims=True))", "    dS = P * dP"),
+    "bwd_key_scale_missing": (
+        "    dK[:L] = (dS.T @ q) / np.sqrt(d)", "    dK[:L] = dS.T @ q"),
+    "bwd_shared_head_on_last_group": (
+        "        dK[b, 0] += dk\n", "        dK[b, G - 1] += dk\n"),
+    "bwd_obar_not_fed_back": (
+        "        dO_r = hard + w[..., None] * dobar[:, None, None, :]", "        dO_r = hard"),
+    "bwd_router_not_renormalised": (
+        "    dp_sel = (dw - np.sum(dw * wsel, axis=-1, keepdims=True)) / ssum", "    dp_sel = dw / ssum"),
     "obar_mean_over_groups": (
         "        obar = np.sum(w[..., None] * O_r, axis=(1, 2))",
         "        obar = np.sum(w[..., None] * O_r, axis=(1, 2)) / G"),
