@@ -51,7 +51,7 @@ __all__ = [
     "build_lists", "attend_rows", "prefill", "decode", "assemble", "out_proj",
     "layer", "kv_bytes", "prefill_flops", "check_dims", "project",
     "project_decode", "project_flops", "attend_rows_bwd", "prefill_bwd",
-    "out_proj_bwd", "route_bwd",
+    "out_proj_bwd", "route_bwd", "lse_rows", "prefill_lse",
 ]
 
 
@@ -205,6 +205,46 @@ def prefill(Q, K, V, idx, M: int, positions=None):
                 O_r[b, :, g, j] = attend_rows(Q[b, pos, heads, :], pos, K[b, g], V[b, g])
         O_s[b] = attend_rows(Q[b, pos, N, :], pos, K[b, 0], V[b, 0])
     return O_r, O_s
+
+
+def lse_rows(q, pos, K):
+    """Log of the softmax normaliser of each query row: ln sum_{j <= pos}
+    exp(q . k_j / sqrt(d)), the same visible scores as attend_rows
+    ([GQA-zone] §技术深化). A training forward keeps it so that the
+    backward can rebuild P = exp(s - lse) without the running max.
+    q: [n, d]; pos: [n]; K: [S, d]. Returns [n].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    n, d = q.shape
+    if n == 0:
+        return np.zeros(0)
+    L = int(pos.max()) + 1
+    sc = (q @ np.asarray(K, dtype=np.float64)[:L].T) / np.sqrt(d)
+    sc = np.where(np.arange(L)[None, :] <= pos[:, None], sc, -np.inf)
+    top = np.max(sc, axis=1)
+    return top + np.log(np.sum(np.exp(sc - top[:, None]), axis=1))
+
+
+def prefill_lse(Q, K, idx, M: int):
+    """lse_rows for every row prefill computes: (lse_r [B, S, G, k],
+    lse_s [B, S]), same head mapping and shared head as prefill."""
+    Q = np.asarray(Q, dtype=np.float64)
+    B, S, H1, d = Q.shape
+    G = K.shape[1]
+    k = idx.shape[-1]
+    N = H1 - 1
+    check_dims(N, G, k)
+    pos = np.arange(S)
+    lse_r = np.zeros((B, S, G, k))
+    lse_s = np.zeros((B, S))
+    for b in range(B):
+        for g in range(G):
+            for j in range(k):
+                heads = g * M + idx[b, :, g, j]
+                lse_r[b, :, g, j] = lse_rows(Q[b, pos, heads, :], pos, K[b, g])
+        lse_s[b] = lse_rows(Q[b, :, N, :], pos, K[b, 0])
+    return lse_r, lse_s
 
 
 def decode(q, K, V, kv_len, idx, M: int, kv_start=None):

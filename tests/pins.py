@@ -464,6 +464,35 @@ def pin_single_key_backward(O):
     _close(dV[1:], np.zeros((2, 4)), 1e-12, "invisible keys dV")
 
 
+def pin_lse_closed_forms(O):
+    """Row log-sum-exp: at position 0 only key 0 is visible, so lse =
+    q.k_0/sqrt(d); with every key equal, lse_i = q.k/sqrt(d) + ln(i + 1).
+    Per-head queries differ, so a wrong head or KV head shows up."""
+    rng = np.random.default_rng(31)
+    B, S, G, M, k, d = 2, 6, 2, 3, 2, 4
+    N = G * M
+    Q = rng.standard_normal((B, S, N + 1, d))
+    K = rng.standard_normal((B, G, S, d))
+    idx = np.sort(np.stack([rng.permutation(M)[:k] for _ in range(B * S * G)]).reshape(B, S, G, k), axis=-1)
+    lse_r, lse_s = O.prefill_lse(Q, K, idx, M)
+    for b in range(B):
+        for g in range(G):
+            for j in range(k):
+                h = g * M + idx[b, 0, g, j]
+                _close(lse_r[b, 0, g, j], Q[b, 0, h] @ K[b, g, 0] / 2.0, 1e-12, "lse at position 0")
+        _close(lse_s[b, 0], Q[b, 0, N] @ K[b, 0, 0] / 2.0, 1e-12, "shared lse at position 0")
+    Kc = np.repeat(K[:, :, :1], S, axis=2)  # every key equal to key 0
+    lse_r, lse_s = O.prefill_lse(Q, Kc, idx, M)
+    ln = np.log(np.arange(1, S + 1))
+    for b in range(B):
+        _close(lse_s[b], Q[b, :, N] @ K[b, 0, 0] / 2.0 + ln, 1e-12, "shared lse, equal keys")
+        for g in range(G):
+            for j in range(k):
+                h = g * M + idx[b, :, g, j]
+                sc = np.einsum("sd,d->s", Q[b, np.arange(S), h], K[b, g, 0]) / 2.0
+                _close(lse_r[b, :, g, j], sc + ln, 1e-12, "lse, equal keys")
+
+
 def pin_out_proj_bwd_central_differences(O):
     """dO_r, dw, dO_s, dW_O of y = A W_O (all three slot layouts) against
     central differences of sum(dy * y)."""

@@ -54,6 +54,16 @@ MUTANTS = {
         "O_s[b] = attend_rows(q[b, :, N, :], pos, K[b, G - 1, s0:n], V[b, G - 1, s0:n])"),
     "decode_padding_ignored": (
         "        s0 = 0 if kv_start is None else int(kv_start[b])", "        s0 = 0"),
+    "lse_without_max": (
+        "return top + np.log(np.sum(np.exp(sc - top[:, None]), axis=1))",
+        "return np.log(np.sum(np.exp(sc - top[:, None]), axis=1))"),
+    "lse_mask_excludes_diagonal": (
+        "sc = np.where(np.arange(L)[None, :] <= pos[:, None], sc, -np.inf)",
+        "sc = np.where(np.arange(L)[None, :] < np.maximum(pos[:, None], 1), sc, -np.inf)"),
+    "lse_shared_on_last_group": (
+        "lse_s[b] = lse_rows(Q[b, :, N, :], pos, K[b, 0])", "lse_s[b] = lse_rows(Q[b, :, N, :], pos, K[b, G - 1])"),
+    "lse_head_mapping_transposed": (
+        "heads = g * M + idx[b, :, g, j]\n                lse_r", "heads = idx[b, :, g, j] * G + g\n                lse_r"),
     "weighted_variant_unscaled": (
         "        return np.concatenate([(w[..., None] * O_r).reshape(T, G * k * d), shared], axis=1)",
         "        return np.concatenate([O_r.reshape(T, G * k * d), shared], axis=1)"),
