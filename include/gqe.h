@@ -124,6 +124,49 @@ int gqe_attn_prefill(const gqe_dims* dims, const void* q, const void* k,
                      const void* v, const int32_t* topk_idx, void* o_routed,
                      void* o_shared, void* stream);
 
+/* Training forward: gqe_attn_prefill plus each row's log-sum-exp, the
+ * softmax normaliser the backward pass rebuilds P from (GQE review, section
+ * 二: the routed and shared heads are trained end to end).
+ *   lse_routed [B, S, G, k] fp32 out: ln sum_{t<=i} exp(q.k_t / sqrt(d))
+ *   lse_shared [B, S]       fp32 out
+ * In the bf16 path the scores are those of the bf16 kernel (q scaled and
+ * rounded to bf16 before the product). Same errors as gqe_attn_prefill, and
+ * GQE_ERR_INVALID_ARG for a NULL lse pointer. */
+int gqe_attn_prefill_train(const gqe_dims* dims, const void* q, const void* k,
+                           const void* v, const int32_t* topk_idx, void* o_routed,
+                           void* o_shared, float* lse_routed, float* lse_shared,
+                           void* stream);
+
+/* Bytes of device workspace gqe_attn_prefill_bwd needs (0 for invalid dims):
+ * packed q and dO rows, two fp32 scalars per row and, for bf16, fp32 partial
+ * sums of KV head 0's dK and dV. */
+size_t gqe_attn_prefill_bwd_workspace_bytes(const gqe_dims* dims);
+
+/* Backward of gqe_attn_prefill. With P = softmax(q.k/sqrt(d)) over the
+ * visible keys and o = P V (GQA tutorial, 技术深化):
+ *   dV_t += P_t dO,  dS_t = P_t (dO.v_t - dO.o),
+ *   dq = sum_t dS_t k_t / sqrt(d),  dK_t += dS_t q / sqrt(d).
+ * dK and dV of a KV head are summed over every query row that reads it: the
+ * selected heads of its group and, for KV head 0, the shared head (GQA-zone
+ * page, 训练与部署: shared keys and values sum the gradients of their query
+ * heads).
+ *   q, k, v, topk_idx          as given to the forward
+ *   o_routed, o_shared         the forward's outputs
+ *   lse_routed, lse_shared     from gqe_attn_prefill_train on the same inputs
+ *   do_routed [B, S, G, k, d], do_shared [B, S, d]   dtype, the output gradients
+ *   dq [B, S, N+1, d]  dtype out: written for the selected heads and the
+ *                      shared head only; the caller owns (and zeroes, if it
+ *                      needs them) the rows of unselected heads
+ *   dk, dv [B, G, S, d] dtype out, fully written
+ *   workspace >= gqe_attn_prefill_bwd_workspace_bytes(dims) device bytes.
+ * Deterministic: no atomics; the same inputs give the same bits. */
+int gqe_attn_prefill_bwd(const gqe_dims* dims, const void* q, const void* k,
+                         const void* v, const int32_t* topk_idx, const void* o_routed,
+                         const void* o_shared, const float* lse_routed,
+                         const float* lse_shared, const void* do_routed,
+                         const void* do_shared, void* dq, void* dk, void* dv,
+                         void* workspace, size_t ws_bytes, void* stream);
+
 /* Bytes of workspace gqe_attn_decode needs (split-sequence partials). */
 size_t gqe_decode_workspace_bytes(const gqe_dims* dims, int32_t q_len);
 

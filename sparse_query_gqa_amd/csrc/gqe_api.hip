@@ -50,6 +50,54 @@ int hip_status(hipError_t e) {
   return GQE_ERR_HIP;
 }
 
+int prefill_common(const gqe_dims* d, const void* q, const void* k, const void* v,
+                   const int32_t* topk_idx, void* o_routed, void* o_shared, float* lse_r,
+                   float* lse_s, void* stream) {
+  int st = check_dims(d, false);
+  if (st) return st;
+  if (!q || !k || !v || !topk_idx || !o_routed || !o_shared) return GQE_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, topk_idx, o_routed, o_shared, lse_r, lse_s};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GQE_ERR_ALIGNMENT;
+  // rows per (sequence, group) and tile counts must stay in int32
+  if ((int64_t)d->S * d->k > (int64_t)INT32_MAX / 2) return GQE_ERR_UNSUPPORTED;
+  if (d->B == 0 || d->S == 0) return GQE_OK;
+  PrefillParams pp{q, k, v, topk_idx, o_routed, o_shared, d->B, d->S, d->N, d->G, d->N / d->G,
+                   d->k, (float)(1.0 / sqrt((double)d->d)), lse_r, lse_s};
+  if (trace_on())
+    fprintf(stderr, "[gqe] prefill B=%d S=%d N=%d G=%d k=%d d=%d dtype=%d lse=%d\n", d->B, d->S,
+            d->N, d->G, d->k, d->d, d->dtype, lse_r != nullptr);
+  return hip_status(launch_prefill(pp, d->d, d->dtype == GQE_BF16, (hipStream_t)stream));
+}
+
+// Backward workspace: packed q and dO rows, -lse*sqrt(d) and -dO.O per row,
+// and (bf16) the two fp32 partial sums of KV head 0's dK and dV.
+struct BwdLayout {
+  int Rp;
+  size_t qp, dop, nlse, ndel, part, part_bytes, total;
+};
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+BwdLayout bwd_layout(const gqe_dims* d) {
+  BwdLayout L{};
+  L.Rp = (int)((((int64_t)d->S * d->k) + 31) / 32 * 32);
+  const size_t rows = (size_t)d->B * (d->G + 1) * (size_t)L.Rp;
+  const size_t esz = d->dtype == GQE_BF16 ? 2 : 4;
+  size_t off = 0;
+  L.qp = off;
+  off += round256(rows * d->d * esz);
+  L.dop = off;
+  off += round256(rows * d->d * esz);
+  L.nlse = off;
+  off += round256(rows * 4);
+  L.ndel = off;
+  off += round256(rows * 4);
+  L.part = off;
+  L.part_bytes = d->dtype == GQE_BF16 ? round256((size_t)4 * d->B * d->S * d->d * 4) : 0;
+  off += L.part_bytes;
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,21 +154,61 @@ int gqe_route(const gqe_dims* d, const void* x, const void* w_router, const floa
 
 int gqe_attn_prefill(const gqe_dims* d, const void* q, const void* k, const void* v,
                      const int32_t* topk_idx, void* o_routed, void* o_shared, void* stream) {
+  return prefill_common(d, q, k, v, topk_idx, o_routed, o_shared, nullptr, nullptr, stream);
+}
+
+int gqe_attn_prefill_train(const gqe_dims* d, const void* q, const void* k, const void* v,
+                           const int32_t* topk_idx, void* o_routed, void* o_shared,
+                           float* lse_routed, float* lse_shared, void* stream) {
+  if (!lse_routed || !lse_shared) return GQE_ERR_INVALID_ARG;
+  return prefill_common(d, q, k, v, topk_idx, o_routed, o_shared, lse_routed, lse_shared, stream);
+}
+
+size_t gqe_attn_prefill_bwd_workspace_bytes(const gqe_dims* d) {
+  if (check_dims(d, false) != GQE_OK) return 0;
+  if ((int64_t)d->S * d->k > (int64_t)INT32_MAX / 2) return 0;
+  return bwd_layout(d).total;
+}
+
+int gqe_attn_prefill_bwd(const gqe_dims* d, const void* q, const void* k, const void* v,
+                         const int32_t* topk_idx, const void* o_routed, const void* o_shared,
+                         const float* lse_routed, const float* lse_shared, const void* do_routed,
+                         const void* do_shared, void* dq, void* dk, void* dv, void* workspace,
+                         size_t ws_bytes, void* stream) {
   int st = check_dims(d, false);
   if (st) return st;
-  if (!q || !k || !v || !topk_idx || !o_routed || !o_shared) return GQE_ERR_INVALID_ARG;
-  const void* ptrs[] = {q, k, v, topk_idx, o_routed, o_shared};
+  if (!q || !k || !v || !topk_idx || !o_routed || !o_shared || !lse_routed || !lse_shared ||
+      !do_routed || !do_shared || !dq || !dk || !dv)
+    return GQE_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, topk_idx, o_routed, o_shared, lse_routed, lse_shared,
+                        do_routed, do_shared, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return GQE_ERR_ALIGNMENT;
-  // rows per (sequence, group) and tile counts must stay in int32
   if ((int64_t)d->S * d->k > (int64_t)INT32_MAX / 2) return GQE_ERR_UNSUPPORTED;
   if (d->B == 0 || d->S == 0) return GQE_OK;
-  PrefillParams pp{q, k, v, topk_idx, o_routed, o_shared, d->B, d->S, d->N, d->G, d->N / d->G,
-                   d->k, (float)(1.0 / sqrt((double)d->d))};
+  const BwdLayout L = bwd_layout(d);
+  if (!workspace || ws_bytes < L.total) return GQE_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GQE_ERR_ALIGNMENT;
+  char* ws = (char*)workspace;
+  BwdParams bp{};
+  bp.f = PrefillParams{q, k, v, topk_idx, const_cast<void*>(o_routed), const_cast<void*>(o_shared),
+                       d->B, d->S, d->N, d->G, d->N / d->G, d->k, (float)(1.0 / sqrt((double)d->d)),
+                       const_cast<float*>(lse_routed), const_cast<float*>(lse_shared)};
+  bp.do_r = do_routed;
+  bp.do_s = do_shared;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  bp.qp = ws + L.qp;
+  bp.dop = ws + L.dop;
+  bp.nlse = (float*)(ws + L.nlse);
+  bp.ndel = (float*)(ws + L.ndel);
+  bp.part = L.part_bytes ? (float*)(ws + L.part) : nullptr;
+  bp.Rp = L.Rp;
   if (trace_on())
-    fprintf(stderr, "[gqe] prefill B=%d S=%d N=%d G=%d k=%d d=%d dtype=%d\n", d->B, d->S, d->N,
-            d->G, d->k, d->d, d->dtype);
-  return hip_status(launch_prefill(pp, d->d, d->dtype == GQE_BF16, (hipStream_t)stream));
+    fprintf(stderr, "[gqe] prefill_bwd B=%d S=%d N=%d G=%d k=%d d=%d dtype=%d Rp=%d\n", d->B, d->S,
+            d->N, d->G, d->k, d->d, d->dtype, L.Rp);
+  return hip_status(launch_prefill_bwd(bp, d->d, d->dtype == GQE_BF16, (hipStream_t)stream));
 }
 
 size_t gqe_decode_workspace_bytes(const gqe_dims* d, int32_t q_len) {

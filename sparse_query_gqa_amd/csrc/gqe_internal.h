@@ -49,6 +49,26 @@ struct PrefillParams {
   void* o_s;              // [B, S, d]
   int B, S, N, G, M, K;
   float scale;            // 1/sqrt(d)
+  // optional (training): per row ln sum_j exp(q.k_j / sqrt(d)), the softmax
+  // normaliser the backward pass recomputes P with; null = not written
+  float* lse_r;           // [B, S, G, k]
+  float* lse_s;           // [B, S]
+};
+
+struct BwdParams {
+  PrefillParams f;        // forward inputs and outputs (o_r, o_s) and the row lse
+  const void* do_r;       // [B, S, G, k, d]
+  const void* do_s;       // [B, S, d]
+  void* dq;               // [B, S, N+1, d] (rows of unselected heads untouched)
+  void* dk;               // [B, G, S, d]
+  void* dv;               // [B, G, S, d]
+  // workspace: rows packed per (b, v), row r of (b, v) at (b*(G+1) + v)*Rp + r
+  void* qp;               // [B, G+1, Rp, d] q of the row
+  void* dop;              // [B, G+1, Rp, d] dO of the row
+  float* nlse;            // [B, G+1, Rp] -lse*sqrt(d)
+  float* ndel;            // [B, G+1, Rp] -dO.O
+  float* part;            // [2 (dK, dV), 2 (group 0, shared head), B, S, d] (bf16 path)
+  int Rp;                 // S*k rounded up to a multiple of 32
 };
 
 struct DecodeParams {
@@ -111,6 +131,7 @@ hipError_t launch_prefill(const PrefillParams& p, int d, bool bf16, hipStream_t 
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s);
 hipError_t launch_out_proj(const OutProjParams& p, bool bf16, hipStream_t s);
 hipError_t launch_proj(const ProjParams& p, bool bf16, hipStream_t s);
+hipError_t launch_prefill_bwd(const BwdParams& p, int d, bool bf16, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Small device helpers

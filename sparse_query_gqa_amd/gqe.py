@@ -33,6 +33,7 @@ EXPORTED = [
     "gqe_status_string", "gqe_version", "gqe_route_workspace_bytes", "gqe_route",
     "gqe_attn_prefill", "gqe_decode_workspace_bytes", "gqe_attn_decode", "gqe_out_proj",
     "gqe_qkv_proj", "gqe_qkv_proj_decode", "gqe_attn_decode_paged", "gqe_out_proj_variant",
+    "gqe_attn_prefill_train", "gqe_attn_prefill_bwd_workspace_bytes", "gqe_attn_prefill_bwd",
 ]
 
 
@@ -91,6 +92,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gqe_qkv_proj_decode": (ctypes.c_int, [D, I32, P, P, P, P, P, P, P, P, P, P]),
         "gqe_attn_decode_paged": (ctypes.c_int, [D, I32, P, P, P, P, I32, P, P, P, P, P, P, SZ, P]),
         "gqe_out_proj_variant": (ctypes.c_int, [D, I32, I64, P, P, P, P, P, P]),
+        "gqe_attn_prefill_train": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P]),
+        "gqe_attn_prefill_bwd_workspace_bytes": (SZ, [D]),
+        "gqe_attn_prefill_bwd": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -174,6 +178,46 @@ def gqe_attn_prefill(dims, q, k, v, topk_idx, o_routed, o_shared, stream=None):
                                          _ptr(topk_idx), _ptr(o_routed), _ptr(o_shared),
                                          _stream(stream))
     _raise(st, "gqe_attn_prefill")
+
+
+def gqe_attn_prefill_train(dims, q, k, v, topk_idx, o_routed, o_shared, lse_routed, lse_shared,
+                           stream=None):
+    B, S, N, G, kk, d, dt = dims.B, dims.S, dims.N, dims.G, dims.k, dims.d, dims.torch_dtype
+    _check(q, "q", (B, S, N + 1, d), dt)
+    _check(k, "k", (B, G, S, d), dt)
+    _check(v, "v", (B, G, S, d), dt)
+    _check(topk_idx, "topk_idx", (B * S, G, kk), torch.int32)
+    _check(o_routed, "o_routed", (B, S, G, kk, d), dt)
+    _check(o_shared, "o_shared", (B, S, d), dt)
+    _check(lse_routed, "lse_routed", (B, S, G, kk), torch.float32)
+    _check(lse_shared, "lse_shared", (B, S), torch.float32)
+    st = load_library().gqe_attn_prefill_train(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
+                                               _ptr(topk_idx), _ptr(o_routed), _ptr(o_shared),
+                                               _ptr(lse_routed), _ptr(lse_shared), _stream(stream))
+    _raise(st, "gqe_attn_prefill_train")
+
+
+def gqe_attn_prefill_bwd_workspace_bytes(dims: gqe_dims) -> int:
+    return load_library().gqe_attn_prefill_bwd_workspace_bytes(ctypes.byref(dims))
+
+
+def gqe_attn_prefill_bwd(dims, q, k, v, topk_idx, o_routed, o_shared, lse_routed, lse_shared,
+                         do_routed, do_shared, dq, dk, dv, workspace, stream=None):
+    B, S, N, G, kk, d, dt = dims.B, dims.S, dims.N, dims.G, dims.k, dims.d, dims.torch_dtype
+    for t, name, shape in ((q, "q", (B, S, N + 1, d)), (k, "k", (B, G, S, d)), (v, "v", (B, G, S, d)),
+                           (o_routed, "o_routed", (B, S, G, kk, d)), (o_shared, "o_shared", (B, S, d)),
+                           (do_routed, "do_routed", (B, S, G, kk, d)), (do_shared, "do_shared", (B, S, d)),
+                           (dq, "dq", (B, S, N + 1, d)), (dk, "dk", (B, G, S, d)), (dv, "dv", (B, G, S, d))):
+        _check(t, name, shape, dt)
+    _check(topk_idx, "topk_idx", (B * S, G, kk), torch.int32)
+    _check(lse_routed, "lse_routed", (B, S, G, kk), torch.float32)
+    _check(lse_shared, "lse_shared", (B, S), torch.float32)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().gqe_attn_prefill_bwd(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(topk_idx), _ptr(o_routed), _ptr(o_shared),
+        _ptr(lse_routed), _ptr(lse_shared), _ptr(do_routed), _ptr(do_shared), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(workspace), ws_bytes, _stream(stream))
+    _raise(st, "gqe_attn_prefill_bwd")
 
 
 def gqe_attn_decode(dims, q_len, q, k_cache, v_cache, kv_len, topk_idx, o_routed, o_shared,
@@ -301,6 +345,29 @@ def prefill(dims, q, k, v, topk_idx, stream=None):
     o_s = torch.empty((dims.B, dims.S, dims.d), dtype=q.dtype, device=q.device)
     gqe_attn_prefill(dims, q, k, v, topk_idx, o_r, o_s, stream)
     return o_r, o_s
+
+
+def prefill_train(dims, q, k, v, topk_idx, stream=None):
+    """Forward that also returns each row's log-sum-exp: (o_r, o_s, lse_r, lse_s)."""
+    o_r, o_s = (torch.empty(s, dtype=q.dtype, device=q.device)
+                for s in ((dims.B, dims.S, dims.G, dims.k, dims.d), (dims.B, dims.S, dims.d)))
+    lse_r = torch.empty((dims.B, dims.S, dims.G, dims.k), dtype=torch.float32, device=q.device)
+    lse_s = torch.empty((dims.B, dims.S), dtype=torch.float32, device=q.device)
+    gqe_attn_prefill_train(dims, q, k, v, topk_idx, o_r, o_s, lse_r, lse_s, stream)
+    return o_r, o_s, lse_r, lse_s
+
+
+def prefill_bwd(dims, q, k, v, topk_idx, o_r, o_s, lse_r, lse_s, do_r, do_s, workspace=None, stream=None):
+    """Attention backward: (dq, dk, dv); dq is zero in the rows of unselected heads."""
+    if workspace is None:
+        workspace = torch.empty((max(gqe_attn_prefill_bwd_workspace_bytes(dims), 16),), dtype=torch.uint8,
+                                device=q.device)
+    dq = torch.zeros_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    gqe_attn_prefill_bwd(dims, q, k, v, topk_idx, o_r, o_s, lse_r, lse_s, do_r, do_s, dq, dk, dv, workspace,
+                         stream)
+    return dq, dk, dv
 
 
 def decode_workspace(dims, q_len, device) -> torch.Tensor:

@@ -209,6 +209,48 @@ def test_decode_paged_validation():
     assert call(d, L=0) == gqe.GQE_OK
 
 
+def test_prefill_train_validation():
+    lib = _lib()
+
+    def call(dims, q=A, lr=A, ls=A):
+        return lib.gqe_attn_prefill_train(ctypes.byref(dims), P(q), P(A), P(A), P(A), P(A), P(A), P(lr), P(ls),
+                                          None)
+
+    assert call(_dims(), lr=0) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), ls=0) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), lr=MIS) == gqe.GQE_ERR_ALIGNMENT
+    assert call(_dims(), q=MIS) == gqe.GQE_ERR_ALIGNMENT
+    assert call(_dims(d=96)) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(B=0)) == gqe.GQE_OK
+
+
+def test_prefill_bwd_validation():
+    lib = _lib()
+
+    def call(dims, dq=A, do=A, ws=A, nbytes=1 << 40):
+        return lib.gqe_attn_prefill_bwd(ctypes.byref(dims), P(A), P(A), P(A), P(A), P(A), P(A), P(A), P(A), P(do),
+                                        P(A), P(dq), P(A), P(A), P(ws), nbytes, None)
+
+    assert call(_dims(), dq=0) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), do=0) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), dq=MIS) == gqe.GQE_ERR_ALIGNMENT
+    assert call(_dims(), ws=0) == gqe.GQE_ERR_WORKSPACE
+    assert call(_dims(), nbytes=16) == gqe.GQE_ERR_WORKSPACE
+    assert call(_dims(), ws=MIS) == gqe.GQE_ERR_ALIGNMENT
+    assert call(_dims(N=8, G=3)) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(B=0), ws=0) == gqe.GQE_OK
+    assert call(_dims(S=0), ws=0) == gqe.GQE_OK
+    # packed rows: B*(G+1)*Rp with Rp = S*k rounded up to 32; bf16 adds 4 fp32 planes of B*S*d
+    d = _dims(B=2, S=100, N=8, G=2, k=2, d=64)
+    rows = 2 * 3 * 224
+    r256 = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    want = 2 * r256(rows * 64 * 2) + 2 * r256(rows * 4) + r256(4 * 2 * 100 * 64 * 4)
+    assert lib.gqe_attn_prefill_bwd_workspace_bytes(ctypes.byref(d)) == want
+    d32 = _dims(B=2, S=100, N=8, G=2, k=2, d=64, dtype=gqe.GQE_F32)
+    assert lib.gqe_attn_prefill_bwd_workspace_bytes(ctypes.byref(d32)) == 2 * r256(rows * 64 * 4) + 2 * r256(rows * 4)
+    assert lib.gqe_attn_prefill_bwd_workspace_bytes(ctypes.byref(_dims(N=8, G=3))) == 0
+
+
 def test_workspace_sizes_closed_form():
     lib = _lib()
     d = _dims(B=16, S=65536, N=32, G=8, k=2, d=128)
