@@ -51,7 +51,7 @@ __all__ = [
     "build_lists", "attend_rows", "prefill", "decode", "assemble", "out_proj",
     "layer", "kv_bytes", "prefill_flops", "check_dims", "project",
     "project_decode", "project_flops", "attend_rows_bwd", "prefill_bwd",
-    "out_proj_bwd", "route_bwd", "lse_rows", "prefill_lse",
+    "out_proj_bwd", "route_bwd", "lse_rows", "prefill_lse", "load_balance_loss",
 ]
 
 
@@ -509,12 +509,35 @@ def out_proj_bwd(O_r, w, O_s, W_O, dy, mode: str = "full"):
     return dO_r, dw, dO_s, dW_O
 
 
-def route_bwd(x, w_r, z, idx, dw, G: int, M: int):
+def load_balance_loss(z, idx, M: int, coef: float) -> float:
+    """Auxiliary load-balancing loss of the routers ([GQE-review] §二 notes
+    that training adds the standard MoE balance loss against routing
+    collapse, without a formula). Reading: the usual form, per group router
+    and averaged over the G groups: f_{g,m} = share of the T*k selections of
+    group g that chose m, P_{g,m} = mean over tokens of p_{t,g,m};
+    loss = coef * M * mean_g sum_m f_{g,m} P_{g,m}. Balanced routing with
+    uniform p gives exactly coef. f is a count and carries no gradient.
+    z: [T, G, M]; idx: [T, G, k].
+    """
+    z = np.asarray(z, dtype=np.float64)
+    idx = np.asarray(idx)
+    T, G, k = idx.shape
+    p = softmax(z, axis=-1)
+    f = np.zeros((G, M))
+    for g in range(G):
+        f[g] = np.bincount(idx[:, g, :].reshape(-1), minlength=M)[:M] / (T * k)
+    P = p.mean(axis=0)
+    return float(coef * M * np.mean(np.sum(f * P, axis=-1)))
+
+
+def route_bwd(x, w_r, z, idx, dw, G: int, M: int, aux_coef: float = 0.0):
     """Gradients of the router given dw [T, G, k] (the gradient of the
     renormalised weights). p = softmax(z), w_j = p_{m_j} / sum_{j'} p_{m_j'}
     over the selected experts ([GQE-review] §二, the w equation); the
     selection itself is piecewise constant. dp_{m_j} = (dw_j - sum_j' dw_j'
-    w_j') / sum_j' p_{m_j'} on the selected experts, 0 elsewhere;
+    w_j') / sum_j' p_{m_j'} on the selected experts, 0 elsewhere; with
+    aux_coef the balance loss (load_balance_loss) adds
+    coef * M * f_{g,m} / (T * G) to dp of every expert;
     dz = p * (dp - p . dp); dW_r = dz^T x, db_r = sum_t dz, dx = dz W_r.
     x: [T, D]; w_r: [G*M, D]; z: [T, G, M]; idx: [T, G, k].
     Returns (dz [T, G, M], dW_r [G*M, D], db_r [G*M], dx [T, D]).
@@ -531,6 +554,11 @@ def route_bwd(x, w_r, z, idx, dw, G: int, M: int):
     dp_sel = (dw - np.sum(dw * wsel, axis=-1, keepdims=True)) / ssum
     dp = np.zeros_like(p)
     np.put_along_axis(dp, idx, dp_sel, axis=-1)
+    if aux_coef:
+        k = idx.shape[-1]
+        for g in range(G):
+            share = np.bincount(idx[:, g, :].reshape(-1), minlength=M)[:M] / (T * k)
+            dp[:, g, :] += aux_coef * M * share / (T * G)
     dz = p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
     dz2 = dz.reshape(T, G * M)
     w_r = np.asarray(w_r, dtype=np.float64)

@@ -537,6 +537,52 @@ def pin_route_bwd_central_differences(O):
     _close(dx, _central(loss, x), 1e-6, "dx")
 
 
+def pin_load_balance_closed_forms(O):
+    """Balance loss: equal logits with every expert chosen equally often
+    give exactly coef; every token on expert 0 with p_0 -> 1 gives coef*M;
+    a router with p uniform but all tokens on one expert gives coef (f . P
+    = 1/M)."""
+    T, G, M, k, coef = 8, 2, 4, 1, 0.01
+    idx = np.tile(np.arange(T) % M, (G, 1)).T.reshape(T, G, k)
+    _close(O.load_balance_loss(np.zeros((T, G, M)), idx, M, coef), coef, 1e-15, "balanced")
+    z = np.zeros((T, G, M))
+    z[..., 0] = 60.0
+    one = np.zeros((T, G, k), dtype=np.int64)
+    _close(O.load_balance_loss(z, one, M, coef), coef * M, 1e-12, "collapsed")
+    _close(O.load_balance_loss(np.zeros((T, G, M)), one, M, coef), coef, 1e-15, "uniform p, one expert")
+    idx2 = np.stack([np.sort(np.random.default_rng(t).permutation(M)[:2]) for t in range(T * G)]).reshape(T, G, 2)
+    _close(O.load_balance_loss(np.zeros((T, G, M)), idx2, M, coef), coef, 1e-15, "uniform p, k = 2")
+
+
+def pin_route_bwd_balance_loss_central_differences(O):
+    """dz of the balance loss (route_bwd with dw = 0) against central
+    differences in the logits with the selection held fixed, and dz of
+    route_bwd (dw and balance loss together) against differences of their
+    sum."""
+    rng = np.random.default_rng(25)
+    T, D, G, M, k, coef = 5, 6, 2, 4, 2, 0.3
+    x = rng.standard_normal((T, D))
+    w_r = rng.standard_normal((G * M, D))
+    z = rng.standard_normal((T, G, M))
+    idx = np.sort(np.argsort(-z, axis=-1)[..., :k], axis=-1)
+    dw = rng.standard_normal((T, G, k))
+
+    def loss():
+        p = O.softmax(z, axis=-1)
+        ps = np.take_along_axis(p, idx, -1)
+        ww = ps / ps.sum(-1, keepdims=True)
+        return float(np.sum(dw * ww)) + O.load_balance_loss(z, idx, M, coef)
+
+    dz0, _, _, _ = O.route_bwd(x, w_r, z, idx, np.zeros_like(dw), G, M, aux_coef=coef)
+
+    def aux_only():
+        return O.load_balance_loss(z, idx, M, coef)
+
+    _close(dz0, _central(aux_only, z), 1e-8, "balance-loss dz")
+    dz, _, _, _ = O.route_bwd(x, w_r, z, idx, dw, G, M, aux_coef=coef)
+    _close(dz, _central(loss, z), 1e-7, "dz with balance loss")
+
+
 # --------------------------------------------------------------------------
 # Projections: token-compacted Q, dense K/V, decode append
 # --------------------------------------------------------------------------

@@ -54,6 +54,14 @@ MUTANTS = {
         "O_s[b] = attend_rows(q[b, :, N, :], pos, K[b, G - 1, s0:n], V[b, G - 1, s0:n])"),
     "decode_padding_ignored": (
         "        s0 = 0 if kv_start is None else int(kv_start[b])", "        s0 = 0"),
+    "balance_grad_without_M": (
+        "dp[:, g, :] += aux_coef * M * share / (T * G)", "dp[:, g, :] += aux_coef * share / (T * G)"),
+    "balance_grad_not_averaged_over_groups": (
+        "dp[:, g, :] += aux_coef * M * share / (T * G)", "dp[:, g, :] += aux_coef * M * share / T"),
+    "balance_share_per_token": (
+        "f[g] = np.bincount(idx[:, g, :].reshape(-1), minlength=M)[:M] / (T * k)",
+        "f[g] = np.bincount(idx[:, g, :].reshape(-1), minlength=M)[:M] / T"),
+    "balance_prob_summed": ("P = p.mean(axis=0)", "P = p.sum(axis=0)"),
     "lse_without_max": (
         "return top + np.log(np.sum(np.exp(sc - top[:, None]), axis=1))",
         "return np.log(np.sum(np.exp(sc - top[:, None]), axis=1))"),
