@@ -234,6 +234,58 @@ int gqe_out_proj_variant(const gqe_dims* dims, int32_t mode, int64_t T,
                          const void* o_shared, const void* w_o, void* y,
                          void* stream);
 
+/* Bytes of device workspace gqe_out_proj_bwd needs (0 for invalid input). */
+size_t gqe_out_proj_bwd_workspace_bytes(const gqe_dims* dims, int32_t mode, int64_t T);
+
+/* Backward of gqe_out_proj_variant (GQE review, section 二: y = A W_O with
+ * A = Concat(O, obar, s) and obar = sum over groups and selected experts of
+ * w * o). With dA = dy W_O^T split into its slots:
+ *   dW_O = A^T dy;  dO_s = dA[s];
+ *   GQE_SLOTS_FULL:     dO_r = dA[O] + w dA[obar],  dw = o . dA[obar]
+ *                       (the renormalised slot is what gives the router a
+ *                       gradient, section 二);
+ *   GQE_SLOTS_HARD:     dO_r = dA[O], dw = 0;
+ *   GQE_SLOTS_WEIGHTED: dO_r = w dA[w O], dw = o . dA[w O].
+ *   o_routed [T, G, k, d], topk_w [T, G, k] fp32, o_shared [T, d], w_o as
+ *   for the forward, dy [T, D]                                    inputs
+ *   do_routed [T, G, k, d] dtype, dw [T, G, k] fp32, do_shared [T, d] dtype,
+ *   dw_o [rows of w_o, D] fp32                                    outputs
+ *   workspace >= gqe_out_proj_bwd_workspace_bytes(dims, mode, T) device bytes.
+ * Deterministic (weight gradient summed over token ranges in a fixed order).
+ * In the bf16 path the products take bf16 operands (A rounded as in the
+ * forward) with fp32 accumulation. */
+int gqe_out_proj_bwd(const gqe_dims* dims, int32_t mode, int64_t T,
+                     const void* o_routed, const float* topk_w, const void* o_shared,
+                     const void* w_o, const void* dy, void* do_routed, float* dw,
+                     void* do_shared, float* dw_o, void* workspace, size_t ws_bytes,
+                     void* stream);
+
+/* Bytes of device workspace gqe_route_bwd needs (0 for invalid dims). */
+size_t gqe_route_bwd_workspace_bytes(const gqe_dims* dims);
+
+/* Backward of gqe_route's weights for T = B*S tokens (GQE review, section
+ * 二: p = softmax(z), w = p_sel / sum p_sel over the TopK set, which is
+ * piecewise constant and carries no gradient):
+ *   dp_sel = (dw - sum_j dw_j w_j) / sum p_sel on the selected experts, 0 on
+ *   the others; dz = p (dp - p . dp); dW_r = dz^T x; db_r = sum_t dz;
+ *   dx = dz W_r.
+ * aux_coef > 0 adds the load-balancing loss the review says training uses
+ * (its formula is not given; reading: per group router, averaged over the
+ * groups) L = aux_coef * M * mean_g sum_m f_{g,m} P_{g,m}, f the share of the
+ * T*k selections of group g that chose m, P the mean of p over tokens; f is
+ * a count and carries no gradient, so dp gains aux_coef*M*f/(T*G).
+ *   x [B*S, D] dtype, w_router [G*M, D] dtype, logits [B*S, G, M] fp32 (as
+ *   written by gqe_route), topk_idx [B*S, G, k], dw [B*S, G, k] fp32  inputs
+ *   dz_or_null [B*S, G, M] fp32, dx [B*S, D] dtype, dw_router [G*M, D] fp32,
+ *   db_router [G*M] fp32, aux_loss_or_null [1] fp32 (the loss value) outputs
+ *   workspace >= gqe_route_bwd_workspace_bytes(dims) device bytes.
+ * aux_coef must be finite and >= 0 (GQE_ERR_INVALID_ARG). */
+int gqe_route_bwd(const gqe_dims* dims, const void* x, const void* w_router,
+                  const float* logits, const int32_t* topk_idx, const float* dw,
+                  float aux_coef, float* dz_or_null, void* dx, float* dw_router,
+                  float* db_router, float* aux_loss_or_null, void* workspace,
+                  size_t ws_bytes, void* stream);
+
 /* Query, key and value projections of a prefill with token-compacted
  * queries. GQE review, section 二: only the selected query heads take part in
  * attention, the others are skipped, so only their query rows are projected;

@@ -10,6 +10,6 @@ from .gqe import (  # noqa: F401
     GQE_SLOTS_WEIGHTED, GQEError, LIB_PATH, decode,
     decode_paged, decode_workspace, gqe_attn_decode, gqe_attn_decode_paged, gqe_attn_prefill, gqe_attn_prefill_bwd,
     gqe_attn_prefill_bwd_workspace_bytes, gqe_attn_prefill_train, gqe_decode_workspace_bytes, gqe_dims,
-    gqe_out_proj, gqe_out_proj_variant, gqe_qkv_proj, gqe_qkv_proj_decode, gqe_route, gqe_route_workspace_bytes,
-    load_library, out_proj, prefill, prefill_bwd, prefill_train, qkv_proj, route, status_string,
+    gqe_out_proj, gqe_out_proj_bwd, gqe_out_proj_bwd_workspace_bytes, gqe_out_proj_variant, gqe_qkv_proj, gqe_qkv_proj_decode, gqe_route, gqe_route_bwd, gqe_route_bwd_workspace_bytes, gqe_route_workspace_bytes,
+    load_library, out_proj, out_proj_bwd, prefill, prefill_bwd, prefill_train, qkv_proj, route, route_bwd, status_string,
 )

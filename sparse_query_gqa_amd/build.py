@@ -21,7 +21,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgqe.so")
 ARCH = os.environ.get("GQE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["gqe_api.hip", "route.hip", "prefill.hip", "decode.hip", "out_proj.hip", "qkv_proj.hip", "prefill_bwd.hip"]
+SOURCES = ["gqe_api.hip", "route.hip", "prefill.hip", "decode.hip", "out_proj.hip", "qkv_proj.hip", "prefill_bwd.hip",
+           "layer_bwd.hip"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -98,6 +98,62 @@ BwdLayout bwd_layout(const gqe_dims* d) {
   return L;
 }
 
+// Output-projection backward workspace: dA (fp32), the slot vectors
+// (dtype) and the split partials of dW_O.
+struct OutProjBwdLayout {
+  int Kd, nsplit, kchunk;
+  size_t da, a, part, total;
+};
+OutProjBwdLayout out_proj_bwd_layout(const gqe_dims* d, int32_t mode, int64_t T) {
+  OutProjBwdLayout L{};
+  L.Kd = d->G * d->k * d->d + (mode == GQE_SLOTS_FULL ? d->d : 0) + d->d;
+  const int tiles = ((L.Kd + 127) / 128) * ((d->D + 127) / 128);
+  gemm_split(T, tiles, L.nsplit, L.kchunk);
+  const size_t esz = d->dtype == GQE_BF16 ? 2 : 4;
+  size_t off = 0;
+  L.da = off;
+  off += round256((size_t)T * L.Kd * 4);
+  L.a = off;
+  off += round256((size_t)T * L.Kd * esz);
+  L.part = off;
+  if (L.nsplit > 1) off += round256((size_t)L.nsplit * L.Kd * d->D * 4);
+  L.total = off;
+  return L;
+}
+
+// Router backward workspace: dz (fp32, when the caller takes none), dz in
+// the storage dtype padded to GMp columns, the softmax (balance loss), the
+// selection counts, the column-sum partials and the split partials of dW_r.
+struct RouteBwdLayout {
+  int GM, GMp, nchunk, nsplit, kchunk;
+  size_t dz, dzb, pbuf, counts, colpart, part, total;
+};
+RouteBwdLayout route_bwd_layout(const gqe_dims* d) {
+  RouteBwdLayout L{};
+  const int64_t T = (int64_t)d->B * d->S;
+  L.GM = d->N;
+  L.GMp = (L.GM + 31) / 32 * 32;
+  L.nchunk = (int)((T + kColChunk - 1) / kColChunk);
+  const int tiles = ((L.GM + 127) / 128) * ((d->D + 127) / 128);
+  gemm_split(T, tiles, L.nsplit, L.kchunk);
+  const size_t esz = d->dtype == GQE_BF16 ? 2 : 4;
+  size_t off = 0;
+  L.dz = off;
+  off += round256((size_t)T * L.GM * 4);
+  L.dzb = off;
+  off += round256((size_t)T * L.GMp * esz);
+  L.pbuf = off;
+  off += round256((size_t)T * L.GM * 4);
+  L.counts = off;
+  off += round256((size_t)L.GM * 4);
+  L.colpart = off;
+  off += round256((size_t)2 * L.nchunk * L.GM * 4);
+  L.part = off;
+  if (L.nsplit > 1) off += round256((size_t)L.nsplit * L.GM * d->D * 4);
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -363,6 +419,117 @@ int gqe_qkv_proj_decode(const gqe_dims* d, int32_t q_len, const void* x, const v
     fprintf(stderr, "[gqe] qkv_proj_decode B=%d L=%d Smax=%d D=%d N=%d G=%d k=%d d=%d\n", d->B,
             q_len, d->S, d->D, d->N, d->G, d->k, d->d);
   return hip_status(launch_proj(pp, d->dtype == GQE_BF16, (hipStream_t)stream));
+}
+
+
+size_t gqe_out_proj_bwd_workspace_bytes(const gqe_dims* d, int32_t mode, int64_t T) {
+  if (check_dims(d) != GQE_OK || T < 0 || T > (int64_t)INT32_MAX) return 0;
+  if (mode != GQE_SLOTS_FULL && mode != GQE_SLOTS_HARD && mode != GQE_SLOTS_WEIGHTED) return 0;
+  return out_proj_bwd_layout(d, mode, T).total;
+}
+
+int gqe_out_proj_bwd(const gqe_dims* d, int32_t mode, int64_t T, const void* o_routed,
+                     const float* topk_w, const void* o_shared, const void* w_o, const void* dy,
+                     void* do_routed, float* dw, void* do_shared, float* dw_o, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  if (T < 0) return GQE_ERR_INVALID_ARG;
+  if (mode != GQE_SLOTS_FULL && mode != GQE_SLOTS_HARD && mode != GQE_SLOTS_WEIGHTED)
+    return GQE_ERR_UNSUPPORTED;
+  if (!o_routed || !topk_w || !o_shared || !w_o || !dy || !do_routed || !dw || !do_shared || !dw_o)
+    return GQE_ERR_INVALID_ARG;
+  const void* ptrs[] = {o_routed, topk_w, o_shared, w_o, dy, do_routed, dw, do_shared, dw_o};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GQE_ERR_ALIGNMENT;
+  if (T > (int64_t)INT32_MAX) return GQE_ERR_UNSUPPORTED;
+  if (T == 0) return GQE_OK;
+  const OutProjBwdLayout L = out_proj_bwd_layout(d, mode, T);
+  if (!workspace || ws_bytes < L.total) return GQE_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GQE_ERR_ALIGNMENT;
+  char* ws = (char*)workspace;
+  OutProjBwdParams bp{};
+  bp.o_r = o_routed;
+  bp.w = topk_w;
+  bp.o_s = o_shared;
+  bp.w_o = w_o;
+  bp.dy = dy;
+  bp.do_r = do_routed;
+  bp.dw = dw;
+  bp.do_s = do_shared;
+  bp.dw_o = dw_o;
+  bp.da = (float*)(ws + L.da);
+  bp.a = ws + L.a;
+  bp.part = (float*)(ws + L.part);
+  bp.T = T;
+  bp.Gk = d->G * d->k;
+  bp.d = d->d;
+  bp.Dout = d->D;
+  bp.Kd = L.Kd;
+  bp.nob = mode == GQE_SLOTS_FULL ? d->d : 0;
+  bp.weighted = mode == GQE_SLOTS_WEIGHTED ? 1 : 0;
+  bp.nsplit = L.nsplit;
+  bp.kchunk = L.kchunk;
+  if (trace_on())
+    fprintf(stderr, "[gqe] out_proj_bwd mode=%d T=%lld Kd=%d D=%d nsplit=%d\n", mode, (long long)T,
+            L.Kd, d->D, L.nsplit);
+  return hip_status(launch_out_proj_bwd(bp, d->dtype == GQE_BF16, (hipStream_t)stream));
+}
+
+size_t gqe_route_bwd_workspace_bytes(const gqe_dims* d) {
+  if (check_dims(d) != GQE_OK) return 0;
+  return route_bwd_layout(d).total;
+}
+
+int gqe_route_bwd(const gqe_dims* d, const void* x, const void* w_router, const float* logits,
+                  const int32_t* topk_idx, const float* dw, float aux_coef, float* dz_or_null,
+                  void* dx, float* dw_router, float* db_router, float* aux_loss_or_null,
+                  void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  if (!x || !w_router || !logits || !topk_idx || !dw || !dx || !dw_router || !db_router)
+    return GQE_ERR_INVALID_ARG;
+  if (!(aux_coef >= 0.f) || aux_coef > 1e30f) return GQE_ERR_INVALID_ARG;  // rejects NaN too
+  const void* ptrs[] = {x, w_router, logits, topk_idx, dw, dz_or_null, dx, dw_router, db_router,
+                        aux_loss_or_null};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GQE_ERR_ALIGNMENT;
+  const int64_t T = (int64_t)d->B * d->S;
+  if (T == 0) return GQE_OK;
+  const RouteBwdLayout L = route_bwd_layout(d);
+  if (!workspace || ws_bytes < L.total) return GQE_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GQE_ERR_ALIGNMENT;
+  char* ws = (char*)workspace;
+  RouteBwdParams rp{};
+  rp.x = x;
+  rp.w = w_router;
+  rp.z = logits;
+  rp.topk = topk_idx;
+  rp.dw = dw;
+  rp.dz = dz_or_null ? dz_or_null : (float*)(ws + L.dz);
+  rp.dzb = ws + L.dzb;
+  rp.pbuf = aux_loss_or_null ? (float*)(ws + L.pbuf) : nullptr;
+  rp.counts = (int32_t*)(ws + L.counts);
+  rp.colpart = (float*)(ws + L.colpart);
+  rp.dx = dx;
+  rp.dw_r = dw_router;
+  rp.db_r = db_router;
+  rp.aux_loss = aux_loss_or_null;
+  rp.part = (float*)(ws + L.part);
+  rp.aux_coef = aux_coef;
+  rp.T = T;
+  rp.D = d->D;
+  rp.G = d->G;
+  rp.M = d->N / d->G;
+  rp.K = d->k;
+  rp.GMp = L.GMp;
+  rp.nchunk = L.nchunk;
+  rp.nsplit = L.nsplit;
+  rp.kchunk = L.kchunk;
+  if (trace_on())
+    fprintf(stderr, "[gqe] route_bwd T=%lld D=%d G=%d M=%d k=%d aux=%g nsplit=%d\n", (long long)T,
+            d->D, d->G, rp.M, d->k, (double)aux_coef, L.nsplit);
+  return hip_status(launch_route_bwd(rp, d->dtype == GQE_BF16, (hipStream_t)stream));
 }
 
 }  // extern "C"

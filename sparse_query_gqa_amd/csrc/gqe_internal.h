@@ -71,6 +71,46 @@ struct BwdParams {
   int Rp;                 // S*k rounded up to a multiple of 32
 };
 
+// Output projection backward (slot layouts as in OutProjParams).
+struct OutProjBwdParams {
+  const void* o_r;        // [T, G*k*d]
+  const float* w;         // [T, G*k]
+  const void* o_s;        // [T, d]
+  const void* w_o;        // [Kd, Dout]
+  const void* dy;         // [T, Dout]
+  void* do_r;             // [T, G*k*d] out
+  float* dw;              // [T, G*k] out
+  void* do_s;             // [T, d] out
+  float* dw_o;            // [Kd, Dout] out (fp32)
+  float* da;              // workspace [T, Kd] fp32: dy W_O^T
+  void* a;                // workspace [T, Kd] dtype: the slot vectors
+  float* part;            // workspace [nsplit, Kd, Dout] fp32 (nsplit > 1)
+  int64_t T;
+  int Gk, d, Dout, Kd, nob, weighted, nsplit, kchunk;
+};
+
+// Router backward.
+struct RouteBwdParams {
+  const void* x;          // [T, D]
+  const void* w;          // [GM, D]
+  const float* z;         // [T, G, M] logits
+  const int32_t* topk;    // [T, G, k]
+  const float* dw;        // [T, G, k]
+  float* dz;              // [T, GM] out (workspace when the caller wants none)
+  void* dzb;              // workspace [T, GMp] dtype, zero past GM
+  float* pbuf;            // workspace [T, GM] softmax (balance loss only)
+  int32_t* counts;        // workspace [G*M]
+  float* colpart;         // workspace [2, nchunk, GM]
+  void* dx;               // [T, D] out
+  float* dw_r;            // [GM, D] out
+  float* db_r;            // [GM] out
+  float* aux_loss;        // [1] out or null
+  float* part;            // workspace [nsplit, GM, D] (nsplit > 1)
+  float aux_coef;
+  int64_t T;
+  int D, G, M, K, GMp, nchunk, nsplit, kchunk;
+};
+
 struct DecodeParams {
   const void* q;          // [B, L, N+1, d]
   const void* k;          // [B, G, Smax, d]
@@ -132,6 +172,12 @@ hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s)
 hipError_t launch_out_proj(const OutProjParams& p, bool bf16, hipStream_t s);
 hipError_t launch_proj(const ProjParams& p, bool bf16, hipStream_t s);
 hipError_t launch_prefill_bwd(const BwdParams& p, int d, bool bf16, hipStream_t s);
+hipError_t launch_out_proj_bwd(const OutProjBwdParams& p, bool bf16, hipStream_t s);
+hipError_t launch_route_bwd(const RouteBwdParams& p, bool bf16, hipStream_t s);
+// split of a long contraction for the weight-gradient products: kchunk is a
+// multiple of 32, nsplit * kchunk >= K
+void gemm_split(int64_t K, int tiles, int& nsplit, int& kchunk);
+constexpr int kColChunk = 1024;  // tokens per partial of the router's column sums
 
 // ---------------------------------------------------------------------------
 // Small device helpers

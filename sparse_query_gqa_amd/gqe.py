@@ -34,6 +34,7 @@ EXPORTED = [
     "gqe_attn_prefill", "gqe_decode_workspace_bytes", "gqe_attn_decode", "gqe_out_proj",
     "gqe_qkv_proj", "gqe_qkv_proj_decode", "gqe_attn_decode_paged", "gqe_out_proj_variant",
     "gqe_attn_prefill_train", "gqe_attn_prefill_bwd_workspace_bytes", "gqe_attn_prefill_bwd",
+    "gqe_out_proj_bwd_workspace_bytes", "gqe_out_proj_bwd", "gqe_route_bwd_workspace_bytes", "gqe_route_bwd",
 ]
 
 
@@ -95,6 +96,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gqe_attn_prefill_train": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P]),
         "gqe_attn_prefill_bwd_workspace_bytes": (SZ, [D]),
         "gqe_attn_prefill_bwd": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "gqe_out_proj_bwd_workspace_bytes": (SZ, [D, I32, I64]),
+        "gqe_out_proj_bwd": (ctypes.c_int, [D, I32, I64, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "gqe_route_bwd_workspace_bytes": (SZ, [D]),
+        "gqe_route_bwd": (ctypes.c_int, [D, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -218,6 +223,61 @@ def gqe_attn_prefill_bwd(dims, q, k, v, topk_idx, o_routed, o_shared, lse_routed
         _ptr(lse_routed), _ptr(lse_shared), _ptr(do_routed), _ptr(do_shared), _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(workspace), ws_bytes, _stream(stream))
     _raise(st, "gqe_attn_prefill_bwd")
+
+
+def _slot_rows(dims, mode) -> int:
+    return (dims.G * dims.k + (2 if mode == GQE_SLOTS_FULL else 1)) * dims.d
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def gqe_out_proj_bwd_workspace_bytes(dims, mode, T) -> int:
+    return load_library().gqe_out_proj_bwd_workspace_bytes(ctypes.byref(dims), int(mode), int(T))
+
+
+def gqe_out_proj_bwd(dims, mode, T, o_routed, topk_w, o_shared, w_o, dy, do_routed, dw, do_shared, dw_o,
+                     workspace, stream=None):
+    G, kk, d, D, dt = dims.G, dims.k, dims.d, dims.D, dims.torch_dtype
+    _check(o_routed, "o_routed", (T, G, kk, d), dt)
+    _check(topk_w, "topk_w", (T, G, kk), torch.float32)
+    _check(o_shared, "o_shared", (T, d), dt)
+    _check(w_o, "w_o", (_slot_rows(dims, mode), D), dt)
+    _check(dy, "dy", (T, D), dt)
+    _check(do_routed, "do_routed", (T, G, kk, d), dt)
+    _check(dw, "dw", (T, G, kk), torch.float32)
+    _check(do_shared, "do_shared", (T, d), dt)
+    _check(dw_o, "dw_o", (_slot_rows(dims, mode), D), torch.float32)
+    st = load_library().gqe_out_proj_bwd(ctypes.byref(dims), int(mode), int(T), _ptr(o_routed), _ptr(topk_w),
+                                         _ptr(o_shared), _ptr(w_o), _ptr(dy), _ptr(do_routed), _ptr(dw),
+                                         _ptr(do_shared), _ptr(dw_o), _ptr(workspace), _nbytes(workspace),
+                                         _stream(stream))
+    _raise(st, "gqe_out_proj_bwd")
+
+
+def gqe_route_bwd_workspace_bytes(dims) -> int:
+    return load_library().gqe_route_bwd_workspace_bytes(ctypes.byref(dims))
+
+
+def gqe_route_bwd(dims, x, w_router, logits, topk_idx, dw, aux_coef, dz, dx, dw_router, db_router, aux_loss,
+                  workspace, stream=None):
+    T, D, G, M, kk, dt = dims.B * dims.S, dims.D, dims.G, dims.M, dims.k, dims.torch_dtype
+    _check(x, "x", (T, D), dt)
+    _check(w_router, "w_router", (G * M, D), dt)
+    _check(logits, "logits", (T, G, M), torch.float32)
+    _check(topk_idx, "topk_idx", (T, G, kk), torch.int32)
+    _check(dw, "dw", (T, G, kk), torch.float32)
+    _check(dz, "dz", (T, G, M), torch.float32, optional=True)
+    _check(dx, "dx", (T, D), dt)
+    _check(dw_router, "dw_router", (G * M, D), torch.float32)
+    _check(db_router, "db_router", (G * M,), torch.float32)
+    _check(aux_loss, "aux_loss", (1,), torch.float32, optional=True)
+    st = load_library().gqe_route_bwd(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(logits), _ptr(topk_idx),
+                                      _ptr(dw), float(aux_coef), _ptr(dz), _ptr(dx), _ptr(dw_router),
+                                      _ptr(db_router), _ptr(aux_loss), _ptr(workspace), _nbytes(workspace),
+                                      _stream(stream))
+    _raise(st, "gqe_route_bwd")
 
 
 def gqe_attn_decode(dims, q_len, q, k_cache, v_cache, kv_len, topk_idx, o_routed, o_shared,
@@ -368,6 +428,39 @@ def prefill_bwd(dims, q, k, v, topk_idx, o_r, o_s, lse_r, lse_s, do_r, do_s, wor
     gqe_attn_prefill_bwd(dims, q, k, v, topk_idx, o_r, o_s, lse_r, lse_s, do_r, do_s, dq, dk, dv, workspace,
                          stream)
     return dq, dk, dv
+
+
+def _workspace(nbytes, device):
+    return torch.empty((max(int(nbytes), 16),), dtype=torch.uint8, device=device)
+
+
+def out_proj_bwd(dims, T, o_routed, topk_w, o_shared, w_o, dy, mode=GQE_SLOTS_FULL, stream=None):
+    """Output-projection backward: (do_r [T,G,k,d], dw [T,G,k], do_s [T,d], dw_o fp32)."""
+    dev = dy.device
+    o_routed = o_routed.reshape(T, dims.G, dims.k, dims.d)
+    topk_w = topk_w.reshape(T, dims.G, dims.k)
+    o_shared = o_shared.reshape(T, dims.d)
+    do_r = torch.empty_like(o_routed)
+    dw = torch.empty((T, dims.G, dims.k), dtype=torch.float32, device=dev)
+    do_s = torch.empty_like(o_shared)
+    dw_o = torch.empty(tuple(w_o.shape), dtype=torch.float32, device=dev)
+    ws = _workspace(gqe_out_proj_bwd_workspace_bytes(dims, mode, T), dev)
+    gqe_out_proj_bwd(dims, mode, T, o_routed, topk_w, o_shared, w_o, dy, do_r, dw, do_s, dw_o, ws, stream)
+    return do_r, dw, do_s, dw_o
+
+
+def route_bwd(dims, x, w_router, logits, topk_idx, dw, aux_coef=0.0, stream=None):
+    """Router backward: dict(dz, dx, dw_router, db_router, aux_loss)."""
+    dev = x.device
+    T, GM = dims.B * dims.S, dims.N
+    out = dict(dz=torch.empty((T, dims.G, dims.M), dtype=torch.float32, device=dev), dx=torch.empty_like(x),
+               dw_router=torch.empty((GM, dims.D), dtype=torch.float32, device=dev),
+               db_router=torch.empty((GM,), dtype=torch.float32, device=dev),
+               aux_loss=torch.zeros((1,), dtype=torch.float32, device=dev))
+    ws = _workspace(gqe_route_bwd_workspace_bytes(dims), dev)
+    gqe_route_bwd(dims, x, w_router, logits, topk_idx, dw, aux_coef, out["dz"], out["dx"], out["dw_router"],
+                  out["db_router"], out["aux_loss"], ws, stream)
+    return out
 
 
 def decode_workspace(dims, q_len, device) -> torch.Tensor:
