@@ -309,6 +309,70 @@ def main():
     del kp, vp
     paged_gbps = kv / t_paged.mean() / 1e9
 
+    # The training backward of the same layer (attention, output projection,
+    # router with the balance loss), timed after the steps on seeded output
+    # gradients; the training forward supplies the rows' log-sum-exp.
+    gen = torch.Generator(device=dev).manual_seed(5)
+    lse_r = torch.empty((cfg.B, cfg.S, G, k), dtype=torch.float32, device=dev)
+    lse_s = torch.empty((cfg.B, cfg.S), dtype=torch.float32, device=dev)
+    gqe.gqe_attn_prefill_train(dims, g["q"], g["k"], g["v"], r_out["topk_idx"], o_r, o_s, lse_r, lse_s)
+    do_r = torch.randn(o_r.shape, device=dev, generator=gen).to(torch.bfloat16)
+    do_s = torch.randn(o_s.shape, device=dev, generator=gen).to(torch.bfloat16)
+    dq_t = torch.zeros_like(g["q"])
+    dk_t = torch.empty_like(g["k"])
+    dv_t = torch.empty_like(g["v"])
+    b_ws = torch.empty((max(gqe.gqe_attn_prefill_bwd_workspace_bytes(dims), 16),), dtype=torch.uint8, device=dev)
+
+    def attn_bwd_call():
+        gqe.gqe_attn_prefill_bwd(dims, g["q"], g["k"], g["v"], r_out["topk_idx"], o_r, o_s, lse_r, lse_s,
+                                 do_r, do_s, dq_t, dk_t, dv_t, b_ws)
+
+    t_abwd = timed(attn_bwd_call, max(2, args.steps // 2))
+    del b_ws
+    dy = torch.randn((T, cfg.D), device=dev, generator=gen).to(torch.bfloat16)
+    dor_t, dos_t = torch.empty((T, G, k, d), dtype=torch.bfloat16, device=dev), torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    dw_t = torch.empty((T, G, k), dtype=torch.float32, device=dev)
+    dwo_t = torch.empty(tuple(g["w_o"].shape), dtype=torch.float32, device=dev)
+    o_ws = torch.empty((max(gqe.gqe_out_proj_bwd_workspace_bytes(dims, gqe.GQE_SLOTS_FULL, T), 16),),
+                       dtype=torch.uint8, device=dev)
+
+    def oproj_bwd_call():
+        gqe.gqe_out_proj_bwd(dims, gqe.GQE_SLOTS_FULL, T, o_r.view(T, G, k, d), r_out["topk_w"], o_s.view(T, d),
+                             g["w_o"], dy, dor_t, dw_t, dos_t, dwo_t, o_ws)
+
+    t_obwd = timed(oproj_bwd_call, args.steps)
+    del o_ws
+    z_t = torch.empty((T, G, M), dtype=torch.float32, device=dev)
+    gqe.gqe_route(dims, g["x"], g["w_r"], g["b_r"], z_t, r_out["topk_idx"], r_out["topk_w"], None, None, None)
+    dz_t, dx_t = torch.empty_like(z_t), torch.empty_like(g["x"])
+    dwr_t = torch.empty((G * M, cfg.D), dtype=torch.float32, device=dev)
+    dbr_t = torch.empty((G * M,), dtype=torch.float32, device=dev)
+    aux_t = torch.empty((1,), dtype=torch.float32, device=dev)
+    rb_ws = torch.empty((max(gqe.gqe_route_bwd_workspace_bytes(dims), 16),), dtype=torch.uint8, device=dev)
+
+    def route_bwd_call():
+        gqe.gqe_route_bwd(dims, g["x"], g["w_r"], z_t, r_out["topk_idx"], dw_t, 0.01, dz_t, dx_t, dwr_t, dbr_t,
+                          aux_t, rb_ws)
+
+    t_rbwd = timed(route_bwd_call, args.steps)
+    del rb_ws
+    # five products per (row, visible key) pair, the forward's two plus three
+    abwd_flop = fl["attention"] * 5 // 2
+    slot_cols = (G * k + 2) * d
+    obwd_flop = 2 * 2 * T * slot_cols * cfg.D  # dA = dy W_O^T and dW_O = A^T dy
+    rbwd_flop = 2 * 2 * T * G * M * cfg.D      # dW_r = dz^T x and dx = dz W_r
+    train_bwd = {
+        "attention_ms": round(t_abwd.mean() * 1e3, 4),
+        "attention_tflops": round(abwd_flop / t_abwd.mean() / 1e12, 2),
+        "attention_frac": round(abwd_flop / t_abwd.mean() / PEAK_BF16_FLOPS, 4),
+        "attention_flop": int(abwd_flop),
+        "out_proj_ms": round(t_obwd.mean() * 1e3, 4),
+        "out_proj_tflops": round(obwd_flop / t_obwd.mean() / 1e12, 2),
+        "route_ms": round(t_rbwd.mean() * 1e3, 4),
+        "route_tflops": round(rbwd_flop / t_rbwd.mean() / 1e12, 2),
+        "balance_loss_coef": 0.01,
+    }
+
     traffic = measured_traffic("prefill.hip", "prefill_long_s128k_pmc.txt")
     dtraffic = measured_traffic("decode.hip", "decode_kv64k_pmc.txt")
     result = {
@@ -369,6 +433,7 @@ def main():
             "attention_max_ms": round(t_attn.max() * 1e3, 4),
         },
         "qkv_proj": qkv,
+        "train_bwd": train_bwd,
         "flop_per_step": fl,
         "wall_s": round(wall, 3),
     }

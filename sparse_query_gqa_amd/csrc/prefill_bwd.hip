@@ -13,8 +13,10 @@
 //
 // Passes, all on the forward's row packing (rows of (b, v) token-major, k per
 // token for a routed group, one for the shared head v = G):
-//  1. prep: per row, copy q and dO into contiguous packed rows and store
-//     -lse*sqrt(d) and -dO.O (rows past the end of a packed block are zero);
+//  1. prep: per row, copy q (bf16: times scale*log2(e), so that q.k comes
+//     out of the MFMA as an exp2 argument) and dO into contiguous packed rows
+//     and store the lse offset and -dO.O (rows past the end of a packed
+//     block are zero);
 //  2. dK/dV: a workgroup per (sequence, virtual group, key block) holds the
 //     block's K and V fragments in registers and streams every row that can
 //     see the block; each of its four wavefronts takes every fourth 32-row
@@ -26,6 +28,8 @@
 //     go to an fp32 workspace and the last pass adds them.
 // bf16 products run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; the
 // fp32 path is plain VALU arithmetic.
+#include <type_traits>
+
 #include "prefill_tiles.h"
 
 namespace gqe {
@@ -67,7 +71,17 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   const uint4 qv = ((const uint4*)((const T*)f.q + (tok * (f.N + 1) + head) * D))[seg];
   const uint4 ov = ((const uint4*)((const T*)(v == f.G ? f.o_s : f.o_r) + orow * D))[seg];
   const uint4 gv = ((const uint4*)((const T*)(v == f.G ? p.do_s : p.do_r) + orow * D))[seg];
-  *qd = qv;
+  if constexpr (sizeof(T) == 2) {
+    // bf16: q * scale * log2(e), rounded once (as the forward's scores are)
+    uint4 qs = qv;
+    const __bf16* qe = (const __bf16*)&qv;
+    __bf16* qo = (__bf16*)&qs;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) qo[i] = f2bf((float)qe[i] * (f.scale * 1.44269504088896340736f));
+    *qd = qs;
+  } else {
+    *qd = qv;
+  }
   *dd = gv;
   const T* oe = (const T*)&ov;
   const T* ge = (const T*)&gv;
@@ -78,7 +92,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   for (int o = TPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
   if (seg == 0) {
     const float lse = (v == f.G) ? f.lse_s[tok] : f.lse_r[orow];
-    p.nlse[row] = -lse / f.scale;
+    // bf16: -lse*log2(e), the exp2 argument's offset for prescaled q;
+    // fp32: -lse*sqrt(d), the offset of the raw product q.k
+    p.nlse[row] = sizeof(T) == 2 ? -lse * 1.44269504088896340736f : -lse / f.scale;
     p.ndel[row] = -acc;
   }
 }
@@ -130,15 +146,19 @@ struct TrOffsets {
 // ---------------------------------------------------------------------------
 // Workgroup (b, v, kb): keys key0 = kb*KB .. +KB-1 of KV head (v == G ? 0 :
 // v); the rows that can see key0 start at row key0*kk (kk rows per token).
-// Per 32-row tile and 32-key half h a wavefront computes
-//   S  = Q K^T - lse*sqrt(d)   (MFMA, initial accumulator = the lse term)
-//   dPm = dO V^T - dO.O
-//   P = exp2(scale*log2(e) * S),  dS = P * dPm,
-//   dV += P^T dO,  dK += dS^T Q
+// With q' = q * scale * log2(e) (packed) and per-row offsets -lse*log2(e)
+// and -delta as the MFMAs' initial accumulators, per 32-row tile and 32-key
+// half h a wavefront computes
+//   S  = Q' K^T - lse*log2(e),  P = exp2(S)   (= exp(q.k/sqrt(d) - lse))
+//   dPm = dO V^T - delta,  dS = P * dPm,
+//   dV += P^T dO,  dK += dS^T Q'   (times ln 2 at the end: scale/(scale*log2 e))
 // In the S layout lane (half, l32) holds key 32h + l32 and rows 8(t/4) +
 // 4 half + t%4, which is exactly the A operand P^T / dS^T of the dV / dK
 // products (contraction over rows), so P and dS never leave registers; the
-// B operands dO and Q come from transposing LDS reads.
+// B operands dO and Q' come from transposing LDS reads. With two key halves
+// (d <= 64) a tile runs as four phases: S, dP of half 0 | S, dP of half 1
+// beside the exponentials of half 0 and the transposing reads | dV, dK of
+// half 0 beside the exponentials of half 1 | dV, dK of half 1.
 //
 // Grid: chunks of kBwdChunk consecutive key blocks of one (b, v), longest
 // rows first (chunk index c = kb-chunk * U + u); chunk c runs on XCD c % 8,
@@ -152,7 +172,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p, int nkb) {
   constexpr int TB = 32 * ROWB;       // one 32-row tile of Q or dO
   constexpr int NQ = TB / 1024;       // 1 KiB LDS-DMA chunks per tile
   constexpr int RPC = 1024 / ROWB;    // rows per chunk
-  constexpr int BUFB = 2 * TB + 256;  // Q tile, dO tile, -lse*sqrt(d)[32], -delta[32]
+  constexpr int BUFB = 2 * TB + 256;  // Q tile, dO tile, lse offsets[32], -delta[32]
   constexpr int NBUF = 2;
   constexpr int NDMA = 2 * NQ + 1;    // LDS-DMA instructions per tile
   __shared__ __attribute__((aligned(1024))) char lds[4][NBUF][BUFB];
@@ -179,7 +199,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p, int nkb) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
 
-  // K and V fragments (B operands of Q K^T and dO V^T): lane (half, l32)
+  // K and V fragments (B operands of Q' K^T and dO V^T): lane (half, l32)
   // holds key key0 + 32h + l32 (the last key past the end), d 16s + 8 half.
   bf16x8 kf[NH][KS], vf[NH][KS];
   {
@@ -231,7 +251,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p, int nkb) {
 #pragma unroll
   for (int s = 0; s < KS; ++s) k_off[s] = l32 * ROWB + 16 * ((2 * s + half) ^ tile_swz<D>(l32));
   const TrOffsets<D> tr(lane);
-  const float c2 = f.scale * 1.44269504088896340736f;
 
   f32x16 dk[NH][DB], dv[NH][DB];
 #pragma unroll
@@ -241,7 +260,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p, int nkb) {
 #pragma unroll
       for (int t = 0; t < 16; ++t) dk[h][db][t] = dv[h][db][t] = 0.f;
 
-  auto tile = [&](const int bf, const int tr0) __attribute__((always_inline)) {
+  auto tile = [&](const int bf, const int tr0, auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const char* qt = lds[wave][bf];
     const char* gt = qt + TB;
     const float* ld = (const float*)(qt + 2 * TB);
@@ -262,52 +282,96 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p, int nkb) {
         nd[4 * j + i] = e[i];
       }
     }
-    // rows below (last key)*kk, or past the end, need the mask
-    const bool masked = tr0 < (key0 + KB - 1) * kk || tr0 + 32 > R;
+    f32x16 sc[NH], dp[NH];
     bf16x8 pa[NH][2], sa[NH][2];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      f32x16 sc = nl, dp = nd;
+    bf16x8 gtr[2][DB], qtr[2][DB];
+    auto sdp = [&](const int h) __attribute__((always_inline)) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[h][s], sc, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[s], vf[h][s], dp, 0, 0, 0);
+        sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[h][s], s ? sc[h] : nl, 0, 0, 0);
+        dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[s], vf[h][s], s ? dp[h] : nd, 0, 0, 0);
       }
-      const int key = key0 + 32 * h + l32;
+    };
+    auto soft = [&](const int h) __attribute__((always_inline)) {
+      const int lim = (key0 + 32 * h + l32) * kk;  // rows below this cannot see the lane's key
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        float pv = __builtin_amdgcn_exp2f(sc[t] * c2);
-        if (masked) {
+      for (int t = 0; t < 16; t += 2) {
+        float p0 = __builtin_amdgcn_exp2f(sc[h][t]), p1 = __builtin_amdgcn_exp2f(sc[h][t + 1]);
+        if constexpr (MASKED) {
           const int r = tr0 + 8 * (t >> 2) + 4 * half + (t & 3);
-          if (r >= R || r < key * kk) pv = 0.f;
+          if (r >= R || r < lim) p0 = 0.f;
+          if (r + 1 >= R || r + 1 < lim) p1 = 0.f;
         }
-        pa[h][t >> 3][t & 7] = f2bf(pv);
-        sa[h][t >> 3][t & 7] = f2bf(pv * dp[t]);
+        pa[h][t >> 3][t & 7] = f2bf(p0);
+        pa[h][t >> 3][(t & 7) + 1] = f2bf(p1);
+        sa[h][t >> 3][t & 7] = f2bf(p0 * dp[h][t]);
+        sa[h][t >> 3][(t & 7) + 1] = f2bf(p1 * dp[h][t + 1]);
       }
+    };
+    auto reads_tr = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          gtr[st][db] = tr.read(gt, st, db);
+          qtr[st][db] = tr.read(qt, st, db);
+        }
+    };
+    auto dvdk = [&](const int h) __attribute__((always_inline)) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dv[h][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[h][st], gtr[st][db], dv[h][db], 0, 0, 0);
+          dk[h][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[h][st], qtr[st][db], dk[h][db], 0, 0, 0);
+        }
+    };
+    if constexpr (NH == 2) {
+      sdp(0);
+      __builtin_amdgcn_sched_barrier(0);
+      sdp(1);
+      soft(0);
+      reads_tr();
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      dvdk(0);
+      soft(1);
+#pragma unroll
+      for (int i = 0; i < 4 * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      dvdk(1);
+    } else {
+      reads_tr();
+      sdp(0);
+      soft(0);
+      dvdk(0);
     }
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x8 gtr = tr.read(gt, st, db);
-        const bf16x8 qtr = tr.read(qt, st, db);
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          dv[h][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[h][st], gtr, dv[h][db], 0, 0, 0);
-          dk[h][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[h][st], qtr, dk[h][db], 0, 0, 0);
-        }
-      }
   };
 
+  using kNo = std::integral_constant<bool, false>;
+  using kYes = std::integral_constant<bool, true>;
   if (ntw > 0) {
     dma(0, 0);
     dma(1, 1);
     for (int i = 0; i < ntw; ++i) {
       const int bf = i & 1;
+      const int tr0 = row0 + 32 * (wave + 4 * i);
       // tile i is complete once only tile i+1's loads remain in flight; a
       // wavefront reads only what its own loads wrote
       __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA) : "memory");
-      tile(bf, row0 + 32 * (wave + 4 * i));
+      // rows below (last key)*kk, or past the end, need the mask
+      if (tr0 < (key0 + KB - 1) * kk || tr0 + 32 > R)
+        tile(bf, tr0, kYes());
+      else
+        tile(bf, tr0, kNo());
       __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of bf done before it is refilled
       dma(i + 2, bf);
     }
@@ -343,7 +407,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p, int nkb) {
       }
     }
   };
-  reduce_store(dk, 0, f.scale);
+  reduce_store(dk, 0, 0.69314718055994531f);  // dS^T Q' carries scale*log2(e); dK needs scale
   reduce_store(dv, 1, 1.f);
 }
 
@@ -352,10 +416,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p, int nkb) {
 // ---------------------------------------------------------------------------
 // The forward's tiles: 256 rows of one (b, v), RH 32-row halves per
 // wavefront. Per 64-key block (in LDS) and 32-key half sb:
-//   S^T = K Q^T,  dP^T = V dO^T   (lane (half, l32) holds row l32: its lse
-//   and delta are per-lane scalars)
-//   P = exp2(scale*log2(e) * S^T - lse*log2(e)),  dS^T = P (dP^T - delta)
-//   dQ^T += K^T dS^T   (K^T from transposing LDS reads)
+//   S^T = K Q'^T - lse*log2(e),  dP^T = V dO^T - delta   (lane (half, l32)
+//   holds row l32, so both offsets are per-lane initial accumulators)
+//   P = exp2(S^T),  dS^T = P dP^T,  dQ^T += K^T dS^T   (K^T from
+//   transposing LDS reads)
+// With two row halves (d <= 64) a key half runs as four phases, as in the
+// dK/dV kernel.
 template <int D>
 __global__ __launch_bounds__(D <= 64 ? 256 : 512) void bwd_dq_kernel(BwdParams p, int tiles_r, int tiles_s) {
   static_assert(D == 32 || D == 64 || D == 128, "head dim");
@@ -383,14 +449,18 @@ __global__ __launch_bounds__(D <= 64 ? 256 : 512) void bwd_dq_kernel(BwdParams p
   row_info(f, b, v, last_r, pos_last, s_, h_);
   row_info(f, b, v, r0, pos_first, s_, h_);
   const int64_t pbase = ((int64_t)b * (f.G + 1) + v) * p.Rp;
-  const float c2 = f.scale * 1.44269504088896340736f;
 
-  // Q and dO rows (B operands): lane (half, l32) holds row l32 of half h, d
-  // 16s + 8 half .. +7.
+  // Q' and dO rows (B operands): lane (half, l32) holds row l32 of half h,
+  // d 16s + 8 half .. +7; the row's offsets as pinned 16-register tuples
+  // (the MFMAs' initial accumulators).
+  // (d = 128 keeps the offsets as scalars and adds them in the softmax: its
+  // register budget has no room for the tuples)
+  constexpr bool TUPLES = RH == 2;
   int pos[RH], slot[RH], head[RH];
   bool row_ok[RH];
   bf16x8 qf[RH][KS], gf[RH][KS];
-  float ncl[RH], nd[RH];
+  f32x16 bl[RH] = {}, bd[RH] = {};
+  float nls[RH], nds[RH];
 #pragma unroll
   for (int h = 0; h < RH; ++h) {
     const int r = r0 + wave * 32 * RH + h * 32 + l32;
@@ -404,15 +474,22 @@ __global__ __launch_bounds__(D <= 64 ? 256 : 512) void bwd_dq_kernel(BwdParams p
       qf[h][s] = *(const bf16x8*)(qrow + 16 * s + 8 * half);
       gf[h][s] = *(const bf16x8*)(grow + 16 * s + 8 * half);
     }
-    ncl[h] = p.nlse[pbase + rr] * c2;
-    nd[h] = p.ndel[pbase + rr];
+    nls[h] = p.nlse[pbase + rr];
+    nds[h] = p.ndel[pbase + rr];
+    if constexpr (TUPLES) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        __asm__("v_mov_b32 %0, %1" : "+v"(bl[h][j]) : "v"(nls[h]));
+        __asm__("v_mov_b32 %0, %1" : "+v"(bd[h][j]) : "v"(nds[h]));
+      }
+    }
   }
   // wait for these loads before the LDS-DMA loop (see the dK/dV kernel)
 #pragma unroll
   for (int h = 0; h < RH; ++h) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) __asm__ volatile("" ::"v"(qf[h][s]), "v"(gf[h][s]));
-    __asm__ volatile("" ::"v"(ncl[h]), "v"(nd[h]), "v"(pos[h]), "v"(head[h]));
+    __asm__ volatile("" ::"v"(pos[h]), "v"(head[h]), "v"(nls[h]), "v"(nds[h]));
   }
 
   const __bf16* kbase = (const __bf16*)f.k + ((int64_t)b * f.G + kvh) * (int64_t)f.S * D;
@@ -462,7 +539,11 @@ __global__ __launch_bounds__(D <= 64 ? 256 : 512) void bwd_dq_kernel(BwdParams p
 #pragma unroll
       for (int t = 0; t < 16; ++t) dq[h][db][t] = 0.f;
 
-  auto block = [&](const int j, const int buf, const bool masked) __attribute__((always_inline)) {
+  // masked_tag: the mask as a compile-time path (two key halves) or, with one
+  // half (d = 128, whose registers do not allow two copies of the loop
+  // body), as a run-time branch on `masked`
+  auto block = [&](const int j, const int buf, auto masked_tag, const bool masked) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       const char* kt = lds[buf][0] + sb * 32 * ROWB;
@@ -473,36 +554,86 @@ __global__ __launch_bounds__(D <= 64 ? 256 : 512) void bwd_dq_kernel(BwdParams p
         ka[s] = *(const bf16x8*)(kt + k_off[s]);
         va[s] = *(const bf16x8*)(vt + k_off[s]);
       }
-      bf16x8 sb16[RH][2];
-#pragma unroll
-      for (int h = 0; h < RH; ++h) {
-        f32x16 sc = {}, dp = {};
+      f32x16 sc[RH], dp[RH];
+      bf16x8 ds16[RH][2];
+      bf16x8 ktr[2][DB];
+      auto sdp = [&](const int h) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[h][s], sc, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s], gf[h][s], dp, 0, 0, 0);
+          const f32x16 zero16 = {};
+          sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[h][s], s ? sc[h] : (TUPLES ? bl[h] : zero16), 0,
+                                                          0, 0);
+          dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s], gf[h][s], s ? dp[h] : (TUPLES ? bd[h] : zero16), 0,
+                                                          0, 0);
         }
+      };
+      auto soft = [&](const int h) __attribute__((always_inline)) {
         // element t <-> key j*64 + sb*32 + 8(t/4) + 4 half + t%4
         const int lim = pos[h] - j * kKeyBlock - sb * 32 - 4 * half;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          float pv = __builtin_amdgcn_exp2f(fmaf(sc[t], c2, ncl[h]));
-          if (masked && 8 * (t >> 2) + (t & 3) > lim) pv = 0.f;
-          sb16[h][t >> 3][t & 7] = f2bf(pv * (dp[t] + nd[h]));
+        for (int t = 0; t < 16; t += 2) {
+          float s0 = sc[h][t], s1 = sc[h][t + 1], d0 = dp[h][t], d1 = dp[h][t + 1];
+          if constexpr (!TUPLES) {  // (x + 0 is not folded away, so only add when needed)
+            s0 += nls[h];
+            s1 += nls[h];
+            d0 += nds[h];
+            d1 += nds[h];
+          }
+          float p0 = __builtin_amdgcn_exp2f(s0), p1 = __builtin_amdgcn_exp2f(s1);
+          if (MASKED || (RH == 1 && masked)) {
+            if (8 * (t >> 2) + (t & 3) > lim) p0 = 0.f;
+            if (8 * (t >> 2) + (t & 3) + 1 > lim) p1 = 0.f;
+          }
+          ds16[h][t >> 3][t & 7] = f2bf(p0 * d0);
+          ds16[h][t >> 3][(t & 7) + 1] = f2bf(p1 * d1);
         }
+      };
+      auto reads_tr = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) ktr[st][db] = tr.read(kt, st, db);
+      };
+      auto dq_mfma = [&](const int h) __attribute__((always_inline)) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            dq[h][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktr[st][db], ds16[h][st], dq[h][db], 0, 0, 0);
+      };
+      if constexpr (RH == 2) {
+        sdp(0);
+        __builtin_amdgcn_sched_barrier(0);
+        sdp(1);
+        soft(0);
+        reads_tr();
+#pragma unroll
+        for (int i = 0; i < 2 * KS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        dq_mfma(0);
+        soft(1);
+#pragma unroll
+        for (int i = 0; i < 2 * DB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        dq_mfma(1);
+      } else {
+        sdp(0);
+        soft(0);
+        reads_tr();
+        dq_mfma(0);
       }
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 ktr = tr.read(kt, st, db);
-#pragma unroll
-          for (int h = 0; h < RH; ++h)
-            dq[h][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktr, sb16[h][st], dq[h][db], 0, 0, 0);
-        }
     }
   };
 
+  using kNo = std::integral_constant<bool, false>;
+  using kYes = std::integral_constant<bool, true>;
   dma(0, 0);
   dma(min(1, nblocks - 1), 1);
   dma(min(2, nblocks - 1), 2);
@@ -514,7 +645,12 @@ __global__ __launch_bounds__(D <= 64 ? 256 : 512) void bwd_dq_kernel(BwdParams p
     __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NPW) : "memory");
     __syncthreads();
     dma(min(j + 3, nblocks - 1), (j + 3) % NBUF);
-    block(j, j % NBUF, j >= nfull);
+    if constexpr (RH == 1)
+      block(j, j % NBUF, kNo(), j >= nfull);
+    else if (j >= nfull)
+      block(j, j % NBUF, kYes(), true);
+    else
+      block(j, j % NBUF, kNo(), false);
   }
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
