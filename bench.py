@@ -65,10 +65,11 @@ def decode_kv_bytes(cfg) -> int:
 
 
 def source_sha(name: str) -> str:
-    """Hash of a kernel source together with the internal header it includes
-    (shared device helpers), so that a change to either retires old counters."""
+    """Hash of a kernel source together with the internal headers (shared
+    device helpers and tile geometry), so that a change to any of them
+    retires old counters."""
     h = hashlib.sha256()
-    for n in (name, "gqe_internal.h"):
+    for n in (name, "gqe_internal.h", "prefill_tiles.h"):
         with open(os.path.join(ROOT, "sparse_query_gqa_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
