@@ -17,11 +17,11 @@
 //     out of the MFMA as an exp2 argument) and dO into contiguous packed rows
 //     and store the lse offset and -dO.O (rows past the end of a packed
 //     block are zero);
-//  2. dK/dV: a workgroup per (sequence, virtual group, key block) holds the
-//     block's K and V fragments in registers and streams every row that can
-//     see the block; each of its four wavefronts takes every fourth 32-row
-//     tile through its own LDS ring, and the four partial sums are added
-//     through LDS at the end;
+//  2. dK/dV: a workgroup per (sequence, virtual group, 32-key block) keeps
+//     the block's K and V in LDS and streams every row that can see the
+//     block; each of its four wavefronts takes every fourth 32-row tile
+//     through its own LDS ring, and the four partial sums are added through
+//     LDS at the end;
 //  3. dQ: the forward's 256-row tiles (one KV head each), with K and V
 //     blocks streamed through LDS as in the forward;
 //  4. KV head 0 receives two sums (routed group 0 and the shared head); both
@@ -144,29 +144,34 @@ struct TrOffsets {
 // ---------------------------------------------------------------------------
 // 2. dK / dV (bf16)
 // ---------------------------------------------------------------------------
-// Workgroup (b, v, kb): keys key0 = kb*KB .. +KB-1 of KV head (v == G ? 0 :
+// Workgroup (b, v, kb): keys key0 = kb*32 .. +31 of KV head (v == G ? 0 :
 // v); the rows that can see key0 start at row key0*kk (kk rows per token).
 // With q' = q * scale * log2(e) (packed) and per-row offsets -lse*log2(e)
-// and -delta as the MFMAs' initial accumulators, per 32-row tile and 32-key
-// half h a wavefront computes
+// and -delta as the MFMAs' initial accumulators, per 32-row tile a
+// wavefront computes
 //   S  = Q' K^T - lse*log2(e),  P = exp2(S)   (= exp(q.k/sqrt(d) - lse))
 //   dPm = dO V^T - delta,  dS = P * dPm,
 //   dV += P^T dO,  dK += dS^T Q'   (times ln 2 at the end: scale/(scale*log2 e))
-// In the S layout lane (half, l32) holds key 32h + l32 and rows 8(t/4) +
-// 4 half + t%4, which is exactly the A operand P^T / dS^T of the dV / dK
-// products (contraction over rows), so P and dS never leave registers; the
-// B operands dO and Q' come from transposing LDS reads. With two key halves
-// (d <= 64) a tile runs as four phases: S, dP of half 0 | S, dP of half 1
-// beside the exponentials of half 0 and the transposing reads | dV, dK of
-// half 0 beside the exponentials of half 1 | dV, dK of half 1.
+// In the S layout lane (half, l32) holds key l32 and rows 8(t/4) + 4 half +
+// t%4, which is exactly the A operand P^T / dS^T of the dV / dK products
+// (contraction over rows), so P and dS never leave registers; the B operands
+// dO and Q' come from transposing LDS reads, K and V from the block's copy
+// in LDS.
+//
+// Registers decide the shape: one 32-key block per workgroup keeps a
+// wavefront's working set (dK and dV accumulators, S and dP, the tile's
+// fragments) within 256 VGPRs, so that the MFMAs write VGPRs (the VALU reads
+// S and dP without copies out of AGPRs) and, for d <= 64, two workgroups
+// share a CU. A 64-key block halves the LDS reads per MFMA but needs AGPR
+// accumulators and one workgroup per CU: it ran 25% slower.
 //
 // Grid: chunks of kBwdChunk consecutive key blocks of one (b, v), longest
 // rows first (chunk index c = kb-chunk * U + u); chunk c runs on XCD c % 8,
 // so the workgroups an XCD runs at once stream the same rows through its L2.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p, int nkb) {
+__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParams p, int nkb) {
   static_assert(D == 32 || D == 64 || D == 128, "head dim");
-  constexpr int NH = D <= 64 ? 2 : 1;  // 32-key halves per workgroup
+  constexpr int NH = 1;  // 32-key halves per workgroup (one: see the note on registers above)
   constexpr int KB = 32 * NH;
   constexpr int KS = D / 16, DB = D / 32, ROWB = 2 * D;
   constexpr int TB = 32 * ROWB;       // one 32-row tile of Q or dO
@@ -176,6 +181,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p, int nkb) {
   constexpr int NBUF = 2;
   constexpr int NDMA = 2 * NQ + 1;    // LDS-DMA instructions per tile
   __shared__ __attribute__((aligned(1024))) char lds[4][NBUF][BUFB];
+  __shared__ __attribute__((aligned(1024))) char kvl[2][KB * ROWB];  // the block's K and V rows
   static_assert(sizeof(lds) >= 4 * KB * D * sizeof(float), "reduction space");
 
   const PrefillParams& f = p.f;
@@ -199,27 +205,21 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p, int nkb) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
 
-  // K and V fragments (B operands of Q' K^T and dO V^T): lane (half, l32)
-  // holds key key0 + 32h + l32 (the last key past the end), d 16s + 8 half.
-  bf16x8 kf[NH][KS], vf[NH][KS];
+  // The block's K and V rows (keys past the end repeat the last key) go to
+  // LDS once, in the tile layout; each tile reads its B operands of Q' K^T
+  // and dO V^T from there (lane (half, l32): key 32h + l32, d 16s + 8 half),
+  // which keeps them out of the register budget.
   {
     const int64_t hb = ((int64_t)b * f.G + kvh) * (int64_t)f.S * D;
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      const int key = min(key0 + 32 * h + l32, f.S - 1);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        kf[h][s] = *(const bf16x8*)((const __bf16*)f.k + hb + (int64_t)key * D + 16 * s + 8 * half);
-        vf[h][s] = *(const bf16x8*)((const __bf16*)f.v + hb + (int64_t)key * D + 16 * s + 8 * half);
-      }
+    constexpr int CPR = D / 8;
+    for (int ch = tid; ch < KB * CPR; ch += 256) {
+      const int r = ch / CPR, cc = ch % CPR;
+      const int key = min(key0 + r, f.S - 1);
+      const int off = r * ROWB + 16 * (cc ^ tile_swz<D>(r));
+      *(uint4*)(kvl[0] + off) = *(const uint4*)((const __bf16*)f.k + hb + (int64_t)key * D + 8 * cc);
+      *(uint4*)(kvl[1] + off) = *(const uint4*)((const __bf16*)f.v + hb + (int64_t)key * D + 8 * cc);
     }
-    // Take the wait for these loads here: the loop's LDS-DMA loads are not
-    // seen by the compiler, and a first use inside the loop would make it
-    // wait for every load on each pass.
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-      for (int s = 0; s < KS; ++s) __asm__ volatile("" ::"v"(kf[h][s]), "v"(vf[h][s]));
+    __syncthreads();
   }
 
   // this wavefront's tiles: wave, wave + 4, ...
@@ -288,8 +288,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p, int nkb) {
     auto sdp = [&](const int h) __attribute__((always_inline)) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[h][s], s ? sc[h] : nl, 0, 0, 0);
-        dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[s], vf[h][s], s ? dp[h] : nd, 0, 0, 0);
+        const bf16x8 kf = *(const bf16x8*)(kvl[0] + 32 * h * ROWB + k_off[s]);
+        const bf16x8 vf = *(const bf16x8*)(kvl[1] + 32 * h * ROWB + k_off[s]);
+        sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf, s ? sc[h] : nl, 0, 0, 0);
+        dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[s], vf, s ? dp[h] : nd, 0, 0, 0);
       }
     };
     auto soft = [&](const int h) __attribute__((always_inline)) {
@@ -326,34 +328,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p, int nkb) {
           dk[h][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[h][st], qtr[st][db], dk[h][db], 0, 0, 0);
         }
     };
-    if constexpr (NH == 2) {
-      sdp(0);
-      __builtin_amdgcn_sched_barrier(0);
-      sdp(1);
-      soft(0);
-      reads_tr();
-#pragma unroll
-      for (int i = 0; i < 2 * KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      dvdk(0);
-      soft(1);
-#pragma unroll
-      for (int i = 0; i < 4 * DB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      dvdk(1);
-    } else {
-      reads_tr();
-      sdp(0);
-      soft(0);
-      dvdk(0);
-    }
+    reads_tr();
+    sdp(0);
+    soft(0);
+    dvdk(0);
   };
 
   using kNo = std::integral_constant<bool, false>;
@@ -420,12 +398,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p, int nkb) {
 //   holds row l32, so both offsets are per-lane initial accumulators)
 //   P = exp2(S^T),  dS^T = P dP^T,  dQ^T += K^T dS^T   (K^T from
 //   transposing LDS reads)
-// With two row halves (d <= 64) a key half runs as four phases, as in the
-// dK/dV kernel.
+// A wavefront owns 32 rows (eight wavefronts) so that its working set fits
+// 128 VGPRs (d = 64) and four wavefronts share a SIMD; d = 32 takes two
+// 32-row halves per wavefront (four wavefronts: its K/V blocks are too small
+// to split over eight), which then run as four phases: S^T, dP^T of half 0 |
+// S^T, dP^T of half 1 beside half 0's exponentials | dQ of half 0 beside
+// half 1's exponentials | dQ of half 1.
 template <int D>
-__global__ __launch_bounds__(D <= 64 ? 256 : 512) void bwd_dq_kernel(BwdParams p, int tiles_r, int tiles_s) {
+__global__ __launch_bounds__(D == 32 ? 256 : 512) void bwd_dq_kernel(BwdParams p, int tiles_r, int tiles_s) {
   static_assert(D == 32 || D == 64 || D == 128, "head dim");
-  constexpr int RH = D <= 64 ? 2 : 1;  // 32-row halves per wavefront
+  constexpr int RH = D == 32 ? 2 : 1;  // 32-row halves per wavefront
   constexpr int NW = 8 / RH;           // wavefronts: 256 rows per workgroup
   constexpr int KS = D / 16, DB = D / 32, ROWB = 2 * D;
   constexpr int MATB = kKeyBlock * ROWB;  // one K or V block
@@ -539,8 +521,8 @@ __global__ __launch_bounds__(D <= 64 ? 256 : 512) void bwd_dq_kernel(BwdParams p
 #pragma unroll
       for (int t = 0; t < 16; ++t) dq[h][db][t] = 0.f;
 
-  // masked_tag: the mask as a compile-time path (two key halves) or, with one
-  // half (d = 128, whose registers do not allow two copies of the loop
+  // masked_tag: the mask as a compile-time path (two row halves, d = 32) or,
+  // with one half (whose registers do not allow two copies of the loop
   // body), as a run-time branch on `masked`
   auto block = [&](const int j, const int buf, auto masked_tag, const bool masked) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
@@ -572,20 +554,14 @@ __global__ __launch_bounds__(D <= 64 ? 256 : 512) void bwd_dq_kernel(BwdParams p
         const int lim = pos[h] - j * kKeyBlock - sb * 32 - 4 * half;
 #pragma unroll
         for (int t = 0; t < 16; t += 2) {
-          float s0 = sc[h][t], s1 = sc[h][t + 1], d0 = dp[h][t], d1 = dp[h][t + 1];
-          if constexpr (!TUPLES) {  // (x + 0 is not folded away, so only add when needed)
-            s0 += nls[h];
-            s1 += nls[h];
-            d0 += nds[h];
-            d1 += nds[h];
-          }
-          float p0 = __builtin_amdgcn_exp2f(s0), p1 = __builtin_amdgcn_exp2f(s1);
+          const float ol = TUPLES ? 0.f : nls[h], od = TUPLES ? 0.f : nds[h];
+          float p0 = __builtin_amdgcn_exp2f(sc[h][t] + ol), p1 = __builtin_amdgcn_exp2f(sc[h][t + 1] + ol);
           if (MASKED || (RH == 1 && masked)) {
             if (8 * (t >> 2) + (t & 3) > lim) p0 = 0.f;
             if (8 * (t >> 2) + (t & 3) + 1 > lim) p1 = 0.f;
           }
-          ds16[h][t >> 3][t & 7] = f2bf(p0 * d0);
-          ds16[h][t >> 3][(t & 7) + 1] = f2bf(p1 * d1);
+          ds16[h][t >> 3][t & 7] = f2bf(p0 * (dp[h][t] + od));
+          ds16[h][t >> 3][(t & 7) + 1] = f2bf(p1 * (dp[h][t + 1] + od));
         }
       };
       auto reads_tr = [&]() __attribute__((always_inline)) {
@@ -823,13 +799,13 @@ template <int D>
 static void launch_bf16(const BwdParams& p, hipStream_t s) {
   const PrefillParams& f = p.f;
   launch_prep<__bf16, D>(p, s);
-  constexpr int KB = D <= 64 ? 64 : 32;
+  constexpr int KB = 32;
   const int nkb = (f.S + KB - 1) / KB;
   const int nchunks = ((nkb + kBwdChunk - 1) / kBwdChunk) * f.B * (f.G + 1);
   const unsigned ng = 8u * kBwdChunk * (unsigned)((nchunks + 7) / 8);
   hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(ng), dim3(256), 0, s, p, nkb);
   const int tiles_r = (f.S * f.K + 255) / 256, tiles_s = (f.S + 255) / 256;
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(tile_grid_blocks(f, tiles_s)), dim3(D <= 64 ? 256 : 512), 0, s, p,
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(tile_grid_blocks(f, tiles_s)), dim3(D == 32 ? 256 : 512), 0, s, p,
                      tiles_r, tiles_s);
   const int64_t n4 = (int64_t)f.B * f.S * D / 4;
   hipLaunchKernelGGL(bwd_combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, p, D);
