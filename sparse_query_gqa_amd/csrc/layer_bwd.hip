@@ -243,66 +243,89 @@ __device__ __forceinline__ void st(void* p, int64_t i, float v) {
   ((T*)p)[i] = (T)v;
 }
 
-// One wavefront per (token, slot j): j < G*k a hard slot (dO_r row and dw),
-// j == G*k the shared slot (dO_s row). Lanes over d.
+// A group of d/4 lanes per (token, slot j), four elements per lane: j < G*k
+// a hard slot (dO_r row and dw), j == G*k the shared slot (dO_s row).
+template <typename T>
+__device__ __forceinline__ f32x4 ld4(const void* p, int64_t i) {
+  if constexpr (sizeof(T) == 2) {
+    const bf16x4 v = *(const bf16x4*)((const __bf16*)p + i);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  } else {
+    return *(const f32x4*)((const float*)p + i);
+  }
+}
+template <typename T>
+__device__ __forceinline__ void st4(void* p, int64_t i, const f32x4 v) {
+  if constexpr (sizeof(T) == 2) {
+    const bf16x4 o = {f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])};
+    *(bf16x4*)((__bf16*)p + i) = o;
+  } else {
+    *(f32x4*)((float*)p + i) = v;
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void slot_bwd_kernel(OutProjBwdParams p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int L = p.d / 4;  // lanes per (token, slot): 8, 16 or 32
+  const int64_t g = ((int64_t)blockIdx.x * 256 + threadIdx.x) / L;
+  const int e = 4 * (threadIdx.x % L);
   const int64_t per = p.Gk + 1;
-  if (gw >= p.T * per) return;
-  const int64_t t = gw / per;
-  const int j = (int)(gw - t * per);
+  if (g >= p.T * per) return;  // (whole lane groups leave together)
+  const int64_t t = g / per;
+  const int j = (int)(g - t * per);
   const float* da = p.da + t * p.Kd;
   const int hard = p.Gk * p.d;
   if (j == p.Gk) {
-    for (int e = lane; e < p.d; e += 64) st<T>(p.do_s, t * p.d + e, da[hard + p.nob + e]);
+    st4<T>(p.do_s, t * p.d + e, *(const f32x4*)(da + hard + p.nob + e));
     return;
   }
   const float w = p.w[t * p.Gk + j];
+  const f32x4 o = ld4<T>(p.o_r, (t * p.Gk + j) * p.d + e);
+  const f32x4 dslot = *(const f32x4*)(da + j * p.d + e);
+  f32x4 gr;
   float dwacc = 0.f;
-  for (int e = lane; e < p.d; e += 64) {
-    const float o = ld<T>(p.o_r, (t * p.Gk + j) * p.d + e);
-    const float dslot = da[j * p.d + e];
-    float g;
-    if (p.nob) {  // [O, obar, s]
-      const float dob = da[hard + e];
-      g = dslot + w * dob;
-      dwacc = fmaf(o, dob, dwacc);
-    } else if (p.weighted) {  // [w O, s]
-      g = w * dslot;
-      dwacc = fmaf(o, dslot, dwacc);
-    } else {  // [O, s]
-      g = dslot;
-    }
-    st<T>(p.do_r, (t * p.Gk + j) * p.d + e, g);
+  if (p.nob) {  // [O, obar, s]
+    const f32x4 dob = *(const f32x4*)(da + hard + e);
+    gr = dslot + w * dob;
+    for (int i = 0; i < 4; ++i) dwacc = fmaf(o[i], dob[i], dwacc);
+  } else if (p.weighted) {  // [w O, s]
+    gr = w * dslot;
+    for (int i = 0; i < 4; ++i) dwacc = fmaf(o[i], dslot[i], dwacc);
+  } else {  // [O, s]
+    gr = dslot;
   }
-  dwacc = wave_sum(dwacc);
-  if (lane == 0) p.dw[t * p.Gk + j] = dwacc;
+  st4<T>(p.do_r, (t * p.Gk + j) * p.d + e, gr);
+  for (int m = L / 2; m > 0; m >>= 1) dwacc += __shfl_xor(dwacc, m, 64);
+  if (e == 0) p.dw[t * p.Gk + j] = dwacc;
 }
 
 // The slot vector A_t (what the forward GEMM multiplies by W_O), stored in
 // the storage dtype: hard slots (scaled by w when weighted), obar in fp32
-// then rounded, shared slot.
+// then rounded, shared slot. Four consecutive columns per thread (d is a
+// multiple of 4, so the four never straddle two slots).
 template <typename T>
 __global__ __launch_bounds__(256) void assemble_kernel(OutProjBwdParams p) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= p.T * p.Kd) return;
-  const int64_t t = i / p.Kd;
-  const int c = (int)(i - t * p.Kd);
+  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i4 >= p.T * p.Kd) return;
+  const int64_t t = i4 / p.Kd;
+  const int c = (int)(i4 - t * p.Kd);
   const int hard = p.Gk * p.d;
-  float v;
+  f32x4 v;
   if (c < hard) {
-    v = ld<T>(p.o_r, t * hard + c);
+    v = ld4<T>(p.o_r, t * hard + c);
     if (p.weighted) v *= p.w[t * p.Gk + c / p.d];
   } else if (c < hard + p.nob) {
     const int e = c - hard;
-    v = 0.f;
-    for (int j = 0; j < p.Gk; ++j) v = fmaf(p.w[t * p.Gk + j], ld<T>(p.o_r, (t * p.Gk + j) * p.d + e), v);
+    v = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < p.Gk; ++j) {
+      const float w = p.w[t * p.Gk + j];
+      const f32x4 o = ld4<T>(p.o_r, (t * p.Gk + j) * p.d + e);
+      for (int q = 0; q < 4; ++q) v[q] = fmaf(w, o[q], v[q]);
+    }
   } else {
-    v = ld<T>(p.o_s, t * p.d + (c - hard - p.nob));
+    v = ld4<T>(p.o_s, t * p.d + (c - hard - p.nob));
   }
-  st<T>(p.a, i, v);
+  st4<T>(p.a, i4, v);
 }
 
 template <typename T>
@@ -325,10 +348,10 @@ static void out_proj_bwd_typed(const OutProjBwdParams& p, bool bf16, hipStream_t
   g.kchunk = (p.Dout + 31) / 32 * 32;
   g.alpha = 1.f;
   run_gemm<false, false>(g, 1, nullptr, bf16, s);
-  const int64_t waves = p.T * (p.Gk + 1);
-  hipLaunchKernelGGL(slot_bwd_kernel<T>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, p);
-  const int64_t n = p.T * p.Kd;
-  hipLaunchKernelGGL(assemble_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
+  const int64_t lanes = p.T * (p.Gk + 1) * (p.d / 4);
+  hipLaunchKernelGGL(slot_bwd_kernel<T>, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s, p);
+  const int64_t n4 = p.T * p.Kd / 4;
+  hipLaunchKernelGGL(assemble_kernel<T>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, p);
   // dW_O = A^T dy: A stored [T][Kd] and dy [T][Dout], both transposed
   Gemm h{};
   h.a = p.a;
@@ -429,16 +452,27 @@ __global__ __launch_bounds__(256) void dz_kernel(RouteBwdParams p) {
 }
 
 // Column sums over tokens, two levels (partials of kColChunk tokens, then
-// their sum in chunk order): which = 0 sums dz into db_r, 1 sums p.
+// their sum in chunk order): which = 0 sums dz into db_r, 1 sums p. In a
+// block, thread (r, c) with c = tid % GM sums column c over the chunk's
+// tokens r, r + R, ... (R = 256 / GM rows of threads, reads coalesced along
+// the columns); the R partials are then added in LDS in row order.
 __global__ __launch_bounds__(256) void colsum_kernel(RouteBwdParams p, int which) {
+  __shared__ float red[256];
   const int GM = p.G * p.M;
-  const int c = blockIdx.y * 256 + threadIdx.x;
-  if (c >= GM) return;
+  const int R = 256 / GM;
+  const int c = threadIdx.x % GM, r = threadIdx.x / GM;
   const float* src = which ? p.pbuf : p.dz;
   const int64_t t0 = (int64_t)blockIdx.x * kColChunk, t1 = min(p.T, t0 + kColChunk);
   float s = 0.f;
-  for (int64_t t = t0; t < t1; ++t) s += src[t * GM + c];
-  p.colpart[((int64_t)which * p.nchunk + blockIdx.x) * GM + c] = s;
+  if (r < R)
+    for (int64_t t = t0 + r; t < t1; t += R) s += src[t * GM + c];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x < GM) {
+    float tot = 0.f;
+    for (int k = 0; k < R; ++k) tot += red[k * GM + threadIdx.x];
+    p.colpart[((int64_t)which * p.nchunk + blockIdx.x) * GM + threadIdx.x] = tot;
+  }
 }
 
 __global__ __launch_bounds__(256) void colsum_final_kernel(RouteBwdParams p) {
@@ -475,8 +509,8 @@ static void route_bwd_typed(const RouteBwdParams& p, bool bf16, hipStream_t s) {
     hipLaunchKernelGGL(count_kernel, dim3(nb), dim3(256), 0, s, p);
   }
   hipLaunchKernelGGL(dz_kernel<T>, dim3((unsigned)((p.T * p.G + 255) / 256)), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(colsum_kernel, dim3(p.nchunk, (GM + 255) / 256), dim3(256), 0, s, p, 0);
-  if (p.aux_loss) hipLaunchKernelGGL(colsum_kernel, dim3(p.nchunk, (GM + 255) / 256), dim3(256), 0, s, p, 1);
+  hipLaunchKernelGGL(colsum_kernel, dim3(p.nchunk), dim3(256), 0, s, p, 0);
+  if (p.aux_loss) hipLaunchKernelGGL(colsum_kernel, dim3(p.nchunk), dim3(256), 0, s, p, 1);
   hipLaunchKernelGGL(colsum_final_kernel, dim3(1), dim3(256), 0, s, p);
   // dW_r = dz^T x: dz stored [T][GMp], x [T][D], both transposed
   Gemm h{};
