@@ -260,8 +260,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
 #pragma unroll
       for (int t = 0; t < 16; ++t) dk[h][db][t] = dv[h][db][t] = 0.f;
 
-  auto tile = [&](const int bf, const int tr0, auto masked_tag) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  auto tile = [&](const int bf, const int tr0, const bool masked) __attribute__((always_inline)) {
     const char* qt = lds[wave][bf];
     const char* gt = qt + TB;
     const float* ld = (const float*)(qt + 2 * TB);
@@ -294,16 +293,24 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
         dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[s], vf, s ? dp[h] : nd, 0, 0, 0);
       }
     };
+    // The mask is a real branch taken on the tiles that need it (one path
+    // through the loop body: two copies made the compiler copy the dK and
+    // dV accumulators between them on every tile).
+    auto mask = [&](const int h) __attribute__((always_inline)) {
+      if (masked) {
+        __asm__ volatile("" ::: "memory");  // keep this a branch
+        const int lim = (key0 + 32 * h + l32) * kk;  // rows below this cannot see the lane's key
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int r = tr0 + 8 * (t >> 2) + 4 * half + (t & 3);
+          if (r >= R || r < lim) sc[h][t] = -INFINITY;
+        }
+      }
+    };
     auto soft = [&](const int h) __attribute__((always_inline)) {
-      const int lim = (key0 + 32 * h + l32) * kk;  // rows below this cannot see the lane's key
 #pragma unroll
       for (int t = 0; t < 16; t += 2) {
-        float p0 = __builtin_amdgcn_exp2f(sc[h][t]), p1 = __builtin_amdgcn_exp2f(sc[h][t + 1]);
-        if constexpr (MASKED) {
-          const int r = tr0 + 8 * (t >> 2) + 4 * half + (t & 3);
-          if (r >= R || r < lim) p0 = 0.f;
-          if (r + 1 >= R || r + 1 < lim) p1 = 0.f;
-        }
+        const float p0 = __builtin_amdgcn_exp2f(sc[h][t]), p1 = __builtin_amdgcn_exp2f(sc[h][t + 1]);
         pa[h][t >> 3][t & 7] = f2bf(p0);
         pa[h][t >> 3][(t & 7) + 1] = f2bf(p1);
         sa[h][t >> 3][t & 7] = f2bf(p0 * dp[h][t]);
@@ -330,12 +337,11 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
     };
     reads_tr();
     sdp(0);
+    mask(0);
     soft(0);
     dvdk(0);
   };
 
-  using kNo = std::integral_constant<bool, false>;
-  using kYes = std::integral_constant<bool, true>;
   if (ntw > 0) {
     dma(0, 0);
     dma(1, 1);
@@ -346,10 +352,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
       // wavefront reads only what its own loads wrote
       __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA) : "memory");
       // rows below (last key)*kk, or past the end, need the mask
-      if (tr0 < (key0 + KB - 1) * kk || tr0 + 32 > R)
-        tile(bf, tr0, kYes());
-      else
-        tile(bf, tr0, kNo());
+      tile(bf, tr0, tr0 < (key0 + KB - 1) * kk || tr0 + 32 > R);
       __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of bf done before it is refilled
       dma(i + 2, bf);
     }
@@ -521,11 +524,9 @@ __global__ __launch_bounds__(D == 32 ? 256 : 512) void bwd_dq_kernel(BwdParams p
 #pragma unroll
       for (int t = 0; t < 16; ++t) dq[h][db][t] = 0.f;
 
-  // masked_tag: the mask as a compile-time path (two row halves, d = 32) or,
-  // with one half (whose registers do not allow two copies of the loop
-  // body), as a run-time branch on `masked`
-  auto block = [&](const int j, const int buf, auto masked_tag, const bool masked) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  // The mask is a real branch taken on the blocks that need it (one path
+  // through the loop body, as in the dK/dV kernel).
+  auto block = [&](const int j, const int buf, const bool masked) __attribute__((always_inline)) {
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       const char* kt = lds[buf][0] + sb * 32 * ROWB;
@@ -549,19 +550,29 @@ __global__ __launch_bounds__(D == 32 ? 256 : 512) void bwd_dq_kernel(BwdParams p
                                                           0, 0);
         }
       };
+      auto mask = [&](const int h) __attribute__((always_inline)) {
+        if (masked) {
+          __asm__ volatile("" ::: "memory");  // keep this a branch
+          // element t <-> key j*64 + sb*32 + 8(t/4) + 4 half + t%4
+          const int lim = pos[h] - j * kKeyBlock - sb * 32 - 4 * half;
+#pragma unroll
+          for (int t = 0; t < 16; ++t)
+            if (8 * (t >> 2) + (t & 3) > lim) sc[h][t] = -INFINITY;
+        }
+      };
       auto soft = [&](const int h) __attribute__((always_inline)) {
-        // element t <-> key j*64 + sb*32 + 8(t/4) + 4 half + t%4
-        const int lim = pos[h] - j * kKeyBlock - sb * 32 - 4 * half;
 #pragma unroll
         for (int t = 0; t < 16; t += 2) {
-          const float ol = TUPLES ? 0.f : nls[h], od = TUPLES ? 0.f : nds[h];
-          float p0 = __builtin_amdgcn_exp2f(sc[h][t] + ol), p1 = __builtin_amdgcn_exp2f(sc[h][t + 1] + ol);
-          if (MASKED || (RH == 1 && masked)) {
-            if (8 * (t >> 2) + (t & 3) > lim) p0 = 0.f;
-            if (8 * (t >> 2) + (t & 3) + 1 > lim) p1 = 0.f;
+          float s0 = sc[h][t], s1 = sc[h][t + 1], d0 = dp[h][t], d1 = dp[h][t + 1];
+          if constexpr (!TUPLES) {  // (x + 0 is not folded away, so only add when needed)
+            s0 += nls[h];
+            s1 += nls[h];
+            d0 += nds[h];
+            d1 += nds[h];
           }
-          ds16[h][t >> 3][t & 7] = f2bf(p0 * (dp[h][t] + od));
-          ds16[h][t >> 3][(t & 7) + 1] = f2bf(p1 * (dp[h][t + 1] + od));
+          const float p0 = __builtin_amdgcn_exp2f(s0), p1 = __builtin_amdgcn_exp2f(s1);
+          ds16[h][t >> 3][t & 7] = f2bf(p0 * d0);
+          ds16[h][t >> 3][(t & 7) + 1] = f2bf(p1 * d1);
         }
       };
       auto reads_tr = [&]() __attribute__((always_inline)) {
@@ -579,6 +590,7 @@ __global__ __launch_bounds__(D == 32 ? 256 : 512) void bwd_dq_kernel(BwdParams p
       };
       if constexpr (RH == 2) {
         sdp(0);
+        mask(0);
         __builtin_amdgcn_sched_barrier(0);
         sdp(1);
         soft(0);
@@ -590,6 +602,7 @@ __global__ __launch_bounds__(D == 32 ? 256 : 512) void bwd_dq_kernel(BwdParams p
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
+        mask(1);
         dq_mfma(0);
         soft(1);
 #pragma unroll
@@ -601,6 +614,7 @@ __global__ __launch_bounds__(D == 32 ? 256 : 512) void bwd_dq_kernel(BwdParams p
         dq_mfma(1);
       } else {
         sdp(0);
+        mask(0);
         soft(0);
         reads_tr();
         dq_mfma(0);
@@ -608,8 +622,6 @@ __global__ __launch_bounds__(D == 32 ? 256 : 512) void bwd_dq_kernel(BwdParams p
     }
   };
 
-  using kNo = std::integral_constant<bool, false>;
-  using kYes = std::integral_constant<bool, true>;
   dma(0, 0);
   dma(min(1, nblocks - 1), 1);
   dma(min(2, nblocks - 1), 2);
@@ -621,12 +633,7 @@ __global__ __launch_bounds__(D == 32 ? 256 : 512) void bwd_dq_kernel(BwdParams p
     __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NPW) : "memory");
     __syncthreads();
     dma(min(j + 3, nblocks - 1), (j + 3) % NBUF);
-    if constexpr (RH == 1)
-      block(j, j % NBUF, kNo(), j >= nfull);
-    else if (j >= nfull)
-      block(j, j % NBUF, kYes(), true);
-    else
-      block(j, j % NBUF, kNo(), false);
+    block(j, j % NBUF, j >= nfull);
   }
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
