@@ -32,6 +32,12 @@ FLAGS = [
 ]
 
 
+# Per-source flags. The attention backward keeps its MFMA accumulators in
+# VGPRs: its exponentials read the score accumulators, and with the AGPR form
+# the d = 128 dK/dV kernel copied them out of AGPRs on every tile.
+EXTRA = {"prefill_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+
+
 def _hipcc() -> str:
     for c in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if c and os.path.exists(c):
@@ -57,7 +63,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        jobs.append([hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(min(8, len(jobs))) as ex:
         for out in ex.map(_run, jobs):
             if verbose and out.strip():

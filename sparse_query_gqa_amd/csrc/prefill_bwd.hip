@@ -335,8 +335,11 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
           dk[h][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[h][st], qtr[st][db], dk[h][db], 0, 0, 0);
         }
     };
-    reads_tr();
+    // (d = 128 reads the transposed fragments after S and dP: 64 more live
+    // registers during those products would not fit)
+    if constexpr (D <= 64) reads_tr();
     sdp(0);
+    if constexpr (D > 64) reads_tr();
     mask(0);
     soft(0);
     dvdk(0);
