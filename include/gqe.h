@@ -180,7 +180,8 @@ size_t gqe_decode_workspace_bytes(const gqe_dims* dims, int32_t q_len);
  *   kv_len   [B] int32 device, valid cache length including the new tokens;
  *            q_len <= kv_len[b] <= S_max is required (not checkable without a
  *            device sync; a violating entry yields unspecified outputs for
- *            that sequence)
+ *            that sequence, and the kernels clamp it to 0..S_max, so nothing
+ *            outside the sequence's cache is read)
  *   topk_idx [B*q_len, G, k] int32
  *   o_routed [B, q_len, G, k, d] dtype out; o_shared [B, q_len, d] dtype out
  *   workspace >= gqe_decode_workspace_bytes(dims, q_len) device bytes. */
@@ -314,8 +315,9 @@ int gqe_qkv_proj(const gqe_dims* dims, const void* x, const void* w_q,
  * 技术深化). No other cache row is touched.
  *   x        [B, q_len, D]   dtype; topk_idx [B*q_len, G, k] int32
  *   kv_len   [B] int32 device, q_len <= kv_len[b] <= S_max = dims->S (not
- *            checkable without a device sync; a violating entry makes that
- *            sequence's writes land in unspecified rows of its own cache)
+ *            checkable without a device sync; with a violating entry the
+ *            rows kv_len[b] - q_len + t outside 0..S_max-1 are not written,
+ *            so no write leaves the sequence's cache)
  *   q        [B, q_len, N+1, d] dtype out (selected heads and shared head)
  *   k_cache, v_cache [B, G, S_max, d] dtype, updated in place
  * bf16 needs D % 64 == 0. */

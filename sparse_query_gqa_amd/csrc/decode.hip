@@ -137,7 +137,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   static_assert(TPK <= 64 && (64 % TPK) == 0, "key row must fit a wavefront");
 
   const int c_split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int kvl = p.kv_len[b];
+  // (a kv_len outside 0..S_max breaks the caller's contract; clamping keeps
+  // every read inside the sequence's cache, the outputs are then unspecified)
+  const int kvl = min(max(p.kv_len[b], 0), p.Smax);
   const int k_begin = c_split * p.chunk;
   if (k_begin >= kvl) return;  // the combine reads only the splits below kv_len
   const int k_end = min(k_begin + p.chunk, kvl);
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
   const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z, e = threadIdx.x;
   const int nrows = p.K * p.L + (g == 0 ? p.L : 0);
   if (r >= nrows) return;
-  const int kvl = p.kv_len[b];
+  const int kvl = min(max(p.kv_len[b], 0), p.Smax);  // as in the split kernel
   const int ns = min(p.nsplit, (kvl + p.chunk - 1) / p.chunk);
   const int64_t rec0 = ((int64_t)b * p.G + g) * p.nsplit;
   float mm = -INFINITY;

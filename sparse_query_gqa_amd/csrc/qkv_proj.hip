@@ -35,7 +35,9 @@ constexpr int kPStages = 3;
 constexpr int kDRows = 32;   // token rows per decode tile
 
 // Output row of token ft for head slot `which` (0..N query heads, then K
-// heads g = 0..G-1, then V heads): the element offset of column 0.
+// heads g = 0..G-1, then V heads): the element offset of column 0, or -1
+// for a cache row outside 0..S_max-1 (a kv_len that breaks the caller's
+// contract: that row is not written, so nothing outside the cache is).
 __device__ __forceinline__ int64_t out_row(const ProjParams& p, int which, int ft, int& kind) {
   if (which <= p.N) {
     kind = 0;
@@ -46,6 +48,7 @@ __device__ __forceinline__ int64_t out_row(const ProjParams& p, int which, int f
   const int g = kv < p.G ? kv : kv - p.G;
   const int b = ft / p.L, t = ft - b * p.L;
   const int pos = p.kv_len ? p.kv_len[b] - p.L + t : t;
+  if (pos < 0 || pos >= p.Smax) return -1;
   return (((int64_t)b * p.G + g) * p.Smax + pos) * p.d;
 }
 
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(256, 2) void proj_prefill_kernel(ProjParams p, int 
         col = c < D ? c : (c - D) % D;
       }
       int kind;
-      const int64_t o = out_row(p, which, ft, kind);
+      const int64_t o = out_row(p, which, ft, kind);  // (prefill: always a valid row)
       __bf16* out = (__bf16*)out_base(p, kind) + o + col;
 #pragma unroll
       for (int jq = 0; jq < 4; ++jq) {
@@ -268,6 +271,7 @@ __global__ __launch_bounds__(256) void proj_f32_kernel(ProjParams p) {
   for (int i = 0; i < p.D; ++i) s = fmaf(xr[i], wr[i], s);
   int kind;
   const int64_t o = out_row(p, which, ft, kind);
+  if (o < 0) return;
   ((float*)out_base(p, kind))[o + c] = s;
 }
 
@@ -346,6 +350,7 @@ __global__ __launch_bounds__(256) void proj_decode_kernel(ProjParams p) {
     if (l32 >= nrows) continue;
     int kind;
     const int64_t o = out_row(p, which, rows[l32], kind);
+    if (o < 0) continue;
     __bf16* out = (__bf16*)out_base(p, kind) + o + col0;
 #pragma unroll
     for (int jq = 0; jq < 4; ++jq) {

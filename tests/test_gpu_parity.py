@@ -481,3 +481,29 @@ def test_layer_main_sampled():
                                   idx.reshape(1, cfg.S, cfg.G, cfg.k), cfg.M, positions=pos)
     yref = oracle.out_proj(ref_r[0].reshape(-1, cfg.G, cfg.k, cfg.d), w[pos], ref_s[0], f64(inp["w_o"]))
     assert_close(y[b * cfg.S + pos], yref, cfg.dtype, "main layer y (sampled)")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_out_of_contract_kv_len_is_contained(dtype):
+    """A kv_len outside q_len..S_max breaks the caller's contract; the kernels
+    clamp it to the cache, so the other sequences' outputs are still exact
+    and nothing outside the caches is read (the violating sequences' outputs
+    are unspecified and not checked)."""
+    H, G, d, Smax, q_len = 8, 2, 64, 300, 1
+    M, k, B = H // G, 2, 4
+    rng = np.random.default_rng(77)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = torch.from_numpy(rng.standard_normal((B, q_len, H + 1, d), dtype=np.float32)).to(tdt)
+    kc = torch.from_numpy(rng.standard_normal((B, G, Smax, d), dtype=np.float32)).to(tdt)
+    vc = torch.from_numpy(rng.standard_normal((B, G, Smax, d), dtype=np.float32)).to(tdt)
+    kv_len = np.array([Smax + 1000, 17, -5, 293], dtype=np.int32)
+    ok = [1, 3]
+    idx = synth.random_selection(B, q_len, G, M, k, 4)
+    dims = gqe.gqe_dims.make(B, Smax, 64, H, G, k, d, dtype)
+    o_r, o_s = gqe.decode(dims, q_len, q.to(DEV), kc.to(DEV), vc.to(DEV), torch.from_numpy(kv_len).to(DEV),
+                          idx.to(DEV))
+    torch.cuda.synchronize()
+    ref_r, ref_s = oracle.decode(f64(q)[ok], f64(kc)[ok], f64(vc)[ok], kv_len[ok],
+                                 idx.numpy().reshape(B, q_len, G, k)[ok], M)
+    assert_close(o_r[ok], ref_r, dtype, "decode beside out-of-contract sequences O_routed")
+    assert_close(o_s[ok], ref_s, dtype, "decode beside out-of-contract sequences O_shared")

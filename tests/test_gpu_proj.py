@@ -179,3 +179,41 @@ def test_qkv_proj_decode_full_size():
     assert_close(kc[:, :, Smax - 1], Kc[:, :, Smax - 1], "bf16", "decode k")
     assert_close(vc[:, :, Smax - 1], Vc[:, :, Smax - 1], "bf16", "decode v")
     assert torch.count_nonzero(kc[:, :, :Smax - 1]) == 0 and torch.count_nonzero(vc[:, :, :Smax - 1]) == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_qkv_proj_decode_out_of_contract_kv_len_writes_nothing_outside(dtype):
+    """A kv_len that puts appended rows outside 0..S_max-1 breaks the caller's
+    contract: those rows are not written (no write lands outside the cache
+    or in another sequence), and the in-contract sequences append exactly."""
+    B, L, Smax, D, N, G, k, d = 3, 2, 40, 256, 8, 2, 1, 64
+    M = N // G
+    rng = np.random.default_rng(91)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x = torch.from_numpy(rng.standard_normal((B, L, D), dtype=np.float32)).to(tdt)
+    w_q, w_k, w_v = _weights(rng, N, G, d, D, tdt, 1.0 / np.sqrt(D))
+    kc0 = torch.from_numpy(rng.standard_normal((B, G, Smax, d), dtype=np.float32)).to(tdt)
+    vc0 = torch.from_numpy(rng.standard_normal((B, G, Smax, d), dtype=np.float32)).to(tdt)
+    kv_len = np.array([Smax + 1, 20, 1], dtype=np.int32)  # rows 39, 40 / 18, 19 / -1, 0
+    idx = synth.random_selection(B, L, G, M, k, 6)
+    dims = gqe.gqe_dims.make(B, Smax, D, N, G, k, d, dtype)
+    q = torch.full((B, L, N + 1, d), SENTINEL, dtype=tdt, device=DEV)
+    kc, vc = kc0.to(DEV), vc0.to(DEV)
+    gqe.gqe_qkv_proj_decode(dims, L, x.to(DEV), w_q.to(DEV), w_k.to(DEV), w_v.to(DEV), idx.to(DEV),
+                            torch.from_numpy(kv_len).to(DEV), q, kc, vc)
+    torch.cuda.synchronize()
+    # projected K/V of every token (the oracle's prefill projection)
+    _, K, V = oracle.project(f64(x), f64(w_q), f64(w_k), f64(w_v),
+                             idx.numpy().reshape(B, L, G, k), N, G)
+    # rows written: sequence 0 row 39 (token 0; its row 40 is skipped),
+    # sequence 1 rows 18, 19, sequence 2 row 0 (token 1; its row -1 is skipped)
+    written = [(0, 39, 0), (1, 18, 0), (1, 19, 1), (2, 0, 1)]
+    new = np.zeros((B, Smax), dtype=bool)
+    for b, row, _t in written:
+        new[b, row] = True
+    for name, got, ref, old in (("k cache", kc, K, kc0), ("v cache", vc, V, vc0)):
+        g64 = f64(got)
+        keep = ~new[:, None, :, None].repeat(G, 1).repeat(d, 3)
+        assert np.array_equal(g64[keep], f64(old)[keep]), f"{name}: a row outside the in-range appends changed"
+        for b, row, t in written:
+            assert_close(g64[b, :, row], ref[b, :, t], dtype, f"{name} sequence {b} row {row}")
