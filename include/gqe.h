@@ -119,7 +119,10 @@ int gqe_route(const gqe_dims* dims, const void* x, const void* w_router,
  *   topk_idx [B*S, G, k]     int32 (as written by gqe_route)
  *   o_routed [B, S, G, k, d] dtype out
  *   o_shared [B, S, d]       dtype out
- * topk_idx entries outside 0..M-1 are undefined behaviour. */
+ * topk_idx entries must lie in 0..M-1. An entry outside breaks the contract:
+ * the kernels clamp it into that range wherever it addresses memory (here,
+ * in decode and in the backward passes), so that row's outputs are
+ * unspecified but nothing outside the buffers is read or written. */
 int gqe_attn_prefill(const gqe_dims* dims, const void* q, const void* k,
                      const void* v, const int32_t* topk_idx, void* o_routed,
                      void* o_shared, void* stream);

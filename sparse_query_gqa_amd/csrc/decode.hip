@@ -162,7 +162,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
       int t, head;
       if (r < p.K * p.L) {
         t = r / p.K;
-        head = g * p.M + p.topk[(((int64_t)b * p.L + t) * p.G + g) * p.K + (r % p.K)];
+        // (clamped as in the prefill: an out-of-range index reads inside q)
+        head = g * p.M + min(max(p.topk[(((int64_t)b * p.L + t) * p.G + g) * p.K + (r % p.K)], 0), p.M - 1);
       } else {
         t = r - p.K * p.L;
         head = p.N;

@@ -398,7 +398,7 @@ __global__ __launch_bounds__(256) void count_kernel(RouteBwdParams p) {
   const int64_t n = p.T * p.G * p.K;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     const int g = (int)((i / p.K) % p.G);
-    atomicAdd(&h[g * p.M + p.topk[i]], 1);
+    atomicAdd(&h[g * p.M + min(max(p.topk[i], 0), p.M - 1)], 1);  // (clamped: stays inside h)
   }
   __syncthreads();
   for (int i = threadIdx.x; i < GM; i += 256)
@@ -427,7 +427,8 @@ __global__ __launch_bounds__(256) void dz_kernel(RouteBwdParams p) {
     pr[m] *= inv;
     dp[m] = 0.f;
   }
-  const int32_t* sel = p.topk + i * p.K;
+  int sel[kMaxExperts];  // (indices clamped to 0..M-1, as everywhere else)
+  for (int j = 0; j < p.K; ++j) sel[j] = min(max(p.topk[i * p.K + j], 0), p.M - 1);
   const float* dw = p.dw + i * p.K;
   float ps = 0.f;
   for (int j = 0; j < p.K; ++j) ps += pr[sel[j]];

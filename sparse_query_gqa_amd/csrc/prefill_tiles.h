@@ -109,7 +109,9 @@ __device__ __forceinline__ void row_info(const PrefillParams& p, int b, int v, i
   } else {
     pos = r / p.K;
     slot = r - pos * p.K;
-    head = v * p.M + p.topk[(((int64_t)b * p.S + pos) * p.G + v) * p.K + slot];
+    // (an index outside 0..M-1 breaks the caller's contract; clamping keeps
+    // the row's query read inside q, the row's outputs are then unspecified)
+    head = v * p.M + min(max(p.topk[(((int64_t)b * p.S + pos) * p.G + v) * p.K + slot], 0), p.M - 1);
   }
 }
 

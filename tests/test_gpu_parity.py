@@ -507,3 +507,23 @@ def test_decode_out_of_contract_kv_len_is_contained(dtype):
                                  idx.numpy().reshape(B, q_len, G, k)[ok], M)
     assert_close(o_r[ok], ref_r, dtype, "decode beside out-of-contract sequences O_routed")
     assert_close(o_s[ok], ref_s, dtype, "decode beside out-of-contract sequences O_shared")
+
+
+def test_prefill_out_of_range_index_is_contained():
+    """A top-k index outside 0..M-1 breaks the caller's contract; the kernel
+    clamps it where it addresses q, so every other row stays exact (the
+    corrupted rows' outputs are unspecified and not checked)."""
+    cfg = small_cfg(1, 200, 64, 8, 2, 2, 64)
+    inp = _prefill_inputs(cfg, False)
+    idx = inp["idx"].clone().view(1, 200, cfg.G, cfg.k)
+    ref_r, ref_s = oracle.prefill(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), idx.numpy(), cfg.M)
+    bad = idx.clone()
+    bad[0, 37, 1, 0] = cfg.M + 1000
+    bad[0, 150, 0, 1] = -7
+    g = to_dev(inp)
+    o_r, o_s = gqe.prefill(dims_of(cfg), g["q"], g["k"], g["v"], bad.view(200, cfg.G, cfg.k).to(DEV))
+    torch.cuda.synchronize()
+    keep = np.ones((1, 200, cfg.G, cfg.k), dtype=bool)
+    keep[0, 37, 1, 0] = keep[0, 150, 0, 1] = False
+    assert_close(f64(o_r)[keep], ref_r[keep], "bf16", "O_routed beside out-of-range indices")
+    assert_close(o_s, ref_s, "bf16", "O_shared beside out-of-range indices")
