@@ -226,24 +226,25 @@ def lse_rows(q, pos, K):
     return top + np.log(np.sum(np.exp(sc - top[:, None]), axis=1))
 
 
-def prefill_lse(Q, K, idx, M: int):
-    """lse_rows for every row prefill computes: (lse_r [B, S, G, k],
-    lse_s [B, S]), same head mapping and shared head as prefill."""
+def prefill_lse(Q, K, idx, M: int, positions=None):
+    """lse_rows for every row prefill computes: (lse_r [B, P, G, k],
+    lse_s [B, P]), same head mapping and shared head as prefill, for the
+    P positions given (default: all S)."""
     Q = np.asarray(Q, dtype=np.float64)
     B, S, H1, d = Q.shape
     G = K.shape[1]
     k = idx.shape[-1]
     N = H1 - 1
     check_dims(N, G, k)
-    pos = np.arange(S)
-    lse_r = np.zeros((B, S, G, k))
-    lse_s = np.zeros((B, S))
+    pos = np.arange(S) if positions is None else np.asarray(positions, dtype=np.int64)
+    lse_r = np.zeros((B, pos.size, G, k))
+    lse_s = np.zeros((B, pos.size))
     for b in range(B):
         for g in range(G):
             for j in range(k):
-                heads = g * M + idx[b, :, g, j]
+                heads = g * M + idx[b, pos, g, j]
                 lse_r[b, :, g, j] = lse_rows(Q[b, pos, heads, :], pos, K[b, g])
-        lse_s[b] = lse_rows(Q[b, :, N, :], pos, K[b, 0])
+        lse_s[b] = lse_rows(Q[b, pos, N, :], pos, K[b, 0])
     return lse_r, lse_s
 
 
@@ -442,13 +443,18 @@ def attend_rows_bwd(q, pos, K, V, dO):
     return dq, dK, dV
 
 
-def prefill_bwd(Q, K, V, idx, M: int, dO_r, dO_s):
+def prefill_bwd(Q, K, V, idx, M: int, dO_r, dO_s, positions=None):
     """Gradients of prefill (the function above) given dO_r [B, S, G, k, d]
     and dO_s [B, S, d]. A KV head's dK and dV are summed over every row that
     reads it: the selected heads of its group and, for head 0, the shared
     head ([GQA-zone] 训练与部署: shared keys/values gather the gradients of
     all their query heads). Returns (dQ [B, S, N+1, d], zero in the rows of
     unselected heads, dK [B, G, S, d], dV [B, G, S, d]).
+    positions: the rows whose outputs enter the loss (default: all S). dQ
+    is then returned for those rows alone ([B, P, N+1, d]) and dK, dV sum
+    those rows' terms only, which is the whole gradient of every key at or
+    after the first position when the positions run from there to S-1
+    (earlier rows cannot see later keys).
     """
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -458,19 +464,20 @@ def prefill_bwd(Q, K, V, idx, M: int, dO_r, dO_s):
     k = idx.shape[-1]
     N = H1 - 1
     check_dims(N, G, k)
-    pos = np.arange(S)
-    dQ = np.zeros_like(Q)
+    pos = np.arange(S) if positions is None else np.asarray(positions, dtype=np.int64)
+    rows = np.arange(pos.size)
+    dQ = np.zeros((B, pos.size, H1, d))
     dK = np.zeros_like(K)
     dV = np.zeros_like(V)
     for b in range(B):
         for g in range(G):
             for j in range(k):
-                heads = g * M + idx[b, :, g, j]
-                dq, dk, dv = attend_rows_bwd(Q[b, pos, heads, :], pos, K[b, g], V[b, g], dO_r[b, :, g, j])
-                dQ[b, pos, heads, :] += dq
+                heads = g * M + idx[b, pos, g, j]
+                dq, dk, dv = attend_rows_bwd(Q[b, pos, heads, :], pos, K[b, g], V[b, g], dO_r[b, pos, g, j])
+                dQ[b, rows, heads, :] += dq
                 dK[b, g] += dk
                 dV[b, g] += dv
-        dq, dk, dv = attend_rows_bwd(Q[b, :, N, :], pos, K[b, 0], V[b, 0], dO_s[b])
+        dq, dk, dv = attend_rows_bwd(Q[b, pos, N, :], pos, K[b, 0], V[b, 0], dO_s[b, pos])
         dQ[b, :, N, :] += dq
         dK[b, 0] += dk
         dV[b, 0] += dv

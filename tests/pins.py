@@ -449,6 +449,31 @@ def pin_prefill_bwd_central_differences(O):
     _close(dV, _central(loss, V), 1e-6, "dV")
 
 
+def pin_prefill_bwd_rows_central_differences(O):
+    """prefill_bwd with positions: the gradients of the loss taken over those
+    rows alone (sum over them of dO_r * O_r + dO_s * O_s), against central
+    differences of that loss; dQ comes back for those rows only."""
+    rng = np.random.default_rng(24)
+    B, S, N, G, k, d = 2, 7, 6, 3, 1, 3
+    M = N // G
+    Q = rng.standard_normal((B, S, N + 1, d))
+    K = rng.standard_normal((B, G, S, d))
+    V = rng.standard_normal((B, G, S, d))
+    idx = _random_idx(rng, B, S, G, M, k)
+    dO_r = rng.standard_normal((B, S, G, k, d))
+    dO_s = rng.standard_normal((B, S, d))
+    for pos in (np.array([1, 4, 5]), np.array([6]), np.arange(3, S)):
+
+        def loss():
+            o_r, o_s = O.prefill(Q, K, V, idx, M, positions=pos)
+            return float(np.sum(dO_r[:, pos] * o_r) + np.sum(dO_s[:, pos] * o_s))
+
+        dQ, dK, dV = O.prefill_bwd(Q, K, V, idx, M, dO_r, dO_s, positions=pos)
+        _close(dQ, _central(loss, Q)[:, pos], 1e-6, f"dQ rows {pos}")
+        _close(dK, _central(loss, K), 1e-6, f"dK rows {pos}")
+        _close(dV, _central(loss, V), 1e-6, f"dV rows {pos}")
+
+
 def pin_single_key_backward(O):
     """One visible key: o = v_0 whatever q is, so dq = 0, dk_0 = 0 and
     dv_0 = dO (closed form)."""
@@ -491,6 +516,25 @@ def pin_lse_closed_forms(O):
                 h = g * M + idx[b, :, g, j]
                 sc = np.einsum("sd,d->s", Q[b, np.arange(S), h], K[b, g, 0]) / 2.0
                 _close(lse_r[b, :, g, j], sc + ln, 1e-12, "lse, equal keys")
+
+
+def pin_lse_positions_closed_form(O):
+    """prefill_lse at chosen positions, every key equal: lse_i = q_i.k/sqrt(d)
+    + ln(i + 1) with the query of the row's own head (closed form)."""
+    rng = np.random.default_rng(32)
+    B, S, G, M, k, d = 1, 9, 2, 2, 1, 4
+    N = G * M
+    Q = rng.standard_normal((B, S, N + 1, d))
+    K = np.repeat(rng.standard_normal((B, G, 1, d)), S, axis=2)
+    idx = rng.integers(0, M, (B, S, G, k))
+    pos = np.array([0, 3, 8])
+    lse_r, lse_s = O.prefill_lse(Q, K, idx, M, positions=pos)
+    ln = np.log(pos + 1.0)
+    _close(lse_s[0], Q[0, pos, N] @ K[0, 0, 0] / 2.0 + ln, 1e-12, "shared lse at positions")
+    for g in range(G):
+        h = g * M + idx[0, pos, g, 0]
+        _close(lse_r[0, :, g, 0], np.einsum("pd,d->p", Q[0, pos, h], K[0, g, 0]) / 2.0 + ln, 1e-12,
+               "lse at positions")
 
 
 def pin_out_proj_bwd_central_differences(O):

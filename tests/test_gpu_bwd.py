@@ -3,17 +3,20 @@ the forward's row log-sum-exp and the attention backward.
 
 Tolerances. fp32: max |error| <= 1e-5 * max(1, max|ref|), relative Frobenius
 error <= 1e-5. bf16 inputs with fp32 accumulation: the backward rounds P and
-dS to bf16 for its products (relative error <= 2^-9 each) and rebuilds P from
+dS to bf16 for its products (relative error <= 2^-8 each) and rebuilds P from
 the forward's lse, whose scores use q*scale*log2(e) rounded to bf16 (relative
-error <= 2^-9 of |s|, |s| <= ~8 here); every gradient element is a sum of such
+error <= 2^-8 of |s|, |s| <= ~8 here); every gradient element is a sum of such
 terms, so the bounds are max |error| <= 2e-2 * max(1, max|ref|) and relative
 Frobenius error <= 2e-2. The lse itself: |error| <= 2e-2 * max(1, |ref|)
 elementwise in bf16, 1e-5 in fp32.
 """
+import functools
+
 import numpy as np
 import pytest
 import torch
 
+import equal_keys
 import oracle
 import sparse_query_gqa_amd as gqe
 import synth
@@ -153,3 +156,98 @@ def test_prefill_bwd_main_workload():
         one["idx"] = inp["idx"].view(cfg.B, cfg.S, cfg.G, cfg.k)[b:b + 1].reshape(cfg.S, cfg.G, cfg.k)
         got = {n: out[n][b:b + 1] for n in ("lse_r", "lse_s", "dq", "dk", "dv")}
         _check(sub, one, got, what=f"b={b} ")
+
+
+@functools.lru_cache(maxsize=1)
+def _long_case():
+    cfg = synth.workload("long_s128k")
+    return cfg, _inputs(cfg)
+
+
+def _rows(t, dim, pos):
+    return t.index_select(dim, torch.as_tensor(pos, dtype=torch.long, device=t.device))
+
+
+def test_prefill_bwd_long_workload_sampled():
+    """The 128k-token bf16 layer (batch 1, N=16, G=8, k=1, d=64) in the launch
+    configuration the benchmark times. The oracle takes 15 rows spread over
+    the sequence and the last 64: the forward's lse and every head's dQ at
+    those rows, and dK, dV of the last 64 keys of every KV head, which no
+    earlier row can see."""
+    cfg, inp = _long_case()
+    out = _run(cfg, inp)
+    S, tail = cfg.S, 64
+    rng = np.random.default_rng(11)
+    spread = rng.choice(np.arange(1, S - tail), size=14, replace=False)
+    pos = np.sort(np.concatenate([[0], spread, np.arange(S - tail, S)]))
+    print(f"long_s128k rows {pos[:15].tolist()} + last {tail}", flush=True)
+    idx = inp["idx"].numpy().reshape(cfg.B, S, cfg.G, cfg.k)
+    Q, K, V = f64(inp["q"]), f64(inp["k"]), f64(inp["v"])
+    lr, ls = oracle.prefill_lse(Q, K, idx, cfg.M, positions=pos)
+    for got, ref, name in ((_rows(out["lse_r"], 1, pos), lr, "lse_r"), (_rows(out["lse_s"], 1, pos), ls, "lse_s")):
+        e = np.abs(f64(got) - ref) / np.maximum(1.0, np.abs(ref))
+        print(f"{name}: max scaled err {float(e.max()):.3e}")
+        assert np.all(np.isfinite(f64(got))) and float(e.max()) <= 2e-2, name
+    dQ, dK, dV = oracle.prefill_bwd(Q, K, V, idx, cfg.M, f64(inp["do_r"]), f64(inp["do_s"]), positions=pos)
+    assert_grad(_rows(out["dq"], 1, pos), dQ, cfg.dtype, "dQ (sampled rows)")
+    assert_grad(out["dk"][:, :, S - tail:], dK[:, :, S - tail:], cfg.dtype, "dK (last keys)")
+    assert_grad(out["dv"][:, :, S - tail:], dV[:, :, S - tail:], cfg.dtype, "dV (last keys)")
+
+
+def test_prefill_bwd_long_workload_equal_keys():
+    """The same layer with every key of a KV head set to its first key: each
+    softmax row is uniform over the visible keys, and the lse of every row and
+    the dK, dV of every key have closed forms (equal_keys), checked in full.
+    dQ is zero in exact arithmetic; what the kernel returns is rounding of a
+    sum whose terms cancel, chiefly from delta_i = dO_i . o_i taken with the
+    stored bf16 o_i, so each element is held to 2e-2 of the size of those
+    terms, scale * |k_c| * sum_c' |dO_ic'| |o_ic'| (at least 1). Rows of
+    unselected heads are exactly zero."""
+    cfg, inp = _long_case()
+    B, S, G, M, k, N, d = cfg.B, cfg.S, cfg.G, cfg.M, cfg.k, cfg.N, cfg.d
+    e = dict(inp)
+    e["k"] = inp["k"][:, :, :1].expand(-1, -1, S, -1).contiguous()
+    out = _run(cfg, e)
+    idx = inp["idx"].view(B, S, G, k).long()
+    rows = torch.arange(S)
+    lse_r, lse_s = f64(out["lse_r"]), f64(out["lse_s"])
+    scale = 1.0 / np.sqrt(d)
+    for b in range(B):
+        dK = np.zeros((G, S, d))
+        dV = np.zeros((G, S, d))
+        used = torch.zeros((S, N + 1), dtype=torch.bool)
+        used[:, N] = True
+        dqb = out["dq"][b].cpu()
+        worst = 0.0
+
+        def check_dq(heads, key, dO, o):
+            nonlocal worst
+            got = f64(dqb[rows, heads])
+            tol = 2e-2 * np.maximum(1.0, scale * np.abs(key)[None, :] * np.sum(np.abs(dO) * np.abs(o), 1)[:, None])
+            worst = max(worst, float(np.max(np.abs(got) / tol)))
+            assert np.all(np.abs(got) <= tol), f"b={b} dQ of heads {heads[:4].tolist()}..."
+
+        for g in range(G):
+            key = f64(e["k"][b, g, 0])
+            for j in range(k):
+                heads = g * M + idx[b, :, g, j]
+                used[rows, heads] = True
+                dO = f64(inp["do_r"][b, :, g, j])
+                lse, o, dk, dv = equal_keys.stream(f64(inp["q"][b, rows, heads]), dO, f64(inp["v"][b, g]), key)
+                dK[g] += dk
+                dV[g] += dv
+                err = np.abs(lse_r[b, :, g, j] - lse) / np.maximum(1.0, np.abs(lse))
+                assert float(err.max()) <= 2e-2, f"lse_r b={b} g={g} j={j}: {float(err.max()):.3e}"
+                check_dq(heads, key, dO, o)
+        key = f64(e["k"][b, 0, 0])
+        dO = f64(inp["do_s"][b])
+        lse, o, dk, dv = equal_keys.stream(f64(inp["q"][b, :, N]), dO, f64(inp["v"][b, 0]), key)
+        dK[0] += dk
+        dV[0] += dv
+        err = np.abs(lse_s[b] - lse) / np.maximum(1.0, np.abs(lse))
+        assert float(err.max()) <= 2e-2, f"lse_s b={b}: {float(err.max()):.3e}"
+        check_dq(torch.full((S,), N), key, dO, o)
+        print(f"b={b} dQ: largest |dQ| / bound = {worst:.3e}")
+        assert_grad(out["dk"][b], dK, cfg.dtype, f"b={b} dK (every key)")
+        assert_grad(out["dv"][b], dV, cfg.dtype, f"b={b} dV (every key)")
+        assert not bool(dqb[~used].any()), f"b={b}: dQ of unselected heads is not zero"

@@ -4,7 +4,7 @@ the C ABI) against the CPU oracle.
 Tolerances. fp32: max |error| <= 1e-5 * max(1, max|ref|), relative Frobenius
 error <= 1e-5. bf16: the products take bf16 operands with fp32 accumulation;
 the slot vector's obar and the router's dz are rounded to bf16 before their
-weight-gradient products (relative error <= 2^-9 per term) and the bf16
+weight-gradient products (relative error <= 2^-8 per term) and the bf16
 outputs are rounded once more, so max |error| <= 2e-2 * max(1, max|ref|) and
 relative Frobenius error <= 1e-2. Quantities the kernels keep in fp32 (dw,
 dz, db_r, the balance loss) are held to 1e-4 relative in both dtypes.
@@ -85,10 +85,13 @@ def test_out_proj_bwd(case, mode):
     assert_close(dw_o, ref[3], tol, "dW_O", rel)
 
 
-def test_out_proj_bwd_main_workload():
-    """The 2k-token bf16 layer's shapes (T = 8*2048 tokens, G*k = 8 slots of
-    d = 64, D = 1024): the weight gradient sums over all 16384 tokens."""
-    cfg = synth.workload("main_s2k")
+@pytest.mark.parametrize("name", ["main_s2k", "long_s128k"])
+def test_out_proj_bwd_workload(name):
+    """The bf16 layers' shapes (2k tokens x 8 sequences and 128k tokens, G*k
+    = 8 slots of d = 64, D = 1024), the second in the launch configuration
+    the benchmark times: every output in full, the weight gradient summing
+    over all 16384 or 131072 tokens."""
+    cfg = synth.workload(name)
     T, G, k, d, D = cfg.T, cfg.G, cfg.k, cfg.d, cfg.D
     rng = np.random.default_rng(9)
     O_r = _tensor(rng.standard_normal((T, G, k, d)), torch.bfloat16)
@@ -144,6 +147,41 @@ def test_route_bwd(case):
     got = float(out["aux_loss"].cpu()[0])
     print(f"aux loss {got:.6e} vs {loss:.6e}")
     assert abs(got - loss) <= 1e-5 * max(1.0, abs(loss))
+
+
+@pytest.mark.parametrize("name", ["main_s2k", "long_s128k"])
+def test_route_bwd_workload(name):
+    """The router backward at the bf16 layers' sizes (G = 8 groups of M = 2
+    experts, top-1, D = 1024) with the balance loss, the 128k-token one in the
+    launch configuration the benchmark times; every output in full."""
+    cfg = synth.workload(name)
+    T, D, G, M, k = cfg.T, cfg.D, cfg.G, cfg.M, cfg.k
+    rng = np.random.default_rng(13)
+    x = _tensor(rng.standard_normal((T, D)), torch.bfloat16)
+    w_r = _tensor(rng.standard_normal((G * M, D)) * 0.02, torch.bfloat16)
+    z = oracle.route_logits(f64(x), f64(w_r), G, M).astype(np.float32)
+    _, idx, _ = oracle.route_select(z.astype(np.float64), k)
+    dw = rng.standard_normal((T, G, k)).astype(np.float32)
+    dims = gqe.gqe_dims.from_config(cfg)
+    out = gqe.route_bwd(dims, x.to(DEV), w_r.to(DEV), torch.from_numpy(z).to(DEV),
+                        torch.from_numpy(idx.astype(np.int32)).to(DEV), torch.from_numpy(dw).to(DEV), aux_coef=0.01)
+    torch.cuda.synchronize()
+    dz, dW_r, db_r, dx = oracle.route_bwd(f64(x), f64(w_r), z.astype(np.float64), idx, dw.astype(np.float64),
+                                          G, M, aux_coef=0.01)
+    # With top-1 the renormalised weight is 1 whatever the logits, so only the
+    # balance loss reaches the router and every gradient is of its (small)
+    # size: the bounds are relative to the largest reference element.
+    for name, ref, tol in (("dz", dz, 1e-4), ("db_router", db_r, 1e-4), ("dw_router", dW_r, 2e-2),
+                           ("dx", dx, 2e-2)):
+        got = f64(out[name])
+        amax = float(np.max(np.abs(ref)))
+        err = float(np.max(np.abs(got - ref)))
+        fro = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        print(f"{name}: max|err|={err:.3e} (max|ref|={amax:.3e}) rel_fro={fro:.3e}")
+        assert amax > 0 and err <= tol * amax and fro <= tol / 2, name
+    loss = oracle.load_balance_loss(z.astype(np.float64), idx, M, 0.01)
+    got = float(out["aux_loss"].cpu()[0])
+    assert abs(got - loss) <= 1e-5 * max(1.0, abs(loss)), (got, loss)
 
 
 def test_route_bwd_deterministic():

@@ -21,7 +21,7 @@ from test_gpu_parity import assert_close as _assert_close_abs
 def assert_close(got, ref, dtype, what):
     """As for the other kernels, except that bf16 projections can exceed 8 in
     magnitude, where storing bf16 alone (8 significant bits) rounds by up to
-    2^-9 relative: the bound per element is 2e-2 * max(1, |ref|)."""
+    2^-8 relative: the bound per element is 2e-2 * max(1, |ref|)."""
     if dtype != "bf16":
         return _assert_close_abs(got, ref, dtype, what)
     g = f64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)

@@ -40,7 +40,7 @@ MUTANTS = {
     "mask_one_too_many": (
         "L = int(pr.max()) + 1", "L = min(int(pr.max()) + 2, K.shape[0])\n        pr = pr + 1"),
     "head_mapping_transposed": (
-        "heads = g * M + idx[b, pos, g, j]", "heads = idx[b, pos, g, j] * G + g"),
+        "heads = g * M + idx[b, pos, g, j]\n                O_r", "heads = idx[b, pos, g, j] * G + g\n                O_r"),
     "shared_head_on_last_group": (
         "O_s[b] = attend_rows(Q[b, pos, N, :], pos, K[b, 0], V[b, 0])",
         "O_s[b] = attend_rows(Q[b, pos, N, :], pos, K[b, G - 1], V[b, G - 1])"),
@@ -69,9 +69,15 @@ MUTANTS = {
         "sc = np.where(np.arange(L)[None, :] <= pos[:, None], sc, -np.inf)",
         "sc = np.where(np.arange(L)[None, :] < np.maximum(pos[:, None], 1), sc, -np.inf)"),
     "lse_shared_on_last_group": (
-        "lse_s[b] = lse_rows(Q[b, :, N, :], pos, K[b, 0])", "lse_s[b] = lse_rows(Q[b, :, N, :], pos, K[b, G - 1])"),
+        "lse_s[b] = lse_rows(Q[b, pos, N, :], pos, K[b, 0])", "lse_s[b] = lse_rows(Q[b, pos, N, :], pos, K[b, G - 1])"),
     "lse_head_mapping_transposed": (
-        "heads = g * M + idx[b, :, g, j]\n                lse_r", "heads = idx[b, :, g, j] * G + g\n                lse_r"),
+        "heads = g * M + idx[b, pos, g, j]\n                lse_r", "heads = idx[b, pos, g, j] * G + g\n                lse_r"),
+    "lse_positions_ignored": (
+        "lse_s[b] = lse_rows(Q[b, pos, N, :], pos, K[b, 0])", "lse_s[b] = lse_rows(Q[b, pos, N, :], pos * 0 + pos.max(), K[b, 0])"),
+    "bwd_head_mapping_transposed": (
+        "heads = g * M + idx[b, pos, g, j]\n                dq", "heads = idx[b, pos, g, j] * G + g\n                dq"),
+    "bwd_rows_take_first_gradients": (
+        "V[b, g], dO_r[b, pos, g, j])", "V[b, g], dO_r[b, :pos.size, g, j])"),
     "weighted_variant_unscaled": (
         "        return np.concatenate([(w[..., None] * O_r).reshape(T, G * k * d), shared], axis=1)",
         "        return np.concatenate([O_r.reshape(T, G * k * d), shared], axis=1)"),
