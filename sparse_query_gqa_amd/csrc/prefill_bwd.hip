@@ -251,6 +251,17 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
 #pragma unroll
   for (int s = 0; s < KS; ++s) k_off[s] = l32 * ROWB + 16 * ((2 * s + half) ^ tile_swz<D>(l32));
   const TrOffsets<D> tr(lane);
+  // For d <= 64 the block's K and V fragments (the same for every tile) stay
+  // in registers: LDS read bandwidth, not the MFMAs, bounds this kernel, and
+  // they were a quarter of each tile's LDS reads.
+  bf16x8 kreg[D <= 64 ? KS : 1], vreg[D <= 64 ? KS : 1];
+  if constexpr (D <= 64) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      kreg[s] = *(const bf16x8*)(kvl[0] + k_off[s]);
+      vreg[s] = *(const bf16x8*)(kvl[1] + k_off[s]);
+    }
+  }
 
   f32x16 dk[NH][DB], dv[NH][DB];
 #pragma unroll
@@ -287,8 +298,14 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(BwdParam
     auto sdp = [&](const int h) __attribute__((always_inline)) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf = *(const bf16x8*)(kvl[0] + 32 * h * ROWB + k_off[s]);
-        const bf16x8 vf = *(const bf16x8*)(kvl[1] + 32 * h * ROWB + k_off[s]);
+        bf16x8 kf, vf;
+        if constexpr (D <= 64) {
+          kf = kreg[s];
+          vf = vreg[s];
+        } else {
+          kf = *(const bf16x8*)(kvl[0] + 32 * h * ROWB + k_off[s]);
+          vf = *(const bf16x8*)(kvl[1] + 32 * h * ROWB + k_off[s]);
+        }
         sc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf, s ? sc[h] : nl, 0, 0, 0);
         dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[s], vf, s ? dp[h] : nd, 0, 0, 0);
       }
