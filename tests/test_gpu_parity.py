@@ -269,6 +269,55 @@ def test_prefill_workloads_sampled(name):
         assert_close(o_s[b:b + 1, pos], ref_s, cfg.dtype, f"{name} b={b} O_shared (sampled)")
 
 
+# Sequences past 8k tokens with ragged row counts: tile edges, skewed lists
+# and the striped tile order (G not a multiple of 8).
+LONG_FORM_CASES = [
+    # B, S, D, N, G, k, skew
+    (2, 8269, 64, 16, 8, 2, True),   # ragged rows, two slots per token, skewed lists
+    (1, 8192, 64, 4, 2, 1, False),   # G not a multiple of 8: striped tile order
+    (1, 9000, 64, 8, 8, 1, False),   # one expert per group (k = M)
+]
+
+
+@pytest.mark.parametrize("case", LONG_FORM_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_long_form(case):
+    """Rows around every 256-row tile edge, the first and last rows and a
+    random sample, against the oracle; also the training forward's lse."""
+    B, S, D, N, G, k, skew = case
+    cfg = small_cfg(B, S, D, N, G, k, 64, seed=7, skew=skew)
+    inp = _prefill_inputs(cfg, peaked=False)
+    inp["idx"] = synth.random_selection(B, S, G, cfg.M, k, 11, skew=skew)
+    g = to_dev(inp)
+    dims = dims_of(cfg)
+    o_r, o_s = gqe.prefill(dims, g["q"], g["k"], g["v"], g["idx"])
+    t_r, t_s, lse_r, lse_s = gqe.prefill_train(dims, g["q"], g["k"], g["v"], g["idx"])
+    torch.cuda.synchronize()
+    assert torch.equal(o_r, t_r) and torch.equal(o_s, t_s)
+    # token positions at the edges of 256-row tiles (routed rows are k per token)
+    edges = set()
+    for rows in (S * k, S):
+        per = k if rows == S * k else 1
+        for e in range(0, rows, 256):
+            for r in (e - 1, e, e + 1):
+                if 0 <= r < rows:
+                    edges.add(r // per)
+    rng = np.random.default_rng(S)
+    extra = rng.choice(np.arange(S), size=64, replace=False)
+    pos = np.unique(np.concatenate([sorted(edges), extra, np.arange(S - 40, S), np.arange(40)]))
+    idx = inp["idx"].numpy().reshape(B, S, G, k)
+    print(f"case {case}: {pos.size} positions", flush=True)
+    for b in range(B):
+        Q, K, V = f64(inp["q"][b:b + 1]), f64(inp["k"][b:b + 1]), f64(inp["v"][b:b + 1])
+        ref_r, ref_s = oracle.prefill(Q, K, V, idx[b:b + 1], cfg.M, positions=pos)
+        assert_close(o_r[b:b + 1, pos], ref_r, cfg.dtype, f"b={b} O_routed")
+        assert_close(o_s[b:b + 1, pos], ref_s, cfg.dtype, f"b={b} O_shared")
+        lr, ls = oracle.prefill_lse(Q, K, idx[b:b + 1], cfg.M, positions=pos)
+        for got, ref, name in ((lse_r[b:b + 1, pos], lr, "lse_r"), (lse_s[b:b + 1, pos], ls, "lse_s")):
+            e = np.abs(f64(got) - ref) / np.maximum(1.0, np.abs(ref))
+            print(f"b={b} {name}: max scaled err {float(e.max()):.3e}")
+            assert float(e.max()) <= 2e-2, name
+
+
 def test_prefill_deterministic():
     cfg = small_cfg(2, 300, 128, 16, 8, 1, 64)
     inp = to_dev(_prefill_inputs(cfg, False))
