@@ -25,7 +25,9 @@ DecodeSplit decode_split(int B, int G, int Smax, int k, int q_len) {
   DecodeSplit s;
   s.rows = (k + 1) * q_len;
   const int bg = B * G > 0 ? B * G : 1;
-  int target = (4096 + bg - 1) / bg;  // aim for ~4k blocks in total
+  // aim for ~2k blocks in total: at 16 x 8 heads x 64k keys, 2k blocks of
+  // 4096 keys ran 1.5% faster than 4k blocks of 2048 (and 8k, 16k slower)
+  int target = (2048 + bg - 1) / bg;
   if (target < 1) target = 1;
   int chunk = (Smax + target - 1) / target;
   chunk = ((chunk + 511) / 512) * 512;  // whole unrolled iterations (at most 512 keys)
