@@ -195,23 +195,6 @@ __global__ __launch_bounds__(512, 1) void out_proj_gemm_kernel(OutProjParams p) 
   const __bf16* wo = (const __bf16*)p.w_o;
   const int64_t tmax = p.T - 1;
 
-  // obar = sum over the G*k slots of w * o, in fp32, rounded to bf16; one
-  // 8-column piece of one token per work item
-  for (int it = tid; nob && it < kGT * (DH / 8); it += 512) {
-    const int row = it / (DH / 8), e = (it % (DH / 8)) * 8;
-    const int64_t t = min(m0 + row, tmax);
-    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < p.Gk; ++j) {
-      const float wj = p.w[t * p.Gk + j];
-      const bf16x8 ov = *(const bf16x8*)(orr + t * hard + j * DH + e);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s[i] = fmaf(wj, (float)ov[i], s[i]);
-    }
-    bf16x8 r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = f2bf(s[i]);
-    *(bf16x8*)&obar[row][e] = r;
-  }
 
   // LDS-DMA of step kt into stage st. A: chunk `wave` = token rows
   // 16*wave + lane/4, 16-byte chunk position lane%4, holding logical chunk
@@ -272,6 +255,26 @@ __global__ __launch_bounds__(512, 1) void out_proj_gemm_kernel(OutProjParams p) 
 
 #pragma unroll
   for (int kt = 0; kt < kGStages - 1; ++kt) dma(kt, kt);
+  // obar = sum over the G*k slots of w * o, in fp32, rounded to bf16; one
+  // 8-column piece of one token per work item. Computed after the first
+  // stages' LDS-DMA is issued, so that those loads are in flight meanwhile
+  // (waiting on these loads also drains the earlier DMA: the counter is in
+  // order); the main loop's first barrier publishes obar.
+  for (int it = tid; nob && it < kGT * (DH / 8); it += 512) {
+    const int row = it / (DH / 8), e = (it % (DH / 8)) * 8;
+    const int64_t t = min(m0 + row, tmax);
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < p.Gk; ++j) {
+      const float wj = p.w[t * p.Gk + j];
+      const bf16x8 ov = *(const bf16x8*)(orr + t * hard + j * DH + e);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] = fmaf(wj, (float)ov[i], s[i]);
+    }
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = f2bf(s[i]);
+    *(bf16x8*)&obar[row][e] = r;
+  }
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt % kGStages;
     // step kt's tile is complete when at most the two later tiles' loads are
