@@ -254,8 +254,8 @@ def test_prefill_bwd_validation():
 def test_workspace_sizes_closed_form():
     lib = _lib()
     d = _dims(B=16, S=65536, N=32, G=8, k=2, d=128)
-    # split geometry: ~4096 blocks over B*G = 128 pairs -> 32 splits of 2048 keys
-    recs = 16 * 8 * 32 * 3
+    # split geometry: ~2048 blocks over B*G = 128 pairs -> 16 splits of 4096 keys
+    recs = 16 * 8 * 16 * 3
     assert lib.gqe_decode_workspace_bytes(ctypes.byref(d), 1) == recs * (128 + 2) * 4
     # small cache: splits are at least 512 keys -> 2 splits of 1000 keys; q_len=2 -> (k+1)*2 rows
     d3 = _dims(B=1, S=1000, N=4, G=2, k=1, d=64)
