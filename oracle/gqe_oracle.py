@@ -35,6 +35,9 @@ Readings where the pages are silent (each is listed in the design notes):
   * The shared head is query column block N and reads KV head 0, causally,
     with scale 1/sqrt(d) and no routing weight.
   * W_O has shape ((G*k + 2) * d, D_out), no bias.
+  * The two ablation rows of [GQE-review] §四 Table 2 keep only the hard
+    slots: "hard" plain, "weighted" scaled by the router probabilities p
+    (not renormalised); neither has ō or the shared head (assemble).
   * A key j is visible to a query at absolute position p iff j <= p.
 
 parity pinned: every function here is checked against values and identities
@@ -52,6 +55,7 @@ __all__ = [
     "layer", "kv_bytes", "prefill_flops", "check_dims", "project",
     "project_decode", "project_flops", "attend_rows_bwd", "prefill_bwd",
     "out_proj_bwd", "route_bwd", "lse_rows", "prefill_lse", "load_balance_loss",
+    "slot_weights", "slot_rows",
 ]
 
 
@@ -289,6 +293,29 @@ def decode(q, K, V, kv_len, idx, M: int, kv_start=None):
     return O_r, O_s
 
 
+def slot_weights(p, idx, w, mode: str = "full"):
+    """Per-slot weights [T, G, k] that each slot layout applies to the
+    selected heads' outputs.
+
+    "full": the renormalised weights w of the ō slot ([GQE-review] §二, the
+    w equation). "weighted": the Table 2 row of [GQE-review] §四 that keeps
+    only a weighted concatenation and removes the renormalised slot, so each
+    hard slot is scaled by the router's own
+    probability p_{i,g,m} (the group softmax over all M experts, not
+    renormalised over the selected set). Renormalised weights would be
+    exactly 1 at the pages' k = 1 and make this row the hard one, which the
+    table's two different scores rule out. "hard": no weights (None).
+    p: [T, G, M]; idx: [T, G, k]; w: [T, G, k].
+    """
+    if mode == "full":
+        return np.asarray(w, dtype=np.float64)
+    if mode == "weighted":
+        return np.take_along_axis(np.asarray(p, dtype=np.float64), np.asarray(idx), axis=-1)
+    if mode == "hard":
+        return None
+    raise ValueError(f"unknown slot mode {mode!r}")
+
+
 def assemble(O_r, w, O_s, mode: str = "full") -> np.ndarray:
     """Slot vector A_i = Concat(O_i, ō_i, s(x_i)) for every token.
 
@@ -296,26 +323,43 @@ def assemble(O_r, w, O_s, mode: str = "full") -> np.ndarray:
     outputs, concatenated), renormalised weighted-sum slot
     ō_i = sum w_{i,g,m} o_{i,g,m} (summed over all groups), and the shared
     head's output s(x_i).
-    The ablation variants of [GQE-review] §四 (Table 2) drop the ō slot:
-    mode "hard" is [O_i, s(x_i)] (hard concatenation only) and mode
-    "weighted" is [w ⊙ O_i, s(x_i)] (weighted concatenation: each hard slot
-    times its renormalised weight). Keeping the shared head in both is a
-    reading; the table does not say.
-    O_r: [T, G, k, d]; w: [T, G, k]; O_s: [T, d]. Returns [T, (G*k+2)*d]
-    (full) or [T, (G*k+1)*d].
+    The ablation rows of [GQE-review] §四 (Table 2) each keep only one kind
+    of concatenation: mode "hard" (hard concatenation only) is A_i = O_i,
+    and mode "weighted" (weighted concatenation only, renormalised slot
+    removed) is A_i = w ⊙ O_i with w the slot weights of
+    slot_weights(..., "weighted"), the router probabilities p. Neither has
+    the ō slot or the shared head: each row's label names the one part it
+    keeps, the note under the table ties the drops to removing the
+    renormalised slot and the shared head / soft signal, and [GQE-summary]
+    (In brief) has the ablations lacking both the renormalised slot and the
+    shared head.
+    O_r: [T, G, k, d]; w: [T, G, k] (mode "full": renormalised weights;
+    "weighted": the slot weights; "hard": unused); O_s: [T, d] (unused by the
+    ablation modes). Returns [T, (G*k+2)*d] (full) or [T, G*k*d].
     """
     O_r = np.asarray(O_r, dtype=np.float64)
     T, G, k, d = O_r.shape
-    w = np.asarray(w, dtype=np.float64)
-    shared = np.asarray(O_s, dtype=np.float64)
     if mode == "full":
+        w = np.asarray(w, dtype=np.float64)
+        shared = np.asarray(O_s, dtype=np.float64)
         hard = O_r.reshape(T, G * k * d)
         obar = np.sum(w[..., None] * O_r, axis=(1, 2))
         return np.concatenate([hard, obar, shared], axis=1)
     if mode == "hard":
-        return np.concatenate([O_r.reshape(T, G * k * d), shared], axis=1)
+        return O_r.reshape(T, G * k * d)
     if mode == "weighted":
-        return np.concatenate([(w[..., None] * O_r).reshape(T, G * k * d), shared], axis=1)
+        w = np.asarray(w, dtype=np.float64)
+        return (w[..., None] * O_r).reshape(T, G * k * d)
+    raise ValueError(f"unknown slot mode {mode!r}")
+
+
+def slot_rows(G: int, k: int, d: int, mode: str = "full") -> int:
+    """Rows of W_O for a slot layout: (G*k+2)*d for the full [O, ō, s],
+    G*k*d for the ablation layouts (hard slots only)."""
+    if mode == "full":
+        return (G * k + 2) * d
+    if mode in ("hard", "weighted"):
+        return G * k * d
     raise ValueError(f"unknown slot mode {mode!r}")
 
 
@@ -325,8 +369,10 @@ def out_proj(O_r, w, O_s, W_O, mode: str = "full") -> np.ndarray:
     return assemble(O_r, w, O_s, mode) @ np.asarray(W_O, dtype=np.float64)
 
 
-def layer(x, w_r, Q, K, V, W_O, G: int, k: int, b_r=None):
-    """Whole prefill layer: route, attend, assemble, project. Returns a dict."""
+def layer(x, w_r, Q, K, V, W_O, G: int, k: int, b_r=None, mode: str = "full"):
+    """Whole prefill layer: route, attend, assemble, project. Returns a dict.
+    mode picks the slot layout (assemble); the slot weights it uses are
+    slot_weights(p, idx, w, mode)."""
     B, S, H1, d = np.asarray(Q).shape
     N = H1 - 1
     M = check_dims(N, G, k)
@@ -334,8 +380,9 @@ def layer(x, w_r, Q, K, V, W_O, G: int, k: int, b_r=None):
     idx4 = idx.reshape(B, S, G, k)
     O_r, O_s = prefill(Q, K, V, idx4, M)
     T = B * S
-    y = out_proj(O_r.reshape(T, G, k, d), w, O_s.reshape(T, d), W_O)
-    return dict(z=z, p=p, idx=idx, w=w, O_r=O_r, O_s=O_s, y=y)
+    sw = slot_weights(p, idx, w, mode)
+    y = out_proj(O_r.reshape(T, G, k, d), sw, O_s.reshape(T, d), W_O, mode)
+    return dict(z=z, p=p, idx=idx, w=w, sw=sw, O_r=O_r, O_s=O_s, y=y)
 
 
 def project(x, W_Q, W_K, W_V, idx, N: int, G: int):
@@ -490,10 +537,13 @@ def out_proj_bwd(O_r, w, O_s, W_O, dy, mode: str = "full"):
     slots, ō and s, and ō = sum w o feeds back into the hard slots (w dō)
     and into the routing weights (dw = o . dō), which is how the router
     receives a gradient ([GQE-review] §二: the renormalised slot).
+    Ablation layouts (assemble): "hard" gives dO_r = dA and no weight
+    gradient; "weighted" (A = w ⊙ O) gives dO_r = w dA and dw = o . dA, the
+    gradient of the slot weights (the router probabilities p); neither reads
+    the shared head, so dO_s = 0.
     Returns (dO_r [T, G, k, d], dw [T, G, k], dO_s [T, d], dW_O).
     """
     O_r = np.asarray(O_r, dtype=np.float64)
-    w = np.asarray(w, dtype=np.float64)
     dy = np.asarray(dy, dtype=np.float64)
     T, G, k, d = O_r.shape
     A = assemble(O_r, w, O_s, mode)
@@ -501,16 +551,18 @@ def out_proj_bwd(O_r, w, O_s, W_O, dy, mode: str = "full"):
     dA = dy @ np.asarray(W_O, dtype=np.float64).T
     hard = dA[:, :G * k * d].reshape(T, G, k, d)
     if mode == "full":
+        w = np.asarray(w, dtype=np.float64)
         dobar = dA[:, G * k * d:G * k * d + d]
         dO_r = hard + w[..., None] * dobar[:, None, None, :]
         dw = np.einsum("tgkd,td->tgk", O_r, dobar)
         dO_s = dA[:, G * k * d + d:]
     elif mode == "hard":
-        dO_r, dw, dO_s = hard, np.zeros_like(w), dA[:, G * k * d:]
+        dO_r, dw, dO_s = hard, np.zeros((T, G, k)), np.zeros((T, d))
     elif mode == "weighted":
+        w = np.asarray(w, dtype=np.float64)
         dO_r = w[..., None] * hard
         dw = np.einsum("tgkd,tgkd->tgk", O_r, hard)
-        dO_s = dA[:, G * k * d:]
+        dO_s = np.zeros((T, d))
     else:
         raise ValueError(f"unknown slot mode {mode!r}")
     return dO_r, dw, dO_s, dW_O
@@ -537,13 +589,15 @@ def load_balance_loss(z, idx, M: int, coef: float) -> float:
     return float(coef * M * np.mean(np.sum(f * P, axis=-1)))
 
 
-def route_bwd(x, w_r, z, idx, dw, G: int, M: int, aux_coef: float = 0.0):
-    """Gradients of the router given dw [T, G, k] (the gradient of the
-    renormalised weights). p = softmax(z), w_j = p_{m_j} / sum_{j'} p_{m_j'}
-    over the selected experts ([GQE-review] §二, the w equation); the
-    selection itself is piecewise constant. dp_{m_j} = (dw_j - sum_j' dw_j'
-    w_j') / sum_j' p_{m_j'} on the selected experts, 0 elsewhere; with
-    aux_coef the balance loss (load_balance_loss) adds
+def route_bwd(x, w_r, z, idx, dw, G: int, M: int, aux_coef: float = 0.0, wrt: str = "w"):
+    """Gradients of the router given dw [T, G, k], the gradient of the slot
+    weights. wrt="w": the renormalised weights of the ō slot. p = softmax(z),
+    w_j = p_{m_j} / sum_{j'} p_{m_j'} over the selected experts
+    ([GQE-review] §二, the w equation); the selection itself is piecewise
+    constant. dp_{m_j} = (dw_j - sum_j' dw_j' w_j') / sum_j' p_{m_j'} on the
+    selected experts, 0 elsewhere. wrt="p": the weights are the selected
+    probabilities themselves (the weighted-concatenation ablation), so
+    dp_{m_j} = dw_j. With aux_coef the balance loss (load_balance_loss) adds
     coef * M * f_{g,m} / (T * G) to dp of every expert;
     dz = p * (dp - p . dp); dW_r = dz^T x, db_r = sum_t dz, dx = dz W_r.
     x: [T, D]; w_r: [G*M, D]; z: [T, G, M]; idx: [T, G, k].
@@ -555,10 +609,15 @@ def route_bwd(x, w_r, z, idx, dw, G: int, M: int, aux_coef: float = 0.0):
     T = x.shape[0]
     p = softmax(z, axis=-1)
     idx = np.asarray(idx)
-    p_sel = np.take_along_axis(p, idx, -1)
-    ssum = np.sum(p_sel, axis=-1, keepdims=True)
-    wsel = p_sel / ssum
-    dp_sel = (dw - np.sum(dw * wsel, axis=-1, keepdims=True)) / ssum
+    if wrt == "w":
+        p_sel = np.take_along_axis(p, idx, -1)
+        ssum = np.sum(p_sel, axis=-1, keepdims=True)
+        wsel = p_sel / ssum
+        dp_sel = (dw - np.sum(dw * wsel, axis=-1, keepdims=True)) / ssum
+    elif wrt == "p":
+        dp_sel = dw
+    else:
+        raise ValueError(f"unknown weight kind {wrt!r}")
     dp = np.zeros_like(p)
     np.put_along_axis(dp, idx, dp_sel, axis=-1)
     if aux_coef:

@@ -383,28 +383,69 @@ def pin_flop_count(O):
         assert O.prefill_flops(B, S, G, k, d) == 4 * d * pairs
 
 
+def _one_token_variant(O, Q, K, V, G, k, z, mode):
+    """The oracle's layer for one token with a given slot layout: the slot
+    weights come from slot_weights (the router's p or w, as the layout
+    says), the slot vector from assemble."""
+    H1, d = Q.shape
+    M = (H1 - 1) // G
+    p, idx, w = O.route_select(np.asarray(z, dtype=np.float64)[None], k)
+    Q4 = np.asarray(Q, dtype=np.float64)[None, None]
+    K4 = np.asarray(K, dtype=np.float64)[None, :, None, :]
+    V4 = np.asarray(V, dtype=np.float64)[None, :, None, :]
+    O_r, O_s = O.prefill(Q4, K4, V4, idx.reshape(1, 1, G, k), M)
+    sw = O.slot_weights(p, idx, w, mode)
+    return O.assemble(O_r.reshape(1, G, k, d), sw, O_s.reshape(1, d), mode).reshape(-1)
+
+
 def pin_ablation_slot_variants(O):
-    """The two ablation layouts: hard concatenation is the hard slots then the
-    shared head (no ō); weighted concatenation scales slot (g, j) by w[g, j]
-    (checked on integer values, exactly); with k = 1 every w is 1, so the two
-    variants coincide."""
+    """The two ablation layouts of the review's Table 2 (section 四), on the
+    GQA worked example with a zero router (p = 1/2 for both experts):
+    hard concatenation only is A = O alone, k=2 -> [1,0,1,0,0,1,0,1] and
+    k=1 (tie -> expert 0) -> [1,0,0,1]; weighted concatenation without the
+    renormalised slot scales each hard slot by the router probability p, so
+    it is half of that, [.5,0,0,.5] at k=1. Renormalised weights would be
+    1 at k=1 and make the two rows coincide; the table scores them
+    differently. Neither layout carries the shared head (a NaN shared output
+    must not reach A) or the obar slot."""
+    g = _golden("gqa_worked_example.json")
+    Q = np.vstack([np.array(g["Q"], float), [[0.3, -0.7]]])
+    K, V = np.array(g["K"], float), np.array(g["V"], float)
+    z0 = np.zeros((2, 2))
+    _close(_one_token_variant(O, Q, K, V, 2, 2, z0, "hard"), g["concat"], what="hard, k=2")
+    _close(_one_token_variant(O, Q, K, V, 2, 1, z0, "hard"), [1, 0, 0, 1], what="hard, k=1")
+    _close(_one_token_variant(O, Q, K, V, 2, 2, z0, "weighted"), 0.5 * np.array(g["concat"], float),
+           what="weighted, k=2")
+    A_w1 = _one_token_variant(O, Q, K, V, 2, 1, z0, "weighted")
+    _close(A_w1, [0.5, 0, 0, 0.5], what="weighted, k=1")
+    # the two rows must differ at k = 1 whenever p < 1
+    assert np.max(np.abs(A_w1 - _one_token_variant(O, Q, K, V, 2, 1, z0, "hard"))) >= 0.5, \
+        "the weighted and hard ablation rows coincide at k = 1"
+    # the slot weights in closed form: logits (ln 3, 0) give p = (3/4, 1/4)
+    p, idx, w = O.route_select(np.array([[[math.log(3.0), 0.0]]]), 1)
+    _close(O.slot_weights(p, idx, w, "weighted"), [[[0.75]]], 1e-15, "weighted slot weight, k=1")
+    _close(O.slot_weights(p, idx, w, "full"), [[[1.0]]], 0.0, "full-layout weight, k=1")
+    assert O.slot_weights(p, idx, w, "hard") is None
+    # M=4, k=2, logits (ln 4, ln 2, 0, ln 2): p = (4,2,1,2)/9, top-2 {0,1}
+    # (tie between 1 and 3 -> 1); slot weights (4/9, 2/9), renormalised (2/3, 1/3)
+    p, idx, w = O.route_select(np.log(np.array([[[4.0, 2.0, 1.0, 2.0]]])), 2)
+    _close(O.slot_weights(p, idx, w, "weighted"), [[[4 / 9, 2 / 9]]], 1e-15, "weighted slot weights, k=2")
+    _close(O.slot_weights(p, idx, w, "full"), [[[2 / 3, 1 / 3]]], 1e-15, "full-layout weights, k=2")
+    # layout on integer values: slot (g, j) at columns (g*k+j)*d, exact
     O_r = np.arange(2 * 2 * 2 * 3, dtype=float).reshape(2, 2, 2, 3)  # T=2, G=2, k=2, d=3
-    w = np.array([[[0.25, 0.75], [0.5, 0.5]], [[1.0, 0.0], [0.125, 0.875]]])
-    O_s = -np.ones((2, 3))
-    A_h = O.assemble(O_r, w, O_s, "hard")
-    A_w = O.assemble(O_r, w, O_s, "weighted")
-    assert A_h.shape == (2, 5 * 3) and A_w.shape == (2, 5 * 3)
+    sw = np.array([[[0.25, 0.75], [0.5, 0.5]], [[1.0, 0.0], [0.125, 0.875]]])
+    O_s = np.full((2, 3), np.nan)
+    A_h = O.assemble(O_r, sw, O_s, "hard")
+    A_w = O.assemble(O_r, sw, O_s, "weighted")
+    assert A_h.shape == (2, 12) and A_w.shape == (2, 12), "ablation layouts hold the hard slots only"
     for t in range(2):
-        for g in range(2):
+        for gg in range(2):
             for j in range(2):
-                c = (g * 2 + j) * 3
-                _close(A_h[t, c:c + 3], O_r[t, g, j], what="hard slot")
-                _close(A_w[t, c:c + 3], w[t, g, j] * O_r[t, g, j], what="weighted slot")
-        _close(A_h[t, 12:], O_s[t], what="shared after the hard slots")
-        _close(A_w[t, 12:], O_s[t], what="shared after the weighted slots")
-    w1 = np.ones((2, 2, 1))
-    _close(O.assemble(O_r[:, :, :1], w1, O_s, "weighted"), O.assemble(O_r[:, :, :1], w1, O_s, "hard"),
-           what="k = 1")
+                c = (gg * 2 + j) * 3
+                _close(A_h[t, c:c + 3], O_r[t, gg, j], 0.0, "hard slot")
+                _close(A_w[t, c:c + 3], sw[t, gg, j] * O_r[t, gg, j], 0.0, "weighted slot")
+    assert O.slot_rows(2, 2, 3, "full") == 18 and O.slot_rows(2, 2, 3, "hard") == 12
+    assert O.slot_rows(2, 2, 3, "weighted") == 12
 
 
 # --------------------------------------------------------------------------
@@ -539,14 +580,16 @@ def pin_lse_positions_closed_form(O):
 
 def pin_out_proj_bwd_central_differences(O):
     """dO_r, dw, dO_s, dW_O of y = A W_O (all three slot layouts) against
-    central differences of sum(dy * y)."""
+    central differences of sum(dy * y). In the ablation layouts the shared
+    head does not reach y, so its gradient is 0; in the hard one the slot
+    weights do not either."""
     rng = np.random.default_rng(23)
     T, G, k, d, D = 3, 2, 2, 2, 5
     O_r = rng.standard_normal((T, G, k, d))
     w = rng.random((T, G, k))
     O_s = rng.standard_normal((T, d))
     dy = rng.standard_normal((T, D))
-    for mode, rows in (("full", (G * k + 2) * d), ("hard", (G * k + 1) * d), ("weighted", (G * k + 1) * d)):
+    for mode, rows in (("full", (G * k + 2) * d), ("hard", G * k * d), ("weighted", G * k * d)):
         W_O = rng.standard_normal((rows, D))
 
         def loss():
@@ -579,6 +622,35 @@ def pin_route_bwd_central_differences(O):
     _close(dW_r, _central(loss, w_r), 1e-6, "dW_r")
     _close(db_r, _central(loss, b_r), 1e-6, "db_r")
     _close(dx, _central(loss, x), 1e-6, "dx")
+
+
+def pin_route_bwd_probability_weights(O):
+    """route_bwd with wrt="p" (the weighted-concatenation ablation, whose
+    slot weights are the selected router probabilities): dW_r, db_r, dx
+    against central differences of sum(dw * p_sel(x, W_r, b_r)), and the
+    closed form at M = 2, k = 1: d p_0 / d z_0 = p_0 p_1."""
+    rng = np.random.default_rng(26)
+    T, D, G, M, k = 4, 6, 2, 4, 2
+    x = rng.standard_normal((T, D))
+    w_r = rng.standard_normal((G * M, D))
+    b_r = rng.standard_normal(G * M) * 3.0
+    dw = rng.standard_normal((T, G, k))
+
+    def loss():
+        _, p, idx_, _ = O.route(x, w_r, G, M, k, b_r)
+        return float(np.sum(dw * np.take_along_axis(p, idx_, -1)))
+
+    z, _, idx, _ = O.route(x, w_r, G, M, k, b_r)
+    dz, dW_r, db_r, dx = O.route_bwd(x, w_r, z, idx, dw, G, M, wrt="p")
+    _close(dW_r, _central(loss, w_r), 1e-6, "dW_r (wrt p)")
+    _close(db_r, _central(loss, b_r), 1e-6, "db_r (wrt p)")
+    _close(dx, _central(loss, x), 1e-6, "dx (wrt p)")
+    # M = 2, k = 1, logits (ln 3, 0): p = (3/4, 1/4), expert 0 selected;
+    # dz = dw * (p0 p1, -p0 p1) = dw * (3/16, -3/16)
+    z1 = np.array([[[math.log(3.0), 0.0]]])
+    dz1, _, _, _ = O.route_bwd(np.zeros((1, 1)), np.zeros((2, 1)), z1, np.array([[[0]]]),
+                               np.array([[[2.0]]]), 1, 2, wrt="p")
+    _close(dz1, [[[0.375, -0.375]]], 1e-15, "dz closed form (wrt p)")
 
 
 def pin_load_balance_closed_forms(O):

@@ -79,11 +79,28 @@ MUTANTS = {
     "bwd_rows_take_first_gradients": (
         "V[b, g], dO_r[b, pos, g, j])", "V[b, g], dO_r[b, :pos.size, g, j])"),
     "weighted_variant_unscaled": (
-        "        return np.concatenate([(w[..., None] * O_r).reshape(T, G * k * d), shared], axis=1)",
-        "        return np.concatenate([O_r.reshape(T, G * k * d), shared], axis=1)"),
-    "hard_variant_without_shared": (
-        "        return np.concatenate([O_r.reshape(T, G * k * d), shared], axis=1)",
+        "        return (w[..., None] * O_r).reshape(T, G * k * d)",
         "        return O_r.reshape(T, G * k * d)"),
+    "weighted_variant_renormalised": (
+        "        return np.take_along_axis(np.asarray(p, dtype=np.float64), np.asarray(idx), axis=-1)",
+        "        return np.asarray(w, dtype=np.float64)"),
+    "hard_variant_keeps_shared": (
+        "        return O_r.reshape(T, G * k * d)\n    if mode == \"weighted\":",
+        "        return np.concatenate([O_r.reshape(T, G * k * d), np.asarray(O_s, dtype=np.float64)], axis=1)\n"
+        "    if mode == \"weighted\":"),
+    "weighted_variant_keeps_shared": (
+        "        return (w[..., None] * O_r).reshape(T, G * k * d)",
+        "        return np.concatenate([(w[..., None] * O_r).reshape(T, G * k * d), np.asarray(O_s, dtype=np.float64)], axis=1)"),
+    "ablation_rows_keep_shared": (
+        "    if mode in (\"hard\", \"weighted\"):\n        return G * k * d",
+        "    if mode in (\"hard\", \"weighted\"):\n        return (G * k + 1) * d"),
+    "ablation_bwd_shared_gradient": (
+        "        dO_r, dw, dO_s = hard, np.zeros((T, G, k)), np.zeros((T, d))",
+        "        dO_r, dw, dO_s = hard, np.zeros((T, G, k)), np.ones((T, d))"),
+    "route_bwd_p_renormalised": (
+        "    elif wrt == \"p\":\n        dp_sel = dw",
+        "    elif wrt == \"p\":\n        p_sel = np.take_along_axis(p, idx, -1)\n"
+        "        dp_sel = (dw - np.sum(dw * p_sel / p_sel.sum(-1, keepdims=True), axis=-1, keepdims=True)) / p_sel.sum(-1, keepdims=True)"),
     "bwd_softmax_without_delta": (
         "    dS = P * (dP - np.sum(dO * o, axis=1, keepdims=True))", "    dS = P * dP"),
     "bwd_key_scale_missing": (
