@@ -57,13 +57,25 @@ typedef enum {
 typedef enum { GQE_BF16 = 0, GQE_F32 = 1 } gqe_dtype;
 
 /* Slot layouts of the output projection: the method's [O, obar, s] and the
- * two ablation variants of GQE review, section 四, Table 2. */
+ * two ablation rows of GQE review, section 四, Table 2, each of which keeps
+ * the hard slots only (no obar slot, no shared head; the row labels name the
+ * one kind of concatenation kept, and the note under the table and the
+ * 1kpapers summary, In brief, tie the drops to removing the renormalised
+ * slot and the shared head). */
 typedef enum {
   GQE_SLOTS_FULL = 0,     /* [O_i, obar_i, s_i], W_O has (G*k+2)*d rows */
-  GQE_SLOTS_HARD = 1,     /* hard concatenation only: [O_i, s_i], (G*k+1)*d rows */
-  GQE_SLOTS_WEIGHTED = 2  /* weighted concatenation: [w * O_i, s_i], each hard
-                             slot scaled by its renormalised weight; (G*k+1)*d rows */
+  GQE_SLOTS_HARD = 1,     /* hard concatenation only: A_i = O_i, G*k*d rows */
+  GQE_SLOTS_WEIGHTED = 2  /* weighted concatenation, renormalised slot removed:
+                             A_i = p * O_i, each hard slot scaled by the router
+                             probability p of its expert (softmax over all M,
+                             not renormalised; gqe_route's topk_p); G*k*d rows */
 } gqe_slot_mode;
+
+/* What the slot weights given to gqe_route_bwd are. */
+typedef enum {
+  GQE_WEIGHTS_RENORM = 0, /* the renormalised weights w (topk_w): GQE_SLOTS_FULL */
+  GQE_WEIGHTS_PROB = 1    /* the selected probabilities p (topk_p): GQE_SLOTS_WEIGHTED */
+} gqe_weight_kind;
 
 /* Layer shape. B sequences of S tokens, model width D, N routed query heads,
  * G KV heads (= groups), top-k per group, head_dim d; M = N/G. The shared
@@ -93,6 +105,8 @@ size_t gqe_route_workspace_bytes(const gqe_dims* dims);
  *   logits_or_null [B*S, G, M]   fp32 out (z, bias included)
  *   topk_idx       [B*S, G, k]   int32 out, expert indices in 0..M-1, ascending
  *   topk_w         [B*S, G, k]   fp32 out, renormalised weights (sum 1; exactly 1 for k=1)
+ *   topk_p_or_null [B*S, G, k]   fp32 out, p of the selected experts (the
+ *                  weights of the GQE_SLOTS_WEIGHTED layout)
  *   list_off_or_null [B, G, M+1] int32 out: list of expert m of group g in
  *                  sequence b is list_tok[b,g, off[m] : off[m+1]]; off[0]=0, off[M]=k*S
  *   list_tok_or_null [B, G, k*S] int32 out: token positions (0..S-1), each
@@ -101,13 +115,21 @@ size_t gqe_route_workspace_bytes(const gqe_dims* dims);
  *                  lists are requested, else may be NULL.
  * list_off and list_tok must be both NULL or both non-NULL. Selection is a
  * pure function of the emitted fp32 logits: same logits, same indices, bit
- * for bit. */
+ * for bit.
+ * Beyond the minimal router call (dims, x, W_r, logits, topk_idx, topk_w,
+ * lists, stream) this takes an optional bias (the skewed-router workloads),
+ * the optional topk_p, and the lists' count workspace (the library allocates
+ * nothing). The lists are the expert-major view of topk_idx for callers that
+ * gather rows by expert; no other entry point reads them: the attention and
+ * projection kernels read topk_idx, position-major. */
 int gqe_route(const gqe_dims* dims, const void* x, const void* w_router,
               const float* b_router, float* logits_or_null, int32_t* topk_idx,
-              float* topk_w, int32_t* list_off_or_null, int32_t* list_tok_or_null,
-              void* workspace, size_t ws_bytes, void* stream);
+              float* topk_w, float* topk_p_or_null, int32_t* list_off_or_null,
+              int32_t* list_tok_or_null, void* workspace, size_t ws_bytes, void* stream);
 
-/* Sparse-query causal prefill attention.
+/* Sparse-query causal prefill attention. The selected rows come from
+ * topk_idx (position-major: every tile holds k rows per token whatever the
+ * routing skew), not from gqe_route's expert-major lists.
  * For token i (absolute position i in its sequence), group g and slot j the
  * head h = g*M + topk_idx[i,g,j] attends KV head g over keys 0..i:
  * o = sum_{t<=i} softmax_t(q_{i,h}.k_t / sqrt(d)) v_t (GQA tutorial,
@@ -228,13 +250,15 @@ int gqe_out_proj(const gqe_dims* dims, int64_t T, const void* o_routed,
                  const float* topk_w, const void* o_shared, const void* w_o,
                  void* y, void* stream);
 
-/* gqe_out_proj with another slot layout (gqe_slot_mode). The ablation
- * variants drop the obar slot (the pages' "仅硬拼接" and "仅加权拼接" rows);
- * both keep the always-on shared head, a reading: the table does not say.
- *   w_o [(G*k+2)*d, D] for GQE_SLOTS_FULL, else [(G*k+1)*d, D]; any other
- *   mode returns GQE_ERR_UNSUPPORTED. */
+/* gqe_out_proj with another slot layout (gqe_slot_mode): y_t = A_t W_O.
+ *   slot_w  [T, G, k] fp32: GQE_SLOTS_FULL the renormalised weights topk_w;
+ *           GQE_SLOTS_WEIGHTED the selected probabilities topk_p (each hard
+ *           slot is scaled by its own); GQE_SLOTS_HARD unused, may be NULL
+ *   o_shared [T, d]: read by GQE_SLOTS_FULL only; NULL allowed otherwise
+ *   w_o [(G*k+2)*d, D] for GQE_SLOTS_FULL, else [G*k*d, D]; any other mode
+ *   returns GQE_ERR_UNSUPPORTED. */
 int gqe_out_proj_variant(const gqe_dims* dims, int32_t mode, int64_t T,
-                         const void* o_routed, const float* topk_w,
+                         const void* o_routed, const float* slot_w,
                          const void* o_shared, const void* w_o, void* y,
                          void* stream);
 
@@ -248,18 +272,22 @@ size_t gqe_out_proj_bwd_workspace_bytes(const gqe_dims* dims, int32_t mode, int6
  *   GQE_SLOTS_FULL:     dO_r = dA[O] + w dA[obar],  dw = o . dA[obar]
  *                       (the renormalised slot is what gives the router a
  *                       gradient, section 二);
- *   GQE_SLOTS_HARD:     dO_r = dA[O], dw = 0;
- *   GQE_SLOTS_WEIGHTED: dO_r = w dA[w O], dw = o . dA[w O].
- *   o_routed [T, G, k, d], topk_w [T, G, k] fp32, o_shared [T, d], w_o as
- *   for the forward, dy [T, D]                                    inputs
+ *   GQE_SLOTS_HARD:     dO_r = dA[O], dw = 0, dO_s = 0;
+ *   GQE_SLOTS_WEIGHTED: dO_r = p dA[p O], dw = o . dA[p O] (the gradient of
+ *                       the slot weights p), dO_s = 0.
+ *   o_routed [T, G, k, d], slot_w [T, G, k] fp32 (as for
+ *   gqe_out_proj_variant), o_shared [T, d], w_o as for the forward,
+ *   dy [T, D]                                                     inputs
  *   do_routed [T, G, k, d] dtype, dw [T, G, k] fp32, do_shared [T, d] dtype,
  *   dw_o [rows of w_o, D] fp32                                    outputs
+ *   In the ablation layouts o_shared and do_shared may be NULL; a given
+ *   do_shared is filled with zeros. slot_w may be NULL for GQE_SLOTS_HARD.
  *   workspace >= gqe_out_proj_bwd_workspace_bytes(dims, mode, T) device bytes.
  * Deterministic (weight gradient summed over token ranges in a fixed order).
  * In the bf16 path the products take bf16 operands (A rounded as in the
  * forward) with fp32 accumulation. */
 int gqe_out_proj_bwd(const gqe_dims* dims, int32_t mode, int64_t T,
-                     const void* o_routed, const float* topk_w, const void* o_shared,
+                     const void* o_routed, const float* slot_w, const void* o_shared,
                      const void* w_o, const void* dy, void* do_routed, float* dw,
                      void* do_shared, float* dw_o, void* workspace, size_t ws_bytes,
                      void* stream);
@@ -270,9 +298,12 @@ size_t gqe_route_bwd_workspace_bytes(const gqe_dims* dims);
 /* Backward of gqe_route's weights for T = B*S tokens (GQE review, section
  * 二: p = softmax(z), w = p_sel / sum p_sel over the TopK set, which is
  * piecewise constant and carries no gradient):
- *   dp_sel = (dw - sum_j dw_j w_j) / sum p_sel on the selected experts, 0 on
- *   the others; dz = p (dp - p . dp); dW_r = dz^T x; db_r = sum_t dz;
- *   dx = dz W_r.
+ *   weights GQE_WEIGHTS_RENORM (dw is the gradient of w):
+ *     dp_sel = (dw - sum_j dw_j w_j) / sum p_sel on the selected experts;
+ *   weights GQE_WEIGHTS_PROB (dw is the gradient of the selected p, as
+ *   gqe_out_proj_bwd gives it for GQE_SLOTS_WEIGHTED): dp_sel = dw;
+ *   0 on the others; dz = p (dp - p . dp); dW_r = dz^T x; db_r = sum_t dz;
+ *   dx = dz W_r. Any other weights value returns GQE_ERR_UNSUPPORTED.
  * aux_coef > 0 adds the load-balancing loss the review says training uses
  * (its formula is not given; reading: per group router, averaged over the
  * groups) L = aux_coef * M * mean_g sum_m f_{g,m} P_{g,m}, f the share of the
@@ -286,7 +317,7 @@ size_t gqe_route_bwd_workspace_bytes(const gqe_dims* dims);
  * aux_coef must be finite and >= 0 (GQE_ERR_INVALID_ARG). */
 int gqe_route_bwd(const gqe_dims* dims, const void* x, const void* w_router,
                   const float* logits, const int32_t* topk_idx, const float* dw,
-                  float aux_coef, float* dz_or_null, void* dx, float* dw_router,
+                  int32_t weights, float aux_coef, float* dz_or_null, void* dx, float* dw_router,
                   float* db_router, float* aux_loss_or_null, void* workspace,
                   size_t ws_bytes, void* stream);
 

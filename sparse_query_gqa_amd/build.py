@@ -27,7 +27,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-variable", "-Wno-unused-but-set-variable",
-    "-fno-honor-nans",  # no NaN canonicalisation around min/max; infinities still honoured
+    # device code only: no NaN canonicalisation around min/max (infinities are
+    # still honoured); the host code keeps IEEE NaN semantics for its argument checks
+    "-Xarch_device", "-fno-honor-nans",
     "-I", os.path.join(ROOT, "include"),
 ]
 

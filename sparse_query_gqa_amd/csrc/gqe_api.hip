@@ -106,7 +106,7 @@ struct OutProjBwdLayout {
 };
 OutProjBwdLayout out_proj_bwd_layout(const gqe_dims* d, int32_t mode, int64_t T) {
   OutProjBwdLayout L{};
-  L.Kd = d->G * d->k * d->d + (mode == GQE_SLOTS_FULL ? d->d : 0) + d->d;
+  L.Kd = d->G * d->k * d->d + (mode == GQE_SLOTS_FULL ? 2 * d->d : 0);
   const int tiles = ((L.Kd + 127) / 128) * ((d->D + 127) / 128);
   gemm_split(T, tiles, L.nsplit, L.kchunk);
   const size_t esz = d->dtype == GQE_BF16 ? 2 : 4;
@@ -179,13 +179,14 @@ size_t gqe_route_workspace_bytes(const gqe_dims* d) {
 }
 
 int gqe_route(const gqe_dims* d, const void* x, const void* w_router, const float* b_router,
-              float* logits, int32_t* topk_idx, float* topk_w, int32_t* list_off,
-              int32_t* list_tok, void* workspace, size_t ws_bytes, void* stream) {
+              float* logits, int32_t* topk_idx, float* topk_w, float* topk_p,
+              int32_t* list_off, int32_t* list_tok, void* workspace, size_t ws_bytes,
+              void* stream) {
   int st = check_dims(d);
   if (st) return st;
   if (!x || !w_router || !topk_idx || !topk_w) return GQE_ERR_INVALID_ARG;
   if ((list_off == nullptr) != (list_tok == nullptr)) return GQE_ERR_INVALID_ARG;
-  const void* ptrs[] = {x, w_router, b_router, logits, topk_idx, topk_w, list_off, list_tok};
+  const void* ptrs[] = {x, w_router, b_router, logits, topk_idx, topk_w, topk_p, list_off, list_tok};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return GQE_ERR_ALIGNMENT;
   const bool lists = list_off != nullptr;
@@ -197,7 +198,7 @@ int gqe_route(const gqe_dims* d, const void* x, const void* w_router, const floa
   const int64_t T = (int64_t)d->B * d->S;
   if (T == 0) return GQE_OK;
   hipStream_t s = (hipStream_t)stream;
-  RouteParams rp{x, w_router, b_router, logits, topk_idx, topk_w, T, d->D, d->G, d->N / d->G, d->k};
+  RouteParams rp{x, w_router, b_router, logits, topk_idx, topk_w, topk_p, T, d->D, d->G, d->N / d->G, d->k};
   if (trace_on())
     fprintf(stderr, "[gqe] route T=%lld D=%d G=%d M=%d k=%d lists=%d\n", (long long)T, d->D, d->G,
             d->N / d->G, d->k, (int)lists);
@@ -351,18 +352,22 @@ static int out_proj_mode(const gqe_dims* d, int32_t mode, int64_t T, const void*
   if (T < 0) return GQE_ERR_INVALID_ARG;
   if (mode != GQE_SLOTS_FULL && mode != GQE_SLOTS_HARD && mode != GQE_SLOTS_WEIGHTED)
     return GQE_ERR_UNSUPPORTED;
-  if (!o_routed || !topk_w || !o_shared || !w_o || !y) return GQE_ERR_INVALID_ARG;
+  // the ablation layouts read no shared output, the hard one no weights
+  const bool full = mode == GQE_SLOTS_FULL;
+  if (!o_routed || (!topk_w && mode != GQE_SLOTS_HARD) || (!o_shared && full) || !w_o || !y)
+    return GQE_ERR_INVALID_ARG;
   const void* ptrs[] = {o_routed, topk_w, o_shared, w_o, y};
   for (const void* p : ptrs)
-    if (!aligned16(p)) return GQE_ERR_ALIGNMENT;
+    if (p && !aligned16(p)) return GQE_ERR_ALIGNMENT;
   if ((T + 127) / 128 > (int64_t)UINT32_MAX) return GQE_ERR_UNSUPPORTED;
   if (T == 0) return GQE_OK;
   OutProjParams op{o_routed, topk_w, o_shared, w_o, y, T, d->G * d->k, d->d, d->D};
-  op.nob = mode == GQE_SLOTS_FULL ? d->d : 0;
+  op.nob = full ? d->d : 0;
+  op.nsh = full ? d->d : 0;
   op.weighted = mode == GQE_SLOTS_WEIGHTED ? 1 : 0;
   if (trace_on())
     fprintf(stderr, "[gqe] out_proj mode=%d T=%lld K=%d D=%d\n", mode, (long long)T,
-            d->G * d->k * d->d + op.nob + d->d, d->D);
+            d->G * d->k * d->d + op.nob + op.nsh, d->D);
   return hip_status(launch_out_proj(op, d->dtype == GQE_BF16, (hipStream_t)stream));
 }
 
@@ -437,11 +442,13 @@ int gqe_out_proj_bwd(const gqe_dims* d, int32_t mode, int64_t T, const void* o_r
   if (T < 0) return GQE_ERR_INVALID_ARG;
   if (mode != GQE_SLOTS_FULL && mode != GQE_SLOTS_HARD && mode != GQE_SLOTS_WEIGHTED)
     return GQE_ERR_UNSUPPORTED;
-  if (!o_routed || !topk_w || !o_shared || !w_o || !dy || !do_routed || !dw || !do_shared || !dw_o)
+  const bool full = mode == GQE_SLOTS_FULL;
+  if (!o_routed || (!topk_w && mode != GQE_SLOTS_HARD) || (!o_shared && full) || !w_o || !dy ||
+      !do_routed || !dw || (!do_shared && full) || !dw_o)
     return GQE_ERR_INVALID_ARG;
   const void* ptrs[] = {o_routed, topk_w, o_shared, w_o, dy, do_routed, dw, do_shared, dw_o};
   for (const void* p : ptrs)
-    if (!aligned16(p)) return GQE_ERR_ALIGNMENT;
+    if (p && !aligned16(p)) return GQE_ERR_ALIGNMENT;
   if (T > (int64_t)INT32_MAX) return GQE_ERR_UNSUPPORTED;
   if (T == 0) return GQE_OK;
   const OutProjBwdLayout L = out_proj_bwd_layout(d, mode, T);
@@ -466,7 +473,8 @@ int gqe_out_proj_bwd(const gqe_dims* d, int32_t mode, int64_t T, const void* o_r
   bp.d = d->d;
   bp.Dout = d->D;
   bp.Kd = L.Kd;
-  bp.nob = mode == GQE_SLOTS_FULL ? d->d : 0;
+  bp.nob = full ? d->d : 0;
+  bp.nsh = full ? d->d : 0;
   bp.weighted = mode == GQE_SLOTS_WEIGHTED ? 1 : 0;
   bp.nsplit = L.nsplit;
   bp.kchunk = L.kchunk;
@@ -482,13 +490,14 @@ size_t gqe_route_bwd_workspace_bytes(const gqe_dims* d) {
 }
 
 int gqe_route_bwd(const gqe_dims* d, const void* x, const void* w_router, const float* logits,
-                  const int32_t* topk_idx, const float* dw, float aux_coef, float* dz_or_null,
-                  void* dx, float* dw_router, float* db_router, float* aux_loss_or_null,
-                  void* workspace, size_t ws_bytes, void* stream) {
+                  const int32_t* topk_idx, const float* dw, int32_t weights, float aux_coef,
+                  float* dz_or_null, void* dx, float* dw_router, float* db_router,
+                  float* aux_loss_or_null, void* workspace, size_t ws_bytes, void* stream) {
   int st = check_dims(d);
   if (st) return st;
   if (!x || !w_router || !logits || !topk_idx || !dw || !dx || !dw_router || !db_router)
     return GQE_ERR_INVALID_ARG;
+  if (weights != GQE_WEIGHTS_RENORM && weights != GQE_WEIGHTS_PROB) return GQE_ERR_UNSUPPORTED;
   if (!(aux_coef >= 0.f) || aux_coef > 1e30f) return GQE_ERR_INVALID_ARG;  // rejects NaN too
   const void* ptrs[] = {x, w_router, logits, topk_idx, dw, dz_or_null, dx, dw_router, db_router,
                         aux_loss_or_null};
@@ -517,6 +526,7 @@ int gqe_route_bwd(const gqe_dims* d, const void* x, const void* w_router, const 
   rp.aux_loss = aux_loss_or_null;
   rp.part = (float*)(ws + L.part);
   rp.aux_coef = aux_coef;
+  rp.wprob = weights == GQE_WEIGHTS_PROB ? 1 : 0;
   rp.T = T;
   rp.D = d->D;
   rp.G = d->G;

@@ -28,6 +28,7 @@ struct RouteParams {
   float* logits;         // [T, G, M] or null
   int32_t* topk_idx;     // [T, G, k]
   float* topk_w;         // [T, G, k]
+  float* topk_p;         // [T, G, k] or null: p of the selected experts
   int64_t T;
   int D, G, M, k;
 };
@@ -86,7 +87,7 @@ struct OutProjBwdParams {
   void* a;                // workspace [T, Kd] dtype: the slot vectors
   float* part;            // workspace [nsplit, Kd, Dout] fp32 (nsplit > 1)
   int64_t T;
-  int Gk, d, Dout, Kd, nob, weighted, nsplit, kchunk;
+  int Gk, d, Dout, Kd, nob, nsh, weighted, nsplit, kchunk;
 };
 
 // Router backward.
@@ -107,6 +108,7 @@ struct RouteBwdParams {
   float* aux_loss;        // [1] out or null
   float* part;            // workspace [nsplit, GM, D] (nsplit > 1)
   float aux_coef;
+  int wprob;              // 1: dw is the gradient of the selected p, 0: of the renormalised w
   int64_t T;
   int D, G, M, K, GMp, nchunk, nsplit, kchunk;
 };
@@ -139,9 +141,10 @@ struct OutProjParams {
   void* y;                // [T, Dout]
   int64_t T;
   int Gk, d, Dout;
-  // slot layout: [hard slots | obar (nob = d columns, or 0) | shared]; with
-  // `weighted` each hard slot is scaled by its renormalised weight
-  int nob, weighted;
+  // slot layout: [hard slots | obar (nob = d columns, or 0) | shared (nsh =
+  // d columns, or 0)]; with `weighted` each hard slot is scaled by its weight
+  // in w (the router probability p in the weighted-concatenation layout)
+  int nob, nsh, weighted;
 };
 
 struct ProjParams {

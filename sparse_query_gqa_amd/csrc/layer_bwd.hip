@@ -5,13 +5,15 @@
 // vector, dW_O = A^T dy and dA = dy W_O^T. dA splits into the hard slots,
 // the obar slot and the shared slot; obar feeds back into every hard slot
 // (w * dobar) and into the routing weights (dw = o . dobar), which is the
-// path that gives the router a gradient. The ablation layouts ([O, s] and
-// [w * O, s], section 四) drop obar; the weighted one scales each hard
-// slot's gradient by w and gives dw = o . dslot.
+// path that gives the router a gradient. The ablation layouts (A = O and
+// A = p * O, section 四, Table 2) hold the hard slots only; the weighted one
+// scales each hard slot's gradient by its weight p and gives dp = o . dslot,
+// and in both the shared head's gradient is zero.
 //
 // Router: p = softmax(z) per group, w = p_sel / sum p_sel on the selected
 // experts (the renormalised weight). dp_sel = (dw - sum dw w) / sum p_sel,
-// 0 on the others; the balance loss (coef * M * mean_g sum_m f P, f the share
+// 0 on the others, or dp_sel = dw when the weights were the selected p
+// themselves (the weighted-concatenation layout); the balance loss (coef * M * mean_g sum_m f P, f the share
 // of selections, P the mean probability; section 二 names the standard MoE
 // balance loss) adds coef * M * f / (T * G) to dp of every expert;
 // dz = p (dp - p . dp); dW_r = dz^T x, db_r = sum_t dz, dx = dz W_r.
@@ -275,11 +277,12 @@ __global__ __launch_bounds__(256) void slot_bwd_kernel(OutProjBwdParams p) {
   const int j = (int)(g - t * per);
   const float* da = p.da + t * p.Kd;
   const int hard = p.Gk * p.d;
-  if (j == p.Gk) {
-    st4<T>(p.do_s, t * p.d + e, *(const f32x4*)(da + hard + p.nob + e));
+  if (j == p.Gk) {  // the shared slot; without one (ablation layouts) its gradient is 0
+    if (p.do_s)
+      st4<T>(p.do_s, t * p.d + e, p.nsh ? *(const f32x4*)(da + hard + p.nob + e) : f32x4{0.f, 0.f, 0.f, 0.f});
     return;
   }
-  const float w = p.w[t * p.Gk + j];
+  const float w = (p.nob || p.weighted) ? p.w[t * p.Gk + j] : 0.f;
   const f32x4 o = ld4<T>(p.o_r, (t * p.Gk + j) * p.d + e);
   const f32x4 dslot = *(const f32x4*)(da + j * p.d + e);
   f32x4 gr;
@@ -288,10 +291,10 @@ __global__ __launch_bounds__(256) void slot_bwd_kernel(OutProjBwdParams p) {
     const f32x4 dob = *(const f32x4*)(da + hard + e);
     gr = dslot + w * dob;
     for (int i = 0; i < 4; ++i) dwacc = fmaf(o[i], dob[i], dwacc);
-  } else if (p.weighted) {  // [w O, s]
+  } else if (p.weighted) {  // [p O]
     gr = w * dslot;
     for (int i = 0; i < 4; ++i) dwacc = fmaf(o[i], dslot[i], dwacc);
-  } else {  // [O, s]
+  } else {  // [O]
     gr = dslot;
   }
   st4<T>(p.do_r, (t * p.Gk + j) * p.d + e, gr);
@@ -405,8 +408,8 @@ __global__ __launch_bounds__(256) void count_kernel(RouteBwdParams p) {
     if (h[i]) atomicAdd(&p.counts[i], h[i]);
 }
 
-// One thread per (token, group): dz of the renormalised weights (and of the
-// balance loss).
+// One thread per (token, group): dz of the renormalised weights or of the
+// selected probabilities (and of the balance loss).
 template <typename T>
 __global__ __launch_bounds__(256) void dz_kernel(RouteBwdParams p) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -434,7 +437,7 @@ __global__ __launch_bounds__(256) void dz_kernel(RouteBwdParams p) {
   for (int j = 0; j < p.K; ++j) ps += pr[sel[j]];
   float dww = 0.f;
   for (int j = 0; j < p.K; ++j) dww = fmaf(dw[j], pr[sel[j]] / ps, dww);
-  for (int j = 0; j < p.K; ++j) dp[sel[j]] = (dw[j] - dww) / ps;
+  for (int j = 0; j < p.K; ++j) dp[sel[j]] = p.wprob ? dw[j] : (dw[j] - dww) / ps;
   if (p.aux_coef != 0.f) {
     const float c = p.aux_coef * p.M / ((float)p.T * p.G) / ((float)p.T * p.K);
     for (int m = 0; m < p.M; ++m) dp[m] += c * (float)p.counts[g * p.M + m];

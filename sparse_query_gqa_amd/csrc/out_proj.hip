@@ -9,10 +9,12 @@
 // columns [G*k*d, G*k*d + d) are obar computed in fp32 from the G*k stored
 // slots and the fp32 weights; the last d columns are o_shared[t].
 //
-// Two further slot layouts serve the ablation variants (GQE review, section
-// 四, Table 2): hard slots only, [O_t, s_t], and weighted concatenation,
-// [w * O_t, s_t], where each hard slot is scaled by its renormalised weight;
-// neither has the obar slot, and W_O has (G*k+1)*d rows.
+// Two further slot layouts serve the ablation rows of GQE review, section
+// 四, Table 2, which keep the hard slots only: A_t = O_t (hard
+// concatenation), and A_t = p * O_t (weighted concatenation without the
+// renormalised slot), each hard slot scaled by its router probability p,
+// which the caller passes in place of w. Neither has the obar slot or the
+// shared head, and W_O has G*k*d rows.
 //
 // Two bf16 kernels: a pipelined GEMM for T >= 256 (below) and, for fewer
 // tokens, a plain 128x128-tile kernel: four wavefronts of 64x64 each on
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(256) void out_proj_bf16_kernel(OutProjParams p) {
   const int64_t m0 = (int64_t)blockIdx.x * kBM;
   const int n0 = blockIdx.y * kBN;
   const int hard = p.Gk * p.d;
-  const int Kd = hard + p.nob + p.d;
+  const int Kd = hard + p.nob + p.nsh;
   const __bf16* orr = (const __bf16*)p.o_r;
   const __bf16* os = (const __bf16*)p.o_s;
   const __bf16* wo = (const __bf16*)p.w_o;
@@ -170,7 +172,7 @@ constexpr int kGN = 256;      // output columns per tile
 constexpr int kGK = 32;       // k per step
 constexpr int kGStages = 4;
 
-template <int DH, int MODE>  // MODE: 0 [O, obar, s], 1 [O, s], 2 [w*O, s]
+template <int DH, int MODE>  // MODE: 0 [O, obar, s], 1 [O], 2 [p*O]
 __global__ __launch_bounds__(512, 1) void out_proj_gemm_kernel(OutProjParams p) {
   constexpr int AB = kGT * kGK * 2;  // A tile: 128 token rows x 64 bytes
   constexpr int BB = kGK * kGN * 2;  // W_O tile: 32 k rows x 512 bytes
@@ -188,8 +190,9 @@ __global__ __launch_bounds__(512, 1) void out_proj_gemm_kernel(OutProjParams p) 
   const int n0 = blockIdx.y * kGN;
   const int hard = p.Gk * DH;
   constexpr int nob = MODE == 0 ? DH : 0;
+  constexpr int nsh = MODE == 0 ? DH : 0;
   constexpr bool weighted = MODE == 2;
-  const int nk = (hard + nob + DH) / kGK;
+  const int nk = (hard + nob + nsh) / kGK;
   const __bf16* orr = (const __bf16*)p.o_r;
   const __bf16* os = (const __bf16*)p.o_s;
   const __bf16* wo = (const __bf16*)p.w_o;
@@ -386,7 +389,7 @@ __global__ __launch_bounds__(512, 1) void out_proj_small_kernel(OutProjParams p)
   const int n0 = slice * 16;
   const int hard = p.Gk * DH;
   const int nob = p.nob;
-  const int nsteps = (hard + nob + DH) / 32;
+  const int nsteps = (hard + nob + p.nsh) / 32;
   const int s_lo = wave * nsteps / 8, s_hi = (wave + 1) * nsteps / 8;
   const __bf16* orr = (const __bf16*)p.o_r;
   const __bf16* os = (const __bf16*)p.o_s;
@@ -474,7 +477,7 @@ __global__ __launch_bounds__(256) void out_proj_f32_kernel(OutProjParams p) {
   const int n = blockIdx.y * 64 + (threadIdx.x & 63);
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= p.Dout || t >= p.T) return;
-  const int Kd = p.Gk * p.d + p.nob + p.d;
+  const int Kd = p.Gk * p.d + p.nob + p.nsh;
   const float* wo = (const float*)p.w_o;
   float acc = 0.f;
   for (int col = 0; col < Kd; ++col)

@@ -26,6 +26,8 @@
 // 64 rows per wavefront for d <= 64 and 32 rows per wavefront for d = 128,
 // both software-pipelined so that MFMAs and the softmax of neighbouring
 // 32x32 score tiles overlap.
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "prefill_tiles.h"
@@ -858,6 +860,17 @@ static int device_cus() {
   return cus[dev];
 }
 
+// Form of the d <= 64 kernel: GQE_PREFILL_FORM=plain or split forces one
+// (both compute the same outputs; tests run every case through both), any
+// other value or none picks by tile count. Read at every launch.
+static int prefill_form_override() {
+  const char* f = getenv("GQE_PREFILL_FORM");
+  if (!f) return -1;
+  if (!strcmp(f, "plain")) return 0;
+  if (!strcmp(f, "split")) return 1;
+  return -1;
+}
+
 template <int D>
 static void launch_prefill_bf16(const PrefillParams& p, hipStream_t s) {
   constexpr int TR = 256;  // rows per tile (workgroup)
@@ -869,7 +882,8 @@ static void launch_prefill_bf16(const PrefillParams& p, hipStream_t s) {
     // longest tile sets the time, and the key-split form halves it (measured:
     // 11-21% faster with 72-288 tiles, 25% slower with 576 tiles on 256 CUs).
     const int64_t ntiles = (int64_t)p.B * ((int64_t)p.G * tiles_r + tiles_s);
-    if (ntiles < 2 * (int64_t)device_cus())
+    const int forced = prefill_form_override();
+    if (forced == 1 || (forced < 0 && ntiles < 2 * (int64_t)device_cus()))
       hipLaunchKernelGGL((prefill_qp_kernel<D, true>), dim3(nblk), dim3(512), 0, s, p, tiles_r, tiles_s);
     else
       hipLaunchKernelGGL((prefill_qp_kernel<D, false>), dim3(nblk), dim3(256), 0, s, p, tiles_r, tiles_s);

@@ -21,7 +21,8 @@ constexpr int kRouteBlockTok = 64;  // tokens per workgroup (bf16)
 // Selection epilogue: z for kRouteTok tokens in LDS ([tok][G*M], bias
 // included). One thread per (token, group): TopK by repeated first-maximum
 // scans (strictly greater wins, so ties keep the lower index), indices
-// written ascending, weights exp(z_m - zmax) / sum over the selected set.
+// written ascending, weights exp(z_m - zmax) / sum over the selected set and,
+// when asked for, the probabilities exp(z_m - zmax) / sum over all M.
 __device__ void route_select_store(const float* zs, int ntok, int64_t tok0,
                                    const RouteParams& p) {
   const int GM = p.G * p.M;
@@ -44,15 +45,20 @@ __device__ void route_select_store(const float* zs, int ntok, int64_t tok0,
       chosen |= 1u << best;
       if (r == 0) zmax = bv;  // the first pick is the maximum
     }
-    float den = 0.f;
-    for (int m = 0; m < p.M; ++m)
-      if ((chosen >> m) & 1u) den += expf(z[m] - zmax);
+    float den = 0.f, all = 0.f;
+    for (int m = 0; m < p.M; ++m) {
+      const float e = expf(z[m] - zmax);
+      all += e;
+      if ((chosen >> m) & 1u) den += e;
+    }
     int j = 0;
     const int64_t o = (tok * p.G + g) * p.k;
     for (int m = 0; m < p.M; ++m) {
       if ((chosen >> m) & 1u) {
+        const float e = expf(z[m] - zmax);
         p.topk_idx[o + j] = m;
-        p.topk_w[o + j] = expf(z[m] - zmax) / den;
+        p.topk_w[o + j] = e / den;
+        if (p.topk_p) p.topk_p[o + j] = e / all;
         ++j;
       }
     }

@@ -28,6 +28,8 @@ GQE_F32 = 1
 GQE_SLOTS_FULL = 0
 GQE_SLOTS_HARD = 1
 GQE_SLOTS_WEIGHTED = 2
+GQE_WEIGHTS_RENORM = 0
+GQE_WEIGHTS_PROB = 1
 
 EXPORTED = [
     "gqe_status_string", "gqe_version", "gqe_route_workspace_bytes", "gqe_route",
@@ -84,7 +86,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gqe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "gqe_version": (ctypes.c_int, []),
         "gqe_route_workspace_bytes": (SZ, [D]),
-        "gqe_route": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "gqe_route": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "gqe_attn_prefill": (ctypes.c_int, [D, P, P, P, P, P, P, P]),
         "gqe_decode_workspace_bytes": (SZ, [D, I32]),
         "gqe_attn_decode": (ctypes.c_int, [D, I32, P, P, P, P, P, P, P, P, SZ, P]),
@@ -99,7 +101,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gqe_out_proj_bwd_workspace_bytes": (SZ, [D, I32, I64]),
         "gqe_out_proj_bwd": (ctypes.c_int, [D, I32, I64, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "gqe_route_bwd_workspace_bytes": (SZ, [D]),
-        "gqe_route_bwd": (ctypes.c_int, [D, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, SZ, P]),
+        "gqe_route_bwd": (ctypes.c_int, [D, P, P, P, P, P, I32, ctypes.c_float, P, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -154,7 +156,7 @@ def gqe_decode_workspace_bytes(dims: gqe_dims, q_len: int) -> int:
 
 
 def gqe_route(dims, x, w_router, b_router, logits, topk_idx, topk_w, list_off, list_tok,
-              workspace, stream=None):
+              workspace, stream=None, topk_p=None):
     T, GM, G, k, dt = dims.B * dims.S, dims.N, dims.G, dims.k, dims.torch_dtype
     _check(x, "x", (T, dims.D), dt)
     _check(w_router, "w_router", (GM, dims.D), dt)
@@ -162,12 +164,14 @@ def gqe_route(dims, x, w_router, b_router, logits, topk_idx, topk_w, list_off, l
     _check(logits, "logits", (T, G, dims.M), torch.float32, optional=True)
     _check(topk_idx, "topk_idx", (T, G, k), torch.int32)
     _check(topk_w, "topk_w", (T, G, k), torch.float32)
+    _check(topk_p, "topk_p", (T, G, k), torch.float32, optional=True)
     _check(list_off, "list_off", (dims.B, G, dims.M + 1), torch.int32, optional=True)
     _check(list_tok, "list_tok", (dims.B, G, k * dims.S), torch.int32, optional=True)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load_library().gqe_route(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(b_router),
-                                  _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(list_off),
-                                  _ptr(list_tok), _ptr(workspace), ws_bytes, _stream(stream))
+                                  _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(topk_p),
+                                  _ptr(list_off), _ptr(list_tok), _ptr(workspace), ws_bytes,
+                                  _stream(stream))
     _raise(st, "gqe_route")
 
 
@@ -226,7 +230,8 @@ def gqe_attn_prefill_bwd(dims, q, k, v, topk_idx, o_routed, o_shared, lse_routed
 
 
 def _slot_rows(dims, mode) -> int:
-    return (dims.G * dims.k + (2 if mode == GQE_SLOTS_FULL else 1)) * dims.d
+    """W_O rows: [O, obar, s] for the full layout, the hard slots alone for the ablation layouts."""
+    return (dims.G * dims.k + (2 if mode == GQE_SLOTS_FULL else 0)) * dims.d
 
 
 def _nbytes(t):
@@ -237,19 +242,20 @@ def gqe_out_proj_bwd_workspace_bytes(dims, mode, T) -> int:
     return load_library().gqe_out_proj_bwd_workspace_bytes(ctypes.byref(dims), int(mode), int(T))
 
 
-def gqe_out_proj_bwd(dims, mode, T, o_routed, topk_w, o_shared, w_o, dy, do_routed, dw, do_shared, dw_o,
+def gqe_out_proj_bwd(dims, mode, T, o_routed, slot_w, o_shared, w_o, dy, do_routed, dw, do_shared, dw_o,
                      workspace, stream=None):
     G, kk, d, D, dt = dims.G, dims.k, dims.d, dims.D, dims.torch_dtype
+    full = mode == GQE_SLOTS_FULL
     _check(o_routed, "o_routed", (T, G, kk, d), dt)
-    _check(topk_w, "topk_w", (T, G, kk), torch.float32)
-    _check(o_shared, "o_shared", (T, d), dt)
+    _check(slot_w, "slot_w", (T, G, kk), torch.float32, optional=mode == GQE_SLOTS_HARD)
+    _check(o_shared, "o_shared", (T, d), dt, optional=not full)
     _check(w_o, "w_o", (_slot_rows(dims, mode), D), dt)
     _check(dy, "dy", (T, D), dt)
     _check(do_routed, "do_routed", (T, G, kk, d), dt)
     _check(dw, "dw", (T, G, kk), torch.float32)
-    _check(do_shared, "do_shared", (T, d), dt)
+    _check(do_shared, "do_shared", (T, d), dt, optional=not full)
     _check(dw_o, "dw_o", (_slot_rows(dims, mode), D), torch.float32)
-    st = load_library().gqe_out_proj_bwd(ctypes.byref(dims), int(mode), int(T), _ptr(o_routed), _ptr(topk_w),
+    st = load_library().gqe_out_proj_bwd(ctypes.byref(dims), int(mode), int(T), _ptr(o_routed), _ptr(slot_w),
                                          _ptr(o_shared), _ptr(w_o), _ptr(dy), _ptr(do_routed), _ptr(dw),
                                          _ptr(do_shared), _ptr(dw_o), _ptr(workspace), _nbytes(workspace),
                                          _stream(stream))
@@ -261,7 +267,7 @@ def gqe_route_bwd_workspace_bytes(dims) -> int:
 
 
 def gqe_route_bwd(dims, x, w_router, logits, topk_idx, dw, aux_coef, dz, dx, dw_router, db_router, aux_loss,
-                  workspace, stream=None):
+                  workspace, stream=None, weights=GQE_WEIGHTS_RENORM):
     T, D, G, M, kk, dt = dims.B * dims.S, dims.D, dims.G, dims.M, dims.k, dims.torch_dtype
     _check(x, "x", (T, D), dt)
     _check(w_router, "w_router", (G * M, D), dt)
@@ -274,7 +280,7 @@ def gqe_route_bwd(dims, x, w_router, logits, topk_idx, dw, aux_coef, dz, dx, dw_
     _check(db_router, "db_router", (G * M,), torch.float32)
     _check(aux_loss, "aux_loss", (1,), torch.float32, optional=True)
     st = load_library().gqe_route_bwd(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(logits), _ptr(topk_idx),
-                                      _ptr(dw), float(aux_coef), _ptr(dz), _ptr(dx), _ptr(dw_router),
+                                      _ptr(dw), int(weights), float(aux_coef), _ptr(dz), _ptr(dx), _ptr(dw_router),
                                       _ptr(db_router), _ptr(aux_loss), _ptr(workspace), _nbytes(workspace),
                                       _stream(stream))
     _raise(st, "gqe_route_bwd")
@@ -320,14 +326,16 @@ def gqe_attn_decode_paged(dims, q_len, q, k_pages, v_pages, block_table, page_si
     _raise(st, "gqe_attn_decode_paged")
 
 
-def gqe_out_proj_variant(dims, mode, T, o_routed, topk_w, o_shared, w_o, y, stream=None):
+def gqe_out_proj_variant(dims, mode, T, o_routed, slot_w, o_shared, w_o, y, stream=None):
+    """slot_w: topk_w for the full layout, topk_p for the weighted one, None allowed for the hard one;
+    o_shared: read by the full layout only (None allowed otherwise)."""
     G, kk, d, D, dt = dims.G, dims.k, dims.d, dims.D, dims.torch_dtype
     _check(o_routed, "o_routed", (T, G, kk, d), dt)
-    _check(topk_w, "topk_w", (T, G, kk), torch.float32)
-    _check(o_shared, "o_shared", (T, d), dt)
-    _check(w_o, "w_o", ((G * kk + (2 if mode == GQE_SLOTS_FULL else 1)) * d, D), dt)
+    _check(slot_w, "slot_w", (T, G, kk), torch.float32, optional=mode == GQE_SLOTS_HARD)
+    _check(o_shared, "o_shared", (T, d), dt, optional=mode != GQE_SLOTS_FULL)
+    _check(w_o, "w_o", (_slot_rows(dims, mode), D), dt)
     _check(y, "y", (T, D), dt)
-    st = load_library().gqe_out_proj_variant(ctypes.byref(dims), mode, T, _ptr(o_routed), _ptr(topk_w),
+    st = load_library().gqe_out_proj_variant(ctypes.byref(dims), mode, T, _ptr(o_routed), _ptr(slot_w),
                                              _ptr(o_shared), _ptr(w_o), _ptr(y), _stream(stream))
     _raise(st, "gqe_out_proj_variant")
 
@@ -381,13 +389,14 @@ def gqe_qkv_proj_decode(dims, q_len, x, w_q, w_k, w_v, topk_idx, kv_len, q, k_ca
 # Allocating wrappers
 # --------------------------------------------------------------------------
 
-def route(dims, x, w_router, b_router=None, want_logits=True, want_lists=True, stream=None):
+def route(dims, x, w_router, b_router=None, want_logits=True, want_lists=True, stream=None, want_p=False):
     dev = x.device
     T, G, M, k = dims.B * dims.S, dims.G, dims.M, dims.k
     out = dict(
         logits=torch.empty((T, G, M), dtype=torch.float32, device=dev) if want_logits else None,
         topk_idx=torch.empty((T, G, k), dtype=torch.int32, device=dev),
         topk_w=torch.empty((T, G, k), dtype=torch.float32, device=dev),
+        topk_p=torch.empty((T, G, k), dtype=torch.float32, device=dev) if want_p else None,
         list_off=torch.empty((dims.B, G, M + 1), dtype=torch.int32, device=dev) if want_lists else None,
         list_tok=torch.empty((dims.B, G, k * dims.S), dtype=torch.int32, device=dev) if want_lists else None,
     )
@@ -396,7 +405,7 @@ def route(dims, x, w_router, b_router=None, want_logits=True, want_lists=True, s
         nbytes = gqe_route_workspace_bytes(dims)
         ws = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=dev)
     gqe_route(dims, x, w_router, b_router, out["logits"], out["topk_idx"], out["topk_w"],
-              out["list_off"], out["list_tok"], ws, stream)
+              out["list_off"], out["list_tok"], ws, stream, topk_p=out["topk_p"])
     return out
 
 
@@ -434,23 +443,25 @@ def _workspace(nbytes, device):
     return torch.empty((max(int(nbytes), 16),), dtype=torch.uint8, device=device)
 
 
-def out_proj_bwd(dims, T, o_routed, topk_w, o_shared, w_o, dy, mode=GQE_SLOTS_FULL, stream=None):
-    """Output-projection backward: (do_r [T,G,k,d], dw [T,G,k], do_s [T,d], dw_o fp32)."""
+def out_proj_bwd(dims, T, o_routed, slot_w, o_shared, w_o, dy, mode=GQE_SLOTS_FULL, stream=None):
+    """Output-projection backward: (do_r [T,G,k,d], dw [T,G,k], do_s [T,d], dw_o fp32).
+    slot_w and o_shared as for gqe_out_proj_variant; do_s is zero in the ablation layouts."""
     dev = dy.device
     o_routed = o_routed.reshape(T, dims.G, dims.k, dims.d)
-    topk_w = topk_w.reshape(T, dims.G, dims.k)
-    o_shared = o_shared.reshape(T, dims.d)
+    slot_w = None if slot_w is None else slot_w.reshape(T, dims.G, dims.k)
+    o_shared = None if o_shared is None else o_shared.reshape(T, dims.d)
     do_r = torch.empty_like(o_routed)
     dw = torch.empty((T, dims.G, dims.k), dtype=torch.float32, device=dev)
-    do_s = torch.empty_like(o_shared)
+    do_s = torch.empty((T, dims.d), dtype=o_routed.dtype, device=dev)
     dw_o = torch.empty(tuple(w_o.shape), dtype=torch.float32, device=dev)
     ws = _workspace(gqe_out_proj_bwd_workspace_bytes(dims, mode, T), dev)
-    gqe_out_proj_bwd(dims, mode, T, o_routed, topk_w, o_shared, w_o, dy, do_r, dw, do_s, dw_o, ws, stream)
+    gqe_out_proj_bwd(dims, mode, T, o_routed, slot_w, o_shared, w_o, dy, do_r, dw, do_s, dw_o, ws, stream)
     return do_r, dw, do_s, dw_o
 
 
-def route_bwd(dims, x, w_router, logits, topk_idx, dw, aux_coef=0.0, stream=None):
-    """Router backward: dict(dz, dx, dw_router, db_router, aux_loss)."""
+def route_bwd(dims, x, w_router, logits, topk_idx, dw, aux_coef=0.0, stream=None, weights=GQE_WEIGHTS_RENORM):
+    """Router backward: dict(dz, dx, dw_router, db_router, aux_loss). weights says whether dw is the
+    gradient of the renormalised weights (GQE_WEIGHTS_RENORM) or of the selected p (GQE_WEIGHTS_PROB)."""
     dev = x.device
     T, GM = dims.B * dims.S, dims.N
     out = dict(dz=torch.empty((T, dims.G, dims.M), dtype=torch.float32, device=dev), dx=torch.empty_like(x),
@@ -459,7 +470,7 @@ def route_bwd(dims, x, w_router, logits, topk_idx, dw, aux_coef=0.0, stream=None
                aux_loss=torch.zeros((1,), dtype=torch.float32, device=dev))
     ws = _workspace(gqe_route_bwd_workspace_bytes(dims), dev)
     gqe_route_bwd(dims, x, w_router, logits, topk_idx, dw, aux_coef, out["dz"], out["dx"], out["dw_router"],
-                  out["db_router"], out["aux_loss"], ws, stream)
+                  out["db_router"], out["aux_loss"], ws, stream, weights=weights)
     return out
 
 

@@ -54,11 +54,12 @@ def test_status_strings_and_version():
     assert lib.gqe_version() == 10000
 
 
-def route(lib, dims, x=A, w=A, b=None, logits=A, idx=A, wt=A, off=None, tok=None, ws=None, nws=0):
+def route(lib, dims, x=A, w=A, b=None, logits=A, idx=A, wt=A, off=None, tok=None, ws=None, nws=0, pr=None):
     return lib.gqe_route(ctypes.byref(dims), P(x), P(w), None if b is None else P(b),
                          None if logits is None else P(logits), None if idx is None else P(idx),
-                         None if wt is None else P(wt), None if off is None else P(off),
-                         None if tok is None else P(tok), None if ws is None else P(ws), nws, None)
+                         None if wt is None else P(wt), None if pr is None else P(pr),
+                         None if off is None else P(off), None if tok is None else P(tok),
+                         None if ws is None else P(ws), nws, None)
 
 
 def test_route_validation():
@@ -76,6 +77,8 @@ def test_route_validation():
     assert route(lib, _dims(), idx=None) == gqe.GQE_ERR_INVALID_ARG
     assert route(lib, _dims(), x=MIS) == gqe.GQE_ERR_ALIGNMENT
     assert route(lib, _dims(), logits=MIS) == gqe.GQE_ERR_ALIGNMENT
+    assert route(lib, _dims(), pr=MIS) == gqe.GQE_ERR_ALIGNMENT
+    assert route(lib, _dims(B=0), pr=A) == gqe.GQE_OK
     assert route(lib, _dims(), off=A) == gqe.GQE_ERR_INVALID_ARG     # off without tok
     need = lib.gqe_route_workspace_bytes(ctypes.byref(_dims()))
     assert need == 2 * 2 * 4 * 2 * 4  # B*G*M*ceil(S/64) int32
@@ -143,8 +146,9 @@ def test_out_proj_validation():
 def test_out_proj_variant_validation():
     lib = _lib()
 
-    def call(dims, mode, T=10, y=A):
-        return lib.gqe_out_proj_variant(ctypes.byref(dims), mode, T, P(A), P(A), P(A), P(A), P(y), None)
+    def call(dims, mode, T=10, y=A, sw=A, os_=A):
+        return lib.gqe_out_proj_variant(ctypes.byref(dims), mode, T, P(A), None if sw is None else P(sw),
+                                        None if os_ is None else P(os_), P(A), P(y), None)
 
     assert call(_dims(), 3) == gqe.GQE_ERR_UNSUPPORTED
     assert call(_dims(), -1) == gqe.GQE_ERR_UNSUPPORTED
@@ -152,6 +156,56 @@ def test_out_proj_variant_validation():
     assert call(_dims(), gqe.GQE_SLOTS_WEIGHTED, T=-1) == gqe.GQE_ERR_INVALID_ARG
     assert call(_dims(), gqe.GQE_SLOTS_WEIGHTED, y=MIS) == gqe.GQE_ERR_ALIGNMENT
     assert call(_dims(), gqe.GQE_SLOTS_HARD, T=0) == gqe.GQE_OK
+    # the ablation layouts read no shared output; the hard one reads no weights
+    assert call(_dims(), gqe.GQE_SLOTS_FULL, os_=None) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), gqe.GQE_SLOTS_FULL, sw=None) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), gqe.GQE_SLOTS_WEIGHTED, sw=None) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), gqe.GQE_SLOTS_WEIGHTED, sw=MIS, os_=None) == gqe.GQE_ERR_ALIGNMENT
+    assert call(_dims(), gqe.GQE_SLOTS_WEIGHTED, T=0, os_=None) == gqe.GQE_OK
+    assert call(_dims(), gqe.GQE_SLOTS_HARD, T=0, sw=None, os_=None) == gqe.GQE_OK
+
+
+def test_out_proj_bwd_validation():
+    lib = _lib()
+
+    def call(dims, mode, T=10, sw=A, os_=A, dos=A, ws=A, nbytes=1 << 40):
+        n = lambda v: None if v is None else P(v)  # noqa: E731
+        return lib.gqe_out_proj_bwd(ctypes.byref(dims), mode, T, P(A), n(sw), n(os_), P(A), P(A), P(A), P(A),
+                                    n(dos), P(A), n(ws), nbytes, None)
+
+    assert call(_dims(), 3) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(), gqe.GQE_SLOTS_FULL, T=-1) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), gqe.GQE_SLOTS_FULL, dos=None) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), gqe.GQE_SLOTS_FULL, os_=None) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), gqe.GQE_SLOTS_WEIGHTED, sw=None) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), gqe.GQE_SLOTS_FULL, ws=None) == gqe.GQE_ERR_WORKSPACE
+    assert call(_dims(), gqe.GQE_SLOTS_HARD, nbytes=16) == gqe.GQE_ERR_WORKSPACE
+    assert call(_dims(), gqe.GQE_SLOTS_WEIGHTED, ws=MIS, os_=None, dos=None) == gqe.GQE_ERR_ALIGNMENT
+    assert call(_dims(), gqe.GQE_SLOTS_HARD, T=0, sw=None, os_=None, dos=None) == gqe.GQE_OK
+    # workspace: fp32 dA and the slot vectors A over Kd columns, Kd = (G*k+2)*d for the
+    # full layout and G*k*d for the ablation layouts (T=16: one split, no partials)
+    r256 = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    d = _dims(B=1, S=16, D=64, N=8, G=2, k=2, d=64)
+    for mode, kd in ((gqe.GQE_SLOTS_FULL, 6 * 64), (gqe.GQE_SLOTS_HARD, 4 * 64), (gqe.GQE_SLOTS_WEIGHTED, 4 * 64)):
+        got = lib.gqe_out_proj_bwd_workspace_bytes(ctypes.byref(d), mode, 16)
+        assert got == r256(16 * kd * 4) + r256(16 * kd * 2), (mode, got)
+
+
+def test_route_bwd_validation():
+    lib = _lib()
+
+    def call(dims, weights=gqe.GQE_WEIGHTS_RENORM, aux=0.0, ws=A, dz=None):
+        return lib.gqe_route_bwd(ctypes.byref(dims), P(A), P(A), P(A), P(A), P(A), weights, aux,
+                                 None if dz is None else P(dz), P(A), P(A), P(A), None, P(ws), 1 << 40, None)
+
+    assert call(_dims(), weights=2) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(), weights=-1) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(), aux=float("nan")) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), aux=-1.0) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), aux=float("inf")) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(), dz=MIS) == gqe.GQE_ERR_ALIGNMENT
+    assert call(_dims(), ws=0) == gqe.GQE_ERR_WORKSPACE
+    assert call(_dims(B=0), weights=gqe.GQE_WEIGHTS_PROB, ws=0) == gqe.GQE_OK
 
 
 def test_qkv_proj_validation():
@@ -272,3 +326,6 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(4, 64)
     with pytest.raises(ValueError, match="device tensor"):
         gqe.gqe_route(dims, x, torch.zeros(4, 64), None, None, x, x, None, None, None)
+    with pytest.raises(ValueError, match="device tensor"):
+        gqe.gqe_out_proj_variant(dims, gqe.GQE_SLOTS_HARD, 4, torch.zeros(4, 2, 1, 32), None, None,
+                                 torch.zeros(64, 64), torch.zeros(4, 64))

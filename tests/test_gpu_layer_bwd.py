@@ -68,16 +68,25 @@ def test_out_proj_bwd(case, mode):
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
     O_r = _tensor(rng.standard_normal((T, G, k, d)), dt)
     wraw = rng.random((T, G, k)) + 0.1
-    w = torch.from_numpy((wraw / wraw.sum(-1, keepdims=True)).astype(np.float32))
+    # slot weights: renormalised w for the full layout, router probabilities
+    # (not summing to 1 over the selected set) for the weighted one, none for
+    # the hard one; the ablation layouts take no shared output
+    if mode == "full":
+        w = torch.from_numpy((wraw / wraw.sum(-1, keepdims=True)).astype(np.float32))
+    else:
+        w = torch.from_numpy((wraw / (wraw.sum(-1, keepdims=True) + 0.5)).astype(np.float32))
     O_s = _tensor(rng.standard_normal((T, d)), dt)
-    rows = (G * k + (2 if mode == "full" else 1)) * d
+    rows = (G * k + (2 if mode == "full" else 0)) * d
     W_O = _tensor(rng.standard_normal((rows, D)) * 0.05, dt)
     dy = _tensor(rng.standard_normal((T, D)), dt)
     dims = gqe.gqe_dims.make(1, T, D, G * max(k, 2), G, k, d, dtype)
-    do_r, dw, do_s, dw_o = gqe.out_proj_bwd(dims, T, O_r.to(DEV), w.to(DEV), O_s.to(DEV), W_O.to(DEV),
-                                            dy.to(DEV), mode=MODES[mode])
+    full = mode == "full"
+    do_r, dw, do_s, dw_o = gqe.out_proj_bwd(dims, T, O_r.to(DEV), None if mode == "hard" else w.to(DEV),
+                                            O_s.to(DEV) if full else None, W_O.to(DEV), dy.to(DEV),
+                                            mode=MODES[mode])
     torch.cuda.synchronize()
-    ref = oracle.out_proj_bwd(f64(O_r), f64(w), f64(O_s), f64(W_O), f64(dy), mode=mode)
+    ref = oracle.out_proj_bwd(f64(O_r), None if mode == "hard" else f64(w), f64(O_s) if full else None,
+                              f64(W_O), f64(dy), mode=mode)
     tol, rel = _tols(dtype)
     assert_close(do_r, ref[0], tol, "dO_r", rel)
     assert_close(dw, ref[1], 1e-4, "dw", 1e-4)
@@ -121,8 +130,12 @@ ROUTE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("wrt", ["w", "p"])
 @pytest.mark.parametrize("case", ROUTE_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_route_bwd(case):
+def test_route_bwd(case, wrt):
+    """dw is the gradient of the renormalised weights (wrt w, the full
+    layout) or of the selected probabilities (wrt p, the weighted
+    ablation layout)."""
     T, D, G, M, k, dtype, aux = case
     rng = np.random.default_rng([T, D, G, M, k])
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -133,11 +146,13 @@ def test_route_bwd(case):
     _, idx, _ = oracle.route_select(z.astype(np.float64), k)
     dw = rng.standard_normal((T, G, k)).astype(np.float32)
     dims = gqe.gqe_dims.make(1, T, D, G * M, G, k, 32, dtype)
+    kind = gqe.GQE_WEIGHTS_RENORM if wrt == "w" else gqe.GQE_WEIGHTS_PROB
     out = gqe.route_bwd(dims, x.to(DEV), w_r.to(DEV), torch.from_numpy(z).to(DEV),
-                        torch.from_numpy(idx.astype(np.int32)).to(DEV), torch.from_numpy(dw).to(DEV), aux_coef=aux)
+                        torch.from_numpy(idx.astype(np.int32)).to(DEV), torch.from_numpy(dw).to(DEV), aux_coef=aux,
+                        weights=kind)
     torch.cuda.synchronize()
     dz, dW_r, db_r, dx = oracle.route_bwd(f64(x), f64(w_r), z.astype(np.float64), idx, dw.astype(np.float64),
-                                          G, M, aux_coef=aux)
+                                          G, M, aux_coef=aux, wrt=wrt)
     tol, rel = _tols(dtype)
     assert_close(out["dz"], dz, 1e-4, "dz", 1e-4)
     assert_close(out["db_router"], db_r, 1e-4, "db_r", 1e-4)

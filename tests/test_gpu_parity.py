@@ -75,13 +75,14 @@ def test_route_exact_with_ties(dtype, B, S, D, G, M, k):
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     xt, wt = torch.from_numpy(x).to(tdt), torch.from_numpy(w).to(tdt)
     dims = gqe.gqe_dims.make(B, S, D, G * M, G, k, 32, dtype)
-    out = gqe.route(dims, xt.to(DEV), wt.to(DEV), torch.from_numpy(bias).to(DEV))
+    out = gqe.route(dims, xt.to(DEV), wt.to(DEV), torch.from_numpy(bias).to(DEV), want_p=True)
     torch.cuda.synchronize()
     z = oracle.route_logits(x, w, G, M, bias)
     p, idx, wref = oracle.route_select(z, k)
     assert np.array_equal(out["logits"].cpu().numpy().astype(np.float64), z), "logits not exact"
     assert np.array_equal(out["topk_idx"].cpu().numpy(), idx), "selection differs"
     assert np.max(np.abs(f64(out["topk_w"]) - wref)) <= 1e-6
+    assert np.max(np.abs(f64(out["topk_p"]) - oracle.slot_weights(p, idx, wref, "weighted"))) <= 1e-6
     if k == 1:
         assert torch.all(out["topk_w"] == 1.0)
     off, tok = oracle.build_lists(idx.reshape(B, S, G, k), M)
@@ -98,7 +99,7 @@ def _route_check(cfg, inp, out):
     x, w = f64(inp["x"]), f64(inp["w_r"])
     b = None if inp["b_r"] is None else f64(inp["b_r"])
     z = oracle.route_logits(x, w, G, M, b)
-    _, idx, wref = oracle.route_select(z, k)
+    p, idx, wref = oracle.route_select(z, k)
     zg = f64(out["logits"])
     scale = (np.abs(x) @ np.abs(w).T).reshape(T, G, M) + 1.0
     bound = 1e-5 * scale
@@ -118,6 +119,9 @@ def _route_check(cfg, inp, out):
     assert np.array_equal(gidx[ok], idx[ok]), "selection differs outside near-ties"
     assert n_excl <= max(2, 1e-4 * T * G)
     assert np.max(np.abs(f64(out["topk_w"])[ok] - wref[ok])) <= 2e-5
+    if out.get("topk_p") is not None:
+        pref = oracle.slot_weights(p, idx, wref, "weighted")
+        assert np.max(np.abs(f64(out["topk_p"])[ok] - pref[ok])) <= 2e-5
     # GPU selection vs GPU logits: selected >= unselected, ties to lower index
     sel = np.zeros((T, G, M), bool)
     np.put_along_axis(sel, gidx.astype(np.int64), True, -1)
@@ -148,11 +152,11 @@ def test_route_workloads(name):
         w_r = synth.round_bf16(rng.standard_normal((cfg.G * cfg.M, cfg.D), dtype=np.float32) * np.float32(0.02))
         inp = dict(x=x, w_r=w_r, b_r=None)
         dims = gqe.gqe_dims.make(cfg.B, cfg.q_len, cfg.D, cfg.N, cfg.G, cfg.k, cfg.d, cfg.dtype)
-        out = gqe.route(dims, x.to(DEV), w_r.to(DEV), None, want_lists=False)
+        out = gqe.route(dims, x.to(DEV), w_r.to(DEV), None, want_lists=False, want_p=True)
     else:
         inp = synth.make_prefill_inputs(cfg)
         out = gqe.route(dims_of(cfg), inp["x"].to(DEV), inp["w_r"].to(DEV),
-                        None if inp["b_r"] is None else inp["b_r"].to(DEV))
+                        None if inp["b_r"] is None else inp["b_r"].to(DEV), want_p=True)
     torch.cuda.synchronize()
     _route_check(cfg, inp, out)
 
@@ -194,9 +198,26 @@ def _prefill_inputs(cfg, peaked):
     return inp
 
 
+# The bf16 d <= 64 kernel has two forms (plain, and key-split for launches
+# with few tiles); the launcher picks by tile count unless GQE_PREFILL_FORM
+# forces one. Cases of that kernel run under each form.
+FORMS = ["auto", "plain", "split"]
+
+
+def _set_form(monkeypatch, form, d, dtype):
+    if form != "auto" and (d > 64 or dtype != "bf16"):
+        pytest.skip("one form only (d = 128 or fp32 kernel)")
+    if form == "auto":
+        monkeypatch.delenv("GQE_PREFILL_FORM", raising=False)
+    else:
+        monkeypatch.setenv("GQE_PREFILL_FORM", form)
+
+
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_prefill_small(case):
+def test_prefill_small(case, form, monkeypatch):
     B, S, D, N, G, k, d, dtype, peaked = case
+    _set_form(monkeypatch, form, d, dtype)
     cfg = small_cfg(B, S, D, N, G, k, d, dtype)
     inp = _prefill_inputs(cfg, peaked)
     g = to_dev(inp)
@@ -223,9 +244,11 @@ RAMP_CASES = [
 ]
 
 
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("case", RAMP_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_prefill_reference_moves(case):
+def test_prefill_reference_moves(case, form, monkeypatch):
     B, S, D, N, G, k, d, rising = case
+    _set_form(monkeypatch, form, d, "bf16")
     cfg = small_cfg(B, S, D, N, G, k, d)
     inp = _prefill_inputs(cfg, False)
     gen = torch.Generator().manual_seed(11)
@@ -254,37 +277,46 @@ def _sample_positions(S, n=256, seed=1):
 
 @pytest.mark.parametrize("name", ["main_s2k", "long_s128k", "llama_s8k_skew"])
 def test_prefill_workloads_sampled(name):
+    """Every sequence of each workload, in the launch configuration the
+    benchmark times. 2048-token sequences (8 of them, each with its shared
+    tiles on its own XCD list) are compared on every row; longer ones on 256
+    sampled positions (first and last included)."""
     cfg = synth.workload(name)
     inp = synth.make_prefill_inputs(cfg)
     inp["idx"] = synth.random_selection(cfg.B, cfg.S, cfg.G, cfg.M, cfg.k, cfg.seed, skew=cfg.skew)
     g = to_dev(inp)
     o_r, o_s = gqe.prefill(dims_of(cfg), g["q"], g["k"], g["v"], g["idx"])
     torch.cuda.synchronize()
-    pos = _sample_positions(cfg.S)
+    full = cfg.S <= 2048
+    pos = np.arange(cfg.S) if full else _sample_positions(cfg.S)
     idx = inp["idx"].numpy().reshape(cfg.B, cfg.S, cfg.G, cfg.k)
-    for b in sorted({0, cfg.B - 1}):
+    what = "every row" if full else "sampled"
+    for b in range(cfg.B):
         ref_r, ref_s = oracle.prefill(f64(inp["q"][b:b + 1]), f64(inp["k"][b:b + 1]), f64(inp["v"][b:b + 1]),
-                                      idx[b:b + 1], cfg.M, positions=pos)
-        assert_close(o_r[b:b + 1, pos], ref_r, cfg.dtype, f"{name} b={b} O_routed (sampled)")
-        assert_close(o_s[b:b + 1, pos], ref_s, cfg.dtype, f"{name} b={b} O_shared (sampled)")
+                                      idx[b:b + 1], cfg.M, positions=None if full else pos)
+        assert_close(o_r[b:b + 1, pos], ref_r, cfg.dtype, f"{name} b={b} O_routed ({what})")
+        assert_close(o_s[b:b + 1, pos], ref_s, cfg.dtype, f"{name} b={b} O_shared ({what})")
 
 
 # Sequences past 8k tokens with ragged row counts: tile edges, skewed lists
 # and the striped tile order (G not a multiple of 8).
 LONG_FORM_CASES = [
-    # B, S, D, N, G, k, skew
-    (2, 8269, 64, 16, 8, 2, True),   # ragged rows, two slots per token, skewed lists
-    (1, 8192, 64, 4, 2, 1, False),   # G not a multiple of 8: striped tile order
-    (1, 9000, 64, 8, 8, 1, False),   # one expert per group (k = M)
+    # B, S, D, N, G, k, d, skew
+    (2, 8269, 64, 16, 8, 2, 64, True),   # ragged rows, two slots per token, skewed lists
+    (1, 8192, 64, 4, 2, 1, 64, False),   # G not a multiple of 8: striped tile order
+    (1, 9000, 64, 8, 8, 1, 64, False),   # one expert per group (k = M)
+    (1, 16384, 64, 16, 8, 1, 32, False),  # d = 32 with 576 tiles: the plain form when not forced
 ]
 
 
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("case", LONG_FORM_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_prefill_long_form(case):
+def test_prefill_long_form(case, form, monkeypatch):
     """Rows around every 256-row tile edge, the first and last rows and a
     random sample, against the oracle; also the training forward's lse."""
-    B, S, D, N, G, k, skew = case
-    cfg = small_cfg(B, S, D, N, G, k, 64, seed=7, skew=skew)
+    B, S, D, N, G, k, d, skew = case
+    _set_form(monkeypatch, form, d, "bf16")
+    cfg = small_cfg(B, S, D, N, G, k, d, seed=7, skew=skew)
     inp = _prefill_inputs(cfg, peaked=False)
     inp["idx"] = synth.random_selection(B, S, G, cfg.M, k, 11, skew=skew)
     g = to_dev(inp)
@@ -412,7 +444,9 @@ def test_decode_matches_prefill_rows():
         assert_close(d_s[:, 0], f64(o_s[:, p]), "bf16", f"decode vs prefill shared p={p}")
 
 
-def test_decode_workload_sampled():
+def test_decode_workload():
+    """All 16 sequences of the 64k-key decode, every output, in the launch
+    configuration the benchmark times."""
     cfg = synth.workload("decode_kv64k")
     inp = synth.make_decode_inputs(cfg)
     idx = synth.random_selection(cfg.B, cfg.q_len, cfg.G, cfg.M, cfg.k, cfg.seed)
@@ -420,11 +454,35 @@ def test_decode_workload_sampled():
     o_r, o_s = gqe.decode(dims_of(cfg), cfg.q_len, g["q"], g["k"], g["v"], g["kv_len"], idx.to(DEV))
     torch.cuda.synchronize()
     idx4 = idx.numpy().reshape(cfg.B, cfg.q_len, cfg.G, cfg.k)
-    for b in (0, 7, cfg.B - 1):
+    for b in range(cfg.B):
         ref_r, ref_s = oracle.decode(f64(inp["q"][b:b + 1]), f64(inp["k"][b:b + 1]), f64(inp["v"][b:b + 1]),
                                      inp["kv_len"].numpy()[b:b + 1], idx4[b:b + 1], cfg.M)
         assert_close(o_r[b:b + 1], ref_r, cfg.dtype, f"decode b={b} O_routed")
         assert_close(o_s[b:b + 1], ref_s, cfg.dtype, f"decode b={b} O_shared")
+
+
+@pytest.mark.parametrize("d,q_len", [(128, 1), (64, 2), (32, 1)])
+def test_decode_deterministic(d, q_len):
+    """Two decode calls on the same inputs give the same bits: the split
+    partials are merged in a fixed order with no atomics. The second call
+    gets a workspace filled with NaN, so a combine that read a partial its
+    own split pass did not write would show."""
+    B, Smax, H, G, k = 4, 40000, 16, 8, 2
+    rng = np.random.default_rng(d + q_len)
+    bf = torch.bfloat16
+    q = torch.from_numpy(rng.standard_normal((B, q_len, H + 1, d), dtype=np.float32)).to(bf).to(DEV)
+    K = torch.from_numpy(rng.standard_normal((B, G, Smax, d), dtype=np.float32)).to(bf).to(DEV)
+    V = torch.from_numpy(rng.standard_normal((B, G, Smax, d), dtype=np.float32)).to(bf).to(DEV)
+    kv_len = torch.tensor([40000, 4097, 2, 23456], dtype=torch.int32, device=DEV)
+    idx = synth.random_selection(B, q_len, G, H // G, k, 5).to(DEV)
+    dims = gqe.gqe_dims.make(B, Smax, 64, H, G, k, d, "bf16")
+    a_r, a_s = gqe.decode(dims, q_len, q, K, V, kv_len, idx)
+    ws = gqe.decode_workspace(dims, q_len, DEV)
+    ws.view(torch.float32)[: ws.numel() // 4].fill_(float("nan"))
+    b_r, b_s = gqe.decode(dims, q_len, q, K, V, kv_len, idx, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a_r, b_r) and torch.equal(a_s, b_s)
+    assert bool(torch.isfinite(a_r.float()).all()) and bool(torch.isfinite(a_s.float()).all())
 
 
 # ---------------------------------------------------------------------------
@@ -457,35 +515,45 @@ def test_out_proj_small(T, G, k, d, D, dtype):
                                              (1000, 4, 2, 128, 8, "bf16"), (130, 2, 2, 64, 72, "f32")])
 def test_out_proj_ablation_variants(mode, T, G, k, d, D, dtype):
     """The two slot layouts of the ablation table through every kernel path
-    (few-token, 128x128-tile, pipelined GEMM, fp32); W_O has (G*k+1)*d rows.
+    (few-token, 128x128-tile, pipelined GEMM, fp32): the hard slots alone,
+    W_O with G*k*d rows, and no shared output (passed as NULL, as is the
+    hard layout's weight pointer). The weighted layout's slot weights are
+    router probabilities, which need not sum to 1 over the selected set.
     The full layout through the same entry point equals gqe_out_proj bit for
     bit."""
     s = synth.make_slot_inputs(T, G, k, d, D, dtype, seed=T + 17)
+    p_sel = torch.from_numpy(np.random.default_rng([T, 18]).uniform(0.05, 0.95, (T, G, k)).astype(np.float32))
     g = to_dev(s)
     dims = gqe.gqe_dims.make(1, T, D, G * k, G, k, d, dtype)
     code = {"hard": gqe.GQE_SLOTS_HARD, "weighted": gqe.GQE_SLOTS_WEIGHTED}[mode]
-    w_o = g["w_o"][:(G * k + 1) * d].contiguous()
+    sw = p_sel.to(DEV) if mode == "weighted" else None
+    w_o = g["w_o"][:G * k * d].contiguous()
     y = torch.empty((T, D), dtype=w_o.dtype, device=DEV)
-    gqe.gqe_out_proj_variant(dims, code, T, g["o_r"], g["w"], g["o_s"], w_o, y)
+    gqe.gqe_out_proj_variant(dims, code, T, g["o_r"], sw, None, w_o, y)
     y_full = torch.empty_like(y)
     gqe.gqe_out_proj_variant(dims, gqe.GQE_SLOTS_FULL, T, g["o_r"], g["w"], g["o_s"], g["w_o"], y_full)
     torch.cuda.synchronize()
-    ref = oracle.out_proj(f64(s["o_r"]), f64(s["w"]), f64(s["o_s"]), f64(w_o), mode=mode)
+    ref = oracle.out_proj(f64(s["o_r"]), None if sw is None else f64(p_sel), None, f64(w_o), mode=mode)
     assert_close(y, ref, dtype, f"out_proj {mode} T={T}")
     assert torch.equal(y_full, gqe.out_proj(dims, T, g["o_r"], g["w"], g["o_s"], g["w_o"]))
 
 
 @pytest.mark.parametrize("name", ["main_s2k", "long_s128k", "llama_s8k_skew", "decode_kv64k"])
-def test_out_proj_workloads_sampled(name):
+def test_out_proj_workloads(name):
+    """Every output row at the d = 64 workloads (16k and 128k tokens) and at
+    decode (16 tokens); 4096 sampled rows of the Llama-shaped one."""
     cfg = synth.workload(name)
     T = cfg.T
     s = synth.make_slot_inputs(T, cfg.G, cfg.k, cfg.d, cfg.D, cfg.dtype, seed=1)
     g = to_dev(s)
     y = gqe.out_proj(dims_of(cfg), T, g["o_r"], g["w"], g["o_s"], g["w_o"])
     torch.cuda.synchronize()
-    rows = _sample_positions(T, 512, seed=2)
-    ref = oracle.out_proj(f64(s["o_r"][rows]), f64(s["w"][rows]), f64(s["o_s"][rows]), f64(s["w_o"]))
-    assert_close(y[rows], ref, cfg.dtype, f"{name} y (sampled rows)")
+    rows = np.arange(T) if cfg.d <= 64 or T <= 16 else _sample_positions(T, 4096, seed=2)
+    w_o = f64(s["w_o"])
+    for c0 in range(0, rows.size, 16384):
+        r = rows[c0:c0 + 16384]
+        ref = oracle.out_proj(f64(s["o_r"][r]), f64(s["w"][r]), f64(s["o_s"][r]), w_o)
+        assert_close(y[r], ref, cfg.dtype, f"{name} y rows {r[0]}..{r[-1]} ({r.size})")
 
 
 # ---------------------------------------------------------------------------
@@ -517,19 +585,55 @@ def test_layer_full(cfg):
     assert_close(y, ref["y"], cfg.dtype, "layer y")
 
 
+@pytest.mark.parametrize("mode", ["hard", "weighted"])
+@pytest.mark.parametrize("cfg", [small_cfg(2, 300, 256, 16, 8, 1, 64),
+                                 small_cfg(1, 333, 512, 32, 8, 2, 128, skew=True),
+                                 small_cfg(1, 130, 256, 4, 2, 1, 32, dtype="f32")],
+                         ids=lambda c: f"{c.dtype}-S{c.S}-N{c.N}-k{c.k}")
+def test_layer_ablation(cfg, mode):
+    """Whole ablation layer on the GPU: route (with the selected p), attend,
+    then the hard-slots-only output projection, against the oracle's layer
+    with the same layout (weights from slot_weights: p, not the renormalised
+    w, so at k = 1 the two layouts give different outputs)."""
+    inp = synth.make_prefill_inputs(cfg)
+    g = to_dev(inp)
+    dims = dims_of(cfg)
+    r = gqe.route(dims, g["x"], g["w_r"], g["b_r"], want_p=True)
+    o_r, o_s = gqe.prefill(dims, g["q"], g["k"], g["v"], r["topk_idx"])
+    T, rows = cfg.T, cfg.G * cfg.k * cfg.d
+    w_o = g["w_o"][:rows].contiguous()
+    code = {"hard": gqe.GQE_SLOTS_HARD, "weighted": gqe.GQE_SLOTS_WEIGHTED}[mode]
+    y = torch.empty((T, cfg.D), dtype=w_o.dtype, device=DEV)
+    gqe.gqe_out_proj_variant(dims, code, T, o_r.view(T, cfg.G, cfg.k, cfg.d),
+                             r["topk_p"] if mode == "weighted" else None, None, w_o, y)
+    torch.cuda.synchronize()
+    ref = oracle.layer(f64(inp["x"]), f64(inp["w_r"]), f64(inp["q"]), f64(inp["k"]), f64(inp["v"]),
+                       f64(inp["w_o"][:rows]), cfg.G, cfg.k, None if inp["b_r"] is None else f64(inp["b_r"]),
+                       mode=mode)
+    assert np.array_equal(r["topk_idx"].cpu().numpy(), ref["idx"]), "routing differs"
+    if mode == "weighted":
+        assert_close(r["topk_p"], ref["sw"], "f32", "selected p")
+        assert np.max(ref["sw"]) < 1.0  # the layout's weights are not the renormalised ones
+    assert_close(y, ref["y"], cfg.dtype, f"layer y ({mode})")
+
+
 def test_layer_main_sampled():
+    """The whole layer at the 8 x 2048-token workload: full routing of every
+    sequence, and y at 128 sampled positions of each of the 8 sequences."""
     cfg = synth.workload("main_s2k")
     inp = synth.make_prefill_inputs(cfg)
     r, o_r, o_s, y = _layer_gpu(cfg, inp)
-    b = 3
-    pos = _sample_positions(cfg.S, 128, seed=3)
-    z, p, idx, w = oracle.route(f64(inp["x"][b * cfg.S:(b + 1) * cfg.S]), f64(inp["w_r"]), cfg.G, cfg.M, cfg.k)
-    gidx = r["topk_idx"].cpu().numpy()[b * cfg.S:(b + 1) * cfg.S]
-    assert np.array_equal(gidx, idx)
-    ref_r, ref_s = oracle.prefill(f64(inp["q"][b:b + 1]), f64(inp["k"][b:b + 1]), f64(inp["v"][b:b + 1]),
-                                  idx.reshape(1, cfg.S, cfg.G, cfg.k), cfg.M, positions=pos)
-    yref = oracle.out_proj(ref_r[0].reshape(-1, cfg.G, cfg.k, cfg.d), w[pos], ref_s[0], f64(inp["w_o"]))
-    assert_close(y[b * cfg.S + pos], yref, cfg.dtype, "main layer y (sampled)")
+    w_o = f64(inp["w_o"])
+    for b in range(cfg.B):
+        pos = _sample_positions(cfg.S, 128, seed=3 + b)
+        z, p, idx, w = oracle.route(f64(inp["x"][b * cfg.S:(b + 1) * cfg.S]), f64(inp["w_r"]), cfg.G, cfg.M,
+                                    cfg.k)
+        gidx = r["topk_idx"].cpu().numpy()[b * cfg.S:(b + 1) * cfg.S]
+        assert np.array_equal(gidx, idx), f"routing differs in sequence {b}"
+        ref_r, ref_s = oracle.prefill(f64(inp["q"][b:b + 1]), f64(inp["k"][b:b + 1]), f64(inp["v"][b:b + 1]),
+                                      idx.reshape(1, cfg.S, cfg.G, cfg.k), cfg.M, positions=pos)
+        yref = oracle.out_proj(ref_r[0].reshape(-1, cfg.G, cfg.k, cfg.d), w[pos], ref_s[0], w_o)
+        assert_close(y[b * cfg.S + pos], yref, cfg.dtype, f"main layer y, sequence {b} (sampled)")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
