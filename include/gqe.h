@@ -51,7 +51,8 @@ typedef enum {
   GQE_ERR_UNSUPPORTED = -2, /* head layout, head_dim, top-k or dtype not supported */
   GQE_ERR_ALIGNMENT = -3,   /* a device pointer is not 16-byte aligned */
   GQE_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
-  GQE_ERR_HIP = -5          /* the HIP runtime refused a launch */
+  GQE_ERR_HIP = -5,         /* the HIP runtime refused a launch */
+  GQE_ERR_SCRATCH = -6      /* the call needs more than the library's static scratch */
 } gqe_status;
 
 typedef enum { GQE_BF16 = 0, GQE_F32 = 1 } gqe_dtype;
@@ -215,6 +216,26 @@ int gqe_attn_decode(const gqe_dims* dims, int32_t q_len, const void* q,
                     const int32_t* kv_len, const int32_t* topk_idx,
                     void* o_routed, void* o_shared, void* workspace,
                     size_t ws_bytes, void* stream);
+
+/* Bytes of the static device scratch of gqe_attn_decode_noalloc (16 MiB). */
+size_t gqe_decode_scratch_bytes(void);
+
+/* gqe_attn_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and kernels, bit for bit, with the split partials in a
+ * static device array of gqe_decode_scratch_bytes() bytes instead of a caller
+ * workspace. The library holds that array on every GPU it runs on until the
+ * process ends; its address is looked up on the first call on each device.
+ * No call allocates or frees memory. A call whose partials
+ * (gqe_decode_workspace_bytes(dims, q_len)) exceed the scratch returns
+ * GQE_ERR_SCRATCH and enqueues nothing. All calls on one GPU share its
+ * scratch: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and give unspecified outputs; calls ordered on one stream
+ * are safe. Arguments and errors otherwise as for gqe_attn_decode. */
+int gqe_attn_decode_noalloc(const gqe_dims* dims, int32_t q_len, const void* q,
+                            const void* k_cache, const void* v_cache,
+                            const int32_t* kv_len, const int32_t* topk_idx,
+                            void* o_routed, void* o_shared, void* stream);
 
 /* gqe_attn_decode against a paged KV cache, with optional left padding.
  * The cache of every sequence is a list of pages of page_size consecutive

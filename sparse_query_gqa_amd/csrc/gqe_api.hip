@@ -8,12 +8,42 @@
 #include <stdlib.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/gqe.h"
 #include "gqe_internal.h"
 
 using namespace gqe;
 
+// Scratch memory of gqe_attn_decode_noalloc: the split partials live in this
+// file-scope device array instead of a caller workspace. Every GPU the library
+// runs on holds its own copy until the process ends. In host code the name
+// stands for a host-side shadow, not a device address: the device address is
+// looked up once per device with hipGetSymbolAddress and only that pointer is
+// ever handed to kernels.
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device. Returns GQE_OK and the address, or GQE_ERR_HIP.
+int scratch_ptr(void** out) {
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GQE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GQE_ERR_HIP;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return GQE_OK;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -166,6 +196,7 @@ const char* gqe_status_string(int status) {
     case GQE_ERR_ALIGNMENT: return "GQE_ERR_ALIGNMENT: device pointer not 16-byte aligned";
     case GQE_ERR_WORKSPACE: return "GQE_ERR_WORKSPACE: workspace missing or too small";
     case GQE_ERR_HIP: return "GQE_ERR_HIP: the HIP runtime refused a launch";
+    case GQE_ERR_SCRATCH: return "GQE_ERR_SCRATCH: the call needs more than the library's static scratch";
     default: return "unknown gqe status";
   }
 }
@@ -276,10 +307,12 @@ size_t gqe_decode_workspace_bytes(const gqe_dims* d, int32_t q_len) {
   return o_bytes + recs * 2 * sizeof(float);
 }
 
-int gqe_attn_decode(const gqe_dims* d, int32_t q_len, const void* q, const void* k_cache,
-                    const void* v_cache, const int32_t* kv_len, const int32_t* topk_idx,
-                    void* o_routed, void* o_shared, void* workspace, size_t ws_bytes,
-                    void* stream) {
+// Argument checks of gqe_attn_decode and gqe_attn_decode_noalloc, everything
+// but the workspace. Returns GQE_OK (with *empty set for a call with nothing
+// to do) or the error.
+static int decode_check(const gqe_dims* d, int32_t q_len, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* kv_len, const int32_t* topk_idx,
+                        void* o_routed, void* o_shared, bool* empty) {
   int st = check_dims(d, false);
   if (st) return st;
   if (q_len < 0) return GQE_ERR_INVALID_ARG;
@@ -290,10 +323,15 @@ int gqe_attn_decode(const gqe_dims* d, int32_t q_len, const void* q, const void*
   const void* ptrs[] = {q, k_cache, v_cache, kv_len, topk_idx, o_routed, o_shared};
   for (const void* p : ptrs)
     if (!aligned16(p)) return GQE_ERR_ALIGNMENT;
-  if (d->B == 0 || q_len == 0) return GQE_OK;
-  const size_t need = gqe_decode_workspace_bytes(d, q_len);
-  if (!workspace || ws_bytes < need) return GQE_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return GQE_ERR_ALIGNMENT;
+  *empty = d->B == 0 || q_len == 0;
+  return GQE_OK;
+}
+
+// Launch of a checked decode call with its split partials at `workspace`
+// (at least gqe_decode_workspace_bytes(d, q_len) bytes, 16-byte aligned).
+static int decode_launch(const gqe_dims* d, int32_t q_len, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* kv_len, const int32_t* topk_idx,
+                         void* o_routed, void* o_shared, void* workspace, void* stream) {
   const DecodeSplit sp = decode_split(d->B, d->G, d->S, d->k, q_len);
   const size_t recs = (size_t)d->B * d->G * sp.nsplit * sp.rows;
   float* ws_o = (float*)workspace;
@@ -305,6 +343,37 @@ int gqe_attn_decode(const gqe_dims* d, int32_t q_len, const void* q, const void*
     fprintf(stderr, "[gqe] decode B=%d L=%d Smax=%d G=%d k=%d d=%d nsplit=%d chunk=%d\n", d->B,
             q_len, d->S, d->G, d->k, d->d, sp.nsplit, sp.chunk);
   return hip_status(launch_decode(dp, d->d, d->dtype == GQE_BF16, (hipStream_t)stream));
+}
+
+int gqe_attn_decode(const gqe_dims* d, int32_t q_len, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* kv_len, const int32_t* topk_idx,
+                    void* o_routed, void* o_shared, void* workspace, size_t ws_bytes,
+                    void* stream) {
+  bool empty = false;
+  int st = decode_check(d, q_len, q, k_cache, v_cache, kv_len, topk_idx, o_routed, o_shared, &empty);
+  if (st || empty) return st;
+  const size_t need = gqe_decode_workspace_bytes(d, q_len);
+  if (!workspace || ws_bytes < need) return GQE_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GQE_ERR_ALIGNMENT;
+  return decode_launch(d, q_len, q, k_cache, v_cache, kv_len, topk_idx, o_routed, o_shared, workspace,
+                       stream);
+}
+
+size_t gqe_decode_scratch_bytes(void) { return kDecodeScratchBytes; }
+
+int gqe_attn_decode_noalloc(const gqe_dims* d, int32_t q_len, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* kv_len, const int32_t* topk_idx,
+                            void* o_routed, void* o_shared, void* stream) {
+  bool empty = false;
+  int st = decode_check(d, q_len, q, k_cache, v_cache, kv_len, topk_idx, o_routed, o_shared, &empty);
+  if (st || empty) return st;
+  if (gqe_decode_workspace_bytes(d, q_len) > kDecodeScratchBytes) return GQE_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = scratch_ptr(&ws);
+  if (st) return st;
+  // nothing in the scratch needs clearing: the split pass writes every
+  // partial that the combine pass reads
+  return decode_launch(d, q_len, q, k_cache, v_cache, kv_len, topk_idx, o_routed, o_shared, ws, stream);
 }
 
 int gqe_attn_decode_paged(const gqe_dims* d, int32_t q_len, const void* q, const void* k_pages,

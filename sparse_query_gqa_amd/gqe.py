@@ -23,6 +23,7 @@ GQE_ERR_UNSUPPORTED = -2
 GQE_ERR_ALIGNMENT = -3
 GQE_ERR_WORKSPACE = -4
 GQE_ERR_HIP = -5
+GQE_ERR_SCRATCH = -6
 GQE_BF16 = 0
 GQE_F32 = 1
 GQE_SLOTS_FULL = 0
@@ -37,6 +38,7 @@ EXPORTED = [
     "gqe_qkv_proj", "gqe_qkv_proj_decode", "gqe_attn_decode_paged", "gqe_out_proj_variant",
     "gqe_attn_prefill_train", "gqe_attn_prefill_bwd_workspace_bytes", "gqe_attn_prefill_bwd",
     "gqe_out_proj_bwd_workspace_bytes", "gqe_out_proj_bwd", "gqe_route_bwd_workspace_bytes", "gqe_route_bwd",
+    "gqe_decode_scratch_bytes", "gqe_attn_decode_noalloc",
 ]
 
 
@@ -90,6 +92,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gqe_attn_prefill": (ctypes.c_int, [D, P, P, P, P, P, P, P]),
         "gqe_decode_workspace_bytes": (SZ, [D, I32]),
         "gqe_attn_decode": (ctypes.c_int, [D, I32, P, P, P, P, P, P, P, P, SZ, P]),
+        "gqe_decode_scratch_bytes": (SZ, []),
+        "gqe_attn_decode_noalloc": (ctypes.c_int, [D, I32, P, P, P, P, P, P, P, P]),
         "gqe_out_proj": (ctypes.c_int, [D, I64, P, P, P, P, P, P]),
         "gqe_qkv_proj": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P]),
         "gqe_qkv_proj_decode": (ctypes.c_int, [D, I32, P, P, P, P, P, P, P, P, P, P]),
@@ -302,6 +306,27 @@ def gqe_attn_decode(dims, q_len, q, k_cache, v_cache, kv_len, topk_idx, o_routed
                                         _ptr(o_routed), _ptr(o_shared), _ptr(workspace), ws_bytes,
                                         _stream(stream))
     _raise(st, "gqe_attn_decode")
+
+
+def gqe_decode_scratch_bytes() -> int:
+    return load_library().gqe_decode_scratch_bytes()
+
+
+def gqe_attn_decode_noalloc(dims, q_len, q, k_cache, v_cache, kv_len, topk_idx, o_routed, o_shared,
+                            stream=None):
+    """gqe_attn_decode with the split partials in the library's static device scratch (no workspace)."""
+    B, S, N, G, kk, d, dt = dims.B, dims.S, dims.N, dims.G, dims.k, dims.d, dims.torch_dtype
+    _check(q, "q", (B, q_len, N + 1, d), dt)
+    _check(k_cache, "k_cache", (B, G, S, d), dt)
+    _check(v_cache, "v_cache", (B, G, S, d), dt)
+    _check(kv_len, "kv_len", (B,), torch.int32)
+    _check(topk_idx, "topk_idx", (B * q_len, G, kk), torch.int32)
+    _check(o_routed, "o_routed", (B, q_len, G, kk, d), dt)
+    _check(o_shared, "o_shared", (B, q_len, d), dt)
+    st = load_library().gqe_attn_decode_noalloc(ctypes.byref(dims), q_len, _ptr(q), _ptr(k_cache),
+                                                _ptr(v_cache), _ptr(kv_len), _ptr(topk_idx),
+                                                _ptr(o_routed), _ptr(o_shared), _stream(stream))
+    _raise(st, "gqe_attn_decode_noalloc")
 
 
 def gqe_attn_decode_paged(dims, q_len, q, k_pages, v_pages, block_table, page_size, kv_start, kv_len,

@@ -47,7 +47,7 @@ def test_header_symbols_exported():
 
 def test_status_strings_and_version():
     lib = _lib()
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         s = lib.gqe_status_string(st).decode()
         assert s.startswith("GQE_")
     assert lib.gqe_status_string(7).decode() == "unknown gqe status"
@@ -127,6 +127,32 @@ def test_decode_validation():
     assert call(_dims(N=8, G=3)) == gqe.GQE_ERR_UNSUPPORTED
     assert call(_dims(B=0)) == gqe.GQE_OK
     assert call(d, L=0) == gqe.GQE_OK
+
+
+def test_decode_noalloc_validation():
+    """The allocation-free decode checks what gqe_attn_decode checks, and
+    rejects a call whose split partials exceed its static scratch before
+    touching the device."""
+    lib = _lib()
+    assert lib.gqe_decode_scratch_bytes() == 16 << 20
+
+    def call(dims, L=1, kv=A, q=A):
+        return lib.gqe_attn_decode_noalloc(ctypes.byref(dims), L, P(q), P(A), P(A), P(kv), P(A), P(A), P(A), None)
+
+    d = _dims(S=65536, N=32, G=8, k=2, d=128)
+    assert lib.gqe_decode_workspace_bytes(ctypes.byref(d), 1) <= 16 << 20
+    assert call(d, L=-1) == gqe.GQE_ERR_INVALID_ARG
+    assert call(d, kv=0) == gqe.GQE_ERR_INVALID_ARG
+    assert call(d, q=MIS) == gqe.GQE_ERR_ALIGNMENT
+    assert call(_dims(S=4), L=5) == gqe.GQE_ERR_INVALID_ARG
+    assert call(_dims(S=100, k=2), L=6) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(N=8, G=3)) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(B=0)) == gqe.GQE_OK
+    assert call(d, L=0) == gqe.GQE_OK
+    # 512 x 8 heads, one split each, 15 rows of d = 128: 4096*15*(128+2)*4 bytes > 16 MiB
+    big = _dims(B=512, S=1024, N=32, G=8, k=4, d=128)
+    assert lib.gqe_decode_workspace_bytes(ctypes.byref(big), 3) == 4096 * 15 * 130 * 4
+    assert call(big, L=3) == gqe.GQE_ERR_SCRATCH
 
 
 def test_out_proj_validation():
