@@ -88,6 +88,32 @@ def measured_traffic(kernel_file: str, summary: str):
     return int(m.group(1))
 
 
+def routing_stats(dims, cfg, x, w_r, b_r, logits, list_off) -> dict:
+    """Realised routing of one prefill: per-(group, expert) token counts
+    summed over the sequences (from gqe_route's lists), their share of each
+    group's T*k selections, and the near ties: (token, group) pairs whose
+    top-k margin in the emitted fp32 logits is within twice the fp32 logit
+    error bound 1e-5 * (1 + sum_j |x_j w_j|), where a different summation
+    order could change the selection. Reporting only (torch on the device)."""
+    T, G, M, k = cfg.T, cfg.G, cfg.M, cfg.k
+    counts = torch.diff(list_off, dim=-1).sum(0).cpu().numpy()  # [G, M]
+    share = counts / float(T * k)
+    near = 0
+    if k < M:
+        z = logits.view(T, G, M)
+        srt = torch.sort(z, dim=-1, descending=True).values
+        margin = srt[..., k - 1] - srt[..., k]
+        for t0 in range(0, T, 16384):
+            t1 = min(T, t0 + 16384)
+            scale = (x[t0:t1].float().abs() @ w_r.float().abs().T).view(t1 - t0, G, M) + 1.0
+            if b_r is not None:
+                scale = scale + b_r.abs().view(1, G, M)
+            near += int((margin[t0:t1] <= 2e-5 * scale.max(-1).values).sum())
+    return {"per_group_expert_tokens": counts.astype(int).tolist(),
+            "max_expert_share": round(float(share.max()), 4), "min_expert_share": round(float(share.min()), 4),
+            "near_tie_pairs": near, "pairs": T * G}
+
+
 def cpu_info() -> str:
     try:
         for ln in open("/proc/cpuinfo"):
@@ -134,6 +160,71 @@ def cpu_baseline(cfg, inp, n_rows: int) -> dict:
             "seconds": dt}
 
 
+def prefill_config_line(name: str, steps: int, warmup: int, dev) -> dict:
+    """One more prefill workload, timed on its own after the step: the router
+    (with lists), the attention and the output projection, each launch
+    bracketed by HIP events on the current stream. The attention's roofline is
+    its FLOP per launch / mean launch time against the bf16 MFMA peak."""
+    cfg = synth.workload(name)
+    inp = synth.make_prefill_inputs(cfg, project=False)
+    g = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
+    B, S, D, N, G, k, d, M, T = cfg.B, cfg.S, cfg.D, cfg.N, cfg.G, cfg.k, cfg.d, cfg.M, cfg.T
+    # Q, K, V prepared on the device in fp32 and rounded to bf16 (input preparation)
+    xf = g["x"].float()
+    q = (xf @ g["w_q"].float().T).to(torch.bfloat16).view(B, S, N + 1, d).contiguous()
+    kk = (xf @ g["w_k"].float().T).to(torch.bfloat16).view(B, S, G, d).permute(0, 2, 1, 3).contiguous()
+    vv = (xf @ g["w_v"].float().T).to(torch.bfloat16).view(B, S, G, d).permute(0, 2, 1, 3).contiguous()
+    del xf
+    dims = gqe.gqe_dims.from_config(cfg)
+    r = gqe.route(dims, g["x"], g["w_r"], g["b_r"])
+    o_r = torch.empty((B, S, G, k, d), dtype=torch.bfloat16, device=dev)
+    o_s = torch.empty((B, S, d), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    r_ws = torch.empty((max(gqe.gqe_route_workspace_bytes(dims), 16),), dtype=torch.uint8, device=dev)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    recs = []
+    for it in range(warmup + steps):
+        e = [ev() for _ in range(4)]
+        e[0].record()
+        gqe.gqe_route(dims, g["x"], g["w_r"], g["b_r"], None, r["topk_idx"], r["topk_w"], r["list_off"],
+                      r["list_tok"], r_ws)
+        e[1].record()
+        gqe.gqe_attn_prefill(dims, q, kk, vv, r["topk_idx"], o_r, o_s)
+        e[2].record()
+        gqe.gqe_out_proj(dims, T, o_r.view(T, G, k, d), r["topk_w"], o_s.view(T, d), g["w_o"], y)
+        e[3].record()
+        if it >= warmup:
+            recs.append(e)
+    torch.cuda.synchronize()
+
+    def span(i, j):
+        return np.array([e[i].elapsed_time(e[j]) for e in recs]) * 1e-3
+
+    fl = prefill_path_flops(cfg)
+    t_attn, t_path, t_proj = span(1, 2), span(0, 3), span(2, 3)
+    a = fl["attention"] / t_attn.mean()
+    pj = 2 * T * (G * k + 2) * d * D
+    kern = "prefill_d128_kernel" if d == 128 else "prefill_qp_kernel<%d>" % d
+    return {
+        "config": {"B": B, "S": S, "D": D, "N": N, "G": G, "M": M, "k": k, "head_dim": d,
+                   "skewed_router": cfg.skew},
+        "value": round(fl["total"] / t_path.mean() / 1e12, 2), "unit": "TFLOP/s",
+        "roofline": {"kernel": f"{kern} (gqe_attn_prefill)", "bound": "mfma", "achieved": round(a / 1e12, 2),
+                     "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s", "frac": round(a / PEAK_BF16_FLOPS, 4),
+                     "flop_per_launch": fl["attention"]},
+        "attention_ms": round(t_attn.mean() * 1e3, 4),
+        "attention_min_ms": round(t_attn.min() * 1e3, 4),
+        "route_ms": round(span(0, 1).mean() * 1e3, 4),
+        "out_proj_ms": round(t_proj.mean() * 1e3, 4),
+        "out_proj_frac": round(pj / t_proj.mean() / PEAK_BF16_FLOPS, 4),
+        "path_ms": round(t_path.mean() * 1e3, 4),
+        "routing": routing_stats(dims, cfg, g["x"], g["w_r"], g["b_r"], r["logits"], r["list_off"]),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +236,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=3072)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--extra", default="main_s2k,llama_s8k_skew",
+                    help="further prefill workloads timed after the step (comma-separated, '' for none)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
@@ -277,6 +370,17 @@ def main():
 
     t_qkv = timed(proj_call, args.steps)
     t_dqkv = timed(dproj_call, args.steps)
+    # for comparison: one dense bf16 product (torch -> hipBLASLt) of every
+    # query head, K and V, the work the token compaction avoids
+    w_all = torch.cat([g["w_q"], g["w_k"], g["w_v"]], 0).contiguous()
+    dense_out = torch.empty((T, w_all.shape[0]), dtype=torch.bfloat16, device=dev)
+
+    def dense_call():
+        torch.matmul(g["x"], w_all.t(), out=dense_out)
+
+    t_dense = timed(dense_call, args.steps)
+    dense_flop = 2 * T * cfg.D * w_all.shape[0]
+    del dense_out, w_all
     qkv_flop = projection_flops(T, cfg.D, G, k, d)
     sel = np.unique(d_idx.view(dT, dcfg.G, dcfg.k).cpu().numpy()
                     + dcfg.M * np.arange(dcfg.G)[None, :, None])
@@ -286,6 +390,9 @@ def main():
         "prefill_tflops": round(qkv_flop / t_qkv.mean() / 1e12, 2),
         "prefill_frac": round(qkv_flop / t_qkv.mean() / PEAK_BF16_FLOPS, 4),
         "prefill_flop": qkv_flop,
+        "dense_all_heads_ms": round(t_dense.mean() * 1e3, 4),
+        "dense_all_heads_flop": dense_flop,
+        "dense_all_heads_tflops": round(dense_flop / t_dense.mean() / 1e12, 2),
         "decode_us": round(t_dqkv.mean() * 1e6, 2),
         "decode_weight_gbps": round(dqkv_bytes / t_dqkv.mean() / 1e9, 1),
         "decode_weight_bytes": int(dqkv_bytes),
@@ -374,6 +481,15 @@ def main():
         "balance_loss_coef": 0.01,
     }
 
+    # realised routing of the step's prefill (z_t holds its logits, r_out its lists)
+    routing = routing_stats(dims, cfg, g["x"], g["w_r"], g["b_r"], z_t, r_out["list_off"])
+    del dz_t, dx_t, z_t
+    extra = {}
+    for name in [n for n in args.extra.split(",") if n]:
+        print(f"[bench] prefill workload {name}", file=sys.stderr, flush=True)
+        extra[name] = prefill_config_line(name, args.steps, args.warmup, dev)
+        torch.cuda.empty_cache()
+
     traffic = measured_traffic("prefill.hip", "prefill_long_s128k_pmc.txt")
     dtraffic = measured_traffic("decode.hip", "decode_kv64k_pmc.txt")
     result = {
@@ -433,6 +549,8 @@ def main():
             "attention_min_ms": round(t_attn.min() * 1e3, 4),
             "attention_max_ms": round(t_attn.max() * 1e3, 4),
         },
+        "routing": routing,
+        "prefill_workloads": extra,
         "qkv_proj": qkv,
         "train_bwd": train_bwd,
         "flop_per_step": fl,
