@@ -85,6 +85,8 @@ int prefill_common(const gqe_dims* d, const void* q, const void* k, const void* 
                    float* lse_s, void* stream) {
   int st = check_dims(d, false);
   if (st) return st;
+  // one KV head's keys are read through a raw buffer of S*d*2 bytes (32-bit size)
+  if ((int64_t)d->S * d->d * 2 > (int64_t)UINT32_MAX) return GQE_ERR_UNSUPPORTED;
   if (!q || !k || !v || !topk_idx || !o_routed || !o_shared) return GQE_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, topk_idx, o_routed, o_shared, lse_r, lse_s};
   for (const void* p : ptrs)

@@ -212,6 +212,33 @@ __device__ __forceinline__ void lds_dma16_s(const void* base, uint32_t off, cons
                    : "memory");
 }
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes): a load at an offset at or
+// past `bytes` returns zeros (the range check of a raw buffer), so a block
+// that runs past the end of a tensor needs no clamped addresses. Word 3
+// selects 32-bit data, as a raw buffer of the gfx9 family needs; the words
+// are made wavefront-uniform (SGPRs).
+__device__ __forceinline__ i32x4 buf_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(a >> 32) & 0xffff);
+  r[2] = __builtin_amdgcn_readfirstlane((int32_t)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from a buffer (this lane's byte offset `off`) straight
+// into LDS bytes [lds + 16 l, +16), as lds_dma16; lanes past the buffer's end
+// write zeros. Five wait states cover resource words a VALU op
+// (readfirstlane) wrote.
+__device__ __forceinline__ void lds_dma16_b(i32x4 rsrc, uint32_t off, const void* lds) {
+  __asm__ volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc),
+                   "{m0}"(lds_addr(lds))
+                   : "memory");
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -159,9 +159,9 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void prefill_qp_k
   // bytes [1024 n + 16 l, +16), i.e. row 1024 n / ROWB + (16 l) / ROWB,
   // chunk position (16 l % ROWB) / 16; it loads the source chunk the swizzle
   // puts there. That lane offset is the same in every block, so a whole block
-  // moves with the scalar base address. Only a block that runs past the
-  // sequence takes per-lane addresses: its keys past the end re-read the
-  // last key (finite data; those keys are masked).
+  // moves with the scalar words of a raw buffer resource that starts at the
+  // block and ends at the head's last key: rows of a block that runs past the
+  // sequence read zeros (and are masked).
   auto swz = [](int r) { return (((r >> 1) & 7) ^ ((r & 2) << 1)) & (CPR - 1); };
   constexpr int RPC = 1024 / ROWB;  // key rows per 1 KiB chunk
   const int dma_r = (16 * lane) / ROWB;
@@ -172,26 +172,19 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void prefill_qp_k
     const int rb = (wave * NPW + i) * RPC + dma_r;  // row in the block
     dma_off[i] = rb * ROWB + 16 * (dma_p ^ swz(rb));
   }
+  // Block kb through raw buffers over the rest of this head's keys: rows past
+  // the sequence read zeros (and are masked).
+  const uint32_t head_bytes = (uint32_t)p.S * ROWB;
   auto dma = [&](const int kb, const int bf) __attribute__((always_inline)) {
-    if ((kb + 1) * kKeyBlock <= p.S) {
-      const __bf16* kblk = kbase + (int64_t)kb * kKeyBlock * D;
-      const __bf16* vblk = vbase + (int64_t)kb * kKeyBlock * D;
+    const uint32_t skip = (uint32_t)kb * MATB;
+    const uint32_t rem = head_bytes > skip ? head_bytes - skip : 0u;
+    const i32x4 rk = buf_rsrc((const char*)kbase + skip, rem);
+    const i32x4 rv = buf_rsrc((const char*)vbase + skip, rem);
 #pragma unroll
-      for (int i = 0; i < NPW; ++i) {
-        const int n = wave * NPW + i;
-        lds_dma16_s(kblk, dma_off[i], lds[bf][0] + n * 1024);
-        lds_dma16_s(vblk, dma_off[i], lds[bf][1] + n * 1024);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NPW; ++i) {
-        const int n = wave * NPW + i;
-        const int rb = n * RPC + dma_r;
-        const int row = min(kb * kKeyBlock + rb, p.S - 1);
-        const int64_t g = (int64_t)row * D + 8 * (dma_p ^ swz(rb));
-        lds_dma16(kbase + g, lds[bf][0] + n * 1024);
-        lds_dma16(vbase + g, lds[bf][1] + n * 1024);
-      }
+    for (int i = 0; i < NPW; ++i) {
+      const int n = wave * NPW + i;
+      lds_dma16_b(rk, dma_off[i], lds[bf][0] + n * 1024);
+      lds_dma16_b(rv, dma_off[i], lds[bf][1] + n * 1024);
     }
   };
 
@@ -483,11 +476,13 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void prefill_qp_k
 // Consecutive halves belong to the same rows, so a reference move in step t
 // also shifts the S^T of half t+1, which that step already computed.
 //
-// K/V go through LDS-DMA into four 32 KiB buffers (one workgroup per CU).
-// Rows are 256 bytes, so every row covers all 64 banks; the chunk swizzle
-// swaps the two 2-bit fields of the row's low 4 bits, which makes a 16-byte
-// K read over 16 rows and a transposing V read over 8 rows x 64 bytes both
-// conflict-free.
+// K/V go through LDS-DMA into four 16 KiB K buffers followed by four 16 KiB
+// V buffers (one workgroup per CU). Rows are 256 bytes, so every row covers
+// all 64 banks; the chunk swizzle swaps the two 2-bit fields of the row's low
+// 4 bits, which makes a 16-byte K read over 16 rows and a transposing V read
+// over 8 rows x 64 bytes both conflict-free. The block loop is unrolled over
+// the four buffers, so that every fragment read is a per-lane register plus
+// an immediate offset (no address arithmetic in the loop).
 template <int D>
 __global__ __launch_bounds__(512, 1) void prefill_d128_kernel(PrefillParams p, int tiles_r, int tiles_s) {
   static_assert(D == 128, "head dim");
@@ -500,7 +495,7 @@ __global__ __launch_bounds__(512, 1) void prefill_d128_kernel(PrefillParams p, i
   constexpr int NPW = MATB / 1024 / kWaves8;    // 1 KiB LDS-DMA chunks per wavefront per matrix
   static_assert(NPW >= 1, "block too small for the LDS-DMA split");
   constexpr int NBUF = 4;
-  __shared__ __attribute__((aligned(1024))) char lds[NBUF][2][MATB];  // [buffer][K, V]
+  __shared__ __attribute__((aligned(1024))) char lds[2][NBUF][MATB];  // [K, V][buffer]
 
   const TileCoord tc = tile_of_block(p, tiles_r, tiles_s);
   if (!tc.valid) return;
@@ -547,34 +542,27 @@ __global__ __launch_bounds__(512, 1) void prefill_d128_kernel(PrefillParams p, i
   constexpr int RPC = 1024 / ROWB;  // key rows per 1 KiB chunk
   const int dma_r = (16 * lane) / ROWB;
   const int dma_p = ((16 * lane) % ROWB) / 16;
-  // as in the d <= 64 form: a fixed per-lane offset and a scalar block base,
-  // per-lane clamped addresses only for a block that runs past the sequence
+  // as in the d <= 64 form: a fixed per-lane offset and a raw buffer resource
+  // per block, which reads zeros past the sequence
   uint32_t dma_off[NPW];
 #pragma unroll
   for (int i = 0; i < NPW; ++i) {
     const int rb = (wave * NPW + i) * RPC + dma_r;
     dma_off[i] = rb * ROWB + 16 * (dma_p ^ swz(rb));
   }
+  // Block kb through raw buffers over the rest of this head's keys: rows past
+  // the sequence read zeros (and are masked).
+  const uint32_t head_bytes = (uint32_t)p.S * ROWB;
   auto dma = [&](const int kb, const int bf) __attribute__((always_inline)) {
-    if ((kb + 1) * kKeyBlock <= p.S) {
-      const __bf16* kblk = kbase + (int64_t)kb * kKeyBlock * D;
-      const __bf16* vblk = vbase + (int64_t)kb * kKeyBlock * D;
+    const uint32_t skip = (uint32_t)kb * MATB;
+    const uint32_t rem = head_bytes > skip ? head_bytes - skip : 0u;
+    const i32x4 rk = buf_rsrc((const char*)kbase + skip, rem);
+    const i32x4 rv = buf_rsrc((const char*)vbase + skip, rem);
 #pragma unroll
-      for (int i = 0; i < NPW; ++i) {
-        const int n = wave * NPW + i;
-        lds_dma16_s(kblk, dma_off[i], lds[bf][0] + n * 1024);
-        lds_dma16_s(vblk, dma_off[i], lds[bf][1] + n * 1024);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NPW; ++i) {
-        const int n = wave * NPW + i;
-        const int rb = n * RPC + dma_r;
-        const int row = min(kb * kKeyBlock + rb, p.S - 1);  // past the sequence: its last key (masked)
-        const int64_t g = (int64_t)row * D + 8 * (dma_p ^ swz(rb));
-        lds_dma16(kbase + g, lds[bf][0] + n * 1024);
-        lds_dma16(vbase + g, lds[bf][1] + n * 1024);
-      }
+    for (int i = 0; i < NPW; ++i) {
+      const int n = wave * NPW + i;
+      lds_dma16_b(rk, dma_off[i], lds[0][bf] + n * 1024);
+      lds_dma16_b(rv, dma_off[i], lds[1][bf] + n * 1024);
     }
   };
 
@@ -588,10 +576,10 @@ __global__ __launch_bounds__(512, 1) void prefill_d128_kernel(PrefillParams p, i
   // K fragment s of key half sb: row sb*32 + l32, chunk 2s + half
   int k_off[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) k_off[s] = l32 * ROWB + 16 * ((2 * s + half) ^ swz(l32));
+  for (int s = 0; s < KS; ++s) k_off[s] = (l32 * ROWB + 16 * ((2 * s + half) ^ swz(l32))) & 0xffff;
   auto read_k = [&](const int buf, const int sb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) kf[s] = *(const bf16x8*)(lds[buf][0] + sb * 32 * ROWB + k_off[s]);
+    for (int s = 0; s < KS; ++s) kf[s] = *(const bf16x8*)(lds[0][buf] + sb * 32 * ROWB + k_off[s]);
   };
   // V^T fragments: as in the quarter form (lane (half, l32) holds d = db*32 +
   // l32, contraction element t <-> key sb*32 + 16*st + 8*(t/4) + 4*half + t%4)
@@ -602,7 +590,23 @@ __global__ __launch_bounds__(512, 1) void prefill_d128_kernel(PrefillParams p, i
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      v_off[tt][db] = (8 * tt + tr_key) * ROWB + 16 * ((4 * db + (tr_d >> 3)) ^ swz(8 * tt + tr_key)) + 2 * (tr_d & 7);
+      v_off[tt][db] = ((8 * tt + tr_key) * ROWB + 16 * ((4 * db + (tr_d >> 3)) ^ swz(8 * tt + tr_key)) + 2 * (tr_d & 7)) & 0xffff;
+  // Per-lane base addresses of the V reads in the first V buffer, kept opaque
+  // (so that the compiler does not fold the V region's 64 KiB start back into
+  // each read) and masked to 17 bits (so that it may add a non-negative
+  // constant in the instruction's 16-bit offset field): with the buffer index
+  // a constant in every unrolled copy of the block loop, each LDS read is a
+  // register plus an immediate, with no address arithmetic in the loop. The K
+  // offsets are masked to 16 bits for the same reason.
+  uint32_t v_base[2][DB];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds[1][0] + v_off[tt][db];
+      __asm__("" : "+v"(a));
+      v_base[tt][db] = a & 0x1ffff;
+    }
   auto read_v = [&](const int buf, const int sb) __attribute__((always_inline)) {
 #pragma unroll
     for (int st = 0; st < 2; ++st)
@@ -611,8 +615,8 @@ __global__ __launch_bounds__(512, 1) void prefill_d128_kernel(PrefillParams p, i
         u32x4 vw;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          const char* a = lds[buf][1] + (sb * 32 + 16 * st) * ROWB + v_off[tt][db];
-          const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a);
+          const uint32_t a = v_base[tt][db] + buf * MATB + (sb * 32 + 16 * st) * ROWB;
+          const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)a);
           const u32x2 w = __builtin_bit_cast(u32x2, x);
           vw[2 * tt] = w[0];
           vw[2 * tt + 1] = w[1];
@@ -757,10 +761,22 @@ __global__ __launch_bounds__(512, 1) void prefill_d128_kernel(PrefillParams p, i
   // block sets the reference (and shifts its key half 1 to it).
   const int nfull = min((pos_first + 1) / kKeyBlock, nblocks);
   iteration(0, 0, 1, nfull < 1, kYes(), kNo());
-  for (int j = 1, buf = 1; j < nblocks; ++j) {
-    const int nbuf = (buf + 1) % NBUF;
-    iteration(j, buf, nbuf, j >= nfull, kNo(), kYes());
-    buf = nbuf;
+  // Block j sits in buffer j % 4. The loop is unrolled over the four buffers
+  // so that every LDS address is a per-lane register plus an immediate.
+  static_assert(NBUF == 4, "unrolled over four buffers");
+  int j = 1;
+  for (; j + 4 <= nblocks; j += 4) {
+    iteration(j, 1, 2, j >= nfull, kNo(), kYes());
+    iteration(j + 1, 2, 3, j + 1 >= nfull, kNo(), kYes());
+    iteration(j + 2, 3, 0, j + 2 >= nfull, kNo(), kYes());
+    iteration(j + 3, 0, 1, j + 3 >= nfull, kNo(), kYes());
+  }
+  if (j < nblocks) {
+    iteration(j, 1, 2, j >= nfull, kNo(), kYes());
+    if (j + 1 < nblocks) {
+      iteration(j + 1, 2, 3, j + 1 >= nfull, kNo(), kYes());
+      if (j + 2 < nblocks) iteration(j + 2, 3, 0, j + 2 >= nfull, kNo(), kYes());
+    }
   }
   pv_mfma(1);
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS-DMA may outlive the workgroup

@@ -104,6 +104,9 @@ def test_prefill_validation():
     assert call(_dims(B=0)) == gqe.GQE_OK
     assert call(_dims(S=0)) == gqe.GQE_OK
     assert lib.gqe_attn_prefill(None, P(), P(), P(), P(), P(), P(), None) == gqe.GQE_ERR_INVALID_ARG
+    # one head's keys (S*d*2 bytes) must fit a 32-bit buffer size
+    assert call(_dims(B=1, S=(1 << 24), d=128)) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(B=0, S=(1 << 24) - 1, d=128)) == gqe.GQE_OK
 
 
 def test_decode_validation():
