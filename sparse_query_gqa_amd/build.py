@@ -56,25 +56,49 @@ def _run(cmd):
     return err
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libgqe.so; returns the library path."""
+# Host-code sanitizers (AddressSanitizer + UndefinedBehaviorSanitizer) for a
+# CPU-only check of the C ABI's argument handling; the device code is built
+# as usual (no GPU sanitizer). Each -fsanitize= goes to the host pass only.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+SAN_BUILD = os.path.join(BUILD, "san")
+SAN_LIB = os.path.join(SAN_BUILD, "libgqe_san.so")
+
+
+def _compile_and_link(build_dir: str, lib: str, extra: list, link_extra: list, verbose: bool) -> str:
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
     objs = []
     jobs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        jobs.append([hipcc, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc, *FLAGS, *extra, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(min(8, len(jobs))) as ex:
         for out in ex.map(_run, jobs):
             if verbose and out.strip():
                 print(out, file=sys.stderr)
-    tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = lib + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, "-o", tmp, *objs])
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link libgqe.so; returns the library path."""
+    return _compile_and_link(BUILD, LIB, [], [], verbose)
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """libgqe_san.so: the same library with host-code ASan + UBSan (for CPU tests
+    of the C ABI; load it with the sanitizer runtime preloaded)."""
+    return _compile_and_link(SAN_BUILD, SAN_LIB, SANITIZE,
+                             ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                              "-shared-libsan"], verbose)
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose=True))
+    else:
+        print(build(verbose=True))

@@ -15,7 +15,9 @@ from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqe.so")
+# GQE_LIB names another build of the same library (the host-sanitizer build
+# the CPU tests load); by default the in-tree libgqe.so
+LIB_PATH = os.environ.get("GQE_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqe.so")
 
 GQE_OK = 0
 GQE_ERR_INVALID_ARG = -1
