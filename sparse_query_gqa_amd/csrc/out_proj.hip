@@ -16,10 +16,10 @@
 // which the caller passes in place of w. Neither has the obar slot or the
 // shared head, and W_O has G*k*d rows.
 //
-// Two bf16 kernels: a pipelined GEMM for T >= 256 (below) and, for fewer
-// tokens, a plain 128x128-tile kernel: four wavefronts of 64x64 each on
-// v_mfma_f32_32x32x16_bf16, W_O's tile transposed into LDS to give the B
-// operand k-contiguous lanes.
+// Three bf16 kernels: a tiled GEMM for T >= 256, a GEMV-shaped one for
+// T <= 16 (decode), and for the tokens between a plain 128x128-tile kernel:
+// four wavefronts of 64x64 each on v_mfma_f32_32x32x16_bf16, W_O's tile
+// transposed into LDS to give the B operand k-contiguous lanes.
 #include "gqe_internal.h"
 
 namespace gqe {
@@ -154,192 +154,255 @@ __global__ __launch_bounds__(256) void out_proj_bf16_kernel(OutProjParams p) {
     }
 }
 
-// bf16 GEMM form. Computed as y^T = W_O^T A^T with v_mfma_f32_32x32x16_bf16:
-// the W_O tile sits in LDS row-major ([k][n], as stored) and its fragments
-// come from ds_read_b64_tr_b16 (four consecutive k of one n per lane); the A
-// tile sits token-major ([t][k]) and is read with 16-byte loads. Each lane
-// then holds four consecutive output columns of one token. A workgroup of 8
-// wavefronts computes 128 tokens x 256 columns (64 x 64 per wavefront), k in
-// steps of 32 through a four-stage LDS ring filled by LDS-DMA
-// (global_load_lds_dwordx4): the hard-slot and shared-head columns of A come
-// straight from o_routed / o_shared, obar is computed once per tile into its
-// own LDS region at the start. Every step issues the same three DMA loads
-// per thread (dummies for obar steps and past the end), so one fixed vmcnt
-// wait before the barrier makes the current step's tile complete. The output
-// tile is staged through LDS and written as whole rows.
-constexpr int kGT = 128;      // tokens per tile
-constexpr int kGN = 256;      // output columns per tile
-constexpr int kGK = 32;       // k per step
-constexpr int kGStages = 4;
+// Tiled form (T >= 256). Computed as y^T = W_O^T A^T with
+// v_mfma_f32_32x32x16_bf16: the W_O tile sits in LDS as stored ([k][n]) and
+// its fragments come from ds_read_b64_tr_b16 (four consecutive k of one n per
+// lane); the A tile sits token-major ([t][k]) and is read with 16-byte loads,
+// so each lane holds four consecutive output columns of one token. The
+// hard-slot and shared-head columns of A come straight from o_routed /
+// o_shared; obar is computed once per tile into its own LDS region (its
+// loads issued eight slots at a time, so their latencies overlap). A
+// workgroup of eight wavefronts computes 256 tokens x 256 columns (128
+// tokens x 64 columns each). The tile is large so that the
+// bytes staged per FLOP are few: a CU then keeps the loads of NS - 1 steps in
+// flight against the latency of L2 and the memory-side cache. k goes in
+// steps of 32 through an NS-stage LDS ring filled by LDS-DMA from raw buffer
+// resources (a step moves with scalar resource words; rows past T read
+// zeros); every step issues the same four loads per thread (a dummy A load
+// on obar steps), so one fixed vmcnt wait makes a stage complete. With four
+// stages the ring advances in the middle of a step and the next step's first
+// fragments are read while the current step's second MFMA half runs.
+// Workgroup i runs on XCD i % 8; XCD x takes token tiles x, x + 8, ... and
+// for each all column tiles in turn, so a token tile's slot rows come from
+// HBM once and W_O stays in each XCD's L2.
+constexpr int kPT = 256;  // tokens per tile
+constexpr int kPN = 256;  // output columns per tile
+constexpr int kPK = 32;   // k per step
 
-template <int DH, int MODE>  // MODE: 0 [O, obar, s], 1 [O], 2 [p*O]
-__global__ __launch_bounds__(512, 1) void out_proj_gemm_kernel(OutProjParams p) {
-  constexpr int AB = kGT * kGK * 2;  // A tile: 128 token rows x 64 bytes
-  constexpr int BB = kGK * kGN * 2;  // W_O tile: 32 k rows x 512 bytes
-  constexpr int SB = AB + BB;
-  constexpr int OPAD = DH + 8;       // obar row stride: 16 bytes of padding keep 16 rows on distinct banks
-  constexpr int YPAD = kGN + 8;      // output staging row stride
-  static_assert(kGT * YPAD * 2 <= kGStages * SB, "output staging must fit the stage ring");
-  __shared__ __attribute__((aligned(1024))) char lds[kGStages * SB];
-  __shared__ __attribute__((aligned(16))) __bf16 obar[kGT][OPAD];
+template <int DH, int MODE, int NS>
+__global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p) {
+  constexpr int AB = kPT * kPK * 2;  // A stage: 256 token rows x 64 bytes
+  constexpr int WB = kPK * kPN * 2;  // W_O stage: 32 k rows x 512 bytes
+  constexpr int SB = AB + WB;
+  constexpr int nob = MODE == 0 ? DH : 0;
+  constexpr int nsh = MODE == 0 ? DH : 0;
+  constexpr bool weighted = MODE == 2;
+  constexpr int OB = MODE == 0 ? kPT * DH * 2 : 0;  // obar tile (unpadded)
+  constexpr int YPAD = kPN + 8;                     // output staging row stride
+  constexpr int LDSB = (NS * SB + OB) > (kPT * YPAD * 2) ? (NS * SB + OB) : (kPT * YPAD * 2);
+  static_assert(LDSB <= 163840, "LDS");
+  __shared__ __attribute__((aligned(1024))) char lds[LDSB];
+  __bf16* obar = (__bf16*)(lds + NS * SB);  // [kPT][DH], 16-byte chunks swizzled per row
+  // obar chunk c of token row t sits at chunk position c ^ oswz(t), so that the
+  // fragment reads (32 consecutive rows, one chunk each) hit distinct banks
+  auto oswz = [](int t) { return DH == 32 ? ((t >> 2) & 3) : DH == 64 ? ((t >> 1) & 7) : (t & 15); };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int wm = wave & 1, wn = wave >> 1;  // token half, column quarter
-  const int64_t m0 = (int64_t)blockIdx.x * kGT;
-  const int n0 = blockIdx.y * kGN;
+  const int ncol = (p.Dout + kPN - 1) / kPN;
+  const int64_t ntok = (p.T + kPT - 1) / kPT;
+  const int xcd = blockIdx.x % 8, jj = blockIdx.x / 8;
+  const int64_t ttile = xcd + 8 * (int64_t)(jj / ncol);
+  if (ttile >= ntok) return;
+  const int64_t m0 = ttile * kPT;
+  const int n0 = (jj % ncol) * kPN;
   const int hard = p.Gk * DH;
-  constexpr int nob = MODE == 0 ? DH : 0;
-  constexpr int nsh = MODE == 0 ? DH : 0;
-  constexpr bool weighted = MODE == 2;
-  const int nk = (hard + nob + nsh) / kGK;
+  const int nk = (hard + nob + nsh) / kPK;
   const __bf16* orr = (const __bf16*)p.o_r;
   const __bf16* os = (const __bf16*)p.o_s;
   const __bf16* wo = (const __bf16*)p.w_o;
   const int64_t tmax = p.T - 1;
+  const uint32_t rows = (uint32_t)min<int64_t>(p.T - m0, kPT);  // valid token rows of this tile
 
-
-  // LDS-DMA of step kt into stage st. A: chunk `wave` = token rows
-  // 16*wave + lane/4, 16-byte chunk position lane%4, holding logical chunk
-  // position ^ ((row >> 2) & 3). W_O: chunks 2*wave + i = k rows 2n + lane/32,
-  // position lane%32 holding logical chunk position ^ ((row & 3) << 2).
-  const int a_row = 16 * wave + (lane >> 2);
-  const int a_c = (lane & 3) ^ ((a_row >> 2) & 3);
-  const int64_t a_t = min(m0 + a_row, tmax);
-  auto dma = [&](const int kt, const int st) __attribute__((always_inline)) {
-    const int k0 = min(kt, nk - 1) * kGK;
-    char* sbase = lds + st * SB;
-    const __bf16* asrc;
-    if (k0 < hard) asrc = orr + a_t * hard + k0 + 8 * a_c;
-    else if (k0 >= hard + nob) asrc = os + a_t * DH + (k0 - hard - nob) + 8 * a_c;
-    else asrc = orr + a_t * hard + 8 * a_c;  // obar step: a dummy load, the tile is not read
-    lds_dma16(asrc, sbase + wave * 1024);
+  // LDS-DMA lane geometry. A: 1 KiB chunk c = 2*wave + i holds token rows
+  // 16c + lane/4, 16-byte piece lane%4 holding the row's logical piece
+  // (lane%4) ^ ((row >> 2) & 3). W_O: chunk c holds k rows 2c + lane/32,
+  // piece lane%32 holding logical column chunk (lane%32) ^ ((row & 3) << 2).
+  uint32_t a_off_r[2], a_off_s[2], w_off_d[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int n = 2 * wave + i;
-      const int row = 2 * n + (lane >> 5);
-      const int c = (lane & 31) ^ ((row & 3) << 2);
-      const int col = min(n0 + 8 * c, p.Dout - 8);
-      lds_dma16(wo + (int64_t)(k0 + row) * p.Dout + col, sbase + AB + n * 1024);
+  for (int i = 0; i < 2; ++i) {
+    const int c = 2 * wave + i;
+    const int row = 16 * c + (lane >> 2);
+    const int lp = (lane & 3) ^ ((row >> 2) & 3);
+    a_off_r[i] = (uint32_t)(row * hard * 2 + lp * 16);
+    a_off_s[i] = (uint32_t)(row * DH * 2 + lp * 16);
+    const int kr = 2 * c + (lane >> 5);
+    const int lc = (lane & 31) ^ ((kr & 3) << 2);
+    w_off_d[i] = (uint32_t)kr * (uint32_t)p.Dout * 2u + (uint32_t)lc * 16u;
+  }
+  auto dma = [&](const int kt, const int st) __attribute__((always_inline)) {
+    const int k0 = min(kt, nk - 1) * kPK;
+    char* sbase = lds + st * SB;
+    // the step's source; the branch selects scalars, the resource is built once
+    const __bf16* abase = orr + m0 * hard;  // obar step: a dummy load of the first slot columns
+    uint32_t anum = rows * (uint32_t)hard * 2u;
+    bool shared_slot = false;
+    if (k0 < hard) {
+      abase = orr + m0 * hard + k0;
+      anum = rows * (uint32_t)hard * 2u - (uint32_t)k0 * 2u;
+    } else if (k0 >= hard + nob) {
+      const int ks = k0 - hard - nob;
+      abase = os + m0 * DH + ks;
+      anum = rows * (uint32_t)DH * 2u - (uint32_t)ks * 2u;
+      shared_slot = true;
     }
+    const i32x4 ra = buf_rsrc(abase, anum);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      lds_dma16_b(ra, shared_slot ? a_off_s[i] : a_off_r[i], sbase + (2 * wave + i) * 1024);
+    const i32x4 rw = buf_rsrc(wo + (int64_t)k0 * p.Dout + n0, (uint32_t)kPK * (uint32_t)p.Dout * 2u - (uint32_t)n0 * 2u);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lds_dma16_b(rw, w_off_d[i], sbase + AB + (2 * wave + i) * 1024);
   };
 
-  // fragment addresses. A^T (B operand): token row t = wm*64 + tb*32 + l32,
+  // Fragment addresses. A^T (B operand): token t = wm*128 + tb*32 + l32,
   // chunk 2*kk + half. W^T (A operand): transposing read; in a 16-lane group
   // source lane i points at k row K0 + i/4, column N0 + 4*(i%4), and output
   // lane i receives k rows K0..K0+3 of column N0 + i.
-  int a_off[2][2];  // [tb][kk]
+  int a_frag[4][2];  // [tb][kk]
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
+  for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const int t = wm * 64 + tb * 32 + l32;
-      a_off[tb][kk] = t * 64 + 16 * ((2 * kk + half) ^ ((t >> 2) & 3));
+      const int t = wm * 128 + tb * 32 + l32;
+      a_frag[tb][kk] = t * 64 + 16 * ((2 * kk + half) ^ ((t >> 2) & 3));
     }
-  const int tr_row = 8 * half + ((lane & 15) >> 2);  // + 16*kk + 4*tt
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + wn*64 + nb*32
-  int w_off[2][2];  // [nb][tt] at kk = 0; kk adds 16 rows (same swizzle)
+  const int tr_row = 8 * half + ((lane & 15) >> 2);              // + 16*kk + 4*tt
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);    // + wn*64 + nb*32
+  int w_frag[2][2];  // [nb][tt] at kk = 0; kk adds 16 rows (same swizzle)
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int row = tr_row + 4 * tt;
       const int col = wn * 64 + nb * 32 + tr_col;
-      w_off[nb][tt] = row * 512 + 16 * ((col >> 3) ^ ((row & 3) << 2)) + 2 * (col & 7);
+      w_frag[nb][tt] = row * 512 + 16 * ((col >> 3) ^ ((row & 3) << 2)) + 2 * (col & 7);
     }
 
-  f32x16 acc[2][2];  // [nb][tb]: 32 columns x 32 tokens
+  f32x16 acc[2][4];  // [nb][tb]: 32 columns x 32 tokens
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
 #pragma unroll
-  for (int kt = 0; kt < kGStages - 1; ++kt) dma(kt, kt);
+  for (int kt = 0; kt < NS - 1; ++kt) dma(kt, kt);
   // obar = sum over the G*k slots of w * o, in fp32, rounded to bf16; one
-  // 8-column piece of one token per work item. Computed after the first
-  // stages' LDS-DMA is issued, so that those loads are in flight meanwhile
-  // (waiting on these loads also drains the earlier DMA: the counter is in
-  // order); the main loop's first barrier publishes obar.
-  for (int it = tid; nob && it < kGT * (DH / 8); it += 512) {
+  // 8-column piece of one token per work item, issued after the first
+  // stages' loads so that they are in flight meanwhile
+  for (int it = tid; nob && it < kPT * (DH / 8); it += 512) {
     const int row = it / (DH / 8), e = (it % (DH / 8)) * 8;
     const int64_t t = min(m0 + row, tmax);
-    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < p.Gk; ++j) {
-      const float wj = p.w[t * p.Gk + j];
-      const bf16x8 ov = *(const bf16x8*)(orr + t * hard + j * DH + e);
+    float sacc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // slots in groups of eight whose loads are all issued before the first
+    // product (a runtime trip count would otherwise serialise their latencies)
+    for (int j0 = 0; j0 < p.Gk; j0 += 8) {
+      bf16x8 ov[8];
+      float wj[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s[i] = fmaf(wj, (float)ov[i], s[i]);
+      for (int u = 0; u < 8; ++u) {
+        const int j = min(j0 + u, p.Gk - 1);
+        ov[u] = *(const bf16x8*)(orr + t * hard + j * DH + e);
+        wj[u] = j0 + u < p.Gk ? p.w[t * p.Gk + j] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sacc[i] = fmaf(wj[u], (float)ov[u][i], sacc[i]);
     }
     bf16x8 r;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = f2bf(s[i]);
-    *(bf16x8*)&obar[row][e] = r;
+    for (int i = 0; i < 8; ++i) r[i] = f2bf(sacc[i]);
+    *(bf16x8*)&obar[row * DH + 8 * ((e >> 3) ^ oswz(row))] = r;
   }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt % kGStages;
-    // step kt's tile is complete when at most the two later tiles' loads are
-    // outstanding; the barrier makes it (and obar) visible and frees the
-    // stage read in step kt-1 for step kt+3
-    __asm__ volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    __syncthreads();
-    dma(kt + kGStages - 1, (kt + kGStages - 1) % kGStages);
-    const char* sbase = lds + st * SB;
-    const int k0 = kt * kGK;
+
+  bf16x8 af[4][2], wf[2][2];  // [tb or nb][kk]
+  auto read_frags = [&](const int kt, const int kk) __attribute__((always_inline)) {
+    const char* sbase = lds + (kt % NS) * SB;
+    const int k0 = kt * kPK;
     const bool ob = k0 >= hard && k0 < hard + nob;
-    // weighted concatenation: this step's hard slot k0 / DH, one weight per token
-    float wsc[2] = {1.f, 1.f};
-    if (weighted && k0 < hard) {
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-        wsc[tb] = p.w[min(m0 + wm * 64 + tb * 32 + l32, tmax) * p.Gk + k0 / DH];
+    for (int tb = 0; tb < 4; ++tb) {
+      if (ob) {
+        const int t = wm * 128 + tb * 32 + l32;
+        af[tb][kk] = *(const bf16x8*)&obar[t * DH + 8 * ((((k0 - hard) >> 3) + 2 * kk + half) ^ oswz(t))];
+      } else {
+        af[tb][kk] = *(const bf16x8*)(sbase + a_frag[tb][kk]);
+      }
+      if (weighted && k0 < hard) {
+        const float wsc = p.w[min(m0 + wm * 128 + tb * 32 + l32, tmax) * p.Gk + k0 / DH];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) af[tb][kk][i] = f2bf((float)af[tb][kk][i] * wsc);
+      }
     }
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 af[2], wf[2];
+    for (int nb = 0; nb < 2; ++nb) {
+      u32x4 w4;
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        if (ob) {
-          const int t = wm * 64 + tb * 32 + l32;
-          af[tb] = *(const bf16x8*)&obar[t][k0 - hard + 16 * kk + 8 * half];
-        } else {
-          af[tb] = *(const bf16x8*)(sbase + a_off[tb][kk]);
-          if (weighted && k0 < hard) af[tb] = scale8(af[tb], wsc[tb]);
-        }
+      for (int tt = 0; tt < 2; ++tt) {
+        const char* a = sbase + AB + kk * 16 * 512 + w_frag[nb][tt];
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a);
+        const u32x2 w2 = __builtin_bit_cast(u32x2, x);
+        w4[2 * tt] = w2[0];
+        w4[2 * tt + 1] = w2[1];
       }
+      wf[nb][kk] = __builtin_bit_cast(bf16x8, w4);
+    }
+  };
+  auto mfmas = [&](const int kk) __attribute__((always_inline)) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        u32x4 w4;
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const char* a = sbase + AB + kk * 16 * 512 + w_off[nb][tt];
-          const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a);
-          const u32x2 w2 = __builtin_bit_cast(u32x2, x);
-          w4[2 * tt] = w2[0];
-          w4[2 * tt + 1] = w2[1];
-        }
-        wf[nb] = __builtin_bit_cast(bf16x8, w4);
-      }
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-          acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], af[tb], acc[nb][tb], 0, 0, 0);
+      for (int tb = 0; tb < 4; ++tb)
+        acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb][kk], af[tb][kk], acc[nb][tb], 0, 0, 0);
+  };
+
+  if constexpr (NS >= 4) {
+    // stage 0 complete (stages 1 .. NS-2 may be in flight); the barrier also
+    // publishes obar
+    __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * (NS - 2)) : "memory");
+    __syncthreads();
+    read_frags(0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      read_frags(kt, 1);
+      mfmas(0);
+      // stage kt+1 complete, later ones in flight; after the barrier every
+      // wavefront has finished its reads of stage kt-1, whose buffer takes
+      // stage kt+NS-1
+      __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * (NS - 3)) : "memory");
+      __syncthreads();
+      dma(kt + NS - 1, (kt + NS - 1) % NS);
+      if (kt + 1 < nk) read_frags(kt + 1, 0);
+      mfmas(1);
+    }
+  } else {
+    for (int kt = 0; kt < nk; ++kt) {
+      // stage kt complete (kt+1 .. kt+NS-2 in flight); after the barrier the
+      // buffer of stage kt-1 takes stage kt+NS-1 (and obar is published)
+      __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * (NS - 2)) : "memory");
+      __syncthreads();
+      dma(kt + NS - 1, (kt + NS - 1) % NS);
+      read_frags(kt, 0);
+      read_frags(kt, 1);
+      mfmas(0);
+      mfmas(1);
     }
   }
 
-  // output tile through LDS: lane (half, l32) of tile (nb, tb) holds token
-  // wm*64 + tb*32 + l32 and columns wn*64 + nb*32 + 8*(r/4) + 4*half + r%4
+  // output tile through LDS (the whole of it: ring and obar are free): lane
+  // (half, l32) of tile (nb, tb) holds token wm*128 + tb*32 + l32 and columns
+  // wn*64 + nb*32 + 8*(r/4) + 4*half + r%4
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   __bf16* ys = (__bf16*)lds;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const int t = wm * 64 + tb * 32 + l32;
+    for (int tb = 0; tb < 4; ++tb) {
+      const int t = wm * 128 + tb * 32 + l32;
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         bf16x4 o4;
@@ -350,8 +413,8 @@ __global__ __launch_bounds__(512, 1) void out_proj_gemm_kernel(OutProjParams p) 
     }
   __syncthreads();
   __bf16* y = (__bf16*)p.y;
-  for (int it = tid; it < kGT * (kGN / 8); it += 512) {
-    const int row = it / (kGN / 8), c8 = (it % (kGN / 8)) * 8;
+  for (int it = tid; it < kPT * (kPN / 8); it += 512) {
+    const int row = it / (kPN / 8), c8 = (it % (kPN / 8)) * 8;
     const int64_t t = m0 + row;
     const int n = n0 + c8;
     if (t < p.T && n < p.Dout) *(bf16x8*)(y + t * p.Dout + n) = *(const bf16x8*)&ys[row * YPAD + c8];
@@ -487,13 +550,14 @@ __global__ __launch_bounds__(256) void out_proj_f32_kernel(OutProjParams p) {
 
 hipError_t launch_out_proj(const OutProjParams& p, bool bf16, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
-  if (bf16 && p.T >= kGT * 2) {
-    const dim3 grid((unsigned)((p.T + kGT - 1) / kGT), (p.Dout + kGN - 1) / kGN);
+  if (bf16 && p.T >= 256) {
+    const int64_t ntok = (p.T + kPT - 1) / kPT;
+    const dim3 grid((unsigned)(8 * ((ntok + 7) / 8) * ((p.Dout + kPN - 1) / kPN)));
     const int mode = p.nob ? 0 : (p.weighted ? 2 : 1);
-#define GQE_OUT_PROJ_GEMM(DH)                                                                    \
-  if (mode == 0) hipLaunchKernelGGL((out_proj_gemm_kernel<DH, 0>), grid, dim3(512), 0, s, p);    \
-  else if (mode == 1) hipLaunchKernelGGL((out_proj_gemm_kernel<DH, 1>), grid, dim3(512), 0, s, p); \
-  else hipLaunchKernelGGL((out_proj_gemm_kernel<DH, 2>), grid, dim3(512), 0, s, p);
+#define GQE_OUT_PROJ_GEMM(DH)                                                                                    \
+  if (mode == 0) hipLaunchKernelGGL((out_proj_tile_kernel<DH, 0, DH <= 64 ? 4 : 3>), grid, dim3(512), 0, s, p); \
+  else if (mode == 1) hipLaunchKernelGGL((out_proj_tile_kernel<DH, 1, 4>), grid, dim3(512), 0, s, p);          \
+  else hipLaunchKernelGGL((out_proj_tile_kernel<DH, 2, 4>), grid, dim3(512), 0, s, p);
     switch (p.d) {
       case 32: GQE_OUT_PROJ_GEMM(32) break;
       case 64: GQE_OUT_PROJ_GEMM(64) break;
