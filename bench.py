@@ -214,7 +214,9 @@ def prefill_config_line(name: str, steps: int, warmup: int, dev) -> dict:
         "value": round(fl["total"] / t_path.mean() / 1e12, 2), "unit": "TFLOP/s",
         "roofline": {"kernel": f"{kern} (gqe_attn_prefill)", "bound": "mfma", "achieved": round(a / 1e12, 2),
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s", "frac": round(a / PEAK_BF16_FLOPS, 4),
-                     "flop_per_launch": fl["attention"]},
+                     "flop_per_launch": fl["attention"],
+                     "traffic": (measured_traffic("prefill.hip", "prefill_d128_llama_s8k_pmc.txt")
+                                 if name == "llama_s8k_skew" else None)},
         "attention_ms": round(t_attn.mean() * 1e3, 4),
         "attention_min_ms": round(t_attn.min() * 1e3, 4),
         "route_ms": round(span(0, 1).mean() * 1e3, 4),
