@@ -59,6 +59,9 @@ PREFILL_CASES = [
     (1, 200, 256, 8, 8, 1, 64, "bf16", False),    # MHA: G = N
     (3, 90, 192, 4, 1, 2, 32, "bf16", False),     # MQA: G = 1 (M = 4, k = 2)
     (1, 1, 64, 4, 2, 1, 32, "bf16", False),       # one token
+    (1, 3000, 256, 16, 4, 1, 64, "bf16", True),   # 1536-token supersteps: shared head and the favoured
+                                                  # experts take more than one 512-row pass
+    (1, 1000, 128, 6, 3, 1, 64, "bf16", False),   # 384 key/value columns: a half-empty 256-column tile
     (1, 128, 256, 4, 2, 1, 32, "f32", False),
     (2, 77, 40, 8, 2, 2, 64, "f32", False),       # fp32 takes any D % 8
 ]
