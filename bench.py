@@ -164,8 +164,12 @@ def prefill_config_line(name: str, steps: int, warmup: int, dev) -> dict:
     """One more prefill workload, timed on its own after the step: the router
     (with lists), the attention and the output projection, each launch
     bracketed by HIP events on the current stream. The attention's roofline is
-    its FLOP per launch / mean launch time against the bf16 MFMA peak."""
+    its FLOP per launch / mean launch time against the bf16 MFMA peak. A
+    sequence of a million tokens (about a second per attention launch) is
+    timed over at most two launches after one warmup."""
     cfg = synth.workload(name)
+    if cfg.S >= 1 << 20:
+        steps, warmup = min(steps, 2), min(warmup, 1)
     inp = synth.make_prefill_inputs(cfg, project=False)
     g = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
     B, S, D, N, G, k, d, M, T = cfg.B, cfg.S, cfg.D, cfg.N, cfg.G, cfg.k, cfg.d, cfg.M, cfg.T
@@ -217,6 +221,7 @@ def prefill_config_line(name: str, steps: int, warmup: int, dev) -> dict:
                      "flop_per_launch": fl["attention"],
                      "traffic": (measured_traffic("prefill.hip", "prefill_d128_llama_s8k_pmc.txt")
                                  if name == "llama_s8k_skew" else None)},
+        "steps": steps, "warmup": warmup,
         "attention_ms": round(t_attn.mean() * 1e3, 4),
         "attention_min_ms": round(t_attn.min() * 1e3, 4),
         "route_ms": round(span(0, 1).mean() * 1e3, 4),
@@ -238,7 +243,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=3072)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (for counter calibration)")
-    ap.add_argument("--extra", default="main_s2k,llama_s8k_skew",
+    ap.add_argument("--extra", default="main_s2k,llama_s8k_skew,long_s1m",
                     help="further prefill workloads timed after the step (comma-separated, '' for none)")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -179,7 +179,7 @@ def attend_rows(q: np.ndarray, pos: np.ndarray, K: np.ndarray, V: np.ndarray,
     return out
 
 
-def prefill(Q, K, V, idx, M: int, positions=None):
+def prefill(Q, K, V, idx, M: int, positions=None, q_rows_only: bool = False):
     """Sparse-query causal attention for a prefill of S tokens per sequence.
 
     Q: [B, S, N+1, d] (head N is the shared head); K, V: [B, G, S, d];
@@ -188,26 +188,28 @@ def prefill(Q, K, V, idx, M: int, positions=None):
     ([GQA-zone] §技术深化: query head i reads KV head floor(i/(H/G)));
     only selected heads are computed ([GQE-review] §二, unselected heads are
     skipped). The shared head attends KV head 0 for every token.
-    positions: token positions to compute (default: all S).
+    positions: token positions to compute (default: all S). With
+    q_rows_only, Q holds just the rows of those positions ([B, P, N+1, d]),
+    for sequences whose whole Q would not fit in memory as float64.
     Returns (O_r [B, P, G, k, d], O_s [B, P, d]) for the P positions.
     """
-    Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
-    B, S, H1, d = Q.shape
-    G = K.shape[1]
+    B, G, S, d = K.shape
     k = idx.shape[-1]
-    N = H1 - 1
+    N = np.shape(Q)[2] - 1
     check_dims(N, G, k)
     pos = np.arange(S) if positions is None else np.asarray(positions, dtype=np.int64)
+    Qp = np.asarray(Q if q_rows_only else np.asarray(Q)[:, pos], dtype=np.float64)  # [B, P, N+1, d]
+    rows = np.arange(pos.size)
     O_r = np.zeros((B, pos.size, G, k, d))
     O_s = np.zeros((B, pos.size, d))
     for b in range(B):
         for g in range(G):
             for j in range(k):
                 heads = g * M + idx[b, pos, g, j]
-                O_r[b, :, g, j] = attend_rows(Q[b, pos, heads, :], pos, K[b, g], V[b, g])
-        O_s[b] = attend_rows(Q[b, pos, N, :], pos, K[b, 0], V[b, 0])
+                O_r[b, :, g, j] = attend_rows(Qp[b, rows, heads, :], pos, K[b, g], V[b, g])
+        O_s[b] = attend_rows(Qp[b, :, N, :], pos, K[b, 0], V[b, 0])
     return O_r, O_s
 
 

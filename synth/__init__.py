@@ -23,6 +23,11 @@ float32 ``standard_normal``):
 * The skewed-router workload adds a router bias of ln 3 to expert
   m* = g mod M of every group g: 3:1 odds for that expert against an equally
   scored rival.
+* attention-only (a sequence too long to project on the host): q
+  [B,S,N+1,d], then k and v [B,G,S,d], drawn directly from
+  ``default_rng([seed, 404])`` as N(0,1) * 0.02 * sqrt(D), the distribution of
+  an entry of x @ W^T above, in chunks of 65536 positions (same draw order),
+  rounded to the workload dtype.
 """
 from __future__ import annotations
 
@@ -37,7 +42,7 @@ import torch
 
 __all__ = [
     "GQEConfig", "WORKLOADS", "workload", "make_prefill_inputs",
-    "make_decode_inputs", "to_f64", "round_bf16",
+    "make_attention_inputs", "make_decode_inputs", "to_f64", "round_bf16",
 ]
 
 
@@ -94,6 +99,8 @@ WORKLOADS = {
     "main_s2k": GQEConfig("main_s2k", B=8, S=2048, D=1024, N=16, G=8, k=1, d=64),
     # long-context prefill, same layer
     "long_s128k": GQEConfig("long_s128k", B=1, S=131072, D=1024, N=16, G=8, k=1, d=64),
+    # the long-context layer at 1,048,576 tokens (the far end of the pages' 4k-1024k range)
+    "long_s1m": GQEConfig("long_s1m", B=1, S=1048576, D=1024, N=16, G=8, k=1, d=64),
     # Llama-shaped layer with a skewed router
     "llama_s8k_skew": GQEConfig("llama_s8k_skew", B=2, S=8192, D=4096, N=32, G=8, k=2,
                                 d=128, skew=True),
@@ -159,6 +166,30 @@ def make_prefill_inputs(cfg: GQEConfig, project: bool = True) -> dict:
         kk = _proj(x, w_k, cfg).reshape(B, S, G, d).permute(0, 2, 1, 3).contiguous()
         vv = _proj(x, w_v, cfg).reshape(B, S, G, d).permute(0, 2, 1, 3).contiguous()
     return dict(x=x, w_r=w_r, b_r=_router_bias(cfg), q=q, k=kk, v=vv, w_o=w_o, w_q=w_q, w_k=w_k, w_v=w_v)
+
+
+def make_attention_inputs(cfg: GQEConfig) -> dict:
+    """CPU tensors q, k, v for the attention alone (see the module docstring),
+    drawn without the projection so that sequences of a million tokens stay
+    cheap to make."""
+    B, S, N, G, d = cfg.B, cfg.S, cfg.N, cfg.G, cfg.d
+    rng = np.random.default_rng([cfg.seed, 404])
+    sd = np.float32(0.02 * math.sqrt(cfg.D))
+    q = torch.empty((B, S, N + 1, d), dtype=cfg.torch_dtype)
+    k = torch.empty((B, G, S, d), dtype=cfg.torch_dtype)
+    v = torch.empty((B, G, S, d), dtype=cfg.torch_dtype)
+    C = 65536
+    for b in range(B):
+        for s0 in range(0, S, C):
+            n = min(C, S - s0)
+            q[b, s0:s0 + n] = _store(rng.standard_normal((n, N + 1, d), dtype=np.float32) * sd, cfg)
+    for t in (k, v):
+        for b in range(B):
+            for g in range(G):
+                for s0 in range(0, S, C):
+                    n = min(C, S - s0)
+                    t[b, g, s0:s0 + n] = _store(rng.standard_normal((n, d), dtype=np.float32) * sd, cfg)
+    return dict(q=q, k=k, v=v)
 
 
 def _cache_block(seed: int, b: int, g: int, t: int, S: int, d: int, bf16: bool):

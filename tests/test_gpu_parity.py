@@ -298,6 +298,30 @@ def test_prefill_workloads_sampled(name):
         assert_close(o_s[b:b + 1, pos], ref_s, cfg.dtype, f"{name} b={b} O_shared ({what})")
 
 
+def test_prefill_million_tokens_sampled():
+    """One sequence of 1,048,576 tokens (the far end of the pages' 4k-1024k
+    range; the long-context layer's shape), in the launch configuration the
+    benchmark times: q, k and v drawn directly (too long to project on the
+    host), rows at tile edges, powers of two, the middle and the end, and a
+    few random positions against the oracle's full causal sums."""
+    cfg = synth.workload("long_s1m")
+    S = cfg.S
+    inp = synth.make_attention_inputs(cfg)
+    idx = synth.random_selection(cfg.B, S, cfg.G, cfg.M, cfg.k, 13)
+    print("long_s1m: inputs made", flush=True)
+    q, kk, vv = inp["q"].to(DEV), inp["k"].to(DEV), inp["v"].to(DEV)
+    o_r, o_s = gqe.prefill(dims_of(cfg), q, kk, vv, idx.to(DEV))
+    torch.cuda.synchronize()
+    print("long_s1m: kernel done", flush=True)
+    rng = np.random.default_rng(17)
+    pos = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, 65535, 65536, S // 2 - 1, S // 2, S - 2, S - 1],
+                                    rng.choice(np.arange(S), size=4, replace=False)]))
+    ref_r, ref_s = oracle.prefill(f64(inp["q"][:, torch.from_numpy(pos)]), f64(inp["k"]), f64(inp["v"]),
+                                  idx.numpy().reshape(1, S, cfg.G, cfg.k), cfg.M, positions=pos, q_rows_only=True)
+    assert_close(o_r[:, pos], ref_r, cfg.dtype, f"long_s1m O_routed ({pos.size} positions)")
+    assert_close(o_s[:, pos], ref_s, cfg.dtype, f"long_s1m O_shared ({pos.size} positions)")
+
+
 # Sequences past 8k tokens with ragged row counts: tile edges, skewed lists
 # and the striped tile order (G not a multiple of 8).
 LONG_FORM_CASES = [

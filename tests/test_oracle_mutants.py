@@ -42,11 +42,11 @@ MUTANTS = {
     "head_mapping_transposed": (
         "heads = g * M + idx[b, pos, g, j]\n                O_r", "heads = idx[b, pos, g, j] * G + g\n                O_r"),
     "shared_head_on_last_group": (
-        "O_s[b] = attend_rows(Q[b, pos, N, :], pos, K[b, 0], V[b, 0])",
-        "O_s[b] = attend_rows(Q[b, pos, N, :], pos, K[b, G - 1], V[b, G - 1])"),
+        "O_s[b] = attend_rows(Qp[b, :, N, :], pos, K[b, 0], V[b, 0])",
+        "O_s[b] = attend_rows(Qp[b, :, N, :], pos, K[b, G - 1], V[b, G - 1])"),
     "shared_head_uses_head0_query": (
-        "O_s[b] = attend_rows(Q[b, pos, N, :], pos, K[b, 0], V[b, 0])",
-        "O_s[b] = attend_rows(Q[b, pos, 0, :], pos, K[b, 0], V[b, 0])"),
+        "O_s[b] = attend_rows(Qp[b, :, N, :], pos, K[b, 0], V[b, 0])",
+        "O_s[b] = attend_rows(Qp[b, :, 0, :], pos, K[b, 0], V[b, 0])"),
     "decode_top_left_mask": (
         "pos = n - L + np.arange(L)", "pos = np.arange(L)"),
     "decode_shared_head_on_last_group": (
