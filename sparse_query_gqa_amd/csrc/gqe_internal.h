@@ -168,6 +168,9 @@ struct DecodeSplit {
 };
 DecodeSplit decode_split(int B, int G, int Smax, int k, int q_len);
 
+// Compute units of the current device (launch shapes that must fill the chip).
+int device_cus();
+
 hipError_t launch_route(const RouteParams& p, bool bf16, hipStream_t s);
 hipError_t launch_lists(const ListParams& p, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int d, bool bf16, hipStream_t s);

@@ -20,6 +20,8 @@
 // T <= 16 (decode), and for the tokens between a plain 128x128-tile kernel:
 // four wavefronts of 64x64 each on v_mfma_f32_32x32x16_bf16, W_O's tile
 // transposed into LDS to give the B operand k-contiguous lanes.
+#include <algorithm>
+
 #include "gqe_internal.h"
 
 namespace gqe {
@@ -180,7 +182,7 @@ constexpr int kPN = 256;  // output columns per tile
 constexpr int kPK = 32;   // k per step
 
 template <int DH, int MODE, int NS>
-__global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p) {
+__global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p, int cpw) {
   constexpr int AB = kPT * kPK * 2;  // A stage: 256 token rows x 64 bytes
   constexpr int WB = kPK * kPN * 2;  // W_O stage: 32 k rows x 512 bytes
   constexpr int SB = AB + WB;
@@ -189,7 +191,8 @@ __global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p) 
   constexpr bool weighted = MODE == 2;
   constexpr int OB = MODE == 0 ? kPT * DH * 2 : 0;  // obar tile (unpadded)
   constexpr int YPAD = kPN + 8;                     // output staging row stride
-  constexpr int LDSB = (NS * SB + OB) > (kPT * YPAD * 2) ? (NS * SB + OB) : (kPT * YPAD * 2);
+  static_assert((kPT / 2) * YPAD * 2 <= NS * SB, "half-tile staging fits in the ring");
+  constexpr int LDSB = NS * SB + OB;
   static_assert(LDSB <= 163840, "LDS");
   __shared__ __attribute__((aligned(1024))) char lds[LDSB];
   __bf16* obar = (__bf16*)(lds + NS * SB);  // [kPT][DH], 16-byte chunks swizzled per row
@@ -200,13 +203,17 @@ __global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p) 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int wm = wave & 1, wn = wave >> 1;  // token half, column quarter
+  // token tile ttile and column tiles c_lo .. c_hi-1 (cpw of them): obar is
+  // formed once and serves every column tile of the workgroup
   const int ncol = (p.Dout + kPN - 1) / kPN;
+  const int ngrp = (ncol + cpw - 1) / cpw;
   const int64_t ntok = (p.T + kPT - 1) / kPT;
   const int xcd = blockIdx.x % 8, jj = blockIdx.x / 8;
-  const int64_t ttile = xcd + 8 * (int64_t)(jj / ncol);
+  const int64_t ttile = xcd + 8 * (int64_t)(jj / ngrp);
   if (ttile >= ntok) return;
   const int64_t m0 = ttile * kPT;
-  const int n0 = (jj % ncol) * kPN;
+  const int c_lo = (jj % ngrp) * cpw, c_hi = min(ncol, c_lo + cpw);
+  int n0 = c_lo * kPN;
   const int hard = p.Gk * DH;
   const int nk = (hard + nob + nsh) / kPK;
   const __bf16* orr = (const __bf16*)p.o_r;
@@ -281,13 +288,8 @@ __global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p) 
     }
 
   f32x16 acc[2][4];  // [nb][tb]: 32 columns x 32 tokens
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // the first column tile's first stages load while obar is formed
 #pragma unroll
   for (int kt = 0; kt < NS - 1; ++kt) dma(kt, kt);
   // obar = sum over the G*k slots of w * o, in fp32, rounded to bf16; one
@@ -360,6 +362,20 @@ __global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p) 
         acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb][kk], af[tb][kk], acc[nb][tb], 0, 0, 0);
   };
 
+  for (int c = c_lo; c < c_hi; ++c) {
+  if (c > c_lo) {
+    // the previous column tile is stored (the barrier ending its epilogue):
+    // the ring takes this one's first stages
+    n0 = c * kPN;
+#pragma unroll
+    for (int kt = 0; kt < NS - 1; ++kt) dma(kt, kt);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   if constexpr (NS >= 4) {
     // stage 0 complete (stages 1 .. NS-2 may be in flight); the barrier also
     // publishes obar
@@ -392,32 +408,38 @@ __global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p) 
     }
   }
 
-  // output tile through LDS (the whole of it: ring and obar are free): lane
-  // (half, l32) of tile (nb, tb) holds token wm*128 + tb*32 + l32 and columns
-  // wn*64 + nb*32 + 8*(r/4) + 4*half + r%4
+  // output tile through the ring's LDS (obar stays for the next column
+  // tile), 128 token rows at a time: lane (half, l32) of tile (nb, tb) holds
+  // token wm*128 + tb*32 + l32 and columns wn*64 + nb*32 + 8*(r/4) + 4*half + r%4
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   __bf16* ys = (__bf16*)lds;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const int t = wm * 128 + tb * 32 + l32;
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        bf16x4 o4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o4[i] = f2bf(acc[nb][tb][4 * rq + i]);
-        *(bf16x4*)&ys[t * YPAD + wn * 64 + nb * 32 + 8 * rq + 4 * half] = o4;
-      }
-    }
-  __syncthreads();
   __bf16* y = (__bf16*)p.y;
-  for (int it = tid; it < kPT * (kPN / 8); it += 512) {
-    const int row = it / (kPN / 8), c8 = (it % (kPN / 8)) * 8;
-    const int64_t t = m0 + row;
-    const int n = n0 + c8;
-    if (t < p.T && n < p.Dout) *(bf16x8*)(y + t * p.Dout + n) = *(const bf16x8*)&ys[row * YPAD + c8];
+  for (int hh = 0; hh < 2; ++hh) {
+    if (wm == hh) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const int t = tb * 32 + l32;
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            bf16x4 o4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o4[i] = f2bf(acc[nb][tb][4 * rq + i]);
+            *(bf16x4*)&ys[t * YPAD + wn * 64 + nb * 32 + 8 * rq + 4 * half] = o4;
+          }
+        }
+    }
+    __syncthreads();
+    for (int it = tid; it < (kPT / 2) * (kPN / 8); it += 512) {
+      const int row = it / (kPN / 8), c8 = (it % (kPN / 8)) * 8;
+      const int64_t t = m0 + hh * (kPT / 2) + row;
+      const int n = n0 + c8;
+      if (t < p.T && n < p.Dout) *(bf16x8*)(y + t * p.Dout + n) = *(const bf16x8*)&ys[row * YPAD + c8];
+    }
+    __syncthreads();  // ys is rewritten next (the other half, or the next column tile's ring)
+  }
   }
 }
 
@@ -552,12 +574,22 @@ hipError_t launch_out_proj(const OutProjParams& p, bool bf16, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
   if (bf16 && p.T >= 256) {
     const int64_t ntok = (p.T + kPT - 1) / kPT;
-    const dim3 grid((unsigned)(8 * ((ntok + 7) / 8) * ((p.Dout + kPN - 1) / kPN)));
+    const int ncol = (p.Dout + kPN - 1) / kPN;
     const int mode = p.nob ? 0 : (p.weighted ? 2 : 1);
+    // With obar (mode 0), a workgroup takes several column tiles of its token
+    // tile, so that obar is formed once for them, as long as two workgroups
+    // per CU remain; otherwise one column tile each.
+    int cpw = 1;
+    if (mode == 0) {
+      const int64_t want = 2 * (int64_t)device_cus();
+      cpw = (int)std::max<int64_t>(1, std::min<int64_t>(ncol, ntok * ncol / want));
+    }
+    const int ngrp = (ncol + cpw - 1) / cpw;
+    const dim3 grid((unsigned)(8 * ((ntok + 7) / 8) * ngrp));
 #define GQE_OUT_PROJ_GEMM(DH)                                                                                    \
-  if (mode == 0) hipLaunchKernelGGL((out_proj_tile_kernel<DH, 0, DH <= 64 ? 4 : 3>), grid, dim3(512), 0, s, p); \
-  else if (mode == 1) hipLaunchKernelGGL((out_proj_tile_kernel<DH, 1, 4>), grid, dim3(512), 0, s, p);          \
-  else hipLaunchKernelGGL((out_proj_tile_kernel<DH, 2, 4>), grid, dim3(512), 0, s, p);
+  if (mode == 0) hipLaunchKernelGGL((out_proj_tile_kernel<DH, 0, DH <= 64 ? 4 : 3>), grid, dim3(512), 0, s, p, cpw); \
+  else if (mode == 1) hipLaunchKernelGGL((out_proj_tile_kernel<DH, 1, 4>), grid, dim3(512), 0, s, p, cpw);          \
+  else hipLaunchKernelGGL((out_proj_tile_kernel<DH, 2, 4>), grid, dim3(512), 0, s, p, cpw);
     switch (p.d) {
       case 32: GQE_OUT_PROJ_GEMM(32) break;
       case 64: GQE_OUT_PROJ_GEMM(64) break;

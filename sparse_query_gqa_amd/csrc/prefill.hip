@@ -26,6 +26,7 @@
 // 64 rows per wavefront for d <= 64 and 32 rows per wavefront for d = 128,
 // both software-pipelined so that MFMAs and the softmax of neighbouring
 // 32x32 score tiles overlap.
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
@@ -864,16 +865,19 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillParams p) {
   }
 }
 
-// Compute units of the current device (cached per device).
-static int device_cus() {
-  static int cus[64] = {};
+// Compute units of the current device (cached per device; a race between
+// two first calls only stores the same value twice).
+int device_cus() {
+  static std::atomic<int> cus[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
+  int c = cus[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
     int n = 0;
-    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+    c = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+    cus[dev].store(c, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return c;
 }
 
 // Form of the d <= 64 kernel: GQE_PREFILL_FORM=plain or split forces one
