@@ -533,6 +533,21 @@ def test_out_proj_small(T, G, k, d, D, dtype):
     assert_close(y, ref, dtype, f"out_proj T={T}")
 
 
+# Token tiles whose workgroup takes several 256-column tiles (obar formed once
+# for them): the group size is chosen from the tile count, so these sizes
+# give two (d = 64, ragged last column tile and token tile) and four (d = 128,
+# two column groups per token tile).
+@pytest.mark.parametrize("T,G,k,d,D", [(65613, 8, 1, 64, 1000), (66000, 8, 2, 128, 2048)])
+def test_out_proj_column_groups(T, G, k, d, D):
+    s = synth.make_slot_inputs(T, G, k, d, D, "bf16", seed=T)
+    g = to_dev(s)
+    dims = gqe.gqe_dims.make(1, T, D, G * k, G, k, d, "bf16")
+    y = gqe.out_proj(dims, T, g["o_r"], g["w"], g["o_s"], g["w_o"])
+    torch.cuda.synchronize()
+    ref = oracle.out_proj(f64(s["o_r"]), f64(s["w"]), f64(s["o_s"]), f64(s["w_o"]))
+    assert_close(y, ref, "bf16", f"out_proj T={T} D={D} (column groups)")
+
+
 @pytest.mark.parametrize("mode", ["hard", "weighted"])
 @pytest.mark.parametrize("T,G,k,d,D,dtype", [(5, 4, 2, 64, 136, "bf16"), (16, 8, 2, 128, 4096, "bf16"),
                                              (100, 8, 2, 64, 264, "bf16"), (300, 8, 1, 64, 1024, "bf16"),

@@ -62,6 +62,7 @@ PREFILL_CASES = [
     (1, 3000, 256, 16, 4, 1, 64, "bf16", True),   # 1536-token supersteps: shared head and the favoured
                                                   # experts take more than one 512-row pass
     (1, 1000, 128, 6, 3, 1, 64, "bf16", False),   # 384 key/value columns: a half-empty 256-column tile
+    (1, 2000, 256, 16, 4, 1, 128, "bf16", True),  # d = 128 head tiles (k32 ring) over several passes
     (1, 128, 256, 4, 2, 1, 32, "f32", False),
     (2, 77, 40, 8, 2, 2, 64, "f32", False),       # fp32 takes any D % 8
 ]
