@@ -279,7 +279,10 @@ __device__ __forceinline__ void stage_out(__bf16* ys, int xr0, int wc0, const f3
 // Loads of one tile stage, lane by lane: loads 0 .. NX-1 are x chunks from
 // `rx` (chunk `xc0 + i` of the stage), loads NX .. NX+NW-1 weight chunks from
 // `rw` (chunk `wc0 + i` of the weight region at byte wbase), or into the
-// sink when `wreal` is false. Offsets advance by `kb` bytes per stage.
+// sink when `wreal` is false. Offsets advance by `kb` bytes per stage. With
+// `skip` (only where every wait is vmcnt(0) or counts the warming loads
+// alone, as in gemm_k64), x chunks from `xlive` on, whose rows all lie past
+// the pass's row count, and weight loads into the sink are not issued.
 template <int NX, int NW>
 struct TileLoads {
   char* lds;
@@ -287,11 +290,16 @@ struct TileLoads {
   bool wreal;
   i32x4 rx, rw;
   uint32_t xoff[NX], woff[NW];
+  bool skip = false;
+  int xlive = NX;
   __device__ __forceinline__ void one(const int kt, const int st, const int i) const {
     const uint32_t k2 = (uint32_t)min(kt, nk - 1) * (uint32_t)kb;
     char* base = lds + st * sb;
-    if (i < NX) lds_dma16_b(rx, xoff[i] + k2, base + (xc0 + i) * 1024);
-    else lds_dma16_b(rw, woff[i - NX] + k2, wreal ? base + wbase + (wc0 + i - NX) * 1024 : lds + sink);
+    if (i < NX) {
+      if (!skip || i < xlive) lds_dma16_b(rx, xoff[i] + k2, base + (xc0 + i) * 1024);
+    } else if (!skip || wreal) {
+      lds_dma16_b(rw, woff[i - NX] + k2, wreal ? base + wbase + (wc0 + i - NX) * 1024 : lds + sink);
+    }
   }
 };
 
@@ -436,6 +444,10 @@ __global__ __launch_bounds__(512, 1) void proj_tile_kernel(ProjParams p, int U, 
         ld.xoff[i] = row < nr ? (uint32_t)rows_s[c0 + row] * rowb + piece_off8(row, lane) : xend;
       }
       ld.woff[0] = (uint32_t)(lane >> 3) * rowb + piece_off8(8 * wave + (lane >> 3), lane);
+      // chunks past the pass's rows carry nothing (a quarter of them at an
+      // expected 384 of 512 rows): gemm_k64 waits for everything, so they go
+      ld.skip = true;
+      ld.xlive = __builtin_amdgcn_readfirstlane(min(8, max(0, (nr - 64 * wave + 7) / 8)));
       gemm_k64<kHR, RBH, CBH, SBH, 9, 2>(lds, p.D / 64, WR * wm, 64 * wn, WR * wm < nr, ld, pf, acc);
     } else {
       // x chunks 4 wave + i: rows 64 wave + 16 i + lane / 4 of the pass
