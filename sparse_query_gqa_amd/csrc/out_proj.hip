@@ -293,32 +293,52 @@ __global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p, 
 #pragma unroll
   for (int kt = 0; kt < NS - 1; ++kt) dma(kt, kt);
   // obar = sum over the G*k slots of w * o, in fp32, rounded to bf16; one
-  // 8-column piece of one token per work item, issued after the first
-  // stages' loads so that they are in flight meanwhile
-  for (int it = tid; nob && it < kPT * (DH / 8); it += 512) {
-    const int row = it / (DH / 8), e = (it % (DH / 8)) * 8;
-    const int64_t t = min(m0 + row, tmax);
-    float sacc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    // slots in groups of eight whose loads are all issued before the first
-    // product (a runtime trip count would otherwise serialise their latencies)
-    for (int j0 = 0; j0 < p.Gk; j0 += 8) {
-      bf16x8 ov[8];
-      float wj[8];
+  // 8-column piece of one token per work item, DH/16 items per thread. The
+  // loads of up to four items (eight slots each) are issued together before
+  // their products, beside the first stages' loads (the MFMA accumulators are
+  // not live yet, so the registers are there): with a runtime slot count the
+  // compiler would otherwise serialise their latencies.
+  constexpr int NIT = DH / 16;           // items per thread
+  constexpr int IB = NIT < 4 ? NIT : 4;  // items per batch
+  for (int b0 = 0; nob && b0 < NIT; b0 += IB) {
+    int row[IB], e[IB];
+    int64_t t[IB];
+    float sacc[IB][8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = min(j0 + u, p.Gk - 1);
-        ov[u] = *(const bf16x8*)(orr + t * hard + j * DH + e);
-        wj[u] = j0 + u < p.Gk ? p.w[t * p.Gk + j] : 0.f;
-      }
+    for (int b = 0; b < IB; ++b) {
+      const int it = tid + 512 * (b0 + b);
+      row[b] = it / (DH / 8);
+      e[b] = (it % (DH / 8)) * 8;
+      t[b] = min(m0 + row[b], tmax);
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) sacc[i] = fmaf(wj[u], (float)ov[u][i], sacc[i]);
+      for (int i = 0; i < 8; ++i) sacc[b][i] = 0.f;
     }
-    bf16x8 r;
+    for (int j0 = 0; j0 < p.Gk; j0 += 8) {
+      bf16x8 ov[IB][8];
+      float wj[IB][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = f2bf(sacc[i]);
-    *(bf16x8*)&obar[row * DH + 8 * ((e >> 3) ^ oswz(row))] = r;
+      for (int b = 0; b < IB; ++b)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int j = min(j0 + u, p.Gk - 1);
+          ov[b][u] = *(const bf16x8*)(orr + t[b] * hard + j * DH + e[b]);
+          wj[b][u] = j0 + u < p.Gk ? p.w[t[b] * p.Gk + j] : 0.f;
+        }
+      // slots in order, as one item at a time would add them
+#pragma unroll
+      for (int b = 0; b < IB; ++b)
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sacc[b][i] = fmaf(wj[b][u], (float)ov[b][u][i], sacc[b][i]);
+    }
+#pragma unroll
+    for (int b = 0; b < IB; ++b) {
+      bf16x8 r;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r[i] = f2bf(sacc[b][i]);
+      *(bf16x8*)&obar[row[b] * DH + 8 * ((e[b] >> 3) ^ oswz(row[b]))] = r;
+    }
   }
 
   bf16x8 af[4][2], wf[2][2];  // [tb or nb][kk]
@@ -577,11 +597,11 @@ hipError_t launch_out_proj(const OutProjParams& p, bool bf16, hipStream_t s) {
     const int ncol = (p.Dout + kPN - 1) / kPN;
     const int mode = p.nob ? 0 : (p.weighted ? 2 : 1);
     // With obar (mode 0), a workgroup takes several column tiles of its token
-    // tile, so that obar is formed once for them, as long as two workgroups
-    // per CU remain; otherwise one column tile each.
+    // tile, so that obar is formed once for them, as long as every CU still
+    // gets a workgroup (one runs per CU); otherwise one column tile each.
     int cpw = 1;
     if (mode == 0) {
-      const int64_t want = 2 * (int64_t)device_cus();
+      const int64_t want = (int64_t)device_cus();
       cpw = (int)std::max<int64_t>(1, std::min<int64_t>(ncol, ntok * ncol / want));
     }
     const int ngrp = (ncol + cpw - 1) / cpw;
