@@ -522,7 +522,9 @@ def test_decode_deterministic(d, q_len):
                                              (16, 1, 1, 32, 8, "bf16"), (5, 4, 2, 64, 136, "bf16"),
                                              (11, 32, 4, 128, 264, "bf16"),
                                              # GEMM kernel: d=32, ragged columns and tokens
-                                             (256, 2, 3, 32, 264, "bf16"), (1000, 4, 2, 128, 8, "bf16")])
+                                             (256, 2, 3, 32, 264, "bf16"), (1000, 4, 2, 128, 8, "bf16"),
+                                             # 64-k GEMM form (d=64): 16 and 9 hard slots, ragged tiles
+                                             (513, 8, 2, 64, 264, "bf16"), (700, 3, 3, 64, 520, "bf16")])
 def test_out_proj_small(T, G, k, d, D, dtype):
     s = synth.make_slot_inputs(T, G, k, d, D, dtype, seed=T)
     g = to_dev(s)
@@ -551,7 +553,8 @@ def test_out_proj_column_groups(T, G, k, d, D):
 @pytest.mark.parametrize("mode", ["hard", "weighted"])
 @pytest.mark.parametrize("T,G,k,d,D,dtype", [(5, 4, 2, 64, 136, "bf16"), (16, 8, 2, 128, 4096, "bf16"),
                                              (100, 8, 2, 64, 264, "bf16"), (300, 8, 1, 64, 1024, "bf16"),
-                                             (1000, 4, 2, 128, 8, "bf16"), (130, 2, 2, 64, 72, "f32")])
+                                             (1000, 4, 2, 128, 8, "bf16"), (130, 2, 2, 64, 72, "f32"),
+                                             (700, 3, 3, 64, 520, "bf16")])
 def test_out_proj_ablation_variants(mode, T, G, k, d, D, dtype):
     """The two slot layouts of the ablation table through every kernel path
     (few-token, 128x128-tile, pipelined GEMM, fp32): the hard slots alone,
