@@ -377,6 +377,32 @@ def main():
 
     t_qkv = timed(proj_call, args.steps)
     t_dqkv = timed(dproj_call, args.steps)
+
+    # The whole decode step (routing, projections with the K/V append,
+    # attention, output projection) launched call by call, and the same calls
+    # captured once in a HIP graph and replayed: a step of small launches,
+    # where the graph removes the gaps between them.
+    def dstep_calls():
+        gqe.gqe_route(rdims, dg["x"], dg["w_r"], dg["b_r"], None, d_idx, d_w, None, None, None)
+        gqe.gqe_qkv_proj_decode(ddims, dcfg.q_len, dx3, dg["w_q"], dg["w_k"], dg["w_v"], d_idx,
+                                dg["kv_len"], dq_p, dg["k"], dg["v"])
+        gqe.gqe_attn_decode(ddims, dcfg.q_len, dq_p, dg["k"], dg["v"], dg["kv_len"], d_idx, d_or, d_os, d_ws)
+        gqe.gqe_out_proj(ddims, dT, d_or.view(dT, dcfg.G, dcfg.k, dcfg.d), d_w, d_os.view(dT, dcfg.d),
+                         dg["w_o"], d_y)
+
+    t_dstep = timed(dstep_calls, args.steps)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dstep_calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    dgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(dgraph):
+        dstep_calls()
+    torch.cuda.synchronize()
+    t_dgraph = timed(dgraph.replay, args.steps)
+    del dgraph
     # for comparison: one dense bf16 product (torch -> hipBLASLt) of every
     # query head, K and V, the work the token compaction avoids
     w_all = torch.cat([g["w_q"], g["w_k"], g["w_v"]], 0).contiguous()
@@ -542,6 +568,8 @@ def main():
             },
             "ms_per_call": round(t_dec.mean() * 1e3, 4),
             "path_ms": round(t_decode.mean() * 1e3, 4),
+            "step_with_projections": {"eager_ms": round(t_dstep.mean() * 1e3, 4),
+                                      "hip_graph_ms": round(t_dgraph.mean() * 1e3, 4)},
             "paged": {"page_size": page, "order": "shuffled", "value": round(paged_gbps, 1), "unit": "GB/s",
                       "frac": round(paged_gbps * 1e9 / PEAK_HBM_BPS, 4),
                       "ms_per_call": round(t_paged.mean() * 1e3, 4)},
