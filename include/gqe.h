@@ -23,7 +23,10 @@
  *     keeps no state between calls.
  *   - stream is a hipStream_t passed as void* (NULL = the default stream).
  *     All work is enqueued asynchronously on it; faults inside a kernel
- *     surface at the caller's next synchronisation.
+ *     surface at the caller's next synchronisation. Every call enqueues
+ *     kernel launches only (no memset, copy or host wait), so it may be
+ *     captured into a HIP graph, and calls on different streams may run
+ *     concurrently (gqe_attn_decode_noalloc excepted: see there).
  *   - Arguments are validated before anything is enqueued. A call that
  *     returns an error has enqueued nothing and written nothing.
  *   - Supported: head_dim d in {32, 64, 128}; G >= 1 dividing N; 1 <= k <= M;
