@@ -391,6 +391,21 @@ def main():
                          dg["w_o"], d_y)
 
     t_dstep = timed(dstep_calls, args.steps)
+
+    # The output projection's ablation slot layouts (hard slots alone; hard
+    # slots times the selected router probabilities), timed on the step's
+    # attention outputs: W_O has G*k*d rows, there is no obar and no shared slot.
+    p_sel = torch.empty((T, G, k), dtype=torch.float32, device=dev)
+    gqe.gqe_route(dims, g["x"], g["w_r"], g["b_r"], None, r_out["topk_idx"], r_out["topk_w"], None, None, None,
+                  topk_p=p_sel)
+    w_o_hard = g["w_o"][:G * k * d].contiguous()
+    y_abl = torch.empty_like(y)
+    t_abl = {}
+    for name, code, sw in (("hard", gqe.GQE_SLOTS_HARD, None), ("weighted", gqe.GQE_SLOTS_WEIGHTED, p_sel)):
+        t_abl[name] = timed(lambda: gqe.gqe_out_proj_variant(dims, code, T, o_r.view(T, G, k, d), sw, None, w_o_hard,
+                                                             y_abl), args.steps)
+    abl_flop = 2 * T * G * k * d * cfg.D
+    del y_abl, w_o_hard, p_sel
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -587,6 +602,11 @@ def main():
         "routing": routing,
         "prefill_workloads": extra,
         "qkv_proj": qkv,
+        "ablation_out_proj": {
+            name: {"ms": round(t_abl[name].mean() * 1e3, 4), "flop": abl_flop,
+                   "tflops": round(abl_flop / t_abl[name].mean() / 1e12, 2),
+                   "frac": round(abl_flop / t_abl[name].mean() / PEAK_BF16_FLOPS, 4)}
+            for name in ("hard", "weighted")},
         "train_bwd": train_bwd,
         "flop_per_step": fl,
         "wall_s": round(wall, 3),
