@@ -193,8 +193,13 @@ __global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p, 
   constexpr int YPAD = kPN + 8;                     // output staging row stride
   static_assert((kPT / 2) * YPAD * 2 <= NS * SB, "half-tile staging fits in the ring");
   constexpr int LDSB = NS * SB + OB;
-  static_assert(LDSB <= 163840, "LDS");
+  // weighted layout: the token tile's slot weights of the first WSL slots,
+  // [slot][token], loaded once (a global load inside the k loop would make its
+  // vmcnt wait drain the LDS-DMA ring, whose loads were issued before it)
+  constexpr int WSL = weighted ? 32 : 0;
+  static_assert(LDSB + kPT * WSL * 4 <= 163840, "LDS");
   __shared__ __attribute__((aligned(1024))) char lds[LDSB];
+  __shared__ float wlds[weighted ? kPT * WSL : 1];
   __bf16* obar = (__bf16*)(lds + NS * SB);  // [kPT][DH], 16-byte chunks swizzled per row
   // obar chunk c of token row t sits at chunk position c ^ oswz(t), so that the
   // fragment reads (32 consecutive rows, one chunk each) hit distinct banks
@@ -289,6 +294,13 @@ __global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p, 
 
   f32x16 acc[2][4];  // [nb][tb]: 32 columns x 32 tokens
 
+  if constexpr (weighted) {
+    const int nsl = min(p.Gk, WSL);
+    for (int i = tid; i < kPT * nsl; i += 512) {
+      const int j = i / kPT, t = i % kPT;
+      wlds[j * kPT + t] = p.w[min(m0 + t, tmax) * p.Gk + j];
+    }
+  }
   // the first column tile's first stages load while obar is formed
 #pragma unroll
   for (int kt = 0; kt < NS - 1; ++kt) dma(kt, kt);
@@ -355,7 +367,8 @@ __global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p, 
         af[tb][kk] = *(const bf16x8*)(sbase + a_frag[tb][kk]);
       }
       if (weighted && k0 < hard) {
-        const float wsc = p.w[min(m0 + wm * 128 + tb * 32 + l32, tmax) * p.Gk + k0 / DH];
+        const int tl = wm * 128 + tb * 32 + l32, slot = k0 / DH;
+        const float wsc = slot < WSL ? wlds[slot * kPT + tl] : p.w[min(m0 + tl, tmax) * p.Gk + slot];
 #pragma unroll
         for (int i = 0; i < 8; ++i) af[tb][kk][i] = f2bf((float)af[tb][kk][i] * wsc);
       }
