@@ -34,9 +34,10 @@ struct TileCoord {
 // XCDs. A routed index past the last routed tile (S*k not a multiple of
 // 256) and the unused tail of a shorter XCD list are invalid blocks, which
 // exit at once.
-__device__ __forceinline__ TileCoord tile_of_block(const PrefillParams& p, int tiles_r, int tiles_s) {
+// The map as a function of the block index i, for the host as well (the
+// tests enumerate it); kernels call tile_of_block.
+__host__ __device__ inline TileCoord tile_of_index(const PrefillParams& p, int tiles_r, int tiles_s, int i) {
   TileCoord c;
-  const int i = blockIdx.x;
   int sr, rem;
   int nsh, sh_b0, sh_bstep;   // shared tiles first in rem: b = sh_b0 + sh_bstep*r, r < nsh
   int gsel, gstride, gcount;  // routed groups of this list: gsel + gstride*j, j < gcount
@@ -90,6 +91,10 @@ __device__ __forceinline__ TileCoord tile_of_block(const PrefillParams& p, int t
     if (step >= p.K || c.tile >= tiles_r) c.valid = false;
   }
   return c;
+}
+
+__device__ __forceinline__ TileCoord tile_of_block(const PrefillParams& p, int tiles_r, int tiles_s) {
+  return tile_of_index(p, tiles_r, tiles_s, blockIdx.x);
 }
 
 // Grid size for tile_of_block: 8 lists of tiles_s super-rounds, or striped
