@@ -5,8 +5,9 @@
 // weights w_m = p_m / sum_{m' in K_g} p_{m'}.
 //
 // Router scores are a skinny product z[T, G*M] = x[T, D] W_r^T. For bf16 it
-// runs on MFMA (16x16x32 bf16 -> fp32): a workgroup owns 16 tokens and all
-// G*M experts, its wavefronts splitting the features, streaming x once from
+// runs on MFMA (16x16x32 bf16 -> fp32): a workgroup owns 64 tokens (16 when
+// there are at most 16) and all G*M experts, its wavefronts splitting the
+// features, streaming x once from
 // HBM with 16-byte loads; W_r (at most 256 x D bf16) stays hot in L2. The
 // fp32 path is a plain VALU dot product.
 // The reduction order is fixed, so the emitted logits - and therefore the
@@ -15,8 +16,7 @@
 
 namespace gqe {
 
-constexpr int kRouteTok = 16;       // tokens per workgroup (fp32)
-constexpr int kRouteBlockTok = 64;  // tokens per workgroup (bf16)
+constexpr int kRouteTok = 16;  // tokens per workgroup (fp32)
 
 // Selection epilogue: z for kRouteTok tokens in LDS ([tok][G*M], bias
 // included). One thread per (token, group): TopK by repeated first-maximum
@@ -65,24 +65,25 @@ __device__ void route_select_store(const float* zs, int ntok, int64_t tok0,
   }
 }
 
-// bf16 router scores on MFMA. A block takes 64 tokens (four 16-token tiles)
-// and all G*M experts; its W wavefronts split the 32-wide feature steps, and
-// the W partial score tiles are summed in LDS in wavefront order (fixed, so
-// the logits are deterministic). Each wavefront loads a batch of SB steps -
-// x fragments of its four token tiles and W_r fragments of its NT expert
-// tiles - before the batch's MFMAs, so the loads of a batch are in flight
-// together; each W_r fragment feeds four MFMAs.
+// bf16 router scores on MFMA. A block takes TT 16-token tiles (four; one
+// when there are at most 16 tokens, as in decode, so that the LDS partials
+// leave room for up to 16 wavefronts) and all G*M experts; its W wavefronts
+// split the 32-wide feature steps, and the W partial score tiles are summed
+// in LDS in wavefront order (fixed, so the logits are deterministic). Each
+// wavefront loads a batch of SB steps - x fragments of its TT token tiles and
+// W_r fragments of its NT expert tiles - before the batch's MFMAs, so the
+// loads of a batch are in flight together; each W_r fragment feeds TT MFMAs.
 // 16x16x32 operand layout: lane l holds A[l%16][8*(l/16) .. +8] (token row,
 // 8 consecutive features) and B[8*(l/16) .. +8][l%16] (expert column); the
 // result D[4*(l/16)+i][l%16] lands in register i.
-constexpr int kRouteTT = kRouteBlockTok / 16;  // token tiles per block
 
-template <int NT, int SB, int MAXW>
+template <int NT, int SB, int MAXW, int TT>
 __global__ __launch_bounds__(64 * MAXW) void route_bf16_kernel(RouteParams p) {
+  constexpr int BT = 16 * TT;  // tokens per block
   extern __shared__ float zpart[];  // [W][64][GM]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, W = blockDim.x >> 6;
-  const int64_t tok0 = (int64_t)blockIdx.x * kRouteBlockTok;
-  const int ntok = (int)((p.T - tok0) < kRouteBlockTok ? (p.T - tok0) : kRouteBlockTok);
+  const int64_t tok0 = (int64_t)blockIdx.x * BT;
+  const int ntok = (int)((p.T - tok0) < BT ? (p.T - tok0) : BT);
   const int GM = p.G * p.M;
   const int D = p.D;
   const __bf16* x = (const __bf16*)p.x;
@@ -91,9 +92,9 @@ __global__ __launch_bounds__(64 * MAXW) void route_bf16_kernel(RouteParams p) {
   const int row = lane & 15;
   const int kof = 8 * (lane >> 4);
   // token rows past T read row T-1; their scores are not used
-  const __bf16* xrow[kRouteTT];
+  const __bf16* xrow[TT];
 #pragma unroll
-  for (int tt = 0; tt < kRouteTT; ++tt)
+  for (int tt = 0; tt < TT; ++tt)
     xrow[tt] = x + min(tok0 + tt * 16 + row, p.T - 1) * (int64_t)D;
   // expert rows past G*M read row G*M-1; their scores are not stored
   const __bf16* wrow[NT];
@@ -102,36 +103,36 @@ __global__ __launch_bounds__(64 * MAXW) void route_bf16_kernel(RouteParams p) {
   const int nsteps = (D + 31) / 32;
   const int st0 = (int)((int64_t)w * nsteps / W), st1 = (int)((int64_t)(w + 1) * nsteps / W);
 
-  f32x4 acc[kRouteTT][NT];
+  f32x4 acc[TT][NT];
 #pragma unroll
-  for (int tt = 0; tt < kRouteTT; ++tt)
+  for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
     for (int e = 0; e < NT; ++e) acc[tt][e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const bf16x8 zero8 = {};
   for (int sb = st0; sb < st1; sb += SB) {
-    bf16x8 a[SB][kRouteTT], bw[SB][NT];
+    bf16x8 a[SB][TT], bw[SB][NT];
 #pragma unroll
     for (int i = 0; i < SB; ++i) {
       // D is a multiple of 8; a 32-wide step may run past D only in its tail
       const int c = (sb + i) * 32 + kof;
       const bool ok = sb + i < st1 && c < D;
 #pragma unroll
-      for (int tt = 0; tt < kRouteTT; ++tt) a[i][tt] = ok ? *(const bf16x8*)(xrow[tt] + c) : zero8;
+      for (int tt = 0; tt < TT; ++tt) a[i][tt] = ok ? *(const bf16x8*)(xrow[tt] + c) : zero8;
 #pragma unroll
       for (int e = 0; e < NT; ++e) bw[i][e] = ok ? *(const bf16x8*)(wrow[e] + c) : zero8;
     }
 #pragma unroll
     for (int i = 0; i < SB; ++i)
 #pragma unroll
-      for (int tt = 0; tt < kRouteTT; ++tt)
+      for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
         for (int e = 0; e < NT; ++e)
           acc[tt][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][tt], bw[i][e], acc[tt][e], 0, 0, 0);
   }
-  float* zw = zpart + (size_t)w * kRouteBlockTok * GM;
+  float* zw = zpart + (size_t)w * BT * GM;
 #pragma unroll
-  for (int tt = 0; tt < kRouteTT; ++tt)
+  for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
     for (int e = 0; e < NT; ++e) {
       const int ex = e * 16 + row;  // output column = expert
@@ -142,9 +143,9 @@ __global__ __launch_bounds__(64 * MAXW) void route_bf16_kernel(RouteParams p) {
     }
   __syncthreads();
   // sum the wavefront partials in order, add the bias; result in slice 0
-  for (int idx = threadIdx.x; idx < kRouteBlockTok * GM; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < BT * GM; idx += blockDim.x) {
     float z = zpart[idx];
-    for (int ww = 1; ww < W; ++ww) z += zpart[(size_t)ww * kRouteBlockTok * GM + idx];
+    for (int ww = 1; ww < W; ++ww) z += zpart[(size_t)ww * BT * GM + idx];
     zpart[idx] = z + (p.bias ? p.bias[idx % GM] : 0.f);
   }
   __syncthreads();
@@ -253,16 +254,17 @@ __global__ __launch_bounds__(64) void list_scatter_kernel(ListParams p) {
   }
 }
 
-template <int NT, int SB, int MAXW>
+template <int NT, int SB, int MAXW, int TT>
 static void launch_route_bf16(const RouteParams& p, hipStream_t s) {
   // wavefronts per block: about 256 features each, at most MAXW, and the
-  // [W][64][G*M] fp32 partials within 64 KB of LDS
+  // [W][16*TT][G*M] fp32 partials within 64 KB of LDS
+  constexpr int BT = 16 * TT;
   const int GM = p.G * p.M;
   int W = 1;
-  while (W < MAXW && W * 2 * 256 <= p.D && W * 2 * kRouteBlockTok * GM * 4 <= 65536) W *= 2;
-  const size_t lds = (size_t)W * kRouteBlockTok * GM * sizeof(float);
-  const unsigned nblk = (unsigned)((p.T + kRouteBlockTok - 1) / kRouteBlockTok);
-  hipLaunchKernelGGL((route_bf16_kernel<NT, SB, MAXW>), dim3(nblk), dim3(64 * W), lds, s, p);
+  while (W < MAXW && W * 2 * 256 <= p.D && W * 2 * BT * GM * 4 <= 65536) W *= 2;
+  const size_t lds = (size_t)W * BT * GM * sizeof(float);
+  const unsigned nblk = (unsigned)((p.T + BT - 1) / BT);
+  hipLaunchKernelGGL((route_bf16_kernel<NT, SB, MAXW, TT>), dim3(nblk), dim3(64 * W), lds, s, p);
 }
 
 hipError_t launch_route(const RouteParams& p, bool bf16, hipStream_t s) {
@@ -270,11 +272,19 @@ hipError_t launch_route(const RouteParams& p, bool bf16, hipStream_t s) {
     const int nt = (p.G * p.M + 15) / 16;  // 16-expert tiles
     // batch size and block size keep the fragments and accumulators within
     // the register budget of the block size
-    if (nt <= 1) launch_route_bf16<1, 4, 16>(p, s);
-    else if (nt <= 2) launch_route_bf16<2, 2, 16>(p, s);
-    else if (nt <= 4) launch_route_bf16<4, 1, 16>(p, s);
-    else if (nt <= 8) launch_route_bf16<8, 1, 4>(p, s);
-    else launch_route_bf16<16, 1, 4>(p, s);
+    if (p.T <= 16) {
+      // a few tokens (decode): one token tile per block, so that the partials
+      // leave room for more wavefronts over the features
+      if (nt <= 1) launch_route_bf16<1, 4, 16, 1>(p, s);
+      else if (nt <= 2) launch_route_bf16<2, 4, 16, 1>(p, s);
+      else if (nt <= 4) launch_route_bf16<4, 2, 16, 1>(p, s);
+      else if (nt <= 8) launch_route_bf16<8, 1, 16, 1>(p, s);
+      else launch_route_bf16<16, 1, 8, 1>(p, s);
+    } else if (nt <= 1) launch_route_bf16<1, 4, 16, 4>(p, s);
+    else if (nt <= 2) launch_route_bf16<2, 2, 16, 4>(p, s);
+    else if (nt <= 4) launch_route_bf16<4, 1, 16, 4>(p, s);
+    else if (nt <= 8) launch_route_bf16<8, 1, 4, 4>(p, s);
+    else launch_route_bf16<16, 1, 4, 4>(p, s);
   } else {
     const unsigned nblk = (unsigned)((p.T + kRouteTok - 1) / kRouteTok);
     hipLaunchKernelGGL(route_f32_kernel, dim3(nblk), dim3(64), 0, s, p);

@@ -57,7 +57,10 @@ def small_cfg(B, S, D, N, G, k, d, dtype="bf16", seed=0, skew=False):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("B,S,D,G,M,k", [(1, 1, 8, 1, 1, 1), (2, 77, 40, 3, 4, 2), (1, 130, 64, 8, 2, 1),
                                          (3, 64, 96, 2, 32, 5), (1, 200, 256, 8, 32, 32),
-                                         (2, 150, 128, 16, 16, 3)])
+                                         (2, 150, 128, 16, 16, 3),
+                                         # at most 16 tokens (one token tile per block) and just past
+                                         (2, 8, 512, 8, 4, 2), (4, 4, 4096, 8, 32, 3), (16, 1, 1024, 16, 8, 2),
+                                         (1, 17, 96, 2, 8, 2)])
 def test_route_exact_with_ties(dtype, B, S, D, G, M, k):
     """Integer-valued x and W_r make every logit exact in fp32, so the
     selection must equal the oracle's bit for bit, planted ties included
