@@ -207,17 +207,23 @@ def _prefill_inputs(cfg, peaked):
 FORMS = ["auto", "plain", "split"]
 
 
+def _with_forms(cases, d_of, dtype_of=lambda c: "bf16"):
+    """(case, form) pairs: every case under the launcher's own choice, and the
+    bf16 d <= 64 cases also under each forced form (the d = 128 and fp32
+    kernels have one form)."""
+    return [pytest.param(c, f, id="-".join(map(str, c)) + "-" + f)
+            for c in cases for f in FORMS if f == "auto" or (d_of(c) <= 64 and dtype_of(c) == "bf16")]
+
+
 def _set_form(monkeypatch, form, d, dtype):
-    if form != "auto" and (d > 64 or dtype != "bf16"):
-        pytest.skip("one form only (d = 128 or fp32 kernel)")
+    assert form == "auto" or (d <= 64 and dtype == "bf16")
     if form == "auto":
         monkeypatch.delenv("GQE_PREFILL_FORM", raising=False)
     else:
         monkeypatch.setenv("GQE_PREFILL_FORM", form)
 
 
-@pytest.mark.parametrize("form", FORMS)
-@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("case,form", _with_forms(PREFILL_CASES, lambda c: c[6], lambda c: c[7]))
 def test_prefill_small(case, form, monkeypatch):
     B, S, D, N, G, k, d, dtype, peaked = case
     _set_form(monkeypatch, form, d, dtype)
@@ -247,8 +253,7 @@ RAMP_CASES = [
 ]
 
 
-@pytest.mark.parametrize("form", FORMS)
-@pytest.mark.parametrize("case", RAMP_CASES, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("case,form", _with_forms(RAMP_CASES, lambda c: c[6]))
 def test_prefill_reference_moves(case, form, monkeypatch):
     B, S, D, N, G, k, d, rising = case
     _set_form(monkeypatch, form, d, "bf16")
@@ -336,8 +341,7 @@ LONG_FORM_CASES = [
 ]
 
 
-@pytest.mark.parametrize("form", FORMS)
-@pytest.mark.parametrize("case", LONG_FORM_CASES, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("case,form", _with_forms(LONG_FORM_CASES, lambda c: c[6]))
 def test_prefill_long_form(case, form, monkeypatch):
     """Rows around every 256-row tile edge, the first and last rows and a
     random sample, against the oracle; also the training forward's lse."""
