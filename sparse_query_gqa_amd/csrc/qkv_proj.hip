@@ -79,11 +79,14 @@ __device__ __forceinline__ void* out_base(const ProjParams& p, int kind) {
 // count U k / M near 384, so that one pass almost always takes it.
 // Products: v_mfma_f32_32x32x16_bf16, weight rows as the A operand and x rows
 // as B, 512 threads. Operands reach LDS by raw-buffer LDS-DMA (rows past a
-// tensor's end read zeros), k in steps of 64 in two buffers (k in steps of
-// 32 in three for the d = 128 head tiles, whose two k64 buffers would not fit
-// with the row list); the next stage's loads go out between the products of
-// the current one, so each stage costs one barrier. The tile goes back to
-// HBM through LDS in 16-byte pieces.
+// tensor's end read zeros), k in steps of 64 in two buffers for the dense
+// tiles (and the d = 32 head tiles); the head tiles of d = 64 and 128 take k
+// in steps of 32 through a ring of four and three buffers, so that the
+// gathered x rows of two or three stages are in flight (one k64 stage in
+// flight left their latency exposed; d = 128 has room for three). The next
+// stage's loads go out between the products of the current one, so each
+// stage costs one barrier. The tile goes back to HBM through LDS in 16-byte
+// pieces.
 // ---------------------------------------------------------------------------
 constexpr int kDT = 256;     // dense tile: tokens and columns
 constexpr int kHR = 512;     // head tile: rows per pass
@@ -305,12 +308,12 @@ struct TileLoads {
 
 template <int D>
 __global__ __launch_bounds__(512, 1) void proj_tile_kernel(ProjParams p, int U, int per_super, int n_kv, int per) {
-  constexpr bool H64 = D <= 64;            // head tiles in k64 stages
+  constexpr bool H64 = D <= 32;            // head tiles in k64 stages
   constexpr int RBH = D == 128 ? 4 : 2;    // head tile: wavefront rows / 32
   constexpr int CBH = D == 32 ? 1 : 2;     // head tile: wavefront columns / 32
   constexpr int SBD = 2 * kDT * 128;       // dense stage: 256 x rows + 256 weight rows, k64
   constexpr int SBH = H64 ? (kHR + D) * 128 : (kHR + D) * 64;  // head stage
-  constexpr int NSH = H64 ? 2 : 3;
+  constexpr int NSH = H64 ? 2 : (D == 64 ? 4 : 3);
   constexpr int YPD = kDT + 8, YPH = D + 8;  // staging row strides (elements)
   constexpr int SINK = 2 * SBD > NSH * SBH ? 2 * SBD : NSH * SBH;  // 1 KiB for loads kept nowhere
   constexpr int L1 = kDT * YPD * 2 > kHR * YPH * 2 ? kDT * YPD * 2 : kHR * YPH * 2;
