@@ -79,14 +79,14 @@ __device__ __forceinline__ void* out_base(const ProjParams& p, int kind) {
 // count U k / M near 384, so that one pass almost always takes it.
 // Products: v_mfma_f32_32x32x16_bf16, weight rows as the A operand and x rows
 // as B, 512 threads. Operands reach LDS by raw-buffer LDS-DMA (rows past a
-// tensor's end read zeros), k in steps of 64 in two buffers for the dense
-// tiles (and the d = 32 head tiles); the head tiles of d = 64 and 128 take k
-// in steps of 32 through a ring of four and three buffers, so that the
-// gathered x rows of two or three stages are in flight (one k64 stage in
-// flight left their latency exposed; d = 128 has room for three). The next
-// stage's loads go out between the products of the current one, so each
-// stage costs one barrier. The tile goes back to HBM through LDS in 16-byte
-// pieces.
+// tensor's end read zeros). The dense tiles and the d = 64 head tiles take k
+// in steps of 32 through a ring of four buffers, so that three stages of x
+// rows are in flight (k64 stages in two buffers left one in flight, and the
+// loads' latency exposed); the d = 128 head tiles use a ring of three (four
+// would not fit beside the row list) and the d = 32 head tiles k64 stages in
+// two buffers. The next stage's loads go out between the products of the
+// current one, so each stage costs one barrier. The tile goes back to HBM
+// through LDS in 16-byte pieces.
 // ---------------------------------------------------------------------------
 constexpr int kDT = 256;     // dense tile: tokens and columns
 constexpr int kHR = 512;     // head tile: rows per pass
@@ -311,11 +311,12 @@ __global__ __launch_bounds__(512, 1) void proj_tile_kernel(ProjParams p, int U, 
   constexpr bool H64 = D <= 32;            // head tiles in k64 stages
   constexpr int RBH = D == 128 ? 4 : 2;    // head tile: wavefront rows / 32
   constexpr int CBH = D == 32 ? 1 : 2;     // head tile: wavefront columns / 32
-  constexpr int SBD = 2 * kDT * 128;       // dense stage: 256 x rows + 256 weight rows, k64
+  constexpr int SBD = 2 * kDT * 64;        // dense stage: 256 x rows + 256 weight rows, k32
+  constexpr int NSD = 4;                   // dense stages in the ring
   constexpr int SBH = H64 ? (kHR + D) * 128 : (kHR + D) * 64;  // head stage
   constexpr int NSH = H64 ? 2 : (D == 64 ? 4 : 3);
   constexpr int YPD = kDT + 8, YPH = D + 8;  // staging row strides (elements)
-  constexpr int SINK = 2 * SBD > NSH * SBH ? 2 * SBD : NSH * SBH;  // 1 KiB for loads kept nowhere
+  constexpr int SINK = NSD * SBD > NSH * SBH ? NSD * SBD : NSH * SBH;  // 1 KiB for loads kept nowhere
   constexpr int L1 = kDT * YPD * 2 > kHR * YPH * 2 ? kDT * YPD * 2 : kHR * YPH * 2;
   constexpr int LDSB = SINK + 1024 > L1 ? SINK + 1024 : L1;
   static_assert(LDSB + kUMax * 4 + 64 <= 163840, "LDS");
@@ -347,20 +348,20 @@ __global__ __launch_bounds__(512, 1) void proj_tile_kernel(ProjParams p, int U, 
     const int nv = (int)min<int64_t>(kDT, p.T - t0);
     const int gd = p.G * D, ncols = 2 * gd;
     const int n0 = ct * kDT;
-    // x chunks 4 wave + i (rows 32 wave + 8 i + lane / 8); weight rows
+    // x chunks 2 wave + i (rows 32 wave + 16 i + lane / 4); weight rows
     // n0 + 32 wave .. +31 of [W_K | W_V], all key or all value rows (32
     // divides G*d)
     const int nw = n0 + 32 * wave;
     const __bf16* wb = nw >= ncols ? (const __bf16*)p.w_k
                        : nw < gd   ? (const __bf16*)p.w_k + (int64_t)nw * p.D
                                    : (const __bf16*)p.w_v + (int64_t)(nw - gd) * p.D;
-    TileLoads<4, 4> ld{lds, p.D / 64, SBD, 128, 4 * wave, 4 * wave, kDT * 128, SINK, true,
+    TileLoads<2, 2> ld{lds, p.D / 32, SBD, 64, 2 * wave, 2 * wave, kDT * 64, SINK, true,
                        buf_rsrc(x + t0 * p.D, (uint32_t)nv * rowb), buf_rsrc(wb, nw < ncols ? 32u * rowb : 0u), {}, {}};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 32 * wave + 8 * i + (lane >> 3);
-      ld.xoff[i] = (uint32_t)row * rowb + piece_off8(row, lane);
-      ld.woff[i] = (uint32_t)(8 * i + (lane >> 3)) * rowb + piece_off8(row, lane);
+    for (int i = 0; i < 2; ++i) {
+      const int row = 32 * wave + 16 * i + (lane >> 2);
+      ld.xoff[i] = (uint32_t)row * rowb + piece_off4(row, lane);
+      ld.woff[i] = (uint32_t)(16 * i + (lane >> 2)) * rowb + piece_off4(row, lane);
     }
     auto pf = [&]() __attribute__((always_inline)) {
       lds_dma16_b(rpf, pfoff, lds + SINK);
@@ -368,8 +369,8 @@ __global__ __launch_bounds__(512, 1) void proj_tile_kernel(ProjParams p, int U, 
     };
     const int wm = wave & 1, wn = wave >> 1;  // 128 tokens x 64 columns each
     f32x16 acc[2][4];
-    gemm_k64<kDT, 4, 2, SBD, 8, 2>(lds, p.D / 64, 128 * wm, 64 * wn, 128 * wm < nv && n0 + 64 * wn < ncols, ld, pf,
-                                   acc);
+    gemm_k32<kDT, 4, 2, SBD, NSD, 4, 2>(lds, p.D / 32, 128 * wm, 64 * wn, 128 * wm < nv && n0 + 64 * wn < ncols, ld,
+                                        pf, acc);
     __bf16* ys = (__bf16*)lds;
     stage_out<4, 2, YPD>(ys, 128 * wm, 64 * wn, acc);
     __syncthreads();
