@@ -162,17 +162,21 @@ __global__ __launch_bounds__(256) void out_proj_bf16_kernel(OutProjParams p) {
 // lane); the A tile sits token-major ([t][k]) and is read with 16-byte loads,
 // so each lane holds four consecutive output columns of one token. The
 // hard-slot and shared-head columns of A come straight from o_routed /
-// o_shared; obar is computed once per tile into its own LDS region (its
-// loads issued eight slots at a time, so their latencies overlap). A
+// o_shared; obar is computed once per tile (its loads issued eight slots at
+// a time, so their latencies overlap). At d = 32 it sits in its own LDS
+// region; at d >= 64 each thread keeps its d/16 pieces in registers and
+// writes them into the ring's A region when an obar step is staged (its two
+// A loads then repeat the step's W_O loads), so the 32 or 64 KiB obar would
+// take go to a fifth stage instead. A
 // workgroup of eight wavefronts computes 256 tokens x 256 columns (128
 // tokens x 64 columns each). The tile is large so that the
 // bytes staged per FLOP are few: a CU then keeps the loads of NS - 1 steps in
 // flight against the latency of L2 and the memory-side cache. k goes in
 // steps of 32 through an NS-stage LDS ring filled by LDS-DMA from raw buffer
 // resources (a step moves with scalar resource words; rows past T read
-// zeros); every step issues the same four loads per thread (a dummy A load
+// zeros); every step issues the same four loads per thread (a dummy load
 // on obar steps), so one fixed vmcnt wait makes a stage complete. With four
-// stages the ring advances in the middle of a step and the next step's first
+// or more stages the ring advances in the middle of a step and the next step's first
 // fragments are read while the current step's second MFMA half runs.
 // Workgroup i runs on XCD i % 8; XCD x takes token tiles x, x + 8, ... and
 // for each all column tiles in turn, so a token tile's slot rows come from
@@ -189,7 +193,11 @@ __global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p, 
   constexpr int nob = MODE == 0 ? DH : 0;
   constexpr int nsh = MODE == 0 ? DH : 0;
   constexpr bool weighted = MODE == 2;
-  constexpr int OB = MODE == 0 ? kPT * DH * 2 : 0;  // obar tile (unpadded)
+  // d >= 64: obar stays in registers (DH bytes per thread) and is written
+  // into the A region of its k steps, which frees its LDS for more stages
+  constexpr bool OBR = MODE == 0 && DH >= 64;
+  constexpr int NIT = DH / 16;  // obar items (8-column pieces) per thread
+  constexpr int OB = MODE == 0 && !OBR ? kPT * DH * 2 : 0;  // obar tile (unpadded)
   constexpr int YPAD = kPN + 8;                     // output staging row stride
   static_assert((kPT / 2) * YPAD * 2 <= NS * SB, "half-tile staging fits in the ring");
   constexpr int LDSB = NS * SB + OB;
@@ -243,9 +251,28 @@ __global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p, 
     const int lc = (lane & 31) ^ ((kr & 3) << 2);
     w_off_d[i] = (uint32_t)kr * (uint32_t)p.Dout * 2u + (uint32_t)lc * 16u;
   }
+  // OBR: this thread's obar pieces: token rows tid / (DH/8) + (4096/DH) b,
+  // columns 8 (tid % (DH/8)) .. +7
+  bf16x8 obr[NIT];
   auto dma = [&](const int kt, const int st) __attribute__((always_inline)) {
     const int k0 = min(kt, nk - 1) * kPK;
     char* sbase = lds + st * SB;
+    if (OBR && k0 >= hard && k0 < hard + nob) {
+      // obar columns k0 - hard .. +31 from registers into the A region; the
+      // step's two A loads become a second copy of its W_O loads (same bytes
+      // to the same place), so every step still issues four loads
+      if (((tid % (DH / 8)) >> 2) == (k0 - hard) / kPK) {
+#pragma unroll
+        for (int b = 0; b < NIT; ++b) {
+          const int row = tid / (DH / 8) + (4096 / DH) * b;
+          *(bf16x8*)(sbase + row * 64 + 16 * ((tid & 3) ^ ((row >> 2) & 3))) = obr[b];
+        }
+      }
+      const i32x4 rw = buf_rsrc(wo + (int64_t)k0 * p.Dout + n0, (uint32_t)kPK * (uint32_t)p.Dout * 2u - (uint32_t)n0 * 2u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds_dma16_b(rw, w_off_d[i & 1], sbase + AB + (2 * wave + (i & 1)) * 1024);
+      return;
+    }
     // the step's source; the branch selects scalars, the resource is built once
     const __bf16* abase = orr + m0 * hard;  // obar step: a dummy load of the first slot columns
     uint32_t anum = rows * (uint32_t)hard * 2u;
@@ -301,16 +328,19 @@ __global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p, 
       wlds[j * kPT + t] = p.w[min(m0 + t, tmax) * p.Gk + j];
     }
   }
-  // the first column tile's first stages load while obar is formed
+  // the first column tile's first stages load while obar is formed (unless
+  // one of them is an obar step that takes obar from registers)
+  const bool ob_early = OBR && hard / kPK < NS - 1;
+  if (!ob_early) {
 #pragma unroll
-  for (int kt = 0; kt < NS - 1; ++kt) dma(kt, kt);
+    for (int kt = 0; kt < NS - 1; ++kt) dma(kt, kt);
+  }
   // obar = sum over the G*k slots of w * o, in fp32, rounded to bf16; one
   // 8-column piece of one token per work item, DH/16 items per thread. The
   // loads of up to four items (eight slots each) are issued together before
   // their products, beside the first stages' loads (the MFMA accumulators are
   // not live yet, so the registers are there): with a runtime slot count the
   // compiler would otherwise serialise their latencies.
-  constexpr int NIT = DH / 16;           // items per thread
   constexpr int IB = NIT < 4 ? NIT : 4;  // items per batch
   for (int b0 = 0; nob && b0 < NIT; b0 += IB) {
     int row[IB], e[IB];
@@ -349,15 +379,20 @@ __global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p, 
       bf16x8 r;
 #pragma unroll
       for (int i = 0; i < 8; ++i) r[i] = f2bf(sacc[b][i]);
-      *(bf16x8*)&obar[row[b] * DH + 8 * ((e[b] >> 3) ^ oswz(row[b]))] = r;
+      if constexpr (OBR) obr[b0 + b] = r;
+      else *(bf16x8*)&obar[row[b] * DH + 8 * ((e[b] >> 3) ^ oswz(row[b]))] = r;
     }
+  }
+  if (ob_early) {
+#pragma unroll
+    for (int kt = 0; kt < NS - 1; ++kt) dma(kt, kt);
   }
 
   bf16x8 af[4][2], wf[2][2];  // [tb or nb][kk]
   auto read_frags = [&](const int kt, const int kk) __attribute__((always_inline)) {
     const char* sbase = lds + (kt % NS) * SB;
     const int k0 = kt * kPK;
-    const bool ob = k0 >= hard && k0 < hard + nob;
+    const bool ob = !OBR && k0 >= hard && k0 < hard + nob;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       if (ob) {
@@ -620,7 +655,7 @@ hipError_t launch_out_proj(const OutProjParams& p, bool bf16, hipStream_t s) {
     const int ngrp = (ncol + cpw - 1) / cpw;
     const dim3 grid((unsigned)(8 * ((ntok + 7) / 8) * ngrp));
 #define GQE_OUT_PROJ_GEMM(DH)                                                                                    \
-  if (mode == 0) hipLaunchKernelGGL((out_proj_tile_kernel<DH, 0, DH <= 64 ? 4 : 3>), grid, dim3(512), 0, s, p, cpw); \
+  if (mode == 0) hipLaunchKernelGGL((out_proj_tile_kernel<DH, 0, DH >= 64 ? 5 : 4>), grid, dim3(512), 0, s, p, cpw); \
   else if (mode == 1) hipLaunchKernelGGL((out_proj_tile_kernel<DH, 1, 4>), grid, dim3(512), 0, s, p, cpw);          \
   else hipLaunchKernelGGL((out_proj_tile_kernel<DH, 2, 4>), grid, dim3(512), 0, s, p, cpw);
     switch (p.d) {

@@ -531,7 +531,12 @@ def test_decode_deterministic(d, q_len):
                                              # GEMM kernel: d=32, ragged columns and tokens
                                              (256, 2, 3, 32, 264, "bf16"), (1000, 4, 2, 128, 8, "bf16"),
                                              # 64-k GEMM form (d=64): 16 and 9 hard slots, ragged tiles
-                                             (513, 8, 2, 64, 264, "bf16"), (700, 3, 3, 64, 520, "bf16")])
+                                             (513, 8, 2, 64, 264, "bf16"), (700, 3, 3, 64, 520, "bf16"),
+                                             # obar from registers: its steps among the first stages
+                                             # (d=64, one slot), right after them (two slots at d=64,
+                                             # one at d=128)
+                                             (600, 1, 1, 64, 520, "bf16"), (256, 2, 1, 64, 264, "bf16"),
+                                             (300, 1, 1, 128, 264, "bf16")])
 def test_out_proj_small(T, G, k, d, D, dtype):
     s = synth.make_slot_inputs(T, G, k, d, D, dtype, seed=T)
     g = to_dev(s)
@@ -543,10 +548,12 @@ def test_out_proj_small(T, G, k, d, D, dtype):
 
 
 # Token tiles whose workgroup takes several 256-column tiles (obar formed once
-# for them): the group size is chosen from the tile count, so these sizes
-# give two (d = 64, ragged last column tile and token tile) and four (d = 128,
-# two column groups per token tile).
-@pytest.mark.parametrize("T,G,k,d,D", [(65613, 8, 1, 64, 1000), (66000, 8, 2, 128, 2048)])
+# for them): the group size is chosen from the tile count, and on a 256-CU
+# device these sizes give four column tiles per workgroup (d = 64, ragged last
+# column tile and token tile), eight (d = 128) and four (one slot at d = 64,
+# where every column tile's first stages hold the obar steps).
+@pytest.mark.parametrize("T,G,k,d,D", [(65613, 8, 1, 64, 1000), (66000, 8, 2, 128, 2048),
+                                       (70000, 1, 1, 64, 1024)])
 def test_out_proj_column_groups(T, G, k, d, D):
     s = synth.make_slot_inputs(T, G, k, d, D, "bf16", seed=T)
     g = to_dev(s)
