@@ -430,13 +430,23 @@ __global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p, 
         acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb][kk], af[tb][kk], acc[nb][tb], 0, 0, 0);
   };
 
+  // Output staging sits at the ring's end, so that the stages below it (E of
+  // them) can take the next column tile's first loads before this one's
+  // second-half output stores: each wavefront issues exactly SST of those
+  // (stores count in vmcnt beside the LDS-DMA, in issue order), and the next
+  // tile's first waits count them instead of waiting for them.
+  constexpr int STG = (kPT / 2) * YPAD * 2;
+  constexpr int E = NS >= 4 ? (NS * SB - STG) / SB : 0;
+  constexpr int SST = (kPT / 2) * (kPN / 8) / 512;  // stores of the second half
+  static_assert(E < NS, "staging");
   for (int c = c_lo; c < c_hi; ++c) {
+  const int n_st = c * kPN;  // this column tile's first column
   if (c > c_lo) {
     // the previous column tile is stored (the barrier ending its epilogue):
-    // the ring takes this one's first stages
+    // the ring takes this one's first stages, stages 0 .. E-1 already issued
     n0 = c * kPN;
 #pragma unroll
-    for (int kt = 0; kt < NS - 1; ++kt) dma(kt, kt);
+    for (int kt = E; kt < NS - 1; ++kt) dma(kt, kt);
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -445,9 +455,11 @@ __global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   if constexpr (NS >= 4) {
-    // stage 0 complete (stages 1 .. NS-2 may be in flight); the barrier also
-    // publishes obar
-    __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * (NS - 2)) : "memory");
+    // stage 0 complete (stages 1 .. NS-2 may be in flight, and after a
+    // previous column tile its SST output stores, issued after stage E-1);
+    // the barrier also publishes obar
+    if (c > c_lo && E > 0) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * (NS - 2) + SST) : "memory");
+    else __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * (NS - 2)) : "memory");
     __syncthreads();
     read_frags(0, 0);
     for (int kt = 0; kt < nk; ++kt) {
@@ -456,7 +468,8 @@ __global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p, 
       // stage kt+1 complete, later ones in flight; after the barrier every
       // wavefront has finished its reads of stage kt-1, whose buffer takes
       // stage kt+NS-1
-      __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * (NS - 3)) : "memory");
+      if (kt == 0 && c > c_lo && E > 1) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * (NS - 3) + SST) : "memory");
+      else __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * (NS - 3)) : "memory");
       __syncthreads();
       dma(kt + NS - 1, (kt + NS - 1) % NS);
       if (kt + 1 < nk) read_frags(kt + 1, 0);
@@ -476,13 +489,16 @@ __global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p, 
     }
   }
 
-  // output tile through the ring's LDS (obar stays for the next column
-  // tile), 128 token rows at a time: lane (half, l32) of tile (nb, tb) holds
+  // output tile through the top of the ring's LDS (obar stays for the next
+  // column tile), 128 token rows at a time: lane (half, l32) of tile (nb, tb) holds
   // token wm*128 + tb*32 + l32 and columns wn*64 + nb*32 + 8*(r/4) + 4*half + r%4
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  __bf16* ys = (__bf16*)lds;
-  __bf16* y = (__bf16*)p.y;
+  __bf16* ys = (__bf16*)(lds + NS * SB - STG);
+  // rows past T and columns past Dout go to an offset past the buffer's end,
+  // where the store is dropped: every lane issues every store
+  const uint32_t ynum = rows * (uint32_t)p.Dout * 2u;
+  const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc((__bf16*)p.y + m0 * p.Dout, 0, (int)ynum, 0x00020000);
   for (int hh = 0; hh < 2; ++hh) {
     if (wm == hh) {
 #pragma unroll
@@ -500,11 +516,20 @@ __global__ __launch_bounds__(512, 1) void out_proj_tile_kernel(OutProjParams p, 
         }
     }
     __syncthreads();
-    for (int it = tid; it < (kPT / 2) * (kPN / 8); it += 512) {
+    if (hh == 1 && c + 1 < c_hi) {
+      // the accumulators are staged: the next column tile's first E stages
+      // go out before this half's stores
+      n0 = (c + 1) * kPN;
+#pragma unroll
+      for (int kt = 0; kt < E; ++kt) dma(kt, kt);
+    }
+#pragma unroll 1
+    for (int j = 0; j < SST; ++j) {
+      const int it = tid + 512 * j;
       const int row = it / (kPN / 8), c8 = (it % (kPN / 8)) * 8;
-      const int64_t t = m0 + hh * (kPT / 2) + row;
-      const int n = n0 + c8;
-      if (t < p.T && n < p.Dout) *(bf16x8*)(y + t * p.Dout + n) = *(const bf16x8*)&ys[row * YPAD + c8];
+      const int n = n_st + c8;
+      const uint32_t off = n < p.Dout ? ((uint32_t)(hh * (kPT / 2) + row) * (uint32_t)p.Dout + (uint32_t)n) * 2u : ynum;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, *(const bf16x8*)&ys[row * YPAD + c8]), yr, off, 0, 0);
     }
     __syncthreads();  // ys is rewritten next (the other half, or the next column tile's ring)
   }
