@@ -269,7 +269,9 @@ int gqe_attn_decode_paged(const gqe_dims* dims, int32_t q_len, const void* q,
  *   o_routed [T, G, k, d] dtype; topk_w [T, G, k] fp32; o_shared [T, d] dtype
  *   w_o      [(G*k+2)*d, D] dtype
  *   y        [T, D] dtype out
- * dims->B and dims->S are ignored; T >= 0. */
+ * dims->B and dims->S are ignored; T >= 0. D must be below 2^23 (the tiled
+ * kernel addresses a 256-token output tile through a 32-bit byte range),
+ * else GQE_ERR_UNSUPPORTED. */
 int gqe_out_proj(const gqe_dims* dims, int64_t T, const void* o_routed,
                  const float* topk_w, const void* o_shared, const void* w_o,
                  void* y, void* stream);
@@ -280,7 +282,7 @@ int gqe_out_proj(const gqe_dims* dims, int64_t T, const void* o_routed,
  *           slot is scaled by its own); GQE_SLOTS_HARD unused, may be NULL
  *   o_shared [T, d]: read by GQE_SLOTS_FULL only; NULL allowed otherwise
  *   w_o [(G*k+2)*d, D] for GQE_SLOTS_FULL, else [G*k*d, D]; any other mode
- *   returns GQE_ERR_UNSUPPORTED. */
+ *   returns GQE_ERR_UNSUPPORTED, as does D >= 2^23. */
 int gqe_out_proj_variant(const gqe_dims* dims, int32_t mode, int64_t T,
                          const void* o_routed, const float* slot_w,
                          const void* o_shared, const void* w_o, void* y,

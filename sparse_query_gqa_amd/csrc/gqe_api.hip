@@ -431,6 +431,8 @@ static int out_proj_mode(const gqe_dims* d, int32_t mode, int64_t T, const void*
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return GQE_ERR_ALIGNMENT;
   if ((T + 127) / 128 > (int64_t)UINT32_MAX) return GQE_ERR_UNSUPPORTED;
+  // a 256-token output tile is stored through a raw buffer of 256*D*2 bytes
+  if (d->D >= (1 << 23)) return GQE_ERR_UNSUPPORTED;
   if (T == 0) return GQE_OK;
   OutProjParams op{o_routed, topk_w, o_shared, w_o, y, T, d->G * d->k, d->d, d->D};
   op.nob = full ? d->d : 0;

@@ -170,6 +170,9 @@ def test_out_proj_validation():
     assert call(_dims(D=12)) == gqe.GQE_ERR_UNSUPPORTED
     assert call(_dims(N=8, G=3)) == gqe.GQE_ERR_UNSUPPORTED
     assert call(_dims(), T=0) == gqe.GQE_OK
+    # a 256-token output tile is addressed through 32-bit byte offsets
+    assert call(_dims(D=1 << 23), T=0) == gqe.GQE_ERR_UNSUPPORTED
+    assert call(_dims(D=(1 << 23) - 8), T=0) == gqe.GQE_OK
 
 
 def test_out_proj_variant_validation():
@@ -192,6 +195,7 @@ def test_out_proj_variant_validation():
     assert call(_dims(), gqe.GQE_SLOTS_WEIGHTED, sw=MIS, os_=None) == gqe.GQE_ERR_ALIGNMENT
     assert call(_dims(), gqe.GQE_SLOTS_WEIGHTED, T=0, os_=None) == gqe.GQE_OK
     assert call(_dims(), gqe.GQE_SLOTS_HARD, T=0, sw=None, os_=None) == gqe.GQE_OK
+    assert call(_dims(D=1 << 23), gqe.GQE_SLOTS_HARD, T=0, sw=None, os_=None) == gqe.GQE_ERR_UNSUPPORTED
 
 
 def test_out_proj_bwd_validation():
