@@ -318,13 +318,15 @@ __global__ __launch_bounds__(SPLIT ? 512 : 256, SPLIT ? 1 : 2) void prefill_qp_k
     l_run[q & 1] += ls[q];
   };
   // MFMA / VALU interleave of one step's region: the LDS reads for the next
-  // step spread two per MFMA, and four VALU ops beside each MFMA.
+  // step spread two per MFMA, and up to five VALU ops beside each MFMA (a
+  // step has 34 to 42 of them for its 8 MFMAs; four per MFMA left the rest
+  // after the last MFMA and was about 1% slower at 128k tokens).
   auto interleave = [&](auto n_mfma) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < decltype(n_mfma)::value; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
   };
   using kNo = std::integral_constant<bool, false>;
